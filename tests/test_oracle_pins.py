@@ -1,0 +1,387 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: values the
+pages state (the budget formula), closed forms, special cases that reduce to a
+textbook routine, statistical laws of SimHash, invariants of the estimator and
+an independent brute-force implementation on tiny inputs.  MagicPIG, arXiv
+2410.16179v2 unless noted.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import brute
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# --------------------------------------------------------------------------- bf16
+def test_bf16_rounding_matches_torch_cast():
+    """The oracle's RNE bf16 rounding equals torch's float->bfloat16 cast."""
+    rng = np.random.default_rng(1)
+    vals = [rng.standard_normal(20000), rng.standard_normal(2000) * 1e-30, rng.standard_normal(2000) * 1e30,
+            (rng.integers(0, 2 ** 16, 4000).astype(np.uint32) << 16 | 0x8000).view(np.float32),  # exact ties
+            (rng.integers(0, 2 ** 32, 4000, dtype=np.uint64).astype(np.uint32)).view(np.float32),
+            np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38, -3.3895314e38, 1e-45, -1e-45, np.inf, -np.inf],
+                     np.float32)]
+    x = np.concatenate([np.asarray(v, np.float32) for v in vals])
+    x = x[np.isfinite(x) | np.isinf(x)]
+    ours = oracle.bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------------- key mean
+def test_key_mean_closed_forms():
+    """Section 4.3 'Data pre-processing': k_avg = (1/n) sum k_i."""
+    c = np.full((37, 16), 0.75, np.float32)
+    assert np.array_equal(oracle.key_mean(c), np.full(16, 0.75, np.float32))
+    rng = np.random.default_rng(2)
+    a = rng.standard_normal((50, 16)).astype(np.float32)
+    pm = np.concatenate([a, -a])
+    assert np.array_equal(oracle.key_mean(pm), np.zeros(16, np.float32))
+    r = rng.standard_normal((1000, 32)).astype(np.float32) + 3
+    ref = (r.astype(np.float64).sum(0) / 1000).astype(np.float32)
+    assert np.array_equal(oracle.key_mean(r), ref)
+
+
+# --------------------------------------------------------------------------- SimHash codes
+def test_codes_with_identity_projections_are_coordinate_signs():
+    """Section 2.2: bit = sign(w^T x).  With w_j = e_j the bits are the signs of x."""
+    K, L = 3, 4
+    d = K * L
+    W = np.eye(d, dtype=np.float32)
+    rng = np.random.default_rng(3)
+    keys = rng.standard_normal((40, d)).astype(np.float32)
+    mu = oracle.key_mean(keys)
+    codes = oracle.encode(keys, W, K, L, mu)
+    x = oracle.bf16((keys - mu).astype(np.float32))
+    for r in range(keys.shape[0]):
+        for l in range(L):
+            want = sum(1 << b for b in range(K) if x[r, l * K + b] > 0)
+            assert codes[r, l] == want
+
+
+def test_codes_flip_under_negated_projection():
+    """Negating one projection column flips exactly that bit (z -> -z)."""
+    K, L, d = 4, 5, 16
+    rng = np.random.default_rng(4)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    rows = rng.standard_normal((64, d)).astype(np.float32)
+    base = oracle.encode(rows, W, K, L)
+    j = 7  # table 1, bit 3
+    W2 = W.copy()
+    W2[:, j] *= -1
+    flipped = oracle.encode(rows, W2, K, L)
+    diff = base ^ flipped
+    assert np.all(diff[:, 1] == (1 << 3))
+    assert np.all(np.delete(diff, 1, axis=1) == 0)
+
+
+def test_parallel_vectors_collide_in_every_table():
+    """theta = 0 gives collision probability 1 in every table (Section 2.2)."""
+    K, L, d = 10, 150, 128
+    rng = np.random.default_rng(5)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    v = oracle.bf16(rng.standard_normal(d).astype(np.float32))
+    a = oracle.encode(v, W, K, L)
+    b = oracle.encode((v * 4).astype(np.float32), W, K, L)
+    assert np.array_equal(a, b)
+
+
+def test_margin_is_relative_projection_size():
+    K, L, d = 2, 3, 8
+    rng = np.random.default_rng(6)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    row = rng.standard_normal(d).astype(np.float32)
+    _, mg = oracle.encode(row, W, K, L, with_margin=True)
+    x = oracle.bf16(row).astype(np.float64)
+    Wb = oracle.bf16(W).astype(np.float64)
+    z = x @ Wb
+    rel = np.abs(z) / (np.linalg.norm(x) * np.linalg.norm(Wb, axis=0))
+    assert np.allclose(mg[0], rel.reshape(L, K).min(1), rtol=1e-6)
+
+
+@pytest.mark.parametrize("theta_frac", [0.0, 1 / 6, 1 / 3, 1 / 2, 2 / 3, 5 / 6])
+def test_table_collision_rate_is_one_minus_theta_over_pi_to_the_K(theta_frac):
+    """Section 2.2: one table collides with probability (1 - theta/pi)^K.
+
+    Two vectors at angle theta, 40 000 independent tables of K = 3 Gaussian
+    hyperplanes; the empirical rate must be within 4 sigma of the law.
+    """
+    K, T, d = 3, 40000, 16
+    theta = math.pi * theta_frac
+    x = np.zeros(d, np.float32)
+    y = np.zeros(d, np.float32)
+    x[0] = 1.0
+    y[0], y[1] = math.cos(theta), math.sin(theta)
+    rng = np.random.default_rng(7)
+    W = rng.standard_normal((d, K * T)).astype(np.float32)
+    cx = oracle.encode(x, W, K, T)[0]
+    cy = oracle.encode(y, W, K, T)[0]
+    rate = float(np.mean(cx == cy))
+    p = (1 - theta_frac) ** K
+    assert abs(oracle.table_collision_prob(math.cos(theta), K) - p) < 1e-12
+    sigma = math.sqrt(max(p * (1 - p), 1e-12) / T)
+    # bf16 rounding of y moves theta by < 1e-2 rad / pi at most
+    assert abs(rate - p) <= 4 * sigma + 2e-3, (rate, p)
+
+
+# --------------------------------------------------------------------------- sampling probability
+def test_sampling_probability_special_cases():
+    """Equation 10: L = 2 gives p^2; p = 1 gives 1; p = 0 gives 0."""
+    for p in [0.0, 1e-9, 0.013, 0.5, 0.97, 1.0]:
+        assert oracle.sampling_prob_p(p, 2) == pytest.approx(p * p, rel=1e-14, abs=0)
+    for L in [2, 3, 75, 240]:
+        assert oracle.sampling_prob_p(1.0, L) == pytest.approx(1.0, rel=1e-14)
+        assert oracle.sampling_prob_p(0.0, L) == 0.0
+    # cos = 1 (theta = 0): u = 1 so P = 1 for any K
+    assert oracle.sampling_prob(1.0, 10, 150) == pytest.approx(1.0, rel=1e-14)
+
+
+@pytest.mark.parametrize("K,L", [(8, 75), (9, 120), (10, 150), (10, 240), (3, 6)])
+def test_sampling_probability_equals_equation_10_closed_form(K, L):
+    """Equation 10's closed form 1-(1-p)^L-Lp(1-p)^(L-1), where fp64 evaluates it accurately."""
+    for cosv in np.linspace(-0.2, 0.999, 25):
+        p = (1 - math.acos(cosv) / math.pi) ** K
+        if L * p < 0.05:
+            continue  # closed form cancels catastrophically there
+        closed = 1 - (1 - p) ** L - L * p * (1 - p) ** (L - 1)
+        assert oracle.sampling_prob(cosv, K, L) == pytest.approx(closed, rel=1e-10)
+
+
+def test_sampling_probability_small_p_asymptote():
+    """For p -> 0 the tail is dominated by C(L,2) p^2."""
+    for L in [75, 150, 240]:
+        p = 1e-7
+        assert oracle.sampling_prob_p(p, L) == pytest.approx(L * (L - 1) / 2 * p * p, rel=1e-4)
+
+
+def test_sampling_probability_is_monotone_in_cosine():
+    vals = [oracle.sampling_prob(c, 10, 150) for c in np.linspace(-1, 1, 201)]
+    assert all(b >= a - 1e-13 for a, b in zip(vals, vals[1:]))  # fp64 summation noise near P = 1
+
+
+def test_budget_formula_on_query_orthogonal_keys():
+    """Authors' budget estimate (rebuttal reply to Q1): with per-table collision
+    exactly 0.5^K (keys orthogonal to the query), the sampled fraction equals
+    1-(1-0.5^K)^L-L 0.5^K (1-0.5^K)^(L-1).  Mean over independent projection
+    draws, within 4 standard errors of the stored value."""
+    table = {}
+    with open(os.path.join(GOLDEN, "budget_formula.txt")) as f:
+        for line in f:
+            if line.startswith("#"):
+                continue
+            K, L, v = line.split()
+            table[(int(K), int(L))] = float(v)
+    d, n, draws = 32, 1024, 120
+    for (K, L) in [(8, 75), (4, 10)]:
+        rng = np.random.default_rng(100 + K)
+        q = rng.standard_normal(d)
+        q /= np.linalg.norm(q)
+        fracs = []
+        for _ in range(draws):
+            g = rng.standard_normal((n, d))
+            keys = (g - np.outer(g @ q, q)).astype(np.float32)
+            W = rng.standard_normal((d, K * L)).astype(np.float32)
+            mu = oracle.key_mean(keys)
+            kc = oracle.encode(keys, W, K, L, mu)
+            qc = oracle.encode(q.astype(np.float32), W, K, L)[0]
+            idx, _ = oracle.scan(kc.T, qc)
+            fracs.append(len(idx) / n)
+        fracs = np.array(fracs)
+        sem = fracs.std(ddof=1) / math.sqrt(draws)
+        want = table[(K, L)]
+        assert abs(fracs.mean() - want) <= 4 * sem + 1e-4, (K, L, fracs.mean(), want, sem)
+
+
+def test_inclusion_frequency_matches_sampling_probability_of_centred_angle():
+    """Equation 10 with the angle between q and the centred key (Section 4.3
+    'Data pre-processing'): over random projections each key's inclusion
+    frequency converges to P(cos(q, k - mu)).  The raw-key angle is rejected."""
+    K, L, d, n, draws = 3, 6, 16, 24, 3000
+    rng = np.random.default_rng(11)
+    mu_dir = rng.standard_normal(d)
+    mu_dir /= np.linalg.norm(mu_dir)
+    keys = (rng.standard_normal((n, d)) + 3 * mu_dir).astype(np.float32)
+    q = (rng.standard_normal(d) - 3 * mu_dir).astype(np.float32)
+    q = oracle.bf16(q)
+    mu = oracle.key_mean(keys)
+    c = keys.astype(np.float64) - mu
+    cos_c = c @ q / (np.linalg.norm(c, axis=1) * np.linalg.norm(q))
+    cos_raw = keys.astype(np.float64) @ q / (np.linalg.norm(keys, axis=1) * np.linalg.norm(q))
+    P = np.array([oracle.sampling_prob(v, K, L) for v in cos_c])
+    P_raw = np.array([oracle.sampling_prob(v, K, L) for v in cos_raw])
+    hits = np.zeros(n)
+    for _ in range(draws):
+        W = rng.standard_normal((d, K * L)).astype(np.float32)
+        kc = oracle.encode(keys, W, K, L, mu)
+        qc = oracle.encode(q, W, K, L)[0]
+        idx, _ = oracle.scan(kc.T, qc)
+        hits[idx] += 1
+    freq = hits / draws
+    sig = np.sqrt(P * (1 - P) / draws)
+    assert np.all(np.abs(freq - P) <= 4.5 * sig + 0.01), np.max(np.abs(freq - P) / (sig + 1e-9))
+    # the uncentred angle predicts visibly different rates on this cone
+    assert np.max(np.abs(freq - P_raw)) > 0.1
+
+
+# --------------------------------------------------------------------------- estimator
+def _softmax_attention(q, keys, vals):
+    """Equation 1 (Section 2.1), written with numpy."""
+    s = keys.astype(np.float64) @ q.astype(np.float64) / math.sqrt(q.shape[0])
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    return w @ vals.astype(np.float64), s.max() + math.log(np.exp(s - s.max()).sum())
+
+
+def test_K0_reduces_to_exact_attention():
+    """K = 0: every code is empty, every key collides in all L tables and P = 1,
+    so Equation 11 is the exact softmax attention of Equation 1."""
+    rng = np.random.default_rng(12)
+    d, n, L = 64, 300, 5
+    keys = rng.standard_normal((n, d)).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    W = np.zeros((d, 0), np.float32)
+    mu = oracle.key_mean(keys)
+    kc = oracle.encode(keys, W, 0, L, mu)
+    qc = oracle.encode(q, W, 0, L)[0]
+    idx, forced = oracle.scan(kc.T, qc)
+    assert len(idx) == n
+    out, lse = oracle.attend(q, keys, vals, idx, forced, 0, L, mu)
+    ref, ref_lse = _softmax_attention(q, keys, vals)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    assert abs(lse - ref_lse) < 1e-12
+
+
+def test_all_static_reduces_to_exact_attention():
+    """Forced keys take P = 1 (authors' reply on sink tokens); forcing all keys is Equation 1."""
+    rng = np.random.default_rng(13)
+    d, n, K, L = 32, 200, 8, 10
+    keys = rng.standard_normal((n, d)).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    mu = oracle.key_mean(keys)
+    kc = oracle.encode(keys, W, K, L, mu)
+    qc = oracle.encode(q, W, K, L)[0]
+    idx, forced = oracle.scan(kc.T, qc, n_static_head=n)
+    assert len(idx) == n and forced.all()
+    out, _ = oracle.attend(q, keys, vals, idx, forced, K, L, mu)
+    ref, _ = _softmax_attention(q, keys, vals)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_equal_probabilities_give_softmax_restricted_to_the_set():
+    """If every sampled key has the same P, Equation 9 is plain softmax over S."""
+    rng = np.random.default_rng(14)
+    d, n = 16, 50
+    keys = rng.standard_normal((n, d)).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    idx = np.array([1, 5, 9, 20, 33], np.int32)
+    out, _ = oracle.attend(q, keys, vals, idx, np.ones(5, bool), 8, 10, None)
+    ref, _ = _softmax_attention(q, keys[idx], vals[idx])
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_empty_set_gives_zero_output():
+    d = 8
+    out, lse = oracle.attend(np.ones(d), np.ones((4, d)), np.ones((4, d)), np.zeros(0, np.int32), None, 3, 4)
+    assert np.all(out == 0) and lse == -math.inf
+
+
+def test_estimator_is_invariant_to_key_order():
+    """The estimator is a sum over the set S: permuting keys (with their values
+    and codes) permutes S and leaves the output unchanged."""
+    rng = np.random.default_rng(15)
+    d, n, K, L = 32, 400, 4, 12
+    keys = rng.standard_normal((n, d)).astype(np.float32) + 1
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    mu = oracle.key_mean(keys)
+    kc = oracle.encode(keys, W, K, L, mu)
+    qc = oracle.encode(q, W, K, L)[0]
+    idx, forced = oracle.scan(kc.T, qc)
+    out, lse = oracle.attend(q, keys, vals, idx, forced, K, L, mu)
+    perm = rng.permutation(n)
+    idx2, forced2 = oracle.scan(kc[perm].T, qc)
+    assert sorted(perm[idx2].tolist()) == idx.tolist()
+    out2, lse2 = oracle.attend(q, keys[perm], vals[perm], idx2, forced2, K, L, mu)
+    assert np.max(np.abs(out - out2)) < 1e-12 and abs(lse - lse2) < 1e-12
+
+
+def test_translation_of_keys_leaves_the_estimate_unchanged():
+    """Softmax is translation invariant (Section 4.3 'Data pre-processing'):
+    shifting every key by c shifts every logit by q.c and leaves the centred
+    keys, hence P, unchanged; the output is the same for the same sampled set."""
+    rng = np.random.default_rng(16)
+    d, n, K, L = 32, 300, 4, 12
+    keys = rng.standard_normal((n, d)).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    shift = np.full(d, 0.5, np.float32)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    mu = oracle.key_mean(keys)
+    kc = oracle.encode(keys, W, K, L, mu)
+    qc = oracle.encode(q, W, K, L)[0]
+    idx, forced = oracle.scan(kc.T, qc)
+    out, _ = oracle.attend(q, keys, vals, idx, forced, K, L, mu)
+    keys2 = keys + shift
+    out2, _ = oracle.attend(q, keys2, vals, idx, forced, K, L, oracle.key_mean(keys2))
+    assert np.max(np.abs(out - out2)) < 1e-5
+
+
+@pytest.mark.parametrize("seed,d,n,K,L,nsh,nst", [(20, 4, 12, 2, 3, 0, 0), (21, 8, 16, 3, 4, 0, 0),
+                                                   (22, 8, 16, 1, 4, 1, 2), (23, 4, 9, 3, 2, 0, 0),
+                                                   (24, 8, 16, 0, 3, 0, 0)])
+def test_matches_independent_brute_force(seed, d, n, K, L, nsh, nst):
+    """Tiny inputs: the oracle and an independent pure-Python statement of
+    Section 2.2 + Equations 9-11 agree exactly on sets and to 1e-12 on outputs."""
+    rng = np.random.default_rng(seed)
+    keys = (rng.standard_normal((n, d)) + 0.7).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = (rng.standard_normal(d) - 0.7).astype(np.float32)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    S, bout, blse = brute.decode_head(q.tolist(), keys.tolist(), vals.tolist(), W.tolist(), K, L, nsh, nst)
+    mu = oracle.key_mean(keys)
+    kc = oracle.encode(keys, W, K, L, mu)
+    qc = oracle.encode(q, W, K, L)[0]
+    idx, forced = oracle.scan(kc.T, qc, nsh, nst)
+    assert idx.tolist() == S
+    out, lse = oracle.attend(q, keys, vals, idx, forced, K, L, mu)
+    assert np.max(np.abs(out - np.array(bout))) < 1e-12
+    assert (lse == blse) or abs(lse - blse) < 1e-12
+
+
+def test_decode_composite_matches_per_head_steps():
+    """orc_decode (GQA layer) equals the per-head steps; head h reads KV head h // G."""
+    rng = np.random.default_rng(30)
+    B, Hq, Hkv, d, n, cap, K, L = 2, 4, 2, 16, 90, 96, 3, 6
+    keys = np.zeros((B, Hkv, cap, d), np.float32)
+    keys[:, :, :n] = rng.standard_normal((B, Hkv, n, d)) + 1
+    vals = np.zeros_like(keys)
+    vals[:, :, :n] = rng.standard_normal((B, Hkv, n, d))
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    km, codes = oracle.build_codes(keys.reshape(B * Hkv, cap, d), n, W, K, L)
+    res = oracle.decode(q, keys, vals, codes.reshape(B, Hkv, L, cap), km.reshape(B, Hkv, d), W, K, L, n,
+                        n_static_head=2, want_idx=True)
+    for b in range(B):
+        for h in range(Hq):
+            u = b * Hkv + h // (Hq // Hkv)
+            mu = oracle.key_mean(keys[b, h // 2, :n])
+            assert np.array_equal(mu, km[u])
+            qc = oracle.encode(q[b, h], W, K, L)[0]
+            assert np.array_equal(qc, res["qcodes"][b, h])
+            idx, forced = oracle.scan(codes[u][:, :n], qc, 2, 0)
+            assert res["idx"][b][h].tolist() == idx.tolist()
+            out, lse = oracle.attend(q[b, h], keys[b, h // 2, :n], vals[b, h // 2, :n], idx, forced, K, L, mu)
+            assert np.max(np.abs(res["out"][b, h] - out)) < 1e-6
+            assert abs(res["lse"][b, h] - lse) < 1e-5
