@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Benchmark of the SimHash-sampled decode-attention step on one MI355X.
+
+Workload (default): Llama-3.1-8B-shaped decode at 96K context -- 32 layers x
+(32 query heads, 8 KV heads, d = 128), n = 98304 bf16 keys/values per KV head,
+batch 1, SimHash (K, L) = (10, 150).  Inputs are synthetic (the cone-plus-sink
+generator in ``synth``), resident in HBM before timing starts.
+
+One step = for every layer: append the new token's key/value and codes
+(mp_append), encode the 32 queries (mp_encode_queries), scan + weight +
+split-attend (mp_decode_sample) and merge (mp_decode_merge).  The code store
+is built once beforehand (mp_build_codes), timed separately as the encoder.
+
+Prints one JSON line.  ``value`` = context keys scanned per second over the
+whole step (all layers and KV heads); ``ms_per_step`` = decode-step latency.
+``roofline`` describes the dominant kernel (the scan/attention kernel of
+mp_decode_sample) against the 8 TB/s HBM peak, its duration taken from HIP
+events recorded around every launch in the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LSH-sampled decode attn: context keys/s + latency at 96K, % HBM roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sample_kernel_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "lsh_sampled_sparse_centered_amd", "csrc", "mp_decode.hip")
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha1(f.read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_96k")
+    ap.add_argument("--seed", type=int, default=2024)
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle baseline budget (0 = skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
+    return ap.parse_args()
+
+
+def main() -> int:
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the sampled decode shards by (layer, sequence, KV head) with no "
+              "exchange, so more GPUs are independent copies of this run; --gpus %d is not supported"
+              % max(args.gpus, world), file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import lsh_sampled_sparse_centered_amd as mp
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    nlayers = args.layers or w.layers
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    U, G, d, K, L, n0 = w.batch * w.hkv, w.group, w.d, w.K, w.L, w.n
+    total_steps = args.warmup + args.steps
+    cap = (n0 + total_steps + 8 + 63) // 64 * 64
+    dt = w.torch_dtype
+    log("workload %s: %d layers, B=%d Hq=%d Hkv=%d d=%d n=%d cap=%d (K,L)=(%d,%d)" %
+        (w.name, nlayers, w.batch, w.hq, w.hkv, d, n0, cap, K, L))
+
+    # ------------------------------------------------------------------ inputs + code-store build
+    layers = []
+    build_ms = []
+    ws_build = torch.empty(mp.mp_build_ws_bytes(U, n0), dtype=torch.uint8, device=dev)
+    for l in range(nlayers):
+        Kc = torch.zeros(U, cap, d, dtype=dt, device=dev)
+        Vc = torch.zeros(U, cap, d, dtype=dt, device=dev)
+        for u in range(U):
+            b, h = divmod(u, w.hkv)
+            synth.unit_kv(args.seed, l, b, h, n0, d, dt, dev, out_k=Kc[u, :n0], out_v=Vc[u, :n0])
+        W = synth.projections(args.seed, l, d, K, L, dev)
+        Wp = mp.mp_proj_pack(W, K, L)
+        kmean = torch.empty(U, d, dtype=torch.float32, device=dev)
+        codes = torch.zeros(U, L, cap, dtype=torch.uint16, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mp.mp_build_codes(Kc, n0, Wp, K, L, kmean=kmean, codes=codes, ws=ws_build)
+        e1.record()
+        kn = torch.empty(total_steps, U, d, dtype=dt)
+        vn = torch.empty(total_steps, U, d, dtype=dt)
+        qs = torch.empty(total_steps, w.batch, w.hq, d, dtype=dt)
+        for s in range(total_steps):
+            for u in range(U):
+                b, h = divmod(u, w.hkv)
+                kn[s, u], vn[s, u] = synth.step_kv(args.seed, l, b, h, d, dt, step=s + 1)
+                qs[s, b, h * G:(h + 1) * G] = synth.unit_queries(args.seed, l, b, h, G, d, dt, step=s + 1)
+        kn, vn, qs = kn.to(dev), vn.to(dev), qs.to(dev)
+        layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1)))
+    torch.cuda.synchronize()
+    build_ms = [lay["ev"][0].elapsed_time(lay["ev"][1]) for lay in layers]
+    log("built %d layers; build %.3f ms/layer (median)" % (nlayers, float(np.median(build_ms))))
+
+    ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
+    qc = torch.empty(w.batch, w.hq, L, dtype=torch.uint16, device=dev)
+    outs = [torch.empty(w.batch, w.hq, d, dtype=torch.float32, device=dev) for _ in range(nlayers)]
+    lses = [torch.empty(w.batch, w.hq, dtype=torch.float32, device=dev) for _ in range(nlayers)]
+
+    # ------------------------------------------------------------------ decode steps
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps * nlayers)]
+    n_cur = n0
+    t0 = t1 = 0.0
+    step_ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+    n_timed = []
+    for s in range(total_steps):
+        timed = s >= args.warmup
+        if s == args.warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            step_ev[0].record()
+        for l, lay in enumerate(layers):
+            mp.mp_append(lay["kn"][s], lay["vn"][s], lay["Kc"], lay["Vc"], n_cur, lay["kmean"], lay["Wp"], K, L,
+                         lay["codes"])
+            mp.mp_encode_queries(lay["qs"][s], lay["Wp"], K, L, qcodes=qc)
+            if timed:
+                kev[(s - args.warmup) * nlayers + l][0].record()
+            mp.mp_decode_sample(lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], qc, w.hkv, n_cur + 1,
+                                K, ws)
+            if timed:
+                kev[(s - args.warmup) * nlayers + l][1].record()
+            mp.mp_decode_merge(w.batch, w.hq, w.hkv, n_cur + 1, cap, L, outs[l], ws, lse=lses[l])
+        if timed:
+            n_timed.append(n_cur + 1)
+        n_cur += 1
+    step_ev[1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
+    kern_ms = np.array([a.elapsed_time(b) for a, b in kev])
+    log("step %.3f ms (wall) / %.3f ms (events); sample kernel %.2f us avg over %d launches" %
+        (wall_ms, ev_ms, kern_ms.mean() * 1e3, len(kern_ms)))
+    keys_per_step = float(np.mean(n_timed)) * U * nlayers
+    value = keys_per_step / (wall_ms * 1e-3)
+
+    # ------------------------------------------------------------------ sampled-set sizes (after timing)
+    union_sum = 0
+    head_sum = 0
+    idx = torch.empty(w.batch, w.hq, cap, dtype=torch.int32, device=dev)
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device=dev)
+    s_last = total_steps - 1
+    for lay in layers:
+        mp.mp_decode_attn(lay["qs"][s_last], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], lay["Wp"], w.hkv,
+                          n_cur, K, idx=idx, count=cnt, ws=ws)
+        for b in range(w.batch):
+            for h in range(w.hkv):
+                mask = torch.zeros(n_cur, dtype=torch.bool, device=dev)
+                for g in range(G):
+                    c = int(cnt[b, h * G + g])
+                    mask[idx[b, h * G + g, :c].long()] = True
+                union_sum += int(mask.sum())
+        head_sum += int(cnt.sum())
+    union_per_unit = union_sum / (nlayers * U)
+    head_frac = head_sum / (nlayers * w.batch * w.hq * n_cur)
+    e = 2 if w.dtype == "bf16" else 4
+    n_dec = float(np.mean(n_timed))
+    # algorithmic bytes of one sample launch (one layer): codes of every key once, each distinct sampled
+    # K and V row once, the queries, their codes and the key means
+    bytes_launch = U * (2 * L * n_dec + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
+    achieved = bytes_launch / (kern_ms.mean() * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name:
+            traffic = tr.get("bytes_per_launch")
+    step_bytes = nlayers * bytes_launch
+    log("|S_h|/n = %.4f, union per unit %.0f keys (%.4f of n); %.1f MB algorithmic per launch" %
+        (head_frac, union_per_unit, union_per_unit / n_dec, bytes_launch / 1e6))
+
+    # ------------------------------------------------------------------ encoder (build) figures
+    flops_layer = 2.0 * d * K * L * n0 * U
+    enc_tflops = flops_layer / (float(np.median(build_ms)) * 1e-3) / 1e12
+
+    # ------------------------------------------------------------------ calibration copy (profiling runs only)
+    if args.calib_copy_mib:
+        a = torch.empty(args.calib_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1.0)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copy of %d MiB done" % args.calib_copy_mib)
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, args.seed, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "keys/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
+        "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+                   "head_dim": d, "context": n0, "K": K, "L": L, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "sample_kernel (mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
+                     "algorithmic_bytes_per_launch": bytes_launch},
+        "step": {"latency_ms": wall_ms, "latency_ms_events": ev_ms, "bytes_per_step": step_bytes,
+                 "frac_hbm_step": step_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                 "sampled_frac_per_head": head_frac, "union_keys_per_unit": union_per_unit},
+        "encoder": {"build_ms_per_layer": float(np.median(build_ms)), "tflops": enc_tflops,
+                    "frac_mfma_bf16": enc_tflops / BF16_MFMA_PEAK_TFLOPS,
+                    "note": "build = key mean + projection GEMM + sign pack, per layer"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+def cpu_baseline(w, seed: int, budget_s: float):
+    """The CPU oracle timed on the host on a bounded sample of the same workload.
+
+    Sample: KV heads 0..3 of layer 0 (batch 0) at the full context, with their
+    query heads; keys/values regenerated on the host from the same recipe.
+    The oracle builds its own codes for them (untimed), then its decode over
+    those heads is repeated with successive queries until the budget is spent.
+    """
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+
+    nunits = min(4, w.hkv)
+    G, d, n = w.group, w.d, w.n
+    cap = (n + 63) // 64 * 64
+    keys = np.zeros((1, nunits, cap, d), np.float32)
+    vals = np.zeros_like(keys)
+    for h in range(nunits):
+        k, v = synth.unit_kv(seed, 0, 0, h, n, d, w.torch_dtype, "cpu")
+        keys[0, h, :n] = k.float().numpy()
+        vals[0, h, :n] = v.float().numpy()
+    W = synth.projections(seed, 0, d, w.K, w.L, "cpu").numpy()
+    t = time.perf_counter()
+    km, codes = oracle.build_codes(keys[0], n, W, w.K, w.L)
+    build_s = time.perf_counter() - t
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    reps = 0
+    t = time.perf_counter()
+    while True:
+        q = np.zeros((1, nunits * G, d), np.float32)
+        for h in range(nunits):
+            q[0, h * G:(h + 1) * G] = synth.unit_queries(seed, 0, 0, h, G, d, w.torch_dtype, "cpu",
+                                                         step=reps + 1).float().numpy()
+        oracle.decode(q, keys, vals, codes.reshape(1, nunits, w.L, cap), km.reshape(1, nunits, d), W, w.K, w.L, n)
+        reps += 1
+        el = time.perf_counter() - t
+        if el >= budget_s:
+            break
+    keys_done = reps * nunits * n
+    return {"value": keys_done / el, "unit": "keys/s", "cores": min(threads, nunits * G), "kind": "oracle",
+            "sample": "%d decode passes over %d KV heads x %d keys (%d query heads each), layer 0; "
+                      "oracle build of their codes %.1fs untimed" % (reps, nunits, n, G, build_s),
+            "cpu_model": platform.processor() or platform.machine(), "host_threads": threads,
+            "seconds": el}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,191 @@
+/*
+ * magicpig.h -- C ABI of the MI355X (gfx950) SimHash-sampled decode-attention
+ * library (libmagicpig.so).
+ *
+ * The method is MagicPIG ("MagicPIG: LSH Sampling for Efficient LLM
+ * Generation", arXiv 2410.16179v2).  One decode step of one attention layer
+ * estimates o = softmax(q K^T / sqrt(d)) V (Section 2.1, Equation 1) from a
+ * sampled subset S of the keys:
+ *
+ *   codes   every key k_i is centred by the key mean mu (Section 4.3 "Data
+ *           pre-processing") and hashed by SimHash into L tables of K sign
+ *           bits each (Section 2.2; Section 4.3 "Hash function selection");
+ *   S       key i is sampled for a query when their codes agree in at least
+ *           two of the L tables (Section 4.3, Equation 10);
+ *   weight  each sampled key is weighted by exp(q.k_i/sqrt(d)) / P_i with
+ *           P_i = 1 - (1-p)^L - L p (1-p)^(L-1), p = (1 - theta_i/pi)^K
+ *           (Equations 10 and 11);
+ *   output  the self-normalised estimate sum_S w_i v_i / sum_S w_i
+ *           (Equation 9; Algorithm 1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every pointer except the host pointer of mp_proj_pack's documentation
+ *    example is a DEVICE pointer on the current HIP device.  The caller
+ *    allocates and owns every buffer; the library never allocates, frees or
+ *    keeps pointers after a call returns, and keeps no global state, so calls
+ *    on different streams are independent when their workspaces differ.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it; nothing synchronises the host.  Results are valid
+ *    once the stream has reached the point after the call.
+ *  - Arguments are validated before anything is enqueued: a call that
+ *    returns an error has written nothing.  No call aborts or prints.
+ *  - Shapes: d (head dimension) must be 128.  0 <= K <= 16 bits per table,
+ *    2 <= L <= 512 tables, K*L <= 4096.  Query heads per KV head
+ *    G = Hq / Hkv must divide exactly and be at most 8.  Cache capacities
+ *    `cap` must be multiples of 8 (16-byte code rows).
+ *  - Element types: MP_BF16 (bfloat16) or MP_F32 (float32) for keys, values
+ *    and queries; codes are uint16; means, outputs and lse are float32.
+ *  - Layouts (row-major, innermost last):
+ *      K, V cache    [U][cap][d]     U = B * Hkv units (batch x KV head)
+ *      codes         [U][L][cap]     table-major: code of table l of key i
+ *                                    at codes[u][l][i]; bit b of table l is
+ *                                    projection column l*K + b (LSB first)
+ *      kmean         [U][d]          float32 key mean per unit
+ *      q             [B][Hq][d]      query head h reads KV head h / G
+ *      qcodes        [B][Hq][L]
+ *      out           [B][Hq][d]      float32
+ *      lse, count    [B][Hq]
+ *      idx           [B][Hq][cap]    int32, ascending sampled key indices
+ */
+#ifndef MAGICPIG_H
+#define MAGICPIG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every int-returning entry point. */
+#define MP_OK 0
+#define MP_ERR_ARG (-1)         /* null or inconsistent argument            */
+#define MP_ERR_UNSUPPORTED (-2) /* shape outside the supported set          */
+#define MP_ERR_CAPACITY (-3)    /* n >= cap on append, or n > cap           */
+#define MP_ERR_WORKSPACE (-4)   /* workspace missing or smaller than needed */
+#define MP_ERR_HIP (-5)         /* a HIP launch failed                      */
+
+/* Element types of keys, values and queries. */
+#define MP_BF16 0
+#define MP_F32 1
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *mp_strerror(int status);
+
+/* Library ABI version (incremented on incompatible changes). */
+int mp_version(void);
+
+/*
+ * Projection packing.  W is Algorithm 1's random projector matrix
+ * W in R^{d x (K*L)} (Section 4.3 "Hash function selection"): float32,
+ * row-major [d][K*L], column l*K + b being hyperplane b of table l.  It is
+ * rounded to bf16 (round to nearest even) and rearranged into the operand
+ * order of the encoder's matrix-core tiles.  Wp receives mp_proj_bytes(d,K,L)
+ * bytes.  Both pointers are device pointers.  One packed W serves every
+ * unit of a layer (the paper shares projectors across heads, Section 4.4).
+ * Errors: MP_ERR_ARG (null pointers), MP_ERR_UNSUPPORTED (d, K, L limits).
+ */
+size_t mp_proj_bytes(int d, int K, int L);
+int mp_proj_pack(const float *W, int d, int K, int L, void *Wp, void *stream);
+
+/*
+ * Code-store build (Section 4.3 "Data pre-processing" and "Hash function
+ * selection"; the hash-table construction that the paper overlaps with
+ * prefill, authors' reply to Q2 on page 3).  For each unit u < U:
+ *   kmean[u] = fp32( (1/n) sum_{i<n} K[u][i] )  (fp64 accumulation),
+ *   x_i      = bf16( fp32(K[u][i]) - kmean[u] ),
+ *   bit_j    = ( x_i . bf16(W[:, j]) > 0 ),  code_l = sum_b bit_{l*K+b} << b,
+ * written to codes[u][l][i] for i < n (columns >= n are not touched).  The
+ * mean is frozen: later appends reuse it.
+ *   Kc     [U][cap][d] keys (kv_dtype), first n rows read
+ *   Wp     packed projections from mp_proj_pack
+ *   kmean  out [U][d];  codes out [U][L][cap]
+ *   ws     device workspace of at least mp_build_ws_bytes(U, n, d) bytes
+ * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_CAPACITY (n > cap or n < 1),
+ * MP_ERR_WORKSPACE, MP_ERR_HIP.
+ */
+size_t mp_build_ws_bytes(int64_t U, int64_t n, int d);
+int mp_build_codes(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, int d, const void *Wp, int K,
+                   int L, float *kmean, uint16_t *codes, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Append one decoded token per unit (Algorithm 1 keeps encoding new keys with
+ * the same projections; the mean stays frozen at its build value).
+ * Writes Kc[u][n] = k_new[u], Vc[u][n] = v_new[u] and the L codes of
+ * bf16(k_new[u] - kmean[u]) at codes[u][l][n].  The caller then uses n + 1.
+ *   k_new, v_new  [U][d] (kv_dtype);  Kc, Vc [U][cap][d];  codes [U][L][cap]
+ * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_CAPACITY (n >= cap),
+ * MP_ERR_HIP.
+ */
+int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_dtype, int64_t U, int64_t n,
+              int64_t cap, int d, const float *kmean, const void *Wp, int K, int L, uint16_t *codes, void *stream);
+
+/*
+ * Query encoding (Algorithm 1, "Compute hash code for new query"):
+ * qcodes[r][l] = code of table l of y_r = bf16(q[r]); queries are NOT
+ * centred (centring shifts keys only; softmax is translation invariant).
+ *   q       [nq][d] (q_dtype);  qcodes out [nq][L]
+ * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_HIP.
+ */
+int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void *Wp, int K, int L, uint16_t *qcodes,
+                      void *stream);
+
+/*
+ * Sampled decode attention of one layer (Algorithm 1 for every query head;
+ * Equations 9-11).  For query head h of batch b (KV unit u = b*Hkv + h/G):
+ *   S_h   = { i < n : #{l : codes[u][l][i] == qcode_h[l]} >= 2 }
+ *           plus the forced ranges i < n_static_head and
+ *           i >= n - n_static_tail (probability 1; Algorithm 1's static
+ *           cache K_T, V_T and the authors' reply on sink tokens),
+ *   cos_i = q_h.(K_i - kmean_u) / (|q_h| |K_i - kmean_u|),
+ *   lnP_i = ln(1 - (1-p)^L - L p (1-p)^(L-1)), p = (1 - acos(cos_i)/pi)^K,
+ *   s_i   = q_h.K_i / sqrt(d) - lnP_i,
+ *   out   = sum_{S_h} e^{s_i} V_i / sum_{S_h} e^{s_i},  lse = ln sum e^{s_i}.
+ * All G query heads of a KV head share one pass over its codes; each head
+ * keeps its own set and probabilities.  An empty set gives out = 0,
+ * lse = -inf, count = 0.
+ *   q          [B][Hq][d] (kv_dtype)
+ *   Kc, Vc     [B*Hkv][cap][d];  codes [B*Hkv][L][cap];  kmean [B*Hkv][d]
+ *   Wp         packed projections (read only when qcodes_in is NULL)
+ *   qcodes_in  nullable [B][Hq][L]: use these query codes instead of
+ *              encoding q
+ *   qcodes_out nullable [B][Hq][L]: receives the codes when q is encoded here
+ *   out        [B][Hq][d] float32;  lse nullable [B][Hq] float32
+ *   idx        nullable [B][Hq][cap] int32: the sampled indices, ascending
+ *   count      nullable [B][Hq] int32: |S_h|
+ *   ws         device workspace of mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)
+ *              bytes (the same size for every n <= cap)
+ * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_CAPACITY (n > cap or n < 1),
+ * MP_ERR_WORKSPACE, MP_ERR_HIP.
+ */
+size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L);
+int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   int L, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
+                   uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * The two stages of mp_decode_attn, callable separately (one kernel each),
+ * for callers that schedule or time them apart.  mp_decode_sample runs the
+ * collision scan, the weighting and the split attention (Equations 9-11
+ * over key chunks) and leaves per-chunk partial results in ws;
+ * mp_decode_merge combines them by log-sum-exp (the recursive-attention
+ * merge of Section 4.4 "On-device cache") into out / lse / count / idx.
+ * Both must see the same arguments and the same ws; want_idx must be
+ * non-zero in mp_decode_sample when mp_decode_merge receives idx.
+ * qcodes is required here ([B][Hq][L]).
+ */
+int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
+                     size_t ws_bytes, void *stream);
+int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
+                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAGICPIG_H */

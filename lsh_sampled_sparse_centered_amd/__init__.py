@@ -1,0 +1,255 @@
+"""Python binding of libmagicpig.so, the gfx950 SimHash-sampled decode-attention library.
+
+Every function here has the name of the C entry point it calls and only
+marshals arguments: it checks tensor devices, dtypes, shapes and contiguity,
+passes raw device pointers and the current HIP stream, and raises
+:class:`MPError` on a non-zero status.  All computation runs in the HIP
+kernels.  torch is used for device memory and streams only.
+
+The method is MagicPIG (arXiv 2410.16179v2); see ``include/magicpig.h`` for
+what each call computes, with citations.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmagicpig.so")
+
+MP_BF16 = 0
+MP_F32 = 1
+D = 128
+
+_c_int, _c_i64, _c_sz, _vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+_SIGS = {
+    "mp_strerror": ([_c_int], ctypes.c_char_p),
+    "mp_version": ([], _c_int),
+    "mp_proj_bytes": ([_c_int, _c_int, _c_int], _c_sz),
+    "mp_proj_pack": ([_vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "mp_build_ws_bytes": ([_c_i64, _c_i64, _c_int], _c_sz),
+    "mp_build_codes": ([_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _c_sz, _vp],
+                       _c_int),
+    "mp_append": ([_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _c_int, _c_int, _vp, _vp],
+                  _c_int),
+    "mp_encode_queries": ([_vp, _c_int, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp], _c_int),
+    "mp_decode_ws_bytes": ([_c_int, _c_int, _c_int, _c_i64, _c_int, _c_int], _c_sz),
+    "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
+                        _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
+    "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
+                          _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
+    "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+                        _c_int),
+}
+
+_lib = None
+
+
+class MPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, strerror(status), status))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded native library.  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmagicpig.so is not built (expected at %s); run "
+                               "`python -m lsh_sampled_sparse_centered_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGS)
+
+
+def strerror(status: int) -> str:
+    return lib().mp_strerror(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MPError(fn, status)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MP_BF16
+    if t.dtype == torch.float32:
+        return MP_F32
+    raise ValueError("keys/values/queries must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, shape, name: str):
+    if t.dtype != dtype:
+        raise ValueError("%s: expected %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+# ----------------------------------------------------------------------------- projections
+def mp_proj_bytes(d: int, K: int, L: int) -> int:
+    return lib().mp_proj_bytes(d, K, L)
+
+
+def mp_proj_pack(W: torch.Tensor, K: int, L: int, Wp: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Pack W[d][K*L] fp32 into the encoder's bf16 tile order; returns the uint8 buffer."""
+    d = W.shape[0]
+    _need(W, torch.float32, (d, K * L), "W")
+    nb = mp_proj_bytes(d, K, L)
+    if Wp is None:
+        Wp = torch.empty(max(nb, 16), dtype=torch.uint8, device=W.device)
+    _check("mp_proj_pack", lib().mp_proj_pack(_p(W), d, K, L, _p(Wp), _stream(stream)))
+    return Wp
+
+
+# ----------------------------------------------------------------------------- build / append
+def mp_build_ws_bytes(U: int, n: int, d: int = D) -> int:
+    return lib().mp_build_ws_bytes(U, n, d)
+
+
+def mp_build_codes(Kc: torch.Tensor, n: int, Wp: torch.Tensor, K: int, L: int, kmean: Optional[torch.Tensor] = None,
+                   codes: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Key means and the table-major code store of ``Kc`` ([U][cap][d]) for its first n rows."""
+    U, cap, d = Kc.shape
+    if kmean is None:
+        kmean = torch.empty(U, d, dtype=torch.float32, device=Kc.device)
+    if codes is None:
+        codes = torch.zeros(U, L, cap, dtype=torch.uint16, device=Kc.device)
+    _need(kmean, torch.float32, (U, d), "kmean")
+    _need(codes, torch.uint16, (U, L, cap), "codes")
+    nb = mp_build_ws_bytes(U, max(n, 1), d)
+    if ws is None:
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=Kc.device)
+    _check("mp_build_codes", lib().mp_build_codes(_p(Kc), _kv_dtype(Kc), U, n, cap, d, _p(Wp), K, L, _p(kmean),
+                                                  _p(codes), _p(ws), ws.numel() * ws.element_size(),
+                                                  _stream(stream)))
+    return kmean, codes
+
+
+def mp_append(k_new: torch.Tensor, v_new: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, n: int,
+              kmean: torch.Tensor, Wp: torch.Tensor, K: int, L: int, codes: torch.Tensor, stream=None) -> None:
+    """Write row n of the caches and its codes (frozen mean)."""
+    U, cap, d = Kc.shape
+    _need(k_new, Kc.dtype, (U, d), "k_new")
+    _need(v_new, Kc.dtype, (U, d), "v_new")
+    _need(Vc, Kc.dtype, (U, cap, d), "Vc")
+    _need(codes, torch.uint16, (U, L, cap), "codes")
+    _check("mp_append", lib().mp_append(_p(k_new), _p(v_new), _p(Kc), _p(Vc), _kv_dtype(Kc), U, n, cap, d, _p(kmean),
+                                        _p(Wp), K, L, _p(codes), _stream(stream)))
+
+
+def mp_encode_queries(q: torch.Tensor, Wp: torch.Tensor, K: int, L: int, qcodes: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """SimHash codes of queries ``q`` ([..., d], uncentred); returns uint16 [..., L]."""
+    d = q.shape[-1]
+    nq = q.numel() // d
+    if qcodes is None:
+        qcodes = torch.empty(*q.shape[:-1], L, dtype=torch.uint16, device=q.device)
+    _check("mp_encode_queries", lib().mp_encode_queries(_p(q), _kv_dtype(q), nq, d, _p(Wp), K, L, _p(qcodes),
+                                                        _stream(stream)))
+    return qcodes
+
+
+# ----------------------------------------------------------------------------- decode
+def mp_decode_ws_bytes(B: int, Hq: int, Hkv: int, cap: int, L: int, d: int = D) -> int:
+    return lib().mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)
+
+
+def decode_workspace(B: int, Hq: int, Hkv: int, cap: int, L: int, device) -> torch.Tensor:
+    nb = mp_decode_ws_bytes(B, Hq, Hkv, cap, L)
+    if nb == 0:
+        raise MPError("mp_decode_ws_bytes", -2)
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def _decode_shapes(q, Kc, Vc, codes, kmean, Hkv):
+    B, Hq, d = q.shape
+    U, cap, _ = Kc.shape
+    if U != B * Hkv:
+        raise ValueError("Kc has %d units, expected B*Hkv = %d" % (U, B * Hkv))
+    _need(Vc, Kc.dtype, Kc.shape, "Vc")
+    if q.dtype != Kc.dtype:
+        raise ValueError("q and the caches must share a dtype")
+    L = codes.shape[1]
+    _need(codes, torch.uint16, (U, L, cap), "codes")
+    _need(kmean, torch.float32, (U, d), "kmean")
+    return B, Hq, d, U, cap, L
+
+
+def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor,
+                   Wp: Optional[torch.Tensor], Hkv: int, n: int, K: int, n_static_head: int = 0,
+                   n_static_tail: int = 0, qcodes_in: Optional[torch.Tensor] = None,
+                   qcodes_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                   count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """Sampled decode attention of one layer.  q [B][Hq][d]; caches [B*Hkv][cap][d]."""
+    B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (B, Hq, d), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq), "lse")
+    if count is not None:
+        _need(count, torch.int32, (B, Hq), "count")
+    if idx is not None:
+        _need(idx, torch.int32, (B, Hq, cap), "idx")
+    for name, t in (("qcodes_in", qcodes_in), ("qcodes_out", qcodes_out)):
+        if t is not None:
+            _need(t, torch.uint16, (B, Hq, L), name)
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, cap, L, dev)
+    st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp), B, Hq, Hkv, n, cap,
+                              d, K, L, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
+                              _p(idx), _p(count), _p(ws), ws.numel(), _stream(stream))
+    _check("mp_decode_attn", st)
+    return out
+
+
+def mp_decode_sample(q, Kc, Vc, codes, kmean, qcodes, Hkv: int, n: int, K: int, ws: torch.Tensor,
+                     n_static_head: int = 0, n_static_tail: int = 0, want_idx: bool = False, stream=None) -> None:
+    """Scan + weighting + split attention into the workspace (first stage of mp_decode_attn)."""
+    B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
+    _need(qcodes, torch.uint16, (B, Hq, L), "qcodes")
+    st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(qcodes), B, Hq, Hkv,
+                                n, cap, d, K, L, n_static_head, n_static_tail, int(bool(want_idx)), _p(ws), ws.numel(),
+                                _stream(stream))
+    _check("mp_decode_sample", st)
+
+
+def mp_decode_merge(B: int, Hq: int, Hkv: int, n: int, cap: int, L: int, out: torch.Tensor, ws: torch.Tensor,
+                    lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                    count: Optional[torch.Tensor] = None, d: int = D, stream=None) -> None:
+    """Log-sum-exp merge of the sampled partials (second stage of mp_decode_attn)."""
+    _need(out, torch.float32, (B, Hq, d), "out")
+    st = lib().mp_decode_merge(B, Hq, Hkv, n, cap, d, L, _p(out), _p(lse), _p(idx), _p(count), _p(ws), ws.numel(),
+                               _stream(stream))
+    _check("mp_decode_merge", st)

@@ -1,0 +1,186 @@
+// C ABI of libmagicpig.so: argument validation, workspace carving and kernel
+// launches.  Every check runs before the first enqueue, so a call that
+// returns an error has written nothing.
+#include "magicpig.h"
+#include "mp_internal.h"
+
+using namespace mp;
+
+namespace {
+
+hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+int check_shape(int d, int K, int L) {
+  if (d != D) return MP_ERR_UNSUPPORTED;
+  if (K < 0 || K > 16 || L < 2 || L > MAX_L || K * L > 4096) return MP_ERR_UNSUPPORTED;
+  return MP_OK;
+}
+
+int check_dtype(int t) { return (t == MP_BF16 || t == MP_F32) ? MP_OK : MP_ERR_ARG; }
+
+int check_heads(int B, int Hq, int Hkv) {
+  if (B < 1 || Hq < 1 || Hkv < 1) return MP_ERR_ARG;
+  if (Hq % Hkv != 0) return MP_ERR_ARG;
+  if (Hq / Hkv > MAX_G) return MP_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv > 65535) return MP_ERR_UNSUPPORTED;  // grid.y
+  return MP_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MP_OK : MP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *mp_strerror(int status) {
+  switch (status) {
+    case MP_OK: return "success";
+    case MP_ERR_ARG: return "invalid argument (null pointer or inconsistent sizes)";
+    case MP_ERR_UNSUPPORTED: return "unsupported shape (need d = 128, 0 <= K <= 16, 2 <= L <= 512, K*L <= 4096, "
+                                    "Hq/Hkv <= 8)";
+    case MP_ERR_CAPACITY: return "capacity exceeded (n outside [1, cap], or n >= cap on append)";
+    case MP_ERR_WORKSPACE: return "workspace missing or too small";
+    case MP_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int mp_version(void) { return 1; }
+
+size_t mp_proj_bytes(int d, int K, int L) {
+  if (check_shape(d, K, L) != MP_OK) return 0;
+  return (size_t)enc_ntiles(K, L) * KSTEPS * 64 * 16;
+}
+
+int mp_proj_pack(const float *W, int d, int K, int L, void *Wp, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if (K > 0 && (!W || !Wp)) return MP_ERR_ARG;
+  return hip_status(launch_proj_pack(W, K, L, Wp, as_stream(stream)));
+}
+
+size_t mp_build_ws_bytes(int64_t U, int64_t n, int d) {
+  if (U < 1 || n < 1 || d != D) return 0;
+  return (size_t)U * kmean_parts(n) * D * sizeof(double);
+}
+
+int mp_build_codes(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, int d, const void *Wp, int K,
+                   int L, float *kmean, uint16_t *codes, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if (!Kc || !kmean || !codes || (K > 0 && !Wp) || U < 1 || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (U > 65535) return MP_ERR_UNSUPPORTED;
+  if (n < 1 || n > cap) return MP_ERR_CAPACITY;
+  if (!ws || ws_bytes < mp_build_ws_bytes(U, n, d)) return MP_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = launch_kmean(Kc, kv_dtype, U, n, cap, (double *)ws, kmean_parts(n), kmean, s);
+  if (e != hipSuccess) return MP_ERR_HIP;
+  e = launch_encode(kv_dtype, Kc, cap * D, D, kmean, D, 0, U, n, Wp, K, L, codes, (int64_t)L * cap, 1, cap,
+                    nullptr, 0, 0, nullptr, nullptr, s);
+  return hip_status(e);
+}
+
+int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_dtype, int64_t U, int64_t n,
+              int64_t cap, int d, const float *kmean, const void *Wp, int K, int L, uint16_t *codes, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if (!k_new || !v_new || !Kc || !Vc || !kmean || !codes || (K > 0 && !Wp) || U < 1 || cap < 1 || cap % 8 ||
+      n < 0)
+    return MP_ERR_ARG;
+  if (n >= cap) return MP_ERR_CAPACITY;
+  const size_t es = kv_dtype == MP_BF16 ? 2 : 4;
+  // one "unit" of U rows; row u has its own mean, cache row and code column
+  hipError_t e = launch_encode(kv_dtype, k_new, 0, D, kmean, 0, D, 1, U, Wp, K, L, codes + n, 0, (int64_t)L * cap,
+                               cap, (char *)Kc + (size_t)n * D * es, 0, cap * D, v_new,
+                               (char *)Vc + (size_t)n * D * es, as_stream(stream));
+  return hip_status(e);
+}
+
+int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void *Wp, int K, int L, uint16_t *qcodes,
+                      void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if ((st = check_dtype(q_dtype))) return st;
+  if (!q || !qcodes || (K > 0 && !Wp) || nq < 1) return MP_ERR_ARG;
+  hipError_t e = launch_encode(q_dtype, q, 0, D, nullptr, 0, 0, 1, nq, Wp, K, L, qcodes, 0, L, 1, nullptr, 0, 0,
+                               nullptr, nullptr, as_stream(stream));
+  return hip_status(e);
+}
+
+size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L) {
+  if (check_heads(B, Hq, Hkv) || d != D || cap < 1 || L < 2 || L > MAX_L) return 0;
+  return decode_ws_layout(nullptr, B, Hq, Hkv, cap, L).bytes;
+}
+
+static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                        const float *kmean, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L,
+                        int64_t nsh, int64_t nst, void *ws, size_t ws_bytes) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if ((st = check_heads(B, Hq, Hkv))) return st;
+  if (!q || !Kc || !Vc || !codes || !kmean || cap < 1 || cap % 8 || nsh < 0 || nst < 0) return MP_ERR_ARG;
+  if (n < 0 || n > cap) return MP_ERR_CAPACITY;
+  if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
+  return MP_OK;
+}
+
+int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
+                     size_t ws_bytes, void *stream) {
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, n_static_head,
+                        n_static_tail, ws, ws_bytes);
+  if (st) return st;
+  if (!qcodes) return MP_ERR_ARG;
+  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
+  if (geo.nchunks == 0) return MP_OK;
+  return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L,
+                                  n_static_head, n_static_tail, geo, w, want_idx != 0, as_stream(stream)));
+}
+
+int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
+                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_heads(B, Hq, Hkv);
+  if (st) return st;
+  if (d != D || L < 2 || L > MAX_L) return MP_ERR_UNSUPPORTED;
+  if (!out || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (n < 0 || n > cap) return MP_ERR_CAPACITY;
+  if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
+  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
+  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, as_stream(stream)));
+}
+
+int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   int L, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
+                   uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                   size_t ws_bytes, void *stream) {
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, n_static_head,
+                        n_static_tail, ws, ws_bytes);
+  if (st) return st;
+  if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
+  const uint16_t *qc = qcodes_in;
+  if (!qc) {
+    uint16_t *dst = qcodes_out ? qcodes_out : w.qcodes;
+    hipError_t e = launch_encode(kv_dtype, q, 0, D, nullptr, 0, 0, 1, (int64_t)B * Hq, Wp, K, L, dst, 0, L, 1,
+                                 nullptr, 0, 0, nullptr, nullptr, s);
+    if (e != hipSuccess) return MP_ERR_HIP;
+    qc = dst;
+  }
+  if (geo.nchunks > 0) {
+    hipError_t e = launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, n_static_head,
+                                 n_static_tail, geo, w, idx != nullptr, s);
+    if (e != hipSuccess) return MP_ERR_HIP;
+  }
+  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
+}
+
+}  // extern "C"

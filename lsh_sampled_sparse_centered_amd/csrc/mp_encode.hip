@@ -1,0 +1,320 @@
+// SimHash encoder of MagicPIG (arXiv 2410.16179v2): key mean, projection
+// packing and the bf16 matrix-core projection + sign packing that produces
+// the table-major code store (Section 2.2 "Locality sensitive hashing";
+// Section 4.3 "Hash function selection" and "Data pre-processing").
+#include <algorithm>
+
+#include "mp_internal.h"
+
+namespace mp {
+
+// ---------------------------------------------------------------------------
+// Projection packing: W[d][K*L] fp32 -> bf16 tiles in matrix-core A-operand
+// order.  Element e of lane l in k-step s of tile t is
+//   W[16 s + 8 (l / 32) + e][32 t + enc_row_col(l % 32)]   (0 past K*L).
+// One thread per (tile, k-step, lane) writes 16 bytes.
+__global__ void proj_pack_kernel(const float *__restrict__ W, int ncol, int ntiles, uint4 *__restrict__ Wp) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)ntiles * KSTEPS * 64) return;
+  const int lane = (int)(gid & 63);
+  const int s = (int)((gid >> 6) % KSTEPS);
+  const int t = (int)(gid / (64 * KSTEPS));
+  const int col = 32 * t + enc_row_col(lane & 31);
+  const int d0 = 16 * s + 8 * (lane >> 5);
+  bf16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (__bf16)(col < ncol ? W[(int64_t)(d0 + e) * ncol + col] : 0.0f);
+  Wp[gid] = __builtin_bit_cast(uint4, v);
+}
+
+hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t s) {
+  const int ntiles = enc_ntiles(K, L);
+  const int64_t total = (int64_t)ntiles * KSTEPS * 64;
+  if (total == 0) return hipSuccess;
+  proj_pack_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(W, K * L, ntiles, (uint4 *)Wp);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Key mean k_avg = (1/n) sum_i k_i per unit, accumulated in fp64 and rounded
+// once to fp32.  Stage 1: each block sums KM_ROWS rows of one unit
+// (16 lanes x 8 dims cover a row; 16 rows in flight per pass).  Stage 2: one
+// block per unit adds the stage-1 sums in block order (deterministic).
+constexpr int KM_ROWS = 2048;
+
+int kmean_parts(int64_t n) { return (int)((n + KM_ROWS - 1) / KM_ROWS); }
+
+template <typename T>
+__device__ inline void load8(const T *p, float (&v)[8]);
+template <>
+__device__ inline void load8<float>(const float *p, float (&v)[8]) {
+  const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[e + 4] = b[e]; }
+}
+template <>
+__device__ inline void load8<__bf16>(const __bf16 *p, float (&v)[8]) {
+  const bf16x8 a = *(const bf16x8 *)p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict__ Kc, int64_t n, int64_t cap,
+                                                            int nparts, double *__restrict__ partial) {
+  __shared__ double red[16][D];
+  const int64_t u = blockIdx.y;
+  const int p = blockIdx.x;
+  const int j16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;
+  const int64_t r0 = (int64_t)p * KM_ROWS, r1 = min(n, r0 + KM_ROWS);
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const T *base = Kc + u * cap * D + 8 * j16;
+  for (int64_t r = r0 + rsub; r < r1; r += 16) {
+    float v[8];
+    load8<T>(base + r * D, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += (double)v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rsub][8 * j16 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += red[r][threadIdx.x];
+    partial[(u * nparts + p) * D + threadIdx.x] = s;
+  }
+}
+
+__global__ __launch_bounds__(D) void kmean_final_kernel(const double *__restrict__ partial, int nparts, int64_t n,
+                                                        float *__restrict__ kmean) {
+  const int64_t u = blockIdx.x;
+  double s = 0.0;
+  for (int p = 0; p < nparts; ++p) s += partial[(u * nparts + p) * D + threadIdx.x];
+  kmean[u * D + threadIdx.x] = (float)(s / (double)n);
+}
+
+hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, double *partial,
+                        int nparts, float *kmean, hipStream_t s) {
+  dim3 g1((unsigned)nparts, (unsigned)U);
+  if (kv_dtype == 0)
+    kmean_partial_kernel<__bf16><<<g1, 256, 0, s>>>((const __bf16 *)Kc, n, cap, nparts, partial);
+  else
+    kmean_partial_kernel<float><<<g1, 256, 0, s>>>((const float *)Kc, n, cap, nparts, partial);
+  kmean_final_kernel<<<dim3((unsigned)U), D, 0, s>>>(partial, nparts, n, kmean);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Encoder.  Each block encodes ENC_ROWS rows of one unit for the tables
+// [l0, l1) assigned to blockIdx.z.  Wave w owns rows w*64 .. w*64+63 as two
+// 32-row B operands held in registers (x = bf16(row - mu) for the 128 dims).
+// Packed projection tiles stream through LDS (double buffered, ENC_TG tiles
+// per stage); per tile a wave issues 2 x 8 matrix-core ops (32x32x16 bf16,
+// fp32 accumulate).  Each accumulator's sign gives one bit (z > 0); the
+// 16-bit masks of the two lane halves are exchanged so that lane l holds all
+// 32 bits of row w*64 + l, which are appended to a 64-bit bit queue; every
+// complete group of K bits is one table code, stored to
+// out[u*out_su + l*out_sl + row*out_si].
+//
+// For appends the same pass copies the raw key row (and value row) into the
+// cache when kcopy / vcopy are given.
+template <typename T>
+__device__ inline void load_row8(const T *p, float (&v)[8]) { load8<T>(p, v); }
+
+template <typename T>
+__device__ inline void store_row8(T *p, const float (&v)[8]);
+template <>
+__device__ inline void store_row8<float>(float *p, const float (&v)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { a[e] = v[e]; b[e] = v[e + 4]; }
+  *(f32x4 *)p = a;
+  *(f32x4 *)(p + 4) = b;
+}
+template <>
+__device__ inline void store_row8<__bf16>(__bf16 *p, const float (&v)[8]) {
+  bf16x8 a;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) a[e] = (__bf16)v[e];  // exact: values came from bf16
+  *(bf16x8 *)p = a;
+}
+
+// Bit r of the result is (a[r] > 0): the fp32 pattern read as a signed
+// integer is positive exactly for positive, non-zero values (+0, -0 and
+// negatives give 0).  Each element is copied to a scalar before the bit cast.
+__device__ inline uint32_t sign_bits16(const f32x16 &a) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const float z = a[r];
+    const int32_t i = __builtin_bit_cast(int32_t, z);
+    const int32_t bit = __builtin_elementwise_min(__builtin_elementwise_max(i, 0), 1);
+    m |= (uint32_t)bit << r;
+  }
+  return m;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void encode_kernel(
+    const T *__restrict__ in, int64_t in_su, int64_t in_si, const float *__restrict__ mu, int64_t mu_su,
+    int64_t mu_si, int64_t rows, const uint4 *__restrict__ wp, int K, int L, int tables_per_block,
+    uint16_t *__restrict__ out, int64_t out_su, int64_t out_si, int64_t out_sl, T *__restrict__ kcopy,
+    int64_t kc_su, int64_t kc_si, const T *__restrict__ vin, T *__restrict__ vcopy) {
+  __shared__ uint4 wsh[2][ENC_TG * KSTEPS * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int64_t u = blockIdx.y;
+  const int64_t row_w = (int64_t)blockIdx.x * ENC_ROWS + wave * 64;  // first row of this wave
+  const int l0 = blockIdx.z * tables_per_block;
+  const int l1 = min(L, l0 + tables_per_block);
+  const bool copy_rows = blockIdx.z == 0;  // table-split blocks share rows
+
+  // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.
+  bf16x8 xb[2][KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int64_t r = row_w + 32 * nt + (lane & 31);
+    const bool ok = r < rows;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int d0 = 16 * s + 8 * half;
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok) {
+        load_row8<T>(in + u * in_su + r * in_si + d0, v);
+        if (kcopy && copy_rows) store_row8<T>(kcopy + u * kc_su + r * kc_si + d0, v);
+        if (vcopy && copy_rows) {
+          float w[8];
+          load_row8<T>(vin + u * in_su + r * in_si + d0, w);
+          store_row8<T>(vcopy + u * kc_su + r * kc_si + d0, w);
+        }
+        if (mu) {
+          float m[8];
+          load8<float>(mu + u * mu_su + r * mu_si + d0, m);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] - m[e];  // fp32 subtraction
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[nt][s][e] = (__bf16)v[e];  // round to nearest even
+    }
+  }
+
+  const int64_t my_row = row_w + lane;  // row whose 32-bit words this lane assembles
+  const bool my_ok = my_row < rows;
+  uint16_t *my_out = out + u * out_su + my_row * out_si;
+  int lt = l0;  // next table to emit
+
+  if (K == 0) {
+    for (; lt < l1; ++lt)
+      if (my_ok) my_out[(int64_t)lt * out_sl] = 0;
+    return;
+  }
+
+  const int c0 = l0 * K, c1 = l1 * K;
+  const int t0 = c0 >> 5, t1 = (c1 + 31) >> 5;
+  const int skip = c0 - 32 * t0;
+  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
+  uint64_t q = 0;  // bit queue
+  int nb = 0;
+
+  // Projection tiles [tg, tg + ENC_TG) are staged global -> registers -> LDS.
+  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
+#define MP_FETCH(tg_)                                                        \
+  do {                                                                       \
+    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
+    const uint4 *src_ = wp + (int64_t)(tg_)*KSTEPS * 64 + threadIdx.x;       \
+    const int i_ = threadIdx.x;                                              \
+    if (i_ + 0 * 256 < cnt_) st0 = src_[0 * 256];                            \
+    if (i_ + 1 * 256 < cnt_) st1 = src_[1 * 256];                            \
+    if (i_ + 2 * 256 < cnt_) st2 = src_[2 * 256];                            \
+    if (i_ + 3 * 256 < cnt_) st3 = src_[3 * 256];                            \
+    if (i_ + 4 * 256 < cnt_) st4 = src_[4 * 256];                            \
+    if (i_ + 5 * 256 < cnt_) st5 = src_[5 * 256];                            \
+    if (i_ + 6 * 256 < cnt_) st6 = src_[6 * 256];                            \
+    if (i_ + 7 * 256 < cnt_) st7 = src_[7 * 256];                            \
+  } while (0)
+#define MP_COMMIT(buf_, tg_)                                                 \
+  do {                                                                       \
+    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
+    uint4 *dst_ = &wsh[buf_][threadIdx.x];                                   \
+    const int i_ = threadIdx.x;                                              \
+    if (i_ + 0 * 256 < cnt_) dst_[0 * 256] = st0;                            \
+    if (i_ + 1 * 256 < cnt_) dst_[1 * 256] = st1;                            \
+    if (i_ + 2 * 256 < cnt_) dst_[2 * 256] = st2;                            \
+    if (i_ + 3 * 256 < cnt_) dst_[3 * 256] = st3;                            \
+    if (i_ + 4 * 256 < cnt_) dst_[4 * 256] = st4;                            \
+    if (i_ + 5 * 256 < cnt_) dst_[5 * 256] = st5;                            \
+    if (i_ + 6 * 256 < cnt_) dst_[6 * 256] = st6;                            \
+    if (i_ + 7 * 256 < cnt_) dst_[7 * 256] = st7;                            \
+  } while (0)
+
+  MP_FETCH(t0);
+  MP_COMMIT(0, t0);
+  __syncthreads();
+  int buf = 0;
+  for (int tg = t0; tg < t1; tg += ENC_TG) {
+    const int tnext = tg + ENC_TG;
+    if (tnext < t1) MP_FETCH(tnext);
+    const int ntile = min(ENC_TG, t1 - tg);
+    for (int tt = 0; tt < ntile; ++tt) {
+      f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, wsh[buf][(tt * KSTEPS + s) * 64 + lane]);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[0][s], acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[1][s], acc1, 0, 0, 0);
+      }
+      const uint32_t m0 = sign_bits16(acc0), m1 = sign_bits16(acc1);
+      // lane half 0 keeps row lane (tile 0) and needs the partner's upper 16
+      // columns of it; lane half 1 keeps row 32 + lane%32 (tile 1).
+      const uint32_t send = half ? m0 : m1;
+      const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+      uint32_t word = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+      int nw = 32;
+      if (tg + tt == t0 && skip) {
+        word >>= skip;
+        nw = 32 - skip;
+      }
+      q |= (uint64_t)word << nb;
+      nb += nw;
+      while (nb >= K && lt < l1) {
+        if (my_ok) my_out[(int64_t)lt * out_sl] = (uint16_t)(q & kmask);
+        q >>= K;
+        nb -= K;
+        ++lt;
+      }
+    }
+    if (tnext < t1) MP_COMMIT(buf ^ 1, tnext);
+    __syncthreads();
+    buf ^= 1;
+  }
+#undef MP_FETCH
+#undef MP_COMMIT
+}
+
+hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su,
+                         int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
+                         int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,
+                         const void *vin, void *vcopy, hipStream_t s) {
+  if (units == 0 || rows == 0) return hipSuccess;
+  const int64_t rblocks = (rows + ENC_ROWS - 1) / ENC_ROWS;
+  // Few rows: split the tables over blocks so that the projection pass runs
+  // on many compute units instead of one.
+  int tsplit = 1;
+  const int64_t blocks = rblocks * units;
+  if (blocks < 512) tsplit = (int)std::min<int64_t>((512 + blocks - 1) / blocks, (int64_t)L);
+  int tpb = (L + tsplit - 1) / tsplit;
+  tsplit = (L + tpb - 1) / tpb;
+  dim3 grid((unsigned)rblocks, (unsigned)units, (unsigned)tsplit);
+  if (dtype == 0)
+    encode_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)in, in_su, in_si, mu, mu_su, mu_si, rows,
+                                                (const uint4 *)Wp, K, L, tpb, out, out_su, out_si, out_sl,
+                                                (__bf16 *)kcopy, kc_su, kc_si, (const __bf16 *)vin, (__bf16 *)vcopy);
+  else
+    encode_kernel<float><<<grid, 256, 0, s>>>((const float *)in, in_su, in_si, mu, mu_su, mu_si, rows,
+                                               (const uint4 *)Wp, K, L, tpb, out, out_su, out_si, out_sl,
+                                               (float *)kcopy, kc_su, kc_si, (const float *)vin, (float *)vcopy);
+  return hipGetLastError();
+}
+
+}  // namespace mp

@@ -1,0 +1,72 @@
+// Internal declarations shared by the HIP sources of libmagicpig.so (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int D = 128;          // supported head dimension
+constexpr int KSTEPS = D / 16;  // k-steps of one 32x32x16 bf16 matrix-core op over d
+
+// ---------------------------------------------------------------- encoder
+// Packed projections: [ntiles][KSTEPS][64 lanes][8 bf16], one 32-column tile
+// = 8 KB.  Within a tile, matrix row i (the A-operand row that lane i % 32
+// supplies) carries projection column 32*t + enc_row_col(i); the column order
+// is chosen so that accumulator register r of lane half a holds column
+// 16*a + r, i.e. each lane's 16 sign bits come out in column order.
+constexpr int ENC_ROWS = 256;   // rows (keys or queries) per encoder block
+constexpr int ENC_TG = 4;       // tiles staged in LDS per step (32 KB)
+__host__ __device__ inline int enc_ntiles(int K, int L) { return (K * L + 31) / 32; }
+__host__ __device__ inline int enc_row_col(int i) { return 16 * ((i >> 2) & 1) + (i & 3) + 4 * (i >> 3); }
+
+// ---------------------------------------------------------------- decode
+constexpr int SCAN_TILE = 512;  // keys per scan tile: 64 lanes x 8 keys (16 B of codes per table)
+constexpr int PSTRIDE = 132;    // floats per partial record: m, l, count, pad, o[128]
+constexpr int MAX_G = 8;        // query heads per KV head handled by one pass
+constexpr int MAX_L = 512;
+
+struct DecodeGeom {
+  int64_t U;          // units = B * Hkv
+  int chunk_tiles;    // scan tiles per block
+  int64_t chunk;      // keys per block = chunk_tiles * SCAN_TILE
+  int64_t nchunks;    // blocks per unit for this n
+  int64_t nchunks_max;  // for n = cap (workspace sizing)
+};
+
+// Workspace layout of the decode: [qcodes B*Hq*L u16, 256-aligned]
+// [partials U * nchunks_max * G * PSTRIDE f32] [entries U * nchunks_max * chunk u32]
+// [entry counts U * nchunks_max i32].
+struct DecodeWs {
+  uint16_t *qcodes;
+  float *part;
+  uint32_t *ent;
+  int32_t *ent_cnt;
+  size_t bytes;
+};
+
+DecodeGeom decode_geom(int B, int Hkv, int64_t n, int64_t cap);
+DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L);
+
+// Launchers (defined in the .hip files); they return hipError_t of the launch.
+hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t s);
+hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, double *partial,
+                        int nparts, float *kmean, hipStream_t s);
+int kmean_parts(int64_t n);
+hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su,
+                         int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
+                         int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,
+                         const void *vin, void *vcopy, hipStream_t s);
+hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
+                         const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                         int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
+                         bool want_idx, hipStream_t s);
+hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
+                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s);
+
+}  // namespace mp

@@ -1,0 +1,135 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+entry point, and rejects invalid arguments with the documented status
+before anything is enqueued (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lsh_sampled_sparse_centered_amd as mp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "magicpig.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mp.LIB_PATH), reason="libmagicpig.so not built")
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+OK, ARG, UNSUP, CAP, WS = 0, -1, -2, -3, -4
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_symbols() == sorted(mp.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mp.LIB_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version():
+    for code in (OK, ARG, UNSUP, CAP, WS, -5):
+        assert len(mp.strerror(code)) > 5
+    assert mp.strerror(12345) == "unknown status"
+    assert mp.lib().mp_version() == 1
+
+
+def test_size_queries():
+    assert mp.mp_proj_bytes(128, 10, 150) == 47 * 8 * 64 * 16
+    assert mp.mp_proj_bytes(128, 8, 75) == 19 * 8 * 64 * 16
+    assert mp.mp_proj_bytes(64, 8, 75) == 0
+    assert mp.mp_proj_bytes(128, 17, 75) == 0
+    assert mp.mp_proj_bytes(128, 10, 1) == 0
+    assert mp.mp_build_ws_bytes(8, 16384) == 8 * 8 * 128 * 8
+    a = mp.mp_decode_ws_bytes(1, 32, 8, 98368, 150)
+    b = mp.mp_decode_ws_bytes(1, 32, 8, 2 * 98368, 150)
+    assert 0 < a < b
+    assert mp.mp_decode_ws_bytes(1, 32, 7, 1024, 150) == 0  # Hq % Hkv
+    assert mp.mp_decode_ws_bytes(1, 32, 2, 1024, 150) == 0  # G = 16 > 8
+
+
+def _build(**kw):
+    a = dict(Kc=FAKE, dt=0, U=8, n=100, cap=128, d=128, Wp=FAKE, K=8, L=75, km=FAKE, codes=FAKE, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return mp.lib().mp_build_codes(a["Kc"], a["dt"], a["U"], a["n"], a["cap"], a["d"], a["Wp"], a["K"], a["L"],
+                                   a["km"], a["codes"], a["ws"], a["wsb"], None)
+
+
+def test_build_rejects_invalid_arguments():
+    assert _build(d=64) == UNSUP
+    assert _build(K=17) == UNSUP
+    assert _build(L=1) == UNSUP
+    assert _build(K=16, L=300) == UNSUP
+    assert _build(dt=7) == ARG
+    assert _build(Kc=None) == ARG
+    assert _build(codes=None) == ARG
+    assert _build(cap=100) == ARG  # not a multiple of 8
+    assert _build(n=0) == CAP
+    assert _build(n=129) == CAP
+    assert _build(ws=None) == WS
+    assert _build(wsb=16) == WS
+
+
+def _append(**kw):
+    a = dict(k=FAKE, v=FAKE, Kc=FAKE, Vc=FAKE, dt=0, U=8, n=100, cap=128, d=128, km=FAKE, Wp=FAKE, K=8, L=75,
+             codes=FAKE)
+    a.update(kw)
+    return mp.lib().mp_append(a["k"], a["v"], a["Kc"], a["Vc"], a["dt"], a["U"], a["n"], a["cap"], a["d"], a["km"],
+                              a["Wp"], a["K"], a["L"], a["codes"], None)
+
+
+def test_append_rejects_invalid_arguments():
+    assert _append(n=128) == CAP
+    assert _append(n=500) == CAP
+    assert _append(n=-1) == ARG
+    assert _append(v=None) == ARG
+    assert _append(d=256) == UNSUP
+    assert _append(cap=129) == ARG
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100, cap=128,
+             d=128, K=8, L=75, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
+             wsb=1 << 30)
+    a.update(kw)
+    return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"], a["B"], a["Hq"],
+                                   a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["nsh"], a["nst"], a["qin"],
+                                   a["qout"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
+
+
+def test_decode_rejects_invalid_arguments():
+    assert _decode(Hkv=7) == ARG
+    assert _decode(Hkv=2) == UNSUP  # 16 query heads per KV head
+    assert _decode(B=0) == ARG
+    assert _decode(n=129) == CAP
+    assert _decode(n=-1) == CAP
+    assert _decode(nsh=-1) == ARG
+    assert _decode(out=None) == ARG
+    assert _decode(Wp=None) == ARG  # needed to encode q when no qcodes_in
+    assert _decode(ws=None) == WS
+    assert _decode(wsb=100) == WS
+    assert _decode(d=96) == UNSUP
+    assert _decode(B=70000, Hq=8, Hkv=8) == UNSUP
+
+
+def test_decode_stages_reject_invalid_arguments():
+    L = mp.lib()
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0, FAKE,
+                              1 << 30, None) == ARG  # qcodes required
+    assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, None, None, None, None, FAKE, 1 << 30, None) == ARG
+    assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, FAKE, None, None, None, FAKE, 10, None) == WS
+
+
+def test_encode_queries_rejects_invalid_arguments():
+    L = mp.lib()
+    assert L.mp_encode_queries(FAKE, 0, 0, 128, FAKE, 8, 75, FAKE, None) == ARG
+    assert L.mp_encode_queries(FAKE, 3, 4, 128, FAKE, 8, 75, FAKE, None) == ARG
+    assert L.mp_encode_queries(FAKE, 0, 4, 128, FAKE, 8, 513, FAKE, None) == UNSUP
+    assert L.mp_proj_pack(None, 128, 8, 75, FAKE, None) == ARG

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Bars (floating point is bf16-in / fp32-accumulate on the GPU, fp64 in the
+oracle):
+  * key means: bitwise equal;
+  * codes: equal except bits whose projection is within the rounding band
+    |z| < 1e-5 |x| |w| (the oracle reports each table's smallest margin);
+  * with the oracle's codes injected: sampled index lists and counts equal
+    exactly; outputs within 2e-3 max-abs; lse within 1e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import lsh_sampled_sparse_centered_amd as mp
+import oracle
+import synth
+from tests.common import BAND, code_mismatches_outside_band, host_f32, layer, oracle_codes, oracle_decode, variant
+
+pytestmark = pytest.mark.gpu
+
+OUT_TOL = 2e-3
+LSE_TOL = 1e-3
+
+CASES = {
+    # fp32 keys, one head, (8, 75)
+    "tiny": variant("tiny"),
+    # Llama-3.1-8B-shaped layer: 32 q heads over 8 KV heads, (8, 75)
+    "llama8b_layer": variant("llama8b_layer"),
+    # 8 query heads per KV head, (10, 240), ragged n (not a multiple of 512)
+    "g8_ragged": variant("codellama34b_b4", layers=1, batch=1, n=5000, steps=0),
+    # MHA with batch 3, (9, 120)
+    "mha_b3": variant("codellama13b_b16", layers=1, batch=3, hq=4, hkv=4, n=3000),
+    # 2 query heads per KV head, odd K and L, short n
+    "g2_small": variant("llama8b_layer", hq=4, hkv=2, n=777, K=6, L=33),
+    # 3 query heads per KV head (not a power of two), K = 16
+    "g3_k16": variant("llama8b_layer", hq=6, hkv=2, n=1500, K=16, L=20),
+}
+
+_cache = {}
+
+
+def case(name):
+    if name not in _cache:
+        w = CASES[name]
+        print("[gpu parity] case %s: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d %s" % (name, w.batch, w.hq, w.hkv, w.n, w.K,
+                                                                           w.L, w.dtype), flush=True)
+        lay = layer(w, seed=1234)
+        km, codes, margin, qc = oracle_codes(w, lay)
+        _cache[name] = (w, lay, km, codes, margin, qc)
+    return _cache[name]
+
+
+def gpu_build(w, lay):
+    Wp = mp.mp_proj_pack(lay["W"], w.K, w.L)
+    kmean, codes = mp.mp_build_codes(lay["Kc"], lay["n"], Wp, w.K, w.L)
+    return Wp, kmean, codes
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_key_mean_and_codes(name):
+    w, lay, km, codes, margin, qc = case(name)
+    Wp, kmean, gcodes = gpu_build(w, lay)
+    torch.cuda.synchronize()
+    gk = kmean.cpu().numpy()
+    assert np.array_equal(gk.view(np.uint32), km.view(np.uint32)), "key means differ in %d elements" % int(
+        (gk != km).sum())
+    n = lay["n"]
+    g = gcodes.cpu().numpy()[:, :, :n].transpose(0, 2, 1).reshape(-1, w.L)
+    r = codes[:, :, :n].transpose(0, 2, 1).reshape(-1, w.L)
+    ndiff, nbad = code_mismatches_outside_band(g, r, margin.reshape(-1, w.L))
+    print("[gpu parity] %s: %d of %d codes differ, all inside the band" % (name, ndiff, g.size))
+    assert nbad == 0
+    # columns >= n are untouched
+    assert int(gcodes[:, :, n:].cpu().numpy().astype(np.int64).sum()) == 0
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_query_codes(name):
+    w, lay, km, codes, margin, qc = case(name)
+    Wp = mp.mp_proj_pack(lay["W"], w.K, w.L)
+    gq = mp.mp_encode_queries(lay["q"], Wp, w.K, w.L).cpu().numpy().reshape(-1, w.L)
+    h = lay["host"]
+    ref, mg = oracle.encode(h["q"].reshape(-1, w.d), h["W"], w.K, w.L, with_margin=True)
+    ndiff, nbad = code_mismatches_outside_band(gq, ref, mg)
+    assert nbad == 0
+
+
+def _inject(w, lay, km, codes, qc):
+    U = w.batch * w.hkv
+    kmean = torch.from_numpy(km).cuda()
+    gcodes = torch.from_numpy(codes).cuda()
+    qcodes = torch.from_numpy(qc).cuda()
+    assert gcodes.shape == (U, w.L, lay["cap"])
+    return kmean, gcodes, qcodes
+
+
+def _run_decode(w, lay, kmean, gcodes, qcodes, n=None, nsh=0, nst=0, Wp=None):
+    n = lay["n"] if n is None else n
+    B, Hq, cap = w.batch, w.hq, lay["cap"]
+    out = torch.empty(B, Hq, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, Hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, n, w.K, nsh, nst, qcodes_in=qcodes,
+                      out=out, lse=lse, idx=idx, count=cnt)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def _compare(w, ref, out, lse, idx, cnt, label):
+    worst = 0.0
+    for b in range(w.batch):
+        for h in range(w.hq):
+            c = int(cnt[b, h])
+            assert c == int(ref["count"][b, h]), (label, b, h, c, int(ref["count"][b, h]))
+            assert np.array_equal(idx[b, h, :c], ref["idx"][b][h]), (label, b, h)
+            if c == 0:
+                assert np.all(out[b, h] == 0) and lse[b, h] == -np.inf
+                continue
+            err = float(np.max(np.abs(out[b, h] - ref["out"][b, h])))
+            worst = max(worst, err)
+            assert err <= OUT_TOL, (label, b, h, err)
+            assert abs(float(lse[b, h]) - float(ref["lse"][b, h])) <= LSE_TOL, (label, b, h)
+    print("[gpu parity] %s: worst |out - oracle| = %.3g, mean |S| = %.1f" % (label, worst, np.mean(ref["count"])))
+    return worst
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_with_oracle_codes(name):
+    """Identical codes (injected from the oracle) give identical sets and outputs within tolerance."""
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes)
+    ref = oracle_decode(w, lay, km, codes, qc)
+    _compare(w, ref, out, lse, idx, cnt, name)
+
+
+@pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged"])
+def test_decode_static_ranges(name):
+    """Forced head/tail ranges (probability 1) on top of the sampled set."""
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes, nsh=4, nst=64)
+    ref = oracle_decode(w, lay, km, codes, qc, nsh=4, nst=64)
+    _compare(w, ref, out, lse, idx, cnt, name + "+static")
+
+
+@pytest.mark.parametrize("n", [0, 1, 7, 511, 512, 513, 1025])
+def test_decode_short_and_ragged_n(n):
+    """Edge lengths: empty cache, a single key, tails around the 512-key scan tile."""
+    w, lay, km, codes, margin, qc = case("llama8b_layer")
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes, n=n)
+    ref = oracle_decode(w, lay, km, codes, qc, n=n)
+    _compare(w, ref, out, lse, idx, cnt, "n=%d" % n)
+    if n == 0:
+        assert np.all(cnt == 0) and np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_decode_K0_is_exact_attention():
+    """K = 0: empty codes collide everywhere, P = 1, the estimate is Equation 1."""
+    w = variant("tiny", K=0, L=4, n=2000)
+    lay = layer(w, seed=77)
+    Wp = mp.mp_proj_pack(lay["W"], 0, w.L)
+    kmean, gcodes = mp.mp_build_codes(lay["Kc"], lay["n"], Wp, 0, w.L)
+    out = mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, w.n, 0)
+    torch.cuda.synchronize()
+    h = lay["host"]
+    q = h["q"][0, 0].astype(np.float64)
+    K = h["K"][0, 0, :w.n].astype(np.float64)
+    V = h["V"][0, 0, :w.n].astype(np.float64)
+    s = K @ q / math.sqrt(w.d)
+    p = np.exp(s - s.max())
+    ref = (p / p.sum()) @ V
+    assert np.max(np.abs(out.cpu().numpy()[0, 0] - ref)) <= OUT_TOL
+
+
+def test_end_to_end_gpu_codes():
+    """The whole GPU path (its own means, codes and query codes).  Where every
+    code of a unit equals the oracle's, the sets must be identical."""
+    w, lay, km, codes, margin, qc = case("llama8b_layer")
+    Wp, kmean, gcodes = gpu_build(w, lay)
+    qout = torch.empty(w.batch, w.hq, w.L, dtype=torch.uint16, device="cuda")
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+    idx = torch.full((w.batch, w.hq, lay["cap"]), -1, dtype=torch.int32, device="cuda")
+    out = mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, lay["n"], w.K, qcodes_out=qout,
+                            idx=idx, count=cnt)
+    torch.cuda.synchronize()
+    ref = oracle_decode(w, lay, km, codes, qc)
+    g = gcodes.cpu().numpy()
+    gq = qout.cpu().numpy()
+    G = w.group
+    same = 0
+    for u in range(w.batch * w.hkv):
+        b, kvh = divmod(u, w.hkv)
+        if np.array_equal(g[u], codes[u]) and np.array_equal(gq[b, kvh * G:(kvh + 1) * G], qc[b, kvh * G:(kvh + 1) * G]):
+            same += 1
+            for h in range(kvh * G, (kvh + 1) * G):
+                c = int(cnt[b, h])
+                assert np.array_equal(idx[b, h, :c].cpu().numpy(), ref["idx"][b][h])
+                assert np.max(np.abs(out[b, h].cpu().numpy() - ref["out"][b, h])) <= OUT_TOL
+    print("[gpu parity] end-to-end: %d of %d units have identical codes" % (same, w.batch * w.hkv))
+
+
+def test_decode_stages_equal_composite_and_are_deterministic():
+    w, lay, km, codes, margin, qc = case("g8_ragged")
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    a = _run_decode(w, lay, kmean, gcodes, qcodes)
+    b = _run_decode(w, lay, kmean, gcodes, qcodes)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    ws = mp.decode_workspace(w.batch, w.hq, w.hkv, lay["cap"], w.L, "cuda")
+    mp.mp_decode_sample(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, qcodes, w.hkv, lay["n"], w.K, ws,
+                        want_idx=True)
+    out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
+    idx = torch.full((w.batch, w.hq, lay["cap"]), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_merge(w.batch, w.hq, w.hkv, lay["n"], lay["cap"], w.L, out, ws, lse=lse, idx=idx, count=cnt)
+    torch.cuda.synchronize()
+    for x, y in zip(a, (out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy())):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["llama8b_layer", "tiny"])
+def test_append_then_decode(name):
+    """Append a decoded token per unit (frozen mean): cache rows copied exactly,
+    its codes equal the oracle's encoding (up to the band), and a decode over
+    n + 1 keys matches the oracle."""
+    w = CASES[name]
+    lay = layer(w, seed=99)
+    Wp, kmean, gcodes = gpu_build(w, lay)
+    U, n, cap = w.batch * w.hkv, lay["n"], lay["cap"]
+    kn = torch.stack([synth.step_kv(99, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=1)[0] for u in range(U)])
+    vn = torch.stack([synth.step_kv(99, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=1)[1] for u in range(U)])
+    kn, vn = kn.cuda(), vn.cuda()
+    mp.mp_append(kn, vn, lay["Kc"], lay["Vc"], n, kmean, Wp, w.K, w.L, gcodes)
+    torch.cuda.synchronize()
+    assert torch.equal(lay["Kc"][:, n], kn) and torch.equal(lay["Vc"][:, n], vn)
+    km = kmean.cpu().numpy()
+    h = lay["host"]
+    knh = host_f32(kn)
+    for u in range(U):
+        ref, mg = oracle.encode(knh[u], h["W"], w.K, w.L, mu=km[u], with_margin=True)
+        got = gcodes[u, :, n].cpu().numpy()[None]
+        assert code_mismatches_outside_band(got, ref, mg)[1] == 0
+    # decode over n + 1 keys with the oracle's codes for the whole store
+    keys = host_f32(lay["Kc"]).reshape(w.batch, w.hkv, cap, w.d)
+    vals = host_f32(lay["Vc"]).reshape(w.batch, w.hkv, cap, w.d)
+    codes_o = np.zeros((U, w.L, cap), np.uint16)
+    for u in range(U):
+        codes_o[u][:, :n + 1] = oracle.encode(keys.reshape(U, cap, w.d)[u, :n + 1], h["W"], w.K, w.L, mu=km[u]).T
+    qc = oracle.encode(h["q"].reshape(-1, w.d), h["W"], w.K, w.L).reshape(w.batch, w.hq, w.L)
+    lay2 = dict(lay)
+    lay2["host"] = dict(h, K=keys, V=vals)
+    lay2["n"] = n + 1
+    kmean_t, gcodes_t, qcodes = _inject(w, lay2, km, codes_o, qc)
+    out, lse, idx, cnt = _run_decode(w, lay2, kmean_t, gcodes_t, qcodes)
+    ref = oracle_decode(w, lay2, km, codes_o, qc)
+    _compare(w, ref, out, lse, idx, cnt, name + "+append")
