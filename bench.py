@@ -6,16 +6,17 @@ Workload (default): Llama-3.1-8B-shaped decode at 96K context -- 32 layers x
 batch 1, SimHash (K, L) = (10, 150).  Inputs are synthetic (the cone-plus-sink
 generator in ``synth``), resident in HBM before timing starts.
 
-One step = for every layer: append the new token's key/value and codes
-(mp_append), encode the 32 queries (mp_encode_queries), scan + weight +
-split-attend (mp_decode_sample) and merge (mp_decode_merge).  The code store
-is built once beforehand (mp_build_codes), timed separately as the encoder.
+One step = for every layer: mp_decode_step, i.e. append the new token's
+key/value and codes and encode the 32 queries (one launch), scan + weight +
+split-attend (the sampling kernel) and merge.  The code store is built once
+beforehand (mp_build_codes), timed separately as the encoder.
 
 Prints one JSON line.  ``value`` = context keys scanned per second over the
 whole step (all layers and KV heads); ``ms_per_step`` = decode-step latency.
-``roofline`` describes the dominant kernel (the scan/attention kernel of
-mp_decode_sample) against the 8 TB/s HBM peak, its duration taken from HIP
-events recorded around every launch in the timed region.
+``roofline`` describes the dominant kernel (the sampling kernel: scan,
+weighting, split attention) against the 8 TB/s HBM peak, its duration taken
+from HIP events that mp_decode_step records around every launch of it in the
+timed region.
 """
 from __future__ import annotations
 
@@ -119,16 +120,22 @@ def main() -> int:
     log("built %d layers; build %.3f ms/layer (median)" % (nlayers, float(np.median(build_ms))))
 
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
-    qc = torch.empty(w.batch, w.hq, L, dtype=torch.uint16, device=dev)
     outs = [torch.empty(w.batch, w.hq, d, dtype=torch.float32, device=dev) for _ in range(nlayers)]
     lses = [torch.empty(w.batch, w.hq, dtype=torch.float32, device=dev) for _ in range(nlayers)]
 
     # ------------------------------------------------------------------ decode steps
+    # one step = for every layer: mp_decode_step (append + query encode in one
+    # launch, then the sampling kernel and the merge); HIP events recorded by
+    # the library around every sampling kernel of the timed steps
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps * nlayers)]
+    for pair in kev:
+        for e in pair:
+            e.record()  # create the underlying events before handing them to the library
     n_cur = n0
     t0 = t1 = 0.0
     step_ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
     n_timed = []
+    torch.cuda.synchronize()
     for s in range(total_steps):
         timed = s >= args.warmup
         if s == args.warmup:
@@ -136,16 +143,9 @@ def main() -> int:
             t0 = time.perf_counter()
             step_ev[0].record()
         for l, lay in enumerate(layers):
-            mp.mp_append(lay["kn"][s], lay["vn"][s], lay["Kc"], lay["Vc"], n_cur, lay["kmean"], lay["Wp"], K, L,
-                         lay["codes"])
-            mp.mp_encode_queries(lay["qs"][s], lay["Wp"], K, L, qcodes=qc)
-            if timed:
-                kev[(s - args.warmup) * nlayers + l][0].record()
-            mp.mp_decode_sample(lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], qc, w.hkv, n_cur + 1,
-                                K, ws)
-            if timed:
-                kev[(s - args.warmup) * nlayers + l][1].record()
-            mp.mp_decode_merge(w.batch, w.hq, w.hkv, n_cur + 1, cap, L, outs[l], ws, lse=lses[l])
+            ev = kev[(s - args.warmup) * nlayers + l] if timed else None
+            mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
+                              lay["kmean"], lay["Wp"], w.hkv, n_cur, K, ws, out=outs[l], lse=lses[l], sample_events=ev)
         if timed:
             n_timed.append(n_cur + 1)
         n_cur += 1
@@ -229,7 +229,7 @@ def main() -> int:
                    "head_dim": d, "context": n0, "K": K, "L": L, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "sample_kernel (mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
+                     "kernel": "sample_kernel (mp_decode_step / mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
                      "algorithmic_bytes_per_launch": bytes_launch},
         "step": {"latency_ms": wall_ms, "latency_ms_events": ev_ms, "bytes_per_step": step_bytes,
                  "frac_hbm_step": step_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -20,8 +20,7 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Every pointer except the host pointer of mp_proj_pack's documentation
- *    example is a DEVICE pointer on the current HIP device.  The caller
+ *  - Every pointer is a DEVICE pointer on the current HIP device.  The caller
  *    allocates and owns every buffer; the library never allocates, frees or
  *    keeps pointers after a call returns, and keeps no global state, so calls
  *    on different streams are independent when their workspaces differ.
@@ -183,6 +182,23 @@ int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype
                      size_t ws_bytes, void *stream);
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
                     int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * One decode step of one layer in three launches: append the new token's key
+ * and value to every unit and encode its key (as mp_append; skipped when
+ * k_new is NULL), encode the queries (as mp_encode_queries, into ws) -- both
+ * in one launch -- then sample and merge (as mp_decode_attn) over n + 1 keys
+ * (n keys without an append).  Arguments as in mp_append and
+ * mp_decode_attn; q codes are kept in ws.  sample_events is NULL or points
+ * to two host hipEvent_t handles, recorded on the stream right before and
+ * right after the sampling kernel (for callers that time it).
+ * Errors: as mp_append and mp_decode_attn; MP_ERR_CAPACITY when appending
+ * with n >= cap.
+ */
+int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                   uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
+                   int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream);
 
 #ifdef __cplusplus
 }

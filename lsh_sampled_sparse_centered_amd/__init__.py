@@ -44,6 +44,8 @@ _SIGS = {
                           _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
     "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                         _c_int),
+    "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
+                        _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
 }
 
 _lib = None
@@ -97,6 +99,16 @@ def _p(t: Optional[torch.Tensor]):
 def _stream(stream=None):
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def _event_pair(events):
+    """ctypes array of the two raw hipEvent_t handles of torch events (None: no timing)."""
+    if events is None:
+        return None
+    handles = [int(e.cuda_event) for e in events]
+    if len(handles) != 2 or not all(handles):
+        raise ValueError("sample_events needs two torch.cuda.Event objects that were recorded once")
+    return ctypes.cast((ctypes.c_void_p * 2)(*handles), ctypes.c_void_p)
 
 
 def _kv_dtype(t: torch.Tensor) -> int:
@@ -253,3 +265,32 @@ def mp_decode_merge(B: int, Hq: int, Hkv: int, n: int, cap: int, L: int, out: to
     st = lib().mp_decode_merge(B, Hq, Hkv, n, cap, d, L, _p(out), _p(lse), _p(idx), _p(count), _p(ws), ws.numel(),
                                _stream(stream))
     _check("mp_decode_merge", st)
+
+
+def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor], q: torch.Tensor, Kc: torch.Tensor,
+                   Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor, Wp: torch.Tensor, Hkv: int, n: int,
+                   K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
+                   n_static_tail: int = 0, sample_events=None, stream=None) -> torch.Tensor:
+    """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
+
+    ``sample_events``: optional pair of recorded-once torch.cuda.Event objects,
+    re-recorded around the sampling kernel."""
+    B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
+    if k_new is not None:
+        _need(k_new, Kc.dtype, (U, d), "k_new")
+        _need(v_new, Kc.dtype, (U, d), "v_new")
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=q.device)
+    _need(out, torch.float32, (B, Hq, d), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq), "lse")
+    if count is not None:
+        _need(count, torch.int32, (B, Hq), "count")
+    if idx is not None:
+        _need(idx, torch.int32, (B, Hq, cap), "idx")
+    st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp),
+                              B, Hq, Hkv, n, cap, d, K, L, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),
+                              _p(count), _p(ws), ws.numel(), _event_pair(sample_events), _stream(stream))
+    _check("mp_decode_step", st)
+    return out

@@ -135,7 +135,7 @@ int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!qcodes) return MP_ERR_ARG;
-  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   if (geo.nchunks == 0) return MP_OK;
   return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L,
@@ -150,7 +150,7 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
   if (!out || cap < 1 || cap % 8) return MP_ERR_ARG;
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
   if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
-  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, as_stream(stream)));
 }
@@ -165,7 +165,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   if (st) return st;
   if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
   hipStream_t s = as_stream(stream);
-  const DecodeGeom geo = decode_geom(B, Hkv, n, cap);
+  const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   const uint16_t *qc = qcodes_in;
   if (!qc) {
@@ -181,6 +181,42 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
     if (e != hipSuccess) return MP_ERR_HIP;
   }
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
+}
+
+int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                   uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
+                   int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
+  const bool app = k_new != nullptr;
+  if (app && !v_new) return MP_ERR_ARG;
+  if (app && (n < 0 || n >= cap)) return MP_ERR_CAPACITY;
+  const int64_t nd = app ? n + 1 : n;  // keys the decode sees
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, nd, cap, d, K, L, n_static_head,
+                        n_static_tail, ws, ws_bytes);
+  if (st) return st;
+  if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  const int64_t U = (int64_t)B * Hkv;
+  const DecodeGeom geo = decode_geom(B, Hkv, Hq, nd, cap);
+  const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
+  const size_t es = kv_dtype == MP_BF16 ? 2 : 4;
+  // one launch: the appended keys (frozen means, codes at column n, raw rows
+  // copied) and the queries (uncentred)
+  EncJob jobs[2];
+  int nj = 0;
+  if (app)
+    jobs[nj++] = make_job(k_new, 0, D, kmean, 0, D, 1, U, codes + n, 0, (int64_t)L * cap, cap,
+                          (char *)Kc + (size_t)n * D * es, 0, cap * D, v_new, (char *)Vc + (size_t)n * D * es);
+  jobs[nj++] = make_job(q, 0, D, nullptr, 0, 0, 1, (int64_t)B * Hq, w.qcodes, 0, L, 1, nullptr, 0, 0, nullptr,
+                        nullptr);
+  if (launch_encode_jobs(kv_dtype, jobs, nj, Wp, K, L, s) != hipSuccess) return MP_ERR_HIP;
+  hipEvent_t *ev = (hipEvent_t *)sample_events;
+  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MP_ERR_HIP;
+  if (geo.nchunks > 0 && launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L,
+                                       n_static_head, n_static_tail, geo, w, idx != nullptr, s) != hipSuccess)
+    return MP_ERR_HIP;
+  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MP_ERR_HIP;
+  return hip_status(launch_merge(B, Hq, Hkv, nd, L, geo, w, out, lse, idx, cap, count, s));
 }
 
 }  // extern "C"

@@ -7,18 +7,25 @@
 
 namespace mp {
 
-constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
-constexpr int MAX_CHUNK_TILES = 4;
-constexpr int MAX_CHUNK = MAX_CHUNK_TILES * SCAN_TILE;
+#ifndef MP_OCC
+#define MP_OCC 6  // waves per SIMD the G <= 4 kernels are compiled for
+#endif
+#ifndef MP_SB
+#define MP_SB 8  // code-store rows per load batch of a wave
+#endif
 
-DecodeGeom decode_geom(int B, int Hkv, int64_t n, int64_t cap) {
+constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
+constexpr int ATT_E = 32;  // list entries per attention round
+
+// One 512-key tile per block.
+DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap) {
+  (void)Hq;
   DecodeGeom g;
   g.U = (int64_t)B * Hkv;
-  const int64_t tiles = g.U * ((n + SCAN_TILE - 1) / SCAN_TILE);
-  g.chunk_tiles = tiles < 2048 ? 1 : (tiles < 8192 ? 2 : 4);
-  g.chunk = (int64_t)g.chunk_tiles * SCAN_TILE;
-  g.nchunks = (n + g.chunk - 1) / g.chunk;
-  g.nchunks_max = (cap + SCAN_TILE - 1) / SCAN_TILE;  // bound for any chunk size
+  g.chunk_tiles = 1;
+  g.chunk = SCAN_TILE;
+  g.nchunks = (n + SCAN_TILE - 1) / SCAN_TILE;
+  g.nchunks_max = (cap + SCAN_TILE - 1) / SCAN_TILE;
   return g;
 }
 
@@ -28,7 +35,7 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
   const int64_t U = (int64_t)B * Hkv;
   const int G = Hq / Hkv;
   const int64_t ncm = (cap + SCAN_TILE - 1) / SCAN_TILE;
-  const int64_t ent_per_unit = (cap + MAX_CHUNK - 1) / MAX_CHUNK * MAX_CHUNK;
+  const int64_t ent_per_unit = 2 * ncm * SCAN_TILE;  // up to 1024 entries per block
   size_t off = 0;
   DecodeWs w;
   char *p = (char *)base;
@@ -57,14 +64,14 @@ __device__ inline float log_sampling_prob(float c, int K, int L) {
   if (K == 0) return 0.0f;  // p = 1: every table collides, P = 1
   c = fminf(1.0f, fmaxf(-1.0f, c));
   const float u = acosf(-c) * 0.318309886183790671538f;
-  const float lnp = (float)K * logf(u);
-  const float p = expf(lnp);
+  const float lnp = (float)K * __logf(u);
+  const float p = __expf(lnp);
   const float Lf = (float)L;
   if (Lf * p < 1.0f) {
-    const float r = p / (1.0f - p);
+    const float r = p * __frcp_rn(1.0f - p);
     float term = 1.0f, sum = 1.0f;
     for (int j = 2; j < L && j < 40; ++j) {
-      term *= (float)(L - j) / (float)(j + 1) * r;
+      term *= (float)(L - j) * __frcp_rn((float)(j + 1)) * r;
       sum += term;
       if (term < 1e-8f * sum) break;
     }
@@ -109,6 +116,7 @@ struct Raw8<__bf16> {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (float)b[e];
   }
+  __device__ void store(__bf16 *p) const { *(uint4 *)p = a; }
 };
 template <>
 struct Raw8<float> {
@@ -119,124 +127,266 @@ struct Raw8<float> {
 #pragma unroll
     for (int e = 0; e < 4; ++e) { v[e] = x[e]; v[e + 4] = y[e]; }
   }
+  __device__ void store(float *p) const {
+    *(uint4 *)p = a;
+    *(uint4 *)(p + 4) = b;
+  }
 };
 
-// --------------------------------------------------------------------------
-// One block = one chunk (chunk_tiles x 512 keys) of one unit (batch, KV head)
-// for all G query heads of that KV head.
-//
-// Scan: per 512-key tile, lane l of wave w reads 16 bytes (8 keys) of the
-// codes of tables w, w+4, w+8, ... and counts, for every head, the tables
-// whose code differs from the query's (xor, packed min with 1, packed add:
-// two keys per 32-bit word).  The four waves' counts are added through LDS;
-// key i is sampled for head h when L - mismatches >= 2.  Forced keys (the
-// static head/tail ranges) are sampled for every head with P = 1.
-//
-// Compaction: wave ballots + popcounts give each key's rank, so the chunk's
-// union list (key, head mask) is built in LDS in ascending key order.
-//
-// Attention: 16-lane groups take list entries round robin; a group gathers
-// the key and value rows (16 lanes x 8 elements), reduces q_h.k and |k-mu|^2
-// across its row, lane h of the group turns head h's numbers into the
-// log-weight s - ln P, and every head with its mask bit set folds the value
-// row into an online softmax (m, l, o).  The 16 groups are then merged by
-// log-sum-exp and one partial record per head is written.
+// N consecutive elements of a staged LDS row, as floats.
+template <typename T, int N>
+__device__ inline void ldv(const T *p, float (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = (float)p[i];
+}
+
+// One list entry in a 16-lane group (lane j16 holds elements 8*j16 .. +7):
+// stage the value row slice in LDS and reduce |k - mu|^2 and q_h.k (h < G)
+// over the row.  q and mu are read from LDS.
 template <typename T, int GM>
-__global__ __launch_bounds__(256, 2) void sample_kernel(
+__device__ inline void entry_dots(const Raw8<T> &kr, const Raw8<T> &vr, int el, int j16, int G,
+                                  const float (*qsh)[D], const float *msh, T *vrow, float *dk, float *nc2s) {
+  float kv[8], mv[8];
+  kr.get(kv);
+  vr.store(vrow + 8 * j16);
+  ld8<float>(msh + 8 * j16, mv);
+  float nc2 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const float ct = kv[t] - mv[t];
+    nc2 += ct * ct;
+  }
+  nc2 = row16_sum(nc2);
+  if (j16 == 0) nc2s[el] = nc2;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    if (h < G) {
+      float qv[8];
+      ld8<float>(&qsh[h][8 * j16], qv);
+      float a = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) a += qv[t] * kv[t];
+      a = row16_sum(a);
+      if (j16 == h) dk[h] = a;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// One block = one 512-key tile of one unit (batch, KV head), for all G query
+// heads of that KV head.  Blocks are small and many so that the hardware
+// keeps several per compute unit and balances them dynamically.
+//
+// Scan: lane l of wave w reads 16 bytes (8 keys) of the codes of tables w,
+// w+4, w+8, ... and counts, for every head, the tables whose code differs
+// from the query's (xor, packed min with 1, add: two keys per 32-bit word,
+// two tables per add).  The four waves' counts are added through LDS; key i
+// is sampled for head h when L - mismatches >= 2.  Forced keys (the static
+// head/tail ranges) are sampled for every head with P = 1.
+//
+// Compaction: wave ballots + popcounts rank the keys, giving the tile's
+// union list (key, head mask) in LDS in ascending key order.
+//
+// Attention (Equations 9-11), in rounds of up to ATT_E list entries:
+//  (a) 16-lane groups gather an entry's key and value rows (8 elements per
+//      lane), reduce q_h.k and |k - mu|^2 and stage the value row in LDS;
+//  (b) one thread per (entry, head) forms the log-weight s - ln P, or -inf
+//      when the head did not sample the key;
+//  (c) one thread per (head, dims) folds the round into its running
+//      maximum m, normaliser l and unnormalised output o.
+// The query codes, queries and key mean are fetched while the first batch
+// of codes is in flight.  One partial record (m, l, count, o) per head.
+template <typename T, int GM>
+__global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
-    int64_t cap, int K, int L, int64_t nsh, int64_t nst, int chunk_tiles, int64_t nchunks, float scale,
-    uint32_t one2, float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt) {
-  __shared__ uint32_t qpk[MAX_L * GM];
-  __shared__ uint4 red[4][GM][64];
-  __shared__ uint16_t ukey[MAX_CHUNK];
-  __shared__ uint16_t umask[MAX_CHUNK];
+    int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2,
+    float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt) {
+  // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
+  // words [0, FW) says "at least one of this wave's tables matched", of
+  // words [FW, 2FW) "at least two".
+  constexpr int FW = (GM * 8 + 31) / 32;
+  struct ScanLds {
+    uint32_t flg[4][64][2 * FW];
+  };
+  struct AttnLds {
+    T v[ATT_E][D];         // staged value rows of this round's entries
+    float dk[ATT_E][GM];   // q_h . k
+    float nc2[ATT_E];      // |k - mu|^2
+    float pw[GM][ATT_E];   // exp(s - ln P - M_h) of this round, head-major
+    float rmax[4][GM];     // per-wave maxima of this round's log-weights
+  };
+  __shared__ union {
+    ScanLds s;
+    AttnLds a;
+  } sm;  // scan and attention phases never overlap in time
+  extern __shared__ uint32_t qpk[];  // [L][GM] query codes, each twice per word
+  __shared__ float qsh[GM][D];
+  __shared__ float msh[D];
+  __shared__ float qn_sh[GM], qmu_sh[GM];
+  __shared__ uint16_t lkey[2 * SCAN_TILE];   // union list: key offset from the block's first key
+  __shared__ uint16_t lmask[2 * SCAN_TILE];  // head bits | FORCED
   __shared__ int wtot[4];
   __shared__ int hcnt[GM];
-  __shared__ int nu_sh;
+  __shared__ float hm[GM];  // running maximum of the log-weights per head
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
+  const int j16 = lane & 15, grp = tid >> 4;
   const int64_t u = blockIdx.y;
-  const int64_t c = blockIdx.x;
+  // Tiles run in reverse order within a unit, so that the short last tile is
+  // dispatched first and the blocks left over for a second round start early.
+  const int64_t c = nchunks - 1 - blockIdx.x;
   const int64_t b = u / Hkv, kvh = u % Hkv;
   const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
-  const int64_t chunk = (int64_t)chunk_tiles * SCAN_TILE;
-  const int64_t cbase = c * chunk;
+  const int64_t tbase = c * SCAN_TILE;
+  const int64_t tend = min(n, tbase + SCAN_TILE);
+  const int nsub = 1;
   const uint16_t headbits = (uint16_t)((1u << G) - 1u);
+  const u16x2 one = __builtin_bit_cast(u16x2, one2);
 
+  // This wave's tables are wave, wave+4, ...  A lane reads 16 bytes (8 keys)
+  // at a scalar row base plus its own byte offset.  Loads are unconditional:
+  // lanes past the last key re-read the sub-tile's first 8 keys and tables
+  // past the wave's last re-read its last table (all inside the code store;
+  // their counts are discarded).
+  const int ntw = (L - wave + 3) / 4;
+  const int jlast = ntw - 1;
+  const int64_t rstride = 8 * cap;  // bytes between this wave's consecutive tables
+  const char *rows0 = (const char *)(codes + u * (int64_t)L * cap + (int64_t)wave * cap + tbase);
+  uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
+#define MP_ROW(j) (*(const uint4 *)(rows0 + (int64_t)min((j), jlast) * rstride + lo))
+  uint4 cw[MP_SB];
+  if (ntw > 0) {
+#pragma unroll
+    for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(jj);
+  }
+
+  // ---- prologue: query codes (packed twice per word), queries, key mean
   for (int i = tid; i < L * GM; i += 256) {
     const int l = i / GM, h = i % GM;
     const uint32_t code = h < G ? qcodes[(qrow0 + h) * L + l] : 0u;
     qpk[i] = code | (code << 16);
   }
-  if (tid < GM) hcnt[tid] = 0;
-  if (tid == 0) nu_sh = 0;
+  for (int i = tid; i < GM * D; i += 256) {
+    const int h = i / D, t = i % D;
+    qsh[h][t] = h < G ? (float)q[(qrow0 + h) * D + t] : 0.0f;
+  }
+  if (tid < D) msh[tid] = kmean[u * D + tid];
+  if (tid < GM) {
+    hcnt[tid] = 0;
+    hm[tid] = -INFINITY;
+  }
   __syncthreads();
 
-  const u16x2 one = __builtin_bit_cast(u16x2, one2);
-  const uint16_t *ucodes = codes + u * (int64_t)L * cap;
+  for (int h = wave; h < GM; h += 4) {  // |q_h| and q_h . mu
+    float a = qsh[h][lane] * qsh[h][lane] + qsh[h][lane + 64] * qsh[h][lane + 64];
+    float bq = qsh[h][lane] * msh[lane] + qsh[h][lane + 64] * msh[lane + 64];
+#pragma unroll
+    for (int sh = 32; sh > 0; sh >>= 1) {
+      a += __shfl_xor(a, sh);
+      bq += __shfl_xor(bq, sh);
+    }
+    if (lane == 0) {
+      qn_sh[h] = sqrtf(a);
+      qmu_sh[h] = bq;
+    }
+  }
 
-  // ------------------------------------------------------------ scan + compaction
-  for (int tt = 0; tt < chunk_tiles; ++tt) {
-    const int64_t tbase = cbase + (int64_t)tt * SCAN_TILE;
-    if (tbase >= n) break;
-    const int64_t key0 = tbase + 8 * lane;
-    const bool lane_ok = key0 < n;
+  int nu = 0;  // entries in the union list so far
+  uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
+  for (int st = 0; st < nsub; ++st) {
+    const int64_t sbase = tbase + (int64_t)st * SCAN_TILE;
+    if (st > 0) {
+      rows0 += 2 * SCAN_TILE;  // 512 keys further along every row
+      lo = (sbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
+      if (ntw > 0) {
+#pragma unroll
+        for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(jj);
+      }
+    }
+    // ---- scan
     uint32_t acc[GM][4];
 #pragma unroll
     for (int h = 0; h < GM; ++h)
 #pragma unroll
       for (int w = 0; w < 4; ++w) acc[h][w] = 0;
-
-    const int ntw = (L - wave + 3) / 4;  // tables of this wave: wave, wave+4, ...
-    for (int j0 = 0; j0 < ntw; j0 += 8) {
-      uint4 cw[8];
+#define MP_MIS(word, Q) \
+  __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, (word) ^ (Q)), one))
+    for (int j0 = 0; j0 < ntw; j0 += MP_SB) {
+      if (j0 > 0) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int l = wave + 4 * (j0 + jj);
-        cw[jj] = make_uint4(0, 0, 0, 0);
-        if (j0 + jj < ntw && lane_ok) cw[jj] = *(const uint4 *)(ucodes + (int64_t)l * cap + key0);
+        for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(j0 + jj);
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+      for (int jj = 0; jj < MP_SB; jj += 2) {
         if (j0 + jj < ntw) {
           const int l = wave + 4 * (j0 + jj);
-          const uint32_t w4[4] = {cw[jj].x, cw[jj].y, cw[jj].z, cw[jj].w};
+          const uint32_t a4[4] = {cw[jj].x, cw[jj].y, cw[jj].z, cw[jj].w};
+          const uint32_t b4[4] = {cw[jj + 1].x, cw[jj + 1].y, cw[jj + 1].z, cw[jj + 1].w};
+          const bool two = j0 + jj + 1 < ntw;
 #pragma unroll
           for (int h = 0; h < GM; ++h) {
-            const uint32_t Q = qpk[l * GM + h];
+            const uint32_t Qa = qpk[l * GM + h];
+            const uint32_t Qb = two ? qpk[(l + 4) * GM + h] : 0u;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-              const u16x2 x = __builtin_bit_cast(u16x2, w4[w] ^ Q);
-              acc[h][w] += __builtin_bit_cast(uint32_t, __builtin_elementwise_min(x, one));
+              const uint32_t mb = two ? MP_MIS(b4[w], Qb) : 0u;  // a missing second table adds 0
+              acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa) + mb;
             }
           }
         }
       }
     }
+#undef MP_MIS
+    {  // this wave's matches per (key, head) -> "at least one" / "at least two" flags
+      uint32_t g1[FW], g2[FW];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) red[wave][h][lane] = make_uint4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      for (int f = 0; f < FW; ++f) g1[f] = g2[f] = 0;
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int mlo = ntw - (int)(acc[h][w] & 0xffffu), mhi = ntw - (int)(acc[h][w] >> 16);
+          const int bit = h * 8 + 2 * w;  // keys 2w (low half) and 2w+1 (high half)
+          g1[bit >> 5] |= ((uint32_t)(mlo >= 1) | ((uint32_t)(mhi >= 1) << 1)) << (bit & 31);
+          g2[bit >> 5] |= ((uint32_t)(mlo >= 2) | ((uint32_t)(mhi >= 2) << 1)) << (bit & 31);
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < FW; ++f) {
+        sm.s.flg[wave][lane][f] = g1[f];
+        sm.s.flg[wave][lane][FW + f] = g2[f];
+      }
+    }
     __syncthreads();
 
-    // thread tid owns tile keys 2*tid and 2*tid+1: lane tid/4, word tid%4
-    const int64_t klo = tbase + 2 * tid;
+    // ---- threshold + compaction: thread tid owns sub-tile keys 2*tid, 2*tid+1
+    // (scan lane tid/4, key slots k0 = 2*(tid%4) and k0+1).  At least two
+    // matching tables overall <=> some wave has two, or two waves have one.
+    const int64_t klo = sbase + 2 * tid;
     uint32_t mlo = 0, mhi = 0;
+    {
+      const int sl = tid >> 2, k0 = 2 * (tid & 3);
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        uint32_t s = 0;
+      for (int f = 0; f < FW; ++f) {
+        const uint32_t a1 = sm.s.flg[0][sl][f], b1 = sm.s.flg[1][sl][f], c1 = sm.s.flg[2][sl][f],
+                       d1 = sm.s.flg[3][sl][f];
+        const uint32_t two = sm.s.flg[0][sl][FW + f] | sm.s.flg[1][sl][FW + f] | sm.s.flg[2][sl][FW + f] |
+                             sm.s.flg[3][sl][FW + f] | (a1 & (b1 | c1 | d1)) | (b1 & (c1 | d1)) | (c1 & d1);
 #pragma unroll
-        for (int w = 0; w < 4; ++w) s += ((const uint32_t *)&red[w][h][tid >> 2])[tid & 3];
-        const int mis_lo = (int)(s & 0xffffu), mis_hi = (int)(s >> 16);
-        mlo |= (uint32_t)(L - mis_lo >= 2) << h;
-        mhi |= (uint32_t)(L - mis_hi >= 2) << h;
+        for (int h = 0; h < GM; ++h) {
+          if ((h * 8) >> 5 == f && h < G) {
+            mlo |= ((two >> ((h * 8 + k0) & 31)) & 1u) << h;
+            mhi |= ((two >> ((h * 8 + k0 + 1) & 31)) & 1u) << h;
+          }
+        }
       }
     }
     if (klo < nsh || klo >= n - nst) mlo = headbits | FORCED;
     if (klo + 1 < nsh || klo + 1 >= n - nst) mhi = headbits | FORCED;
-    if (klo >= n) mlo = 0;
-    if (klo + 1 >= n) mhi = 0;
-
+    if (klo >= tend) mlo = 0;
+    if (klo + 1 >= tend) mhi = 0;
     const bool flo = (mlo & headbits) != 0, fhi = (mhi & headbits) != 0;
     const uint64_t blo = __ballot(flo), bhi = __ballot(fhi);
     const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -250,179 +400,124 @@ __global__ __launch_bounds__(256, 2) void sample_kernel(
       }
     }
     __syncthreads();
-    int off = nu_sh;
+    int off = nu;
     for (int w = 0; w < wave; ++w) off += wtot[w];
-    const int64_t kl_local = klo - cbase;
+    nu += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    const int kloc = (int)(klo - tbase);  // offset from the block's first key
     if (flo) {
-      ukey[off + pre] = (uint16_t)kl_local;
-      umask[off + pre] = (uint16_t)mlo;
-      if (ent) ent[(u * nchunks + c) * chunk + off + pre] = (uint32_t)kl_local | ((mlo & headbits) << 16);
+      lkey[off + pre] = (uint16_t)kloc;
+      lmask[off + pre] = (uint16_t)mlo;
+      if (uent) uent[off + pre] = (uint32_t)kloc | ((mlo & headbits) << 16);
     }
     if (fhi) {
       const int p2 = off + pre + (flo ? 1 : 0);
-      ukey[p2] = (uint16_t)(kl_local + 1);
-      umask[p2] = (uint16_t)mhi;
-      if (ent) ent[(u * nchunks + c) * chunk + p2] = (uint32_t)(kl_local + 1) | ((mhi & headbits) << 16);
+      lkey[p2] = (uint16_t)(kloc + 1);
+      lmask[p2] = (uint16_t)mhi;
+      if (uent) uent[p2] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
     }
-    __syncthreads();
-    if (tid == 0) nu_sh += wtot[0] + wtot[1] + wtot[2] + wtot[3];
-    __syncthreads();
+    __syncthreads();  // list complete; red and wtot free for the next sub-tile
   }
-  const int nu = nu_sh;
+#undef MP_ROW
   if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;
 
-  // ------------------------------------------------------------ weighting + attention
-  const int j16 = lane & 15, grp = tid >> 4;
-  float qf[GM][8], mv[8];
-  {
-    ld8<float>(kmean + u * D + 8 * j16, mv);
+  // ---- attention over the union list
+  constexpr int TPH = (256 / GM) < 128 ? (256 / GM) : 128;  // output threads per head
+  constexpr int DPT = D / TPH;                              // dims per output thread
+  const int oh = tid / TPH, od = (tid % TPH) * DPT;
+  const bool othread = oh < G && tid < GM * TPH;
+  float om = -INFINITY, ol = 0.0f, oacc[DPT];
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) ld8<T>(q + (qrow0 + h) * D + 8 * j16, qf[h]);
-      else
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[h][e] = 0.0f;
+  for (int i = 0; i < DPT; ++i) oacc[i] = 0.0f;
+  const T *Ku = Kc + (u * cap + tbase) * D + 8 * j16;
+  const T *Vu = Vc + (u * cap + tbase) * D + 8 * j16;
+  for (int e0 = 0; e0 < nu; e0 += ATT_E) {
+    const int ne = min(ATT_E, nu - e0);
+    static_assert(ATT_E == 32, "two entries per 16-lane group");
+    const int el0 = grp, el1 = grp + 16;
+    {  // (a) both of a group's entries are loaded before either is used
+      Raw8<T> k0, v0, k1, v1;
+      if (el0 < ne) {
+        const int64_t key = lkey[e0 + el0];
+        k0.load(Ku + key * D);
+        v0.load(Vu + key * D);
+      }
+      if (el1 < ne) {
+        const int64_t key = lkey[e0 + el1];
+        k1.load(Ku + key * D);
+        v1.load(Vu + key * D);
+      }
+      if (el0 < ne) entry_dots<T, GM>(k0, v0, el0, j16, G, qsh, msh, sm.a.v[el0], sm.a.dk[el0], sm.a.nc2);
+      if (el1 < ne) entry_dots<T, GM>(k1, v1, el1, j16, G, qsh, msh, sm.a.v[el1], sm.a.dk[el1], sm.a.nc2);
     }
-  }
-  float qn_mine = 1.0f, qmu_mine = 0.0f;  // |q_h| and q_h.mu of head h = j16
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    float a = 0.0f, bq = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { a += qf[h][e] * qf[h][e]; bq += qf[h][e] * mv[e]; }
-    a = row16_sum(a);
-    bq = row16_sum(bq);
-    if (j16 == h) { qn_mine = sqrtf(a); qmu_mine = bq; }
-  }
-
-  float m[GM], lsum[GM], o[GM][8];
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    m[h] = -INFINITY;
-    lsum[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.0f;
-  }
-
-  const T *Ku = Kc + u * cap * D + 8 * j16;
-  const T *Vu = Vc + u * cap * D + 8 * j16;
-  Raw8<T> kr, vr;
-  int e = grp;
-  if (e < nu) {
-    const int64_t key = cbase + ukey[e];
-    kr.load(Ku + key * D);
-    vr.load(Vu + key * D);
-  }
-  for (; e < nu; e += 16) {
-    const uint32_t mk = umask[e];
-    float kv[8], vv[8];
-    kr.get(kv);
-    vr.get(vv);
-    if (e + 16 < nu) {  // prefetch the group's next entry
-      const int64_t key = cbase + ukey[e + 16];
-      kr.load(Ku + key * D);
-      vr.load(Vu + key * D);
-    }
-    float nc2 = 0.0f, dk[GM];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const float ct = kv[t] - mv[t];
-      nc2 += ct * ct;
-    }
-#pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      float a = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) a += qf[h][t] * kv[t];
-      dk[h] = row16_sum(a);
-    }
-    nc2 = row16_sum(nc2);
-    // lane h of the group computes head h's log-weight
-    float my_dk = dk[0];
-#pragma unroll
-    for (int h = 1; h < GM; ++h)
-      if (j16 == h) my_dk = dk[h];
+    __syncthreads();
+    // (b) log-weights, one thread per (entry, head) (ATT_E * GM <= 256), and
+    // this round's maximum per head (lanes of one head are GM apart)
+    const int pel = tid / GM, ph = tid % GM;
     float lw = -INFINITY;
-    if (j16 < G && ((mk >> j16) & 1u)) {
-      float lnP = 0.0f;
-      if (!(mk & FORCED)) {
-        const float den = qn_mine * sqrtf(nc2);
-        const float cosv = den > 0.0f ? (my_dk - qmu_mine) / den : 0.0f;
-        lnP = log_sampling_prob(cosv, K, L);
+    if (pel < ne && ph < G) {
+      const uint32_t mk = lmask[e0 + pel];
+      if ((mk >> ph) & 1u) {
+        const float dk = sm.a.dk[pel][ph];
+        float lnP = 0.0f;
+        if (!(mk & FORCED)) {
+          const float den = qn_sh[ph] * sqrtf(sm.a.nc2[pel]);
+          const float cosv = den > 0.0f ? (dk - qmu_sh[ph]) / den : 0.0f;
+          lnP = log_sampling_prob(cosv, K, L);
+        }
+        lw = dk * scale - lnP;
       }
-      lw = my_dk * scale - lnP;
     }
-    const int gbase = lane & ~15;
+    {
+      float m = lw;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        const float s = __shfl(lw, gbase + h);
-        if (s > -INFINITY) {
-          const float mn = fmaxf(m[h], s);
-          const float alpha = __expf(m[h] - mn);  // 0 when m = -inf
-          const float beta = __expf(s - mn);
-          lsum[h] = lsum[h] * alpha + beta;
+      for (int o = GM; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane < GM) sm.a.rmax[wave][lane] = m;
+    }
+    __syncthreads();
+    // new running maximum per head; probabilities relative to it
+    if (pel < ne && ph < G) {
+      const float M = fmaxf(fmaxf(hm[ph], fmaxf(sm.a.rmax[0][ph], sm.a.rmax[1][ph])),
+                            fmaxf(sm.a.rmax[2][ph], sm.a.rmax[3][ph]));
+      sm.a.pw[ph][pel] = lw > -INFINITY ? __expf(lw - M) : 0.0f;
+    }
+    float Mo = -INFINITY;
+    if (othread) {
+      const float mold = hm[oh];
+      Mo = fmaxf(fmaxf(mold, fmaxf(sm.a.rmax[0][oh], sm.a.rmax[1][oh])), fmaxf(sm.a.rmax[2][oh], sm.a.rmax[3][oh]));
+      const float alpha = mold > -INFINITY ? __expf(mold - Mo) : 0.0f;
+      ol *= alpha;
 #pragma unroll
-          for (int t = 0; t < 8; ++t) o[h][t] = o[h][t] * alpha + beta * vv[t];
-          m[h] = mn;
+      for (int i = 0; i < DPT; ++i) oacc[i] *= alpha;
+    }
+    __syncthreads();
+    // (c) fold the round into (l, o), four entries per vector read of pw
+    if (othread) {
+      for (int el = 0; el < ne; el += 4) {
+        const f32x4 p4 = *(const f32x4 *)&sm.a.pw[oh][el];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if (el + k < ne) {
+            ol += p4[k];
+            float vv[DPT];
+            ldv<T, DPT>(&sm.a.v[el + k][od], vv);
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) oacc[i] += p4[k] * vv[i];
+          }
         }
       }
+      om = Mo;
+      if (tid % TPH == 0) hm[oh] = Mo;
     }
+    __syncthreads();
   }
-
-  // merge the 4 groups of each wave (lanes xor 16, xor 32)
+  if (othread) {
+    float *rec = part + ((u * nchunks + c) * G + oh) * PSTRIDE;
 #pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < G) {
-#pragma unroll
-      for (int sh = 16; sh <= 32; sh <<= 1) {
-        const float m2 = __shfl_xor(m[h], sh);
-        const float l2 = __shfl_xor(lsum[h], sh);
-        const float mn = fmaxf(m[h], m2);
-        const float a = m[h] > -INFINITY ? __expf(m[h] - mn) : 0.0f;
-        const float bb = m2 > -INFINITY ? __expf(m2 - mn) : 0.0f;
-        lsum[h] = lsum[h] * a + l2 * bb;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const float o2 = __shfl_xor(o[h][t], sh);
-          o[h][t] = o[h][t] * a + o2 * bb;
-        }
-        m[h] = mn;
-      }
-    }
-  }
-  __syncthreads();  // red is reused below
-  float *wst = (float *)&red[0][0][0];  // [4 waves][GM][130]: m, l, o[128]
-#pragma unroll
-  for (int h = 0; h < GM; ++h) {
-    if (h < G && lane < 16) {
-      float *r = wst + (wave * GM + h) * 130;
-      if (lane == 0) { r[0] = m[h]; r[1] = lsum[h]; }
-#pragma unroll
-      for (int t = 0; t < 8; ++t) r[2 + 8 * lane + t] = o[h][t];
-    }
-  }
-  __syncthreads();
-  float *pout = part + (u * nchunks + c) * G * PSTRIDE;
-  for (int i = tid; i < G * D; i += 256) {
-    const int h = i / D, t = i % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, wst[(w * GM + h) * 130]);
-    float ls = 0.0f, os = 0.0f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = wst[(w * GM + h) * 130];
-      const float sc = mw > -INFINITY ? __expf(mw - M) : 0.0f;
-      ls += wst[(w * GM + h) * 130 + 1] * sc;
-      os += wst[(w * GM + h) * 130 + 2 + t] * sc;
-    }
-    float *rec = pout + h * PSTRIDE;
-    rec[4 + t] = os;
-    if (t == 0) {
-      rec[0] = M;
-      rec[1] = ls;
-      rec[2] = __builtin_bit_cast(float, hcnt[h]);
+    for (int i = 0; i < DPT; ++i) rec[4 + od + i] = oacc[i];
+    if (tid % TPH == 0) {
+      rec[0] = om;
+      rec[1] = ol;
+      rec[2] = __builtin_bit_cast(float, hcnt[oh]);
       rec[3] = 0.0f;
     }
   }
@@ -438,10 +533,10 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   const uint32_t one2 = 0x00010001u;
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
-#define MP_SAMPLE(T, GMV)                                                                                        \
-  sample_kernel<T, GMV><<<grid, 256, 0, s>>>((const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes,  \
-                                             Hq, Hkv, G, n, cap, K, L, nsh, nst, geo.chunk_tiles, geo.nchunks,  \
-                                             scale, one2, ws.part, ent, ent_cnt)
+#define MP_SAMPLE(T, GMV)                                                                                    \
+  sample_kernel<T, GMV><<<grid, 256, sizeof(uint32_t) * L * GMV, s>>>(                                       \
+      (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L, nsh, nst, \
+      geo.nchunks, scale, one2, ws.part, ent, ent_cnt)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \
@@ -463,16 +558,27 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
 }
 
 // --------------------------------------------------------------------------
-// Log-sum-exp merge of the per-chunk partials of one query head (one block
-// of 128 threads, one output dimension each), and, when idx is requested,
-// the ascending sampled-index list assembled from the chunks' union entries.
-__global__ __launch_bounds__(128) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
+// Log-sum-exp merge of the per-chunk partials of one query head (the
+// recursive-attention merge of Section 4.4): with M = max_c m_c,
+//   l = sum_c l_c e^{m_c - M},  out = sum_c o_c e^{m_c - M} / l,
+//   lse = M + ln l.
+// One block of 256 threads per head: the maximum is found first, then
+// thread (phase, j) accumulates dims 4j..4j+3 over chunks phase, phase+8,
+// ... (independent loads, so many are in flight), and the 8 phases are added
+// through LDS.  When idx is requested the block then assembles the
+// ascending sampled-index list from the chunks' union entries.
+constexpr int MERGE_PH = 16;  // chunk phases per head (x 32 threads of 4 dims = 512 threads)
+
+__global__ __launch_bounds__(512) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                     int64_t nchunks, int64_t chunk, float *__restrict__ out,
                                                     float *__restrict__ lse, int32_t *__restrict__ count,
                                                     int32_t *__restrict__ idx, int64_t cap,
                                                     const uint32_t *__restrict__ ent,
                                                     const int32_t *__restrict__ ent_cnt) {
-  __shared__ int wsum[2];
+  __shared__ f32x4 red_o[MERGE_PH][32];
+  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
+  __shared__ int red_c[MERGE_PH];
+  __shared__ int wsum[8];
   const int64_t bh = blockIdx.x;
   const int64_t b = bh / Hq, h = bh % Hq;
   const int64_t u = b * Hkv + h / G;
@@ -480,32 +586,64 @@ __global__ __launch_bounds__(128) void merge_kernel(const float *__restrict__ pa
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;
-  float M = -INFINITY;
-  for (int64_t ci = 0; ci < nchunks; ++ci) M = fmaxf(M, p0[ci * cs]);
-  float l = 0.0f, acc = 0.0f;
+
+  // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...,
+  // merged online (running maximum, rescaled sums); the loads of successive
+  // chunks do not depend on each other
+  const int ph = t >> 5, j = t & 31;
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int cnt = 0;
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
+#pragma unroll 4
+  for (int64_t ci = ph; ci < nchunks; ci += MERGE_PH) {
     const float *r = p0 + ci * cs;
+    const float mc = r[0], lc = r[1];
+    const f32x4 o4 = *(const f32x4 *)(r + 4 + 4 * j);
     cnt += __builtin_bit_cast(int, r[2]);
-    if (r[0] > -INFINITY) {
-      const float sc = __expf(r[0] - M);
-      l += r[1] * sc;
-      acc += r[4 + t] * sc;
+    if (mc > -INFINITY) {
+      const float mn = fmaxf(m, mc);
+      const float a = __expf(m - mn), bsc = __expf(mc - mn);  // a = 0 while m = -inf
+      l = l * a + lc * bsc;
+      acc = acc * a + o4 * bsc;
+      m = mn;
     }
   }
-  out[bh * D + t] = l > 0.0f ? acc / l : 0.0f;
-  if (t == 0) {
-    if (lse) lse[bh] = l > 0.0f ? M + logf(l) : -INFINITY;
-    if (count) count[bh] = cnt;
+  red_o[ph][j] = acc;
+  if (j == 0) {
+    red_m[ph] = m;
+    red_l[ph] = l;
+    red_c[ph] = cnt;
+  }
+  __syncthreads();
+  if (t < 32) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ls = 0.0f;
+    int cs_ = 0;
+#pragma unroll
+    for (int p = 0; p < MERGE_PH; ++p) {
+      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
+      o += red_o[p][t] * sc;
+      ls += red_l[p] * sc;
+      cs_ += red_c[p];
+    }
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+    *(f32x4 *)(out + bh * D + 4 * t) = o * inv;
+    if (t == 0) {
+      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
+      if (count) count[bh] = cs_;
+    }
   }
   if (!idx) return;
   int32_t *dst = idx + bh * cap;
   int base = 0;
   for (int64_t ci = 0; ci < nchunks; ++ci) {
     // clamp: stays inside the workspace even if the entries were not written
-    const int ne = min(max(ent_cnt[u * nchunks + ci], 0), (int)chunk);
-    const uint32_t *src = ent + (u * nchunks + ci) * chunk;
-    for (int e0 = 0; e0 < ne; e0 += 128) {
+    const int ne = min(max(ent_cnt[u * nchunks + ci], 0), (int)(2 * chunk));
+    const uint32_t *src = ent + (u * nchunks + ci) * (2 * chunk);
+    for (int e0 = 0; e0 < ne; e0 += 512) {
       const int e = e0 + t;
       uint32_t v = 0;
       bool f = false;
@@ -518,9 +656,10 @@ __global__ __launch_bounds__(128) void merge_kernel(const float *__restrict__ pa
       const int pre = __popcll(bal & lt);
       if (lane == 0) wsum[wave] = __popcll(bal);
       __syncthreads();
-      const int off = base + (wave ? wsum[0] : 0);
+      int off = base;
+      for (int w = 0; w < wave; ++w) off += wsum[w];
       if (f && off + pre < cap) dst[off + pre] = (int32_t)(ci * chunk + (v & 0xffffu));
-      base += wsum[0] + wsum[1];
+      for (int w = 0; w < 8; ++w) base += wsum[w];
       __syncthreads();
     }
   }
@@ -531,7 +670,7 @@ hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGe
   (void)n;
   (void)L;
   const int G = Hq / Hkv;
-  merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 128, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
+  merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 512, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
                                                                  lse, count, idx, cap, ws.ent, ws.ent_cnt);
   return hipGetLastError();
 }

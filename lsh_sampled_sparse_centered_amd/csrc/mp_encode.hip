@@ -155,19 +155,37 @@ __device__ inline uint32_t sign_bits16(const f32x16 &a) {
   return m;
 }
 
+// The kernel takes up to two independent row sets ("jobs", e.g. the keys to
+// append and the queries of a decode step) and maps its linear block index
+// onto (job, row block, unit, table group).
 template <typename T>
-__global__ __launch_bounds__(256, 2) void encode_kernel(
-    const T *__restrict__ in, int64_t in_su, int64_t in_si, const float *__restrict__ mu, int64_t mu_su,
-    int64_t mu_si, int64_t rows, const uint4 *__restrict__ wp, int K, int L, int tables_per_block,
-    uint16_t *__restrict__ out, int64_t out_su, int64_t out_si, int64_t out_sl, T *__restrict__ kcopy,
-    int64_t kc_su, int64_t kc_si, const T *__restrict__ vin, T *__restrict__ vcopy) {
+__global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
+                                                        int K, int L) {
   __shared__ uint4 wsh[2][ENC_TG * KSTEPS * 64];
+  const bool second = njobs > 1 && (int64_t)blockIdx.x >= j1.first_block;
+  const EncJob &jb = second ? j1 : j0;
+  const T *__restrict__ in = (const T *)jb.in;
+  const int64_t in_su = jb.in_su, in_si = jb.in_si;
+  const float *__restrict__ mu = jb.mu;
+  const int64_t mu_su = jb.mu_su, mu_si = jb.mu_si, rows = jb.rows;
+  uint16_t *__restrict__ out = jb.out;
+  const int64_t out_su = jb.out_su, out_si = jb.out_si, out_sl = jb.out_sl;
+  T *__restrict__ kcopy = (T *)jb.kcopy;
+  const int64_t kc_su = jb.kc_su, kc_si = jb.kc_si;
+  const T *__restrict__ vin = (const T *)jb.vin;
+  T *__restrict__ vcopy = (T *)jb.vcopy;
+  const int64_t local = (int64_t)blockIdx.x - jb.first_block;
+  const int zt = (int)(local % jb.tsplit);
+  const int64_t rest = local / jb.tsplit;
+  const int64_t rb = rest % jb.rblocks;
+  const int tables_per_block = jb.tpb;
+
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
-  const int64_t u = blockIdx.y;
-  const int64_t row_w = (int64_t)blockIdx.x * ENC_ROWS + wave * 64;  // first row of this wave
-  const int l0 = blockIdx.z * tables_per_block;
+  const int64_t u = rest / jb.rblocks;
+  const int64_t row_w = rb * ENC_ROWS + wave * 64;  // first row of this wave
+  const int l0 = zt * tables_per_block;
   const int l1 = min(L, l0 + tables_per_block);
-  const bool copy_rows = blockIdx.z == 0;  // table-split blocks share rows
+  const bool copy_rows = zt == 0;  // table-split blocks share rows
 
   // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.
   bf16x8 xb[2][KSTEPS];
@@ -292,29 +310,48 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(
 #undef MP_COMMIT
 }
 
+// Grid shape of one job.  Few rows: the tables are split over blocks so that
+// the projection pass runs on many compute units instead of one.
+static void plan_job(EncJob &j, int L, int64_t first_block) {
+  j.rblocks = (j.rows + ENC_ROWS - 1) / ENC_ROWS;
+  const int64_t blocks = j.rblocks * j.units;
+  int tsplit = 1;
+  if (blocks < 512) tsplit = (int)std::min<int64_t>((512 + blocks - 1) / blocks, (int64_t)L);
+  j.tpb = (L + tsplit - 1) / tsplit;
+  j.tsplit = (L + j.tpb - 1) / j.tpb;
+  j.first_block = first_block;
+}
+
+static int64_t job_blocks(const EncJob &j) { return j.rblocks * j.units * j.tsplit; }
+
+hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s) {
+  int64_t total = 0;
+  EncJob j[2];
+  int nj = 0;
+  for (int i = 0; i < njobs; ++i) {
+    if (jobs[i].units == 0 || jobs[i].rows == 0) continue;
+    j[nj] = jobs[i];
+    plan_job(j[nj], L, total);
+    total += job_blocks(j[nj]);
+    ++nj;
+  }
+  if (nj == 0) return hipSuccess;
+  if (nj == 1) j[1] = j[0];
+  const dim3 grid((unsigned)total);
+  if (dtype == 0)
+    encode_kernel<__bf16><<<grid, 256, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
+  else
+    encode_kernel<float><<<grid, 256, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
+  return hipGetLastError();
+}
+
 hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su,
                          int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
                          int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,
                          const void *vin, void *vcopy, hipStream_t s) {
-  if (units == 0 || rows == 0) return hipSuccess;
-  const int64_t rblocks = (rows + ENC_ROWS - 1) / ENC_ROWS;
-  // Few rows: split the tables over blocks so that the projection pass runs
-  // on many compute units instead of one.
-  int tsplit = 1;
-  const int64_t blocks = rblocks * units;
-  if (blocks < 512) tsplit = (int)std::min<int64_t>((512 + blocks - 1) / blocks, (int64_t)L);
-  int tpb = (L + tsplit - 1) / tsplit;
-  tsplit = (L + tpb - 1) / tpb;
-  dim3 grid((unsigned)rblocks, (unsigned)units, (unsigned)tsplit);
-  if (dtype == 0)
-    encode_kernel<__bf16><<<grid, 256, 0, s>>>((const __bf16 *)in, in_su, in_si, mu, mu_su, mu_si, rows,
-                                                (const uint4 *)Wp, K, L, tpb, out, out_su, out_si, out_sl,
-                                                (__bf16 *)kcopy, kc_su, kc_si, (const __bf16 *)vin, (__bf16 *)vcopy);
-  else
-    encode_kernel<float><<<grid, 256, 0, s>>>((const float *)in, in_su, in_si, mu, mu_su, mu_si, rows,
-                                               (const uint4 *)Wp, K, L, tpb, out, out_su, out_si, out_sl,
-                                               (float *)kcopy, kc_su, kc_si, (const float *)vin, (float *)vcopy);
-  return hipGetLastError();
+  EncJob j = make_job(in, in_su, in_si, mu, mu_su, mu_si, units, rows, out, out_su, out_si, out_sl, kcopy, kc_su,
+                      kc_si, vin, vcopy);
+  return launch_encode_jobs(dtype, &j, 1, Wp, K, L, s);
 }
 
 }  // namespace mp

@@ -50,7 +50,7 @@ struct DecodeWs {
   size_t bytes;
 };
 
-DecodeGeom decode_geom(int B, int Hkv, int64_t n, int64_t cap);
+DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap);
 DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L);
 
 // Launchers (defined in the .hip files); they return hipError_t of the launch.
@@ -58,6 +58,53 @@ hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t 
 hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, double *partial,
                         int nparts, float *kmean, hipStream_t s);
 int kmean_parts(int64_t n);
+// One encoder row set: row i of unit u is read at in + u*in_su + i*in_si
+// (elements), centred by mu + u*mu_su + i*mu_si when mu is set, and its code
+// of table l written to out + u*out_su + i*out_si + l*out_sl; when kcopy is
+// set the raw row (and vin's row) are also copied to kcopy/vcopy + u*kc_su +
+// i*kc_si.  The launcher fills the grid fields.
+struct EncJob {
+  const void *in;
+  int64_t in_su, in_si;
+  const float *mu;
+  int64_t mu_su, mu_si;
+  int64_t units, rows;
+  uint16_t *out;
+  int64_t out_su, out_si, out_sl;
+  void *kcopy;
+  int64_t kc_su, kc_si;
+  const void *vin;
+  void *vcopy;
+  int64_t rblocks, first_block;
+  int tsplit, tpb;
+};
+
+inline EncJob make_job(const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su, int64_t mu_si,
+                       int64_t units, int64_t rows, uint16_t *out, int64_t out_su, int64_t out_si, int64_t out_sl,
+                       void *kcopy, int64_t kc_su, int64_t kc_si, const void *vin, void *vcopy) {
+  EncJob j{};
+  j.in = in;
+  j.in_su = in_su;
+  j.in_si = in_si;
+  j.mu = mu;
+  j.mu_su = mu_su;
+  j.mu_si = mu_si;
+  j.units = units;
+  j.rows = rows;
+  j.out = out;
+  j.out_su = out_su;
+  j.out_si = out_si;
+  j.out_sl = out_sl;
+  j.kcopy = kcopy;
+  j.kc_su = kc_su;
+  j.kc_si = kc_si;
+  j.vin = vin;
+  j.vcopy = vcopy;
+  return j;
+}
+
+// Encodes up to two row sets in one launch.
+hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s);
 hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su,
                          int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
                          int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,

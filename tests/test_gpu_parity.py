@@ -149,7 +149,7 @@ def test_decode_static_ranges(name):
     _compare(w, ref, out, lse, idx, cnt, name + "+static")
 
 
-@pytest.mark.parametrize("n", [0, 1, 7, 511, 512, 513, 1025])
+@pytest.mark.parametrize("n", [0, 1, 7, 511, 512, 513, 1023, 1024, 1025, 1535, 2047])
 def test_decode_short_and_ragged_n(n):
     """Edge lengths: empty cache, a single key, tails around the 512-key scan tile."""
     w, lay, km, codes, margin, qc = case("llama8b_layer")
@@ -262,3 +262,42 @@ def test_append_then_decode(name):
     out, lse, idx, cnt = _run_decode(w, lay2, kmean_t, gcodes_t, qcodes)
     ref = oracle_decode(w, lay2, km, codes_o, qc)
     _compare(w, ref, out, lse, idx, cnt, name + "+append")
+
+
+@pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged", "tiny"])
+def test_decode_step_equals_separate_calls(name):
+    """mp_decode_step (append + query encode in one launch, sample, merge)
+    gives bit-identical caches, codes and outputs to mp_append +
+    mp_encode_queries + mp_decode_attn."""
+    w = CASES[name]
+    outs = []
+    for fused in (False, True):
+        lay = layer(w, seed=321)
+        Wp, kmean, gcodes = gpu_build(w, lay)
+        U, n, cap = w.batch * w.hkv, lay["n"], lay["cap"]
+        kn = torch.stack([synth.step_kv(321, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=1)[0]
+                          for u in range(U)]).cuda()
+        vn = torch.stack([synth.step_kv(321, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=1)[1]
+                          for u in range(U)]).cuda()
+        out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+        lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
+        cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+        idx = torch.full((w.batch, w.hq, cap), -3, dtype=torch.int32, device="cuda")
+        ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, w.L, "cuda")
+        if fused:
+            ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for e in ev:
+                e.record()
+            mp.mp_decode_step(kn, vn, lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, n, w.K, ws, out=out,
+                              lse=lse, idx=idx, count=cnt, n_static_head=2, sample_events=ev)
+            torch.cuda.synchronize()
+            assert ev[0].elapsed_time(ev[1]) >= 0.0
+        else:
+            mp.mp_append(kn, vn, lay["Kc"], lay["Vc"], n, kmean, Wp, w.K, w.L, gcodes)
+            mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, n + 1, w.K, 2, 0, out=out,
+                              lse=lse, idx=idx, count=cnt, ws=ws)
+            torch.cuda.synchronize()
+        outs.append([t.detach().cpu().contiguous().view(torch.uint8).numpy()
+                     for t in (lay["Kc"], lay["Vc"], gcodes, out, lse, idx, cnt)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
