@@ -58,11 +58,55 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle baseline budget (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run, both with "
+                         "--calib-copy-mib) into %s and exit" % os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
+
+
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str) -> dict:
+    """HBM bytes per sampling-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for the calibration
+    copy of calib_mib MiB (the largest __amd_rocclr_copyBuffer dispatch)."""
+    import csv
+
+    def per_kernel(path, counter):
+        samp, calib = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if "sample_kernel" in r["Kernel_Name"]:
+                    samp.append(v)
+                elif "copyBuffer" in r["Kernel_Name"]:
+                    calib.append(v)
+        if not samp or not calib:
+            raise SystemExit("%s: no sample_kernel or calibration-copy rows for %s" % (path, counter))
+        return sum(samp) / len(samp), max(calib), len(samp)
+
+    f_s, f_c, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_s, w_c, nw = per_kernel(write_csv, "WRITE_SIZE")
+    calib_bytes = calib_mib * (1 << 20)
+    fetch_scale = calib_bytes / (f_c * 1024.0)
+    write_scale = calib_bytes / (w_c * 1024.0)
+    fetch_b = f_s * 1024.0 * fetch_scale
+    write_b = w_s * 1024.0 * write_scale
+    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "bytes_per_launch": fetch_b + write_b,
+            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
+            "fetch_size_kib_per_launch": f_s, "write_size_kib_per_launch": w_s, "dispatches": [nf, nw],
+            "calibration": {"copy_mib": calib_mib, "fetch_size_kib": f_c, "write_size_kib": w_c,
+                            "fetch_scale": fetch_scale, "write_scale": write_scale}}
 
 
 def main() -> int:
     args = parse()
+    if args.traffic:
+        tr = traffic_from_counters(args.traffic[0], args.traffic[1], args.calib_copy_mib, args.workload)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(tr, f, indent=1)
+        print(json.dumps(tr))
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the sampled decode shards by (layer, sequence, KV head) with no "
@@ -201,11 +245,16 @@ def main() -> int:
 
     # ------------------------------------------------------------------ calibration copy (profiling runs only)
     if args.calib_copy_mib:
-        a = torch.empty(args.calib_copy_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        nb = args.calib_copy_mib * (1 << 20)
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        flush = torch.empty(2 * nb, dtype=torch.uint8, device=dev)
+        flush.fill_(2)  # evicts a from L2 and the last-level cache
         b = torch.empty_like(a)
-        a.fill_(1.0)
-        b.copy_(a)
         torch.cuda.synchronize()
+        b.copy_(a)  # one device-to-device copy of known size
+        torch.cuda.synchronize()
+        del flush
         log("calibration copy of %d MiB done" % args.calib_copy_mib)
 
     cpu = None

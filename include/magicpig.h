@@ -190,8 +190,10 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  * in one launch -- then sample and merge (as mp_decode_attn) over n + 1 keys
  * (n keys without an append).  Arguments as in mp_append and
  * mp_decode_attn; q codes are kept in ws.  sample_events is NULL or points
- * to two host hipEvent_t handles, recorded on the stream right before and
- * right after the sampling kernel (for callers that time it).
+ * to two host hipEvent_t handles that are attached to the sampling kernel's
+ * dispatch, so they record its own start and end (for callers that time it;
+ * with no keys to decode there is no such kernel and both are recorded back to
+ * back).
  * Errors: as mp_append and mp_decode_attn; MP_ERR_CAPACITY when appending
  * with n >= cap.
  */

@@ -210,12 +210,16 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
   jobs[nj++] = make_job(q, 0, D, nullptr, 0, 0, 1, (int64_t)B * Hq, w.qcodes, 0, L, 1, nullptr, 0, 0, nullptr,
                         nullptr);
   if (launch_encode_jobs(kv_dtype, jobs, nj, Wp, K, L, s) != hipSuccess) return MP_ERR_HIP;
+  // the events ride on the sampling kernel's dispatch (its own start and end)
   hipEvent_t *ev = (hipEvent_t *)sample_events;
-  if (ev && hipEventRecord(ev[0], s) != hipSuccess) return MP_ERR_HIP;
-  if (geo.nchunks > 0 && launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L,
-                                       n_static_head, n_static_tail, geo, w, idx != nullptr, s) != hipSuccess)
+  if (geo.nchunks > 0) {
+    if (launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, n_static_head,
+                      n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) !=
+        hipSuccess)
+      return MP_ERR_HIP;
+  } else if (ev && (hipEventRecord(ev[0], s) != hipSuccess || hipEventRecord(ev[1], s) != hipSuccess)) {
     return MP_ERR_HIP;
-  if (ev && hipEventRecord(ev[1], s) != hipSuccess) return MP_ERR_HIP;
+  }
   return hip_status(launch_merge(B, Hq, Hkv, nd, L, geo, w, out, lse, idx, cap, count, s));
 }
 

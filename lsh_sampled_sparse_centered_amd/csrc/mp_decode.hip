@@ -3,6 +3,8 @@
 // store, compaction of the keys that collide in at least two tables, the
 // importance weight exp(q.k/sqrt(d)) / P, split self-normalised attention and
 // the log-sum-exp merge of the splits (Section 4.4 "On-device cache").
+#include <hip/hip_ext.h>
+
 #include "mp_internal.h"
 
 namespace mp {
@@ -526,7 +528,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
-                         bool want_idx, hipStream_t s) {
+                         bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int G = Hq / Hkv;
   const dim3 grid((unsigned)geo.nchunks, (unsigned)geo.U);
   const float scale = 1.0f / sqrtf((float)D);
@@ -534,9 +536,9 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
 #define MP_SAMPLE(T, GMV)                                                                                    \
-  sample_kernel<T, GMV><<<grid, 256, sizeof(uint32_t) * L * GMV, s>>>(                                       \
-      (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L, nsh, nst, \
-      geo.nchunks, scale, one2, ws.part, ent, ent_cnt)
+  hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
+                        (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
+                        nsh, nst, geo.nchunks, scale, one2, ws.part, ent, ent_cnt)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \
@@ -554,124 +556,6 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
     MP_SAMPLE_G(float);
 #undef MP_SAMPLE_G
 #undef MP_SAMPLE
-  return hipGetLastError();
-}
-
-// --------------------------------------------------------------------------
-// Log-sum-exp merge of the per-chunk partials of one query head (the
-// recursive-attention merge of Section 4.4): with M = max_c m_c,
-//   l = sum_c l_c e^{m_c - M},  out = sum_c o_c e^{m_c - M} / l,
-//   lse = M + ln l.
-// One block of 256 threads per head: the maximum is found first, then
-// thread (phase, j) accumulates dims 4j..4j+3 over chunks phase, phase+8,
-// ... (independent loads, so many are in flight), and the 8 phases are added
-// through LDS.  When idx is requested the block then assembles the
-// ascending sampled-index list from the chunks' union entries.
-constexpr int MERGE_PH = 16;  // chunk phases per head (x 32 threads of 4 dims = 512 threads)
-
-__global__ __launch_bounds__(512) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
-                                                    int64_t nchunks, int64_t chunk, float *__restrict__ out,
-                                                    float *__restrict__ lse, int32_t *__restrict__ count,
-                                                    int32_t *__restrict__ idx, int64_t cap,
-                                                    const uint32_t *__restrict__ ent,
-                                                    const int32_t *__restrict__ ent_cnt) {
-  __shared__ f32x4 red_o[MERGE_PH][32];
-  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
-  __shared__ int red_c[MERGE_PH];
-  __shared__ int wsum[8];
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / Hq, h = bh % Hq;
-  const int64_t u = b * Hkv + h / G;
-  const int hg = (int)(h % G);
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
-  const int64_t cs = (int64_t)G * PSTRIDE;
-
-  // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...,
-  // merged online (running maximum, rescaled sums); the loads of successive
-  // chunks do not depend on each other
-  const int ph = t >> 5, j = t & 31;
-  float m = -INFINITY, l = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int cnt = 0;
-#pragma unroll 4
-  for (int64_t ci = ph; ci < nchunks; ci += MERGE_PH) {
-    const float *r = p0 + ci * cs;
-    const float mc = r[0], lc = r[1];
-    const f32x4 o4 = *(const f32x4 *)(r + 4 + 4 * j);
-    cnt += __builtin_bit_cast(int, r[2]);
-    if (mc > -INFINITY) {
-      const float mn = fmaxf(m, mc);
-      const float a = __expf(m - mn), bsc = __expf(mc - mn);  // a = 0 while m = -inf
-      l = l * a + lc * bsc;
-      acc = acc * a + o4 * bsc;
-      m = mn;
-    }
-  }
-  red_o[ph][j] = acc;
-  if (j == 0) {
-    red_m[ph] = m;
-    red_l[ph] = l;
-    red_c[ph] = cnt;
-  }
-  __syncthreads();
-  if (t < 32) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    float ls = 0.0f;
-    int cs_ = 0;
-#pragma unroll
-    for (int p = 0; p < MERGE_PH; ++p) {
-      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
-      o += red_o[p][t] * sc;
-      ls += red_l[p] * sc;
-      cs_ += red_c[p];
-    }
-    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
-    *(f32x4 *)(out + bh * D + 4 * t) = o * inv;
-    if (t == 0) {
-      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
-      if (count) count[bh] = cs_;
-    }
-  }
-  if (!idx) return;
-  int32_t *dst = idx + bh * cap;
-  int base = 0;
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    // clamp: stays inside the workspace even if the entries were not written
-    const int ne = min(max(ent_cnt[u * nchunks + ci], 0), (int)(2 * chunk));
-    const uint32_t *src = ent + (u * nchunks + ci) * (2 * chunk);
-    for (int e0 = 0; e0 < ne; e0 += 512) {
-      const int e = e0 + t;
-      uint32_t v = 0;
-      bool f = false;
-      if (e < ne) {
-        v = src[e];
-        f = (v >> (16 + hg)) & 1u;
-      }
-      const uint64_t bal = __ballot(f);
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const int pre = __popcll(bal & lt);
-      if (lane == 0) wsum[wave] = __popcll(bal);
-      __syncthreads();
-      int off = base;
-      for (int w = 0; w < wave; ++w) off += wsum[w];
-      if (f && off + pre < cap) dst[off + pre] = (int32_t)(ci * chunk + (v & 0xffffu));
-      for (int w = 0; w < 8; ++w) base += wsum[w];
-      __syncthreads();
-    }
-  }
-}
-
-hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
-                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s) {
-  (void)n;
-  (void)L;
-  const int G = Hq / Hkv;
-  merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 512, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
-                                                                 lse, count, idx, cap, ws.ent, ws.ent_cnt);
   return hipGetLastError();
 }
 

@@ -109,10 +109,13 @@ hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si
                          int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
                          int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,
                          const void *vin, void *vcopy, hipStream_t s);
+// When ev_start / ev_stop are set they are attached to the kernel's own
+// dispatch, so they time exactly this launch (no queue gap before it).
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
-                         bool want_idx, hipStream_t s);
+                         bool want_idx, hipStream_t s, hipEvent_t ev_start = nullptr,
+                         hipEvent_t ev_stop = nullptr);
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
                         float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s);
 

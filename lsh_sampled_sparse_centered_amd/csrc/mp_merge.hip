@@ -1,0 +1,144 @@
+// Log-sum-exp merge of the per-chunk partial results of the sampled decode
+// attention (MagicPIG, arXiv 2410.16179v2, Section 4.4 "On-device cache":
+// split attention whose splits are merged through their log-sum-exp).
+#include <math.h>
+
+#include "mp_internal.h"
+
+namespace mp {
+
+// --------------------------------------------------------------------------
+// Log-sum-exp merge of the per-chunk partials of one query head (the
+// recursive-attention merge of Section 4.4): with M = max_c m_c,
+//   l = sum_c l_c e^{m_c - M},  out = sum_c o_c e^{m_c - M} / l,
+//   lse = M + ln l.
+// One block of 1024 threads per head: thread (phase, j) owns dims 4j..4j+3 of
+// chunks phase, phase + 32, ...; it loads 8 of its chunk records at once (so
+// every load of a pass is in flight together), then folds them in with a
+// running maximum.  The 32 phases are combined through LDS.  When idx is
+// requested the block then assembles the ascending sampled-index list from
+// the chunks' union entries.
+constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
+constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
+
+__global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
+                                                     int64_t nchunks, int64_t chunk, float *__restrict__ out,
+                                                     float *__restrict__ lse, int32_t *__restrict__ count,
+                                                     int32_t *__restrict__ idx, int64_t cap,
+                                                     const uint32_t *__restrict__ ent,
+                                                     const int32_t *__restrict__ ent_cnt) {
+  __shared__ f32x4 red_o[MERGE_PH][32];
+  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
+  __shared__ int red_c[MERGE_PH];
+  __shared__ int wsum[16];
+  const int64_t bh = blockIdx.x;
+  const int64_t b = bh / Hq, h = bh % Hq;
+  const int64_t u = b * Hkv + h / G;
+  const int hg = (int)(h % G);
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
+  const int64_t cs = (int64_t)G * PSTRIDE;
+
+  // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...
+  // A pass loads MERGE_CPT records at once (independent loads), then merges
+  // them online (running maximum, rescaled sums).
+  const int ph = t >> 5, j = t & 31;
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int cnt = 0;
+  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
+    float mc[MERGE_CPT], lc[MERGE_CPT];
+    f32x4 oc[MERGE_CPT];
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const int64_t ci = c0 + (int64_t)k * MERGE_PH;
+      mc[k] = -INFINITY;
+      lc[k] = 0.0f;
+      oc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if (ci < nchunks) {
+        const float *r = p0 + ci * cs;
+        mc[k] = r[0];
+        lc[k] = r[1];
+        oc[k] = *(const f32x4 *)(r + 4 + 4 * j);
+        cnt += __builtin_bit_cast(int, r[2]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      if (mc[k] > -INFINITY) {
+        const float mn = fmaxf(m, mc[k]);
+        const float a = __expf(m - mn), bsc = __expf(mc[k] - mn);  // a = 0 while m = -inf
+        l = l * a + lc[k] * bsc;
+        acc = acc * a + oc[k] * bsc;
+        m = mn;
+      }
+    }
+  }
+  red_o[ph][j] = acc;
+  if (j == 0) {
+    red_m[ph] = m;
+    red_l[ph] = l;
+    red_c[ph] = cnt;
+  }
+  __syncthreads();
+  if (t < 32) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ls = 0.0f;
+    int cs_ = 0;
+#pragma unroll
+    for (int p = 0; p < MERGE_PH; ++p) {
+      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
+      o += red_o[p][t] * sc;
+      ls += red_l[p] * sc;
+      cs_ += red_c[p];
+    }
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+    *(f32x4 *)(out + bh * D + 4 * t) = o * inv;
+    if (t == 0) {
+      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
+      if (count) count[bh] = cs_;
+    }
+  }
+  if (!idx) return;
+  int32_t *dst = idx + bh * cap;
+  int base = 0;
+  for (int64_t ci = 0; ci < nchunks; ++ci) {
+    // clamp: stays inside the workspace even if the entries were not written
+    const int ne = min(max(ent_cnt[u * nchunks + ci], 0), (int)(2 * chunk));
+    const uint32_t *src = ent + (u * nchunks + ci) * (2 * chunk);
+    for (int e0 = 0; e0 < ne; e0 += 1024) {
+      const int e = e0 + t;
+      uint32_t v = 0;
+      bool f = false;
+      if (e < ne) {
+        v = src[e];
+        f = (v >> (16 + hg)) & 1u;
+      }
+      const uint64_t bal = __ballot(f);
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const int pre = __popcll(bal & lt);
+      if (lane == 0) wsum[wave] = __popcll(bal);
+      __syncthreads();
+      int off = base;
+      for (int w = 0; w < wave; ++w) off += wsum[w];
+      if (f && off + pre < cap) dst[off + pre] = (int32_t)(ci * chunk + (v & 0xffffu));
+      for (int w = 0; w < 16; ++w) base += wsum[w];
+      __syncthreads();
+    }
+  }
+}
+
+hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
+                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s) {
+  (void)n;
+  (void)L;
+  const int G = Hq / Hkv;
+  merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
+                                                                 lse, count, idx, cap, ws.ent, ws.ent_cnt);
+  return hipGetLastError();
+}
+
+}  // namespace mp
