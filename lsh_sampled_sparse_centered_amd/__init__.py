@@ -274,8 +274,9 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
                    n_static_tail: int = 0, sample_events=None, stream=None) -> torch.Tensor:
     """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
 
-    ``sample_events``: optional pair of recorded-once torch.cuda.Event objects,
-    re-recorded around the sampling kernel."""
+    ``sample_events``: optional pair of torch.cuda.Event objects (created with
+    timing and recorded once, so that their handles exist); they are attached
+    to the sampling kernel's dispatch and record its start and end."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     if k_new is not None:
         _need(k_new, Kc.dtype, (U, d), "k_new")

@@ -187,6 +187,48 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
   const int l1 = min(L, l0 + tables_per_block);
   const bool copy_rows = zt == 0;  // table-split blocks share rows
 
+  const int c0 = l0 * K, c1 = l1 * K;
+  const int t0 = c0 >> 5, t1 = (c1 + 31) >> 5;
+  const int skip = c0 - 32 * t0;
+  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
+  uint64_t q = 0;  // bit queue
+  int nb = 0;
+
+  // Projection tiles [tg, tg + ENC_TG) are staged global -> registers -> LDS.
+  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
+#define MP_FETCH(tg_)                                                        \
+  do {                                                                       \
+    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
+    const uint4 *src_ = wp + (int64_t)(tg_)*KSTEPS * 64 + threadIdx.x;       \
+    const int i_ = threadIdx.x;                                              \
+    if (i_ + 0 * 256 < cnt_) st0 = src_[0 * 256];                            \
+    if (i_ + 1 * 256 < cnt_) st1 = src_[1 * 256];                            \
+    if (i_ + 2 * 256 < cnt_) st2 = src_[2 * 256];                            \
+    if (i_ + 3 * 256 < cnt_) st3 = src_[3 * 256];                            \
+    if (i_ + 4 * 256 < cnt_) st4 = src_[4 * 256];                            \
+    if (i_ + 5 * 256 < cnt_) st5 = src_[5 * 256];                            \
+    if (i_ + 6 * 256 < cnt_) st6 = src_[6 * 256];                            \
+    if (i_ + 7 * 256 < cnt_) st7 = src_[7 * 256];                            \
+  } while (0)
+#define MP_COMMIT(buf_, tg_)                                                 \
+  do {                                                                       \
+    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
+    uint4 *dst_ = &wsh[buf_][threadIdx.x];                                   \
+    const int i_ = threadIdx.x;                                              \
+    if (i_ + 0 * 256 < cnt_) dst_[0 * 256] = st0;                            \
+    if (i_ + 1 * 256 < cnt_) dst_[1 * 256] = st1;                            \
+    if (i_ + 2 * 256 < cnt_) dst_[2 * 256] = st2;                            \
+    if (i_ + 3 * 256 < cnt_) dst_[3 * 256] = st3;                            \
+    if (i_ + 4 * 256 < cnt_) dst_[4 * 256] = st4;                            \
+    if (i_ + 5 * 256 < cnt_) dst_[5 * 256] = st5;                            \
+    if (i_ + 6 * 256 < cnt_) dst_[6 * 256] = st6;                            \
+    if (i_ + 7 * 256 < cnt_) dst_[7 * 256] = st7;                            \
+  } while (0)
+
+  // the first stage's loads are issued before the rows are read, so the two
+  // latencies overlap (this is what bounds small jobs)
+  if (K > 0) MP_FETCH(t0);
+
   // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.
   bf16x8 xb[2][KSTEPS];
 #pragma unroll
@@ -228,45 +270,6 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
     return;
   }
 
-  const int c0 = l0 * K, c1 = l1 * K;
-  const int t0 = c0 >> 5, t1 = (c1 + 31) >> 5;
-  const int skip = c0 - 32 * t0;
-  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
-  uint64_t q = 0;  // bit queue
-  int nb = 0;
-
-  // Projection tiles [tg, tg + ENC_TG) are staged global -> registers -> LDS.
-  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
-#define MP_FETCH(tg_)                                                        \
-  do {                                                                       \
-    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
-    const uint4 *src_ = wp + (int64_t)(tg_)*KSTEPS * 64 + threadIdx.x;       \
-    const int i_ = threadIdx.x;                                              \
-    if (i_ + 0 * 256 < cnt_) st0 = src_[0 * 256];                            \
-    if (i_ + 1 * 256 < cnt_) st1 = src_[1 * 256];                            \
-    if (i_ + 2 * 256 < cnt_) st2 = src_[2 * 256];                            \
-    if (i_ + 3 * 256 < cnt_) st3 = src_[3 * 256];                            \
-    if (i_ + 4 * 256 < cnt_) st4 = src_[4 * 256];                            \
-    if (i_ + 5 * 256 < cnt_) st5 = src_[5 * 256];                            \
-    if (i_ + 6 * 256 < cnt_) st6 = src_[6 * 256];                            \
-    if (i_ + 7 * 256 < cnt_) st7 = src_[7 * 256];                            \
-  } while (0)
-#define MP_COMMIT(buf_, tg_)                                                 \
-  do {                                                                       \
-    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
-    uint4 *dst_ = &wsh[buf_][threadIdx.x];                                   \
-    const int i_ = threadIdx.x;                                              \
-    if (i_ + 0 * 256 < cnt_) dst_[0 * 256] = st0;                            \
-    if (i_ + 1 * 256 < cnt_) dst_[1 * 256] = st1;                            \
-    if (i_ + 2 * 256 < cnt_) dst_[2 * 256] = st2;                            \
-    if (i_ + 3 * 256 < cnt_) dst_[3 * 256] = st3;                            \
-    if (i_ + 4 * 256 < cnt_) dst_[4 * 256] = st4;                            \
-    if (i_ + 5 * 256 < cnt_) dst_[5 * 256] = st5;                            \
-    if (i_ + 6 * 256 < cnt_) dst_[6 * 256] = st6;                            \
-    if (i_ + 7 * 256 < cnt_) dst_[7 * 256] = st7;                            \
-  } while (0)
-
-  MP_FETCH(t0);
   MP_COMMIT(0, t0);
   __syncthreads();
   int buf = 0;
