@@ -103,30 +103,56 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
     }
   }
   if (!idx) return;
+  // Index list: chunk c's keys of this head start at the sum of the earlier
+  // chunks' counts (their partial records hold them).  Chunks are taken 1024
+  // at a time: one exclusive scan of their counts, then each wave copies whole
+  // chunks (ballot + prefix count over the union entries, which are in key
+  // order within a chunk).
+  __shared__ int coff[1024];
   int32_t *dst = idx + bh * cap;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int base = 0;
-  for (int64_t ci = 0; ci < nchunks; ++ci) {
-    // clamp: stays inside the workspace even if the entries were not written
-    const int ne = min(max(ent_cnt[u * nchunks + ci], 0), (int)(2 * chunk));
-    const uint32_t *src = ent + (u * nchunks + ci) * (2 * chunk);
-    for (int e0 = 0; e0 < ne; e0 += 1024) {
-      const int e = e0 + t;
-      uint32_t v = 0;
-      bool f = false;
-      if (e < ne) {
-        v = src[e];
-        f = (v >> (16 + hg)) & 1u;
+  for (int64_t g0 = 0; g0 < nchunks; g0 += 1024) {
+    const int64_t ci = g0 + t;
+    const int c = ci < nchunks ? max(__builtin_bit_cast(int, p0[ci * cs + 2]), 0) : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    __syncthreads();  // wsum / coff of the previous group no longer read
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      wpre += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    coff[t] = base + wpre + incl - c;
+    base += tot;
+    __syncthreads();
+    const int ng = (int)min((int64_t)1024, nchunks - g0);
+    for (int k = wave; k < ng; k += 16) {
+      const int64_t cc = g0 + k;
+      // clamp: stays inside the workspace even if the entries were not written
+      const int ne = min(max(ent_cnt[u * nchunks + cc], 0), (int)(2 * chunk));
+      const uint32_t *src = ent + (u * nchunks + cc) * (2 * chunk);
+      int o = coff[k];
+      for (int e0 = 0; e0 < ne; e0 += 64) {
+        const int e = e0 + lane;
+        uint32_t v = 0;
+        bool f = false;
+        if (e < ne) {
+          v = src[e];
+          f = (v >> (16 + hg)) & 1u;
+        }
+        const uint64_t bal = __ballot(f);
+        const int pre = __popcll(bal & lt);
+        if (f && o + pre < cap) dst[o + pre] = (int32_t)(cc * chunk + (v & 0xffffu));
+        o += __popcll(bal);
       }
-      const uint64_t bal = __ballot(f);
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const int pre = __popcll(bal & lt);
-      if (lane == 0) wsum[wave] = __popcll(bal);
-      __syncthreads();
-      int off = base;
-      for (int w = 0; w < wave; ++w) off += wsum[w];
-      if (f && off + pre < cap) dst[off + pre] = (int32_t)(ci * chunk + (v & 0xffffu));
-      for (int w = 0; w < 16; ++w) base += wsum[w];
-      __syncthreads();
     }
   }
 }

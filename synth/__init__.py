@@ -31,7 +31,7 @@ from typing import Optional
 import numpy as np
 import torch
 
-_KINDS = {"mu": 1, "k": 2, "v": 3, "q": 4, "w": 5, "step_k": 6, "step_v": 7, "step_q": 8}
+_KINDS = {"mu": 1, "k": 2, "v": 3, "q": 4, "w": 5, "step_k": 6, "step_v": 7, "step_q": 8, "codes": 9}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -146,6 +146,15 @@ def step_kv(seed: int, layer: int, b: int, head: int, d: int, dtype: torch.dtype
 def projections(seed: int, layer: int, d: int, K: int, L: int, device="cpu") -> torch.Tensor:
     """Gaussian projection matrix ``W[d][K*L]`` (fp32) of one layer."""
     return randn((d, K * L), stream_seed(seed, "w", layer), device)
+
+
+def unit_codes(seed: int, layer: int, b: int, head: int, K: int, L: int, cap: int, device="cpu") -> torch.Tensor:
+    """Uniform random table codes ``[L][cap]`` (int32 values in [0, 2^K)) for one unit.
+
+    Tests inject them into a code store, on both sides, when the decode is
+    checked independently of how codes were made."""
+    g = _gen(device, stream_seed(seed, "codes", layer, b, head))
+    return torch.randint(0, 1 << K, (L, cap), generator=g, device=device, dtype=torch.int32)
 
 
 def layer_inputs(w: Workload, seed: int, layer: int, device="cpu", n: Optional[int] = None,

@@ -2,19 +2,24 @@
 benchmark times (one ``mp_decode_step`` per layer: append, query encode,
 sample, merge).
 
-The inputs are generated on the device (seeded, by ``synth``); the oracle
-recomputes a sample of units one by one from copies of those inputs:
+Inputs are generated on the device by ``synth`` (seeded).  The oracle gets
+its own copies of them by regenerating each unit from ``synth``; nothing it
+reads comes from memory the HIP path writes.  Checked per layer:
 
-* key means bitwise, codes up to the rounding band (the oracle's margins);
-* the appended key's codes, and the query codes, up to the band;
-* for every sampled unit whose appended and query codes equal the oracle's,
-  the step's own outputs, lse and counts (out within 2e-3, lse within 1e-3,
-  counts exact);
-* for every sampled unit, a decode with the oracle's query codes injected:
-  index lists exact, outputs within 2e-3.
+* key means of every unit, bitwise;
+* codes of a seeded 5% subset of units against the oracle's, up to the
+  rounding band; those units then decode with the oracle's codes, every other
+  unit with seeded uniform random codes (the same on both sides);
+* every appended key: cache rows exact, codes up to the band;
+* every query's codes up to the band;
+* outputs, lse and counts of the step itself for every checked unit whose
+  appended and query codes equal the oracle's (out within 2e-3, lse within
+  1e-3, counts exact);
+* a decode with the oracle's query codes injected: index lists exact and
+  outputs within 2e-3 for every checked unit.
 
-The code store of the sampled units holds the oracle's codes (injected after
-the build was compared), so both sides decode the same sets.
+Which units are checked at which step: every unit at the first and last
+step; at the steps in between, the code subset.
 """
 import numpy as np
 import pytest
@@ -30,6 +35,7 @@ pytestmark = pytest.mark.gpu
 OUT_TOL = 2e-3
 LSE_TOL = 1e-3
 SEED = 2024
+BATCH_UNITS = 64  # units per oracle batch (host memory)
 
 
 def _i16(a: np.ndarray) -> torch.Tensor:
@@ -46,153 +52,214 @@ def _say(msg):
     print("[gpu fullsize] " + msg, flush=True)
 
 
-class Store:
-    """One layer on the device plus the oracle's copy of the sampled units."""
+def code_subset(w, layers):
+    """Seeded 5% of the units of ``layers`` (at least one): list of (layer, unit)."""
+    U = w.batch * w.hkv
+    allu = [(l, u) for l in layers for u in range(U)]
+    k = max(1, round(0.05 * len(allu)))
+    pick = np.random.default_rng([SEED, w.L, len(allu)]).choice(len(allu), size=k, replace=False)
+    return sorted(allu[i] for i in pick)
 
-    def __init__(self, w, layer_idx, units):
-        self.w, self.layer_idx, self.units = w, layer_idx, list(units)
-        _say("%s layer %d: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d, sampled units %s" %
-             (w.name, layer_idx, w.batch, w.hq, w.hkv, w.n, w.K, w.L, self.units))
+
+class LayerRun:
+    """One layer on the device, decoded step by step, checked against the oracle."""
+
+    def __init__(self, w, layer_idx, code_units):
+        self.w, self.li = w, layer_idx
+        self.code_units = sorted(code_units)
         lay = synth.layer_inputs(w, SEED, layer_idx, device="cuda")
-        self.U, self.cap, self.n = w.batch * w.hkv, lay["cap"], lay["n"]
+        self.U, self.cap, self.n0 = w.batch * w.hkv, lay["cap"], lay["n"]
+        self.n = self.n0
         self.Kc = lay["K"].view(self.U, self.cap, w.d)
         self.Vc = lay["V"].view(self.U, self.cap, w.d)
-        self.q0 = lay["q"]
         self.Wh = lay["W"].cpu().numpy().copy()
         self.Wp = mp.mp_proj_pack(lay["W"], w.K, w.L)
-        self.kmean, self.codes = mp.mp_build_codes(self.Kc, self.n, self.Wp, w.K, w.L)
+        self.kmean, self.codes = mp.mp_build_codes(self.Kc, self.n0, self.Wp, w.K, w.L)
         self.c16 = self.codes.view(torch.int16)
         torch.cuda.synchronize()
-        # host copies of the sampled units (rows >= n are zero, as on the device)
-        self.hK = np.stack([host_f32(self.Kc[u]) for u in self.units])
-        self.hV = np.stack([host_f32(self.Vc[u]) for u in self.units])
+        self.kn_h, self.vn_h, self.app = [], [], []  # per step: [U][d] keys/values, [U][L] oracle codes
+        self.oracle_codes = {}  # unit -> oracle codes [L][cap] of the build (code subset)
+        self.km_o = np.zeros((self.U, w.d), np.float32)
+        self.ws = mp.decode_workspace(w.batch, w.hq, w.hkv, self.cap, w.L, "cuda")
+        _say("%s layer %d: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d; code subset %s" %
+             (w.name, layer_idx, w.batch, w.hq, w.hkv, w.n, w.K, w.L, self.code_units))
 
+    # ------------------------------------------------------------ host inputs
+    def host_kv(self, u):
+        """Keys and values of unit u as the oracle sees them: regenerated from
+        synth, with the appended rows of the steps so far."""
+        w = self.w
+        b, h = divmod(u, w.hkv)
+        k, v = synth.unit_kv(SEED, self.li, b, h, self.n0, w.d, w.torch_dtype, device="cuda")
+        K = np.zeros((self.cap, w.d), np.float32)
+        V = np.zeros((self.cap, w.d), np.float32)
+        K[:self.n0], V[:self.n0] = host_f32(k), host_f32(v)
+        for s, (kn, vn) in enumerate(zip(self.kn_h, self.vn_h)):
+            K[self.n0 + s], V[self.n0 + s] = kn[u], vn[u]
+        return K, V
+
+    def host_codes(self, u):
+        """The code store of unit u as the oracle sees it."""
+        w = self.w
+        if u in self.oracle_codes:
+            c = self.oracle_codes[u].copy()
+        else:
+            b, h = divmod(u, w.hkv)
+            c = synth.unit_codes(SEED, self.li, b, h, w.K, w.L, self.cap, device="cuda").cpu().numpy()
+            c = c.astype(np.uint16)
+        for s, a in enumerate(self.app):
+            c[:, self.n0 + s] = a[u]
+        return c
+
+    # ------------------------------------------------------------ build checks
     def check_build_and_inject(self):
         w = self.w
-        km, codes, margin = oracle.build_codes(self.hK, self.n, self.Wh, w.K, w.L, with_margin=True)
-        gk = self.kmean[self.units].cpu().numpy()
-        assert np.array_equal(gk.view(np.uint32), km.view(np.uint32)), "key means differ"
-        g = np.stack([_u16(self.c16[u]) for u in self.units])
-        ndiff, nbad = code_mismatches_outside_band(g[:, :, :self.n].transpose(0, 2, 1).reshape(-1, w.L),
-                                                   codes[:, :, :self.n].transpose(0, 2, 1).reshape(-1, w.L),
-                                                   margin.reshape(-1, w.L))
-        _say("build: %d of %d sampled codes differ, %d outside the band" % (ndiff, g[:, :, :self.n].size, nbad))
-        assert nbad == 0
-        self.km_o, self.codes_o = km, codes
-        for i, u in enumerate(self.units):
-            self.c16[u].copy_(_i16(codes[i]))
+        gk = self.kmean.cpu().numpy()
+        for u in range(self.U):
+            b, h = divmod(u, w.hkv)
+            k, _ = synth.unit_kv(SEED, self.li, b, h, self.n0, w.d, w.torch_dtype, device="cuda")
+            self.km_o[u] = oracle.key_mean(host_f32(k))
+        bad = np.nonzero((gk.view(np.uint32) != self.km_o.view(np.uint32)).any(axis=1))[0]
+        assert len(bad) == 0, "key means differ in units %s" % bad[:10]
+        ndiff = total = 0
+        for u in self.code_units:
+            K, _ = self.host_kv(u)
+            km, codes, margin = oracle.build_codes(K[None], self.n0, self.Wh, w.K, w.L, with_margin=True)
+            assert np.array_equal(km[0].view(np.uint32), self.km_o[u].view(np.uint32))
+            g = _u16(self.c16[u])[:, :self.n0]
+            nd, nbad = code_mismatches_outside_band(g.T, codes[0][:, :self.n0].T, margin[0])
+            assert nbad == 0, (self.li, u, nbad)
+            ndiff, total = ndiff + nd, total + g.size
+            self.oracle_codes[u] = codes[0]
+        for u in range(self.U):
+            if u in self.oracle_codes:
+                self.c16[u].copy_(_i16(self.oracle_codes[u]))
+            else:
+                b, h = divmod(u, w.hkv)
+                self.c16[u].copy_(synth.unit_codes(SEED, self.li, b, h, w.K, w.L, self.cap, device="cuda"))
+        torch.cuda.synchronize()
+        _say("layer %d: %d key means bitwise; %d of %d subset codes differ, all inside the band" %
+             (self.li, self.U, ndiff, total))
 
-    def step_inputs(self, s):
-        """The key/value appended and the queries of decode step s (1-based), on the device."""
-        w = self.w
+    # ------------------------------------------------------------ one step
+    def step(self, s, check_units):
+        w, G = self.w, self.w.group
+        n = self.n
         kn = torch.empty(self.U, w.d, dtype=w.torch_dtype, device="cuda")
         vn = torch.empty_like(kn)
         q = torch.empty(w.batch, w.hq, w.d, dtype=w.torch_dtype, device="cuda")
-        G = w.group
         for b in range(w.batch):
             for h in range(w.hkv):
-                k1, v1 = synth.step_kv(SEED, self.layer_idx, b, h, w.d, w.torch_dtype, s, device="cuda")
-                kn[b * w.hkv + h] = k1
-                vn[b * w.hkv + h] = v1
-                q[b, h * G:(h + 1) * G] = synth.unit_queries(SEED, self.layer_idx, b, h, G, w.d, w.torch_dtype,
+                kn[b * w.hkv + h], vn[b * w.hkv + h] = synth.step_kv(SEED, self.li, b, h, w.d, w.torch_dtype, s,
+                                                                     device="cuda")
+                q[b, h * G:(h + 1) * G] = synth.unit_queries(SEED, self.li, b, h, G, w.d, w.torch_dtype,
                                                              device="cuda", step=s)
-        return kn, vn, q
-
-    def run_step(self, s, ws, check):
-        """One decode step through mp_decode_step at row n; checks the sampled units when ``check``."""
-        w, G = self.w, self.w.group
-        n = self.n
-        kn, vn, q = self.step_inputs(s)
         out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
         lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
         cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
-        mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, ws, out=out,
-                          lse=lse, count=cnt)
+        mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, self.ws,
+                          out=out, lse=lse, count=cnt)
         torch.cuda.synchronize()
-        # the oracle's side of the append: raw rows and codes with the frozen mean
-        same_append = []
-        for i, u in enumerate(self.units):
-            kh, vh = host_f32(kn[u]), host_f32(vn[u])
-            assert torch.equal(self.Kc[u, n], kn[u]) and torch.equal(self.Vc[u, n], vn[u])
-            self.hK[i, n], self.hV[i, n] = kh, vh
-            ref, mg = oracle.encode(kh[None], self.Wh, w.K, w.L, mu=self.km_o[i], with_margin=True)
-            got = _u16(self.c16[u, :, n])[None]
-            ndiff, nbad = code_mismatches_outside_band(got, ref, mg)
+        assert torch.equal(self.Kc[:, n], kn) and torch.equal(self.Vc[:, n], vn)
+        # appended codes (frozen means) of every unit
+        knh, vnh = host_f32(kn), host_f32(vn)
+        got = _u16(self.c16[:, :, n])
+        app = np.zeros((self.U, w.L), np.uint16)
+        app_same = np.zeros(self.U, bool)
+        for u in range(self.U):
+            ref, mg = oracle.encode(knh[u][None], self.Wh, w.K, w.L, mu=self.km_o[u], with_margin=True)
+            nd, nbad = code_mismatches_outside_band(got[u][None], ref, mg)
             assert nbad == 0, (s, u)
-            same_append.append(ndiff == 0)
-            self.codes_o[i][:, n] = ref[0]
-            if ndiff:  # keep both stores identical for later steps
+            app[u], app_same[u] = ref[0], nd == 0
+            if nd:  # keep the stores identical for the later steps
                 self.c16[u, :, n] = _i16(ref[0])
+        self.kn_h.append(knh)
+        self.vn_h.append(vnh)
+        self.app.append(app)
         self.n = n + 1
-        if not check:
-            return
+        # query codes of every head
         qh = host_f32(q)
         gq = _u16(mp.mp_encode_queries(q, self.Wp, w.K, w.L).view(torch.int16))
-        o_out, o_lse, o_cnt = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
-        qc16 = _i16(gq)
-        refs = []
-        direct = 0
-        for i, u in enumerate(self.units):
-            b, h = divmod(u, w.hkv)
-            qu = qh[b, h * G:(h + 1) * G]
-            qref, qmg = oracle.encode(qu, self.Wh, w.K, w.L, with_margin=True)
-            ndiff, nbad = code_mismatches_outside_band(gq[b, h * G:(h + 1) * G], qref, qmg)
-            assert nbad == 0, (s, u)
-            qc16[b, h * G:(h + 1) * G] = _i16(qref)
-            ref = oracle.decode(qu[None], self.hK[i][None, None], self.hV[i][None, None], self.codes_o[i][None, None],
-                                self.km_o[i][None, None], self.Wh, w.K, w.L, self.n, qcodes=qref[None],
-                                want_idx=True)
-            refs.append((b, h, ref))
-            if ndiff == 0 and same_append[i]:
-                direct += 1
-                for g in range(G):
-                    hh = h * G + g
-                    assert int(o_cnt[b, hh]) == int(ref["count"][0, g]), (s, u, g)
-                    if ref["count"][0, g] == 0:
-                        continue
-                    assert np.max(np.abs(o_out[b, hh] - ref["out"][0, g])) <= OUT_TOL, (s, u, g)
-                    assert abs(float(o_lse[b, hh]) - float(ref["lse"][0, g])) <= LSE_TOL, (s, u, g)
-        # the same decode with the oracle's query codes, index lists included
+        qref, qmg = oracle.encode(qh.reshape(-1, w.d), self.Wh, w.K, w.L, with_margin=True)
+        qref = qref.reshape(w.batch, w.hq, w.L)
+        nd_q = gq != qref
+        assert code_mismatches_outside_band(gq.reshape(-1, w.L), qref.reshape(-1, w.L), qmg)[1] == 0, s
+        if not check_units:
+            return
+        # decode of the checked units with the oracle's query codes, index lists included
+        qc16 = _i16(qref)
         out2 = torch.empty_like(out)
         cnt2 = torch.empty_like(cnt)
         idx = torch.full((w.batch, w.hq, self.cap), -1, dtype=torch.int32, device="cuda")
         mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K,
-                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=ws)
+                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws)
         torch.cuda.synchronize()
-        worst, sizes = 0.0, []
-        for b, h, ref in refs:
-            for g in range(G):
-                hh = h * G + g
-                c = int(cnt2[b, hh])
-                assert c == int(ref["count"][0, g]), (s, b, hh)
-                assert np.array_equal(idx[b, hh, :c].cpu().numpy(), ref["idx"][0][g]), (s, b, hh)
-                sizes.append(c)
-                if c:
-                    err = float(np.max(np.abs(out2[b, hh].cpu().numpy() - ref["out"][0, g])))
+        o1, l1, c1 = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
+        o2, c2, ix = out2.cpu().numpy(), cnt2.cpu().numpy(), idx.cpu().numpy()
+        direct, worst, sizes = 0, 0.0, []
+        for i0 in range(0, len(check_units), BATCH_UNITS):
+            us = check_units[i0:i0 + BATCH_UNITS]
+            kv = [self.host_kv(u) for u in us]
+            bh = [divmod(u, w.hkv) for u in us]
+            ref = oracle.decode(np.stack([qh[b, h * G:(h + 1) * G] for b, h in bh]),
+                                np.stack([k for k, _ in kv])[:, None], np.stack([v for _, v in kv])[:, None],
+                                np.stack([self.host_codes(u) for u in us])[:, None], self.km_o[us][:, None],
+                                self.Wh, w.K, w.L, self.n, qcodes=np.stack([qref[b, h * G:(h + 1) * G] for b, h in bh]),
+                                want_idx=True)
+            for j, (u, (b, h)) in enumerate(zip(us, bh)):
+                own = app_same[u] and not nd_q[b, h * G:(h + 1) * G].any()
+                direct += int(own)
+                for g in range(G):
+                    hh = h * G + g
+                    rc = int(ref["count"][j, g])
+                    sizes.append(rc)
+                    assert int(c2[b, hh]) == rc, (s, u, g)
+                    assert np.array_equal(ix[b, hh, :rc], ref["idx"][j][g]), (s, u, g)
+                    if own:
+                        assert int(c1[b, hh]) == rc, (s, u, g)
+                    if rc == 0:
+                        assert np.all(o2[b, hh] == 0)
+                        continue
+                    err = float(np.max(np.abs(o2[b, hh] - ref["out"][j, g])))
                     worst = max(worst, err)
-                    assert err <= OUT_TOL, (s, b, hh, err)
-        _say("step %d (n=%d): %d/%d units checked on the step's own outputs; sets exact; worst |out - oracle| %.3g; "
-             "mean |S| %.0f" % (s, self.n, direct, len(self.units), worst, float(np.mean(sizes))))
+                    assert err <= OUT_TOL, (s, u, g, err)
+                    if own:
+                        assert np.max(np.abs(o1[b, hh] - ref["out"][j, g])) <= OUT_TOL, (s, u, g)
+                        assert abs(float(l1[b, hh]) - float(ref["lse"][j, g])) <= LSE_TOL, (s, u, g)
+        _say("layer %d step %d (n=%d): %d units checked (%d on the step's own outputs); sets exact; worst "
+             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, len(check_units), direct, worst,
+                                                     float(np.mean(sizes))))
 
 
-def _run(w, layer_idx, units, check_steps):
-    st = Store(w, layer_idx, units)
-    st.check_build_and_inject()
-    ws = mp.decode_workspace(w.batch, w.hq, w.hkv, st.cap, w.L, "cuda")
-    for s in range(1, max(check_steps) + 1):
-        st.run_step(s, ws, s in check_steps)
+def _run_layers(w, layers, steps=1, check_every=None):
+    subset = code_subset(w, layers)
+    for li in layers:
+        run = LayerRun(w, li, [u for l, u in subset if l == li])
+        run.check_build_and_inject()
+        allu = list(range(run.U))
+        sub = run.code_units
+        for s in range(1, steps + 1):
+            full = s in (1, steps)
+            run.step(s, allu if full else (sub if check_every and s % check_every == 0 else []))
+        del run
+        torch.cuda.empty_cache()
 
 
-def test_llama8b_96k_layer():
-    """Llama-3.1-8B shape at 96K context: one layer (32 q / 8 KV heads, K=10, L=150), one step."""
-    _run(synth.WORKLOADS["llama8b_96k"], layer_idx=5, units=[0, 3, 7], check_steps=[1])
+@pytest.mark.parametrize("part", range(4))
+def test_llama8b_96k_all_layers(part):
+    """Llama-3.1-8B shape at 96K context (32 q / 8 KV heads, K=10, L=150):
+    every unit of 8 of the 32 layers, one appending step."""
+    w = synth.WORKLOADS["llama8b_96k"]
+    _run_layers(w, list(range(8 * part, 8 * part + 8)))
 
 
-def test_codellama13b_b16_layer():
-    """CodeLlama-13B shape, batch 16, MHA (640 units, K=9, L=120), one step."""
-    _run(synth.WORKLOADS["codellama13b_b16"], layer_idx=0, units=[0, 7 * 40 + 23, 15 * 40 + 39], check_steps=[1])
+@pytest.mark.parametrize("layer_idx", [0, 39])
+def test_codellama13b_b16_layer(layer_idx):
+    """CodeLlama-13B shape, batch 16, MHA (640 units per layer, K=9, L=120), one appending step."""
+    _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx])
 
 
 def test_codellama34b_b4_64_steps():
-    """CodeLlama-34B shape, batch 4, GQA 8 (K=10, L=240): build, then 64 appending decode steps."""
-    _run(synth.WORKLOADS["codellama34b_b4"], layer_idx=0, units=[0, 13, 31], check_steps=[1, 2, 33, 64])
+    """CodeLlama-34B shape, batch 4, GQA 8 (K=10, L=240): build, then 64 appending steps; every unit
+    at steps 1 and 64, the code subset at every other step."""
+    _run_layers(synth.WORKLOADS["codellama34b_b4"], [0], steps=64, check_every=1)
