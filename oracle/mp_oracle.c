@@ -16,7 +16,7 @@
  *   sampling prob.    Section 4.3, Equations 10 and 11
  *   estimator         Section 4.3, Equations 9 and 11; Algorithm 1
  *
- * Readings the pages leave open (each one is listed in the design doc):
+ * Readings taken where the pages leave a step open:
  *   - encoder inputs are rounded to bf16 (the GPU GEMM precision):
  *     x = bf16(fp32(k) - mu), w = bf16(W[:, j]), y = bf16(q); queries are not
  *     centred; the projection z = x.w is evaluated exactly (fp64);
