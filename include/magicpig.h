@@ -32,7 +32,8 @@
  *  - Shapes: d (head dimension) must be 128.  0 <= K <= 16 bits per table,
  *    2 <= L <= 512 tables, K*L <= 4096.  Query heads per KV head
  *    G = Hq / Hkv must divide exactly and be at most 8.  Cache capacities
- *    `cap` must be multiples of 8 (16-byte code rows).
+ *    `cap` must be multiples of 8 (16-byte code rows).  Units U = B * Hkv
+ *    at most 65535, and U * ceil(cap / 512) at most 2^23 for the decode.
  *  - Element types: MP_BF16 (bfloat16) or MP_F32 (float32) for keys, values
  *    and queries; codes are uint16; means, outputs and lse are float32.
  *  - Layouts (row-major, innermost last):

@@ -22,7 +22,7 @@ int check_heads(int B, int Hq, int Hkv) {
   if (B < 1 || Hq < 1 || Hkv < 1) return MP_ERR_ARG;
   if (Hq % Hkv != 0) return MP_ERR_ARG;
   if (Hq / Hkv > MAX_G) return MP_ERR_UNSUPPORTED;
-  if ((int64_t)B * Hkv > 65535) return MP_ERR_UNSUPPORTED;  // grid.y
+  if ((int64_t)B * Hkv > 65535) return MP_ERR_UNSUPPORTED;  // grid.y of the key-mean kernels
   return MP_OK;
 }
 
@@ -37,7 +37,7 @@ const char *mp_strerror(int status) {
     case MP_OK: return "success";
     case MP_ERR_ARG: return "invalid argument (null pointer or inconsistent sizes)";
     case MP_ERR_UNSUPPORTED: return "unsupported shape (need d = 128, 0 <= K <= 16, 2 <= L <= 512, K*L <= 4096, "
-                                    "Hq/Hkv <= 8)";
+                                    "Hq/Hkv <= 8, B*Hkv <= 65535, B*Hkv*ceil(cap/512) <= 2^23)";
     case MP_ERR_CAPACITY: return "capacity exceeded (n outside [1, cap], or n >= cap on append)";
     case MP_ERR_WORKSPACE: return "workspace missing or too small";
     case MP_ERR_HIP: return "HIP kernel launch failed";
@@ -123,6 +123,8 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
   if ((st = check_heads(B, Hq, Hkv))) return st;
   if (!q || !Kc || !Vc || !codes || !kmean || cap < 1 || cap % 8 || nsh < 0 || nst < 0) return MP_ERR_ARG;
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
+  // one sampling block per 512-key tile per unit, in a 1-D grid of < 2^31 threads
+  if ((int64_t)B * Hkv * ((cap + SCAN_TILE - 1) / SCAN_TILE) > ((int64_t)1 << 23)) return MP_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
   return MP_OK;
 }

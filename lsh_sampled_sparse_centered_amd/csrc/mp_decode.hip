@@ -5,6 +5,8 @@
 // the log-sum-exp merge of the splits (Section 4.4 "On-device cache").
 #include <hip/hip_ext.h>
 
+#include <cmath>
+
 #include "mp_internal.h"
 
 namespace mp {
@@ -18,6 +20,18 @@ namespace mp {
 
 constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
 constexpr int ATT_E = 32;  // list entries per attention round
+
+LnPCoef lnp_coef(int L) {
+  LnPCoef c{};
+  double a = 1.0;  // C(L, 2+i) / C(L, 2), by the ratio C(L, k+1) / C(L, k) = (L-k)/(k+1)
+  for (int i = 0; i < LNP_TERMS; ++i) {
+    c.a[i] = (float)a;
+    const int k = 2 + i;
+    a = k < L ? a * (double)(L - k) / (double)(k + 1) : 0.0;
+  }
+  c.lnc2 = (float)std::log(0.5 * (double)L * (double)(L - 1));
+  return c;
+}
 
 // One 512-key tile per block.
 DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap) {
@@ -58,11 +72,14 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
 //   u = 1 - acos(c)/pi = acos(-c)/pi,  p = u^K,
 //   P = 1 - (1-p)^L - L p (1-p)^(L-1)   (at least two of L tables).
 // The closed form cancels for small p, so for L p < 1 it is summed as the
-// binomial tail from j = 2: ln P = ln C(L,2) + 2 ln p + (L-2) ln(1-p)
-// + ln(1 + sum_{j>2} t_j/t_2) with t_{j+1}/t_j = (L-j)/(j+1) * p/(1-p);
-// for L p >= 1 the closed form is evaluated as
+// binomial tail from j = 2:
+//   P = C(L,2) p^2 (1-p)^(L-2) * sum_i a_i r^i,  r = p/(1-p),
+//   a_i = C(L, 2+i) / C(L, 2),
+// with the a_i (i < LNP_TERMS) and ln C(L,2) computed on the host per L;
+// with L p < 1 the terms from i = 12 on are below 3e-11 of the sum.  For
+// L p >= 1 the closed form is evaluated as
 // ln(-expm1((L-1) ln(1-p) + ln(1 + (L-1) p))).
-__device__ inline float log_sampling_prob(float c, int K, int L) {
+__device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &cf) {
   if (K == 0) return 0.0f;  // p = 1: every table collides, P = 1
   c = fminf(1.0f, fmaxf(-1.0f, c));
   const float u = acosf(-c) * 0.318309886183790671538f;
@@ -71,13 +88,10 @@ __device__ inline float log_sampling_prob(float c, int K, int L) {
   const float Lf = (float)L;
   if (Lf * p < 1.0f) {
     const float r = p * __frcp_rn(1.0f - p);
-    float term = 1.0f, sum = 1.0f;
-    for (int j = 2; j < L && j < 40; ++j) {
-      term *= (float)(L - j) * __frcp_rn((float)(j + 1)) * r;
-      sum += term;
-      if (term < 1e-8f * sum) break;
-    }
-    return logf(0.5f * Lf * (Lf - 1.0f)) + 2.0f * lnp + (Lf - 2.0f) * log1pf(-p) + logf(sum);
+    float sum = cf.a[LNP_TERMS - 1];
+#pragma unroll
+    for (int i = LNP_TERMS - 2; i >= 0; --i) sum = fmaf(sum, r, cf.a[i]);
+    return cf.lnc2 + 2.0f * lnp + (Lf - 2.0f) * log1pf(-p) + __logf(sum);
   }
   return logf(-expm1f((Lf - 1.0f) * log1pf(-p) + log1pf((Lf - 1.0f) * p)));
 }
@@ -113,6 +127,7 @@ template <>
 struct Raw8<__bf16> {
   uint4 a;
   __device__ void load(const __bf16 *p) { a = *(const uint4 *)p; }
+  __device__ void zero() { a = uint4{0u, 0u, 0u, 0u}; }
   __device__ void get(float (&v)[8]) const {
     const bf16x8 b = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
@@ -124,6 +139,7 @@ template <>
 struct Raw8<float> {
   uint4 a, b;
   __device__ void load(const float *p) { a = *(const uint4 *)p; b = *(const uint4 *)(p + 4); }
+  __device__ void zero() { a = b = uint4{0u, 0u, 0u, 0u}; }
   __device__ void get(float (&v)[8]) const {
     const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
 #pragma unroll
@@ -142,35 +158,64 @@ __device__ inline void ldv(const T *p, float (&v)[N]) {
   for (int i = 0; i < N; ++i) v[i] = (float)p[i];
 }
 
-// One list entry in a 16-lane group (lane j16 holds elements 8*j16 .. +7):
-// stage the value row slice in LDS and reduce |k - mu|^2 and q_h.k (h < G)
-// over the row.  q and mu are read from LDS.
+// Two list entries in a 16-lane group (lane j16 holds elements 8*j16 .. +7
+// of each row): stage both value row slices in LDS, reduce |k - mu|^2 and
+// q_h.k over the rows (every lane ends with every sum), then lane j16 forms
+// the log-weight s - ln P of entry (j16 < 8 ? e0 : e1) for head j16 % 8, or
+// -inf when that head did not sample the key.  q, mu, |q_h| and q_h.mu come
+// from LDS.  The second entry is ignored when !ok1.
 template <typename T, int GM>
-__device__ inline void entry_dots(const Raw8<T> &kr, const Raw8<T> &vr, int el, int j16, int G,
-                                  const float (*qsh)[D], const float *msh, T *vrow, float *dk, float *nc2s) {
-  float kv[8], mv[8];
-  kr.get(kv);
-  vr.store(vrow + 8 * j16);
+__device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Raw8<T> &k1, const Raw8<T> &v1,
+                                  bool ok1, int e0, int e1, uint32_t mk0, uint32_t mk1, int j16, int G, int K, int L,
+                                  const LnPCoef &cf, float scale, const float (*qsh)[D], const float *msh,
+                                  const float *qn_sh, const float *qmu_sh, T (*vrows)[D], float (*lw)[ATT_E]) {
+  float kv0[8], kv1[8], mv[8];
+  k0.get(kv0);
+  k1.get(kv1);
+  v0.store(vrows[e0] + 8 * j16);
+  if (ok1) v1.store(vrows[e1] + 8 * j16);
   ld8<float>(msh + 8 * j16, mv);
-  float nc2 = 0.0f;
+  float n0 = 0.0f, n1 = 0.0f;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    const float ct = kv[t] - mv[t];
-    nc2 += ct * ct;
+    const float c0 = kv0[t] - mv[t], c1 = kv1[t] - mv[t];
+    n0 += c0 * c0;
+    n1 += c1 * c1;
   }
-  nc2 = row16_sum(nc2);
-  if (j16 == 0) nc2s[el] = nc2;
+  n0 = row16_sum(n0);
+  n1 = row16_sum(n1);
+  const int hh = j16 & 7;
+  const bool second = j16 >= 8;
+  float dk = 0.0f;
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     if (h < G) {
       float qv[8];
       ld8<float>(&qsh[h][8 * j16], qv);
-      float a = 0.0f;
+      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) a += qv[t] * kv[t];
-      a = row16_sum(a);
-      if (j16 == h) dk[h] = a;
+      for (int t = 0; t < 8; ++t) {
+        a0 += qv[t] * kv0[t];
+        a1 += qv[t] * kv1[t];
+      }
+      a0 = row16_sum(a0);
+      a1 = row16_sum(a1);
+      if (hh == h) dk = second ? a1 : a0;
     }
+  }
+  if (hh < G && (!second || ok1)) {
+    const uint32_t mk = second ? mk1 : mk0;
+    float w = -INFINITY;
+    if ((mk >> hh) & 1u) {
+      float lnP = 0.0f;
+      if (!(mk & FORCED)) {
+        const float den = qn_sh[hh] * sqrtf(second ? n1 : n0);
+        const float cosv = den > 0.0f ? (dk - qmu_sh[hh]) / den : 0.0f;
+        lnP = log_sampling_prob(cosv, K, L, cf);
+      }
+      w = dk * scale - lnP;
+    }
+    lw[hh][second ? e1 : e0] = w;
   }
 }
 
@@ -202,7 +247,7 @@ template <typename T, int GM>
 __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
-    int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2,
+    int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
     float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt) {
   // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
   // words [0, FW) says "at least one of this wave's tables matched", of
@@ -212,11 +257,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     uint32_t flg[4][64][2 * FW];
   };
   struct AttnLds {
-    T v[ATT_E][D];         // staged value rows of this round's entries
-    float dk[ATT_E][GM];   // q_h . k
-    float nc2[ATT_E];      // |k - mu|^2
-    float pw[GM][ATT_E];   // exp(s - ln P - M_h) of this round, head-major
-    float rmax[4][GM];     // per-wave maxima of this round's log-weights
+    T v[ATT_E][D];                         // staged value rows of this round's entries
+    alignas(16) float lw[GM][ATT_E];       // log-weights s - ln P (or -inf), head-major
   };
   __shared__ union {
     ScanLds s;
@@ -230,15 +272,16 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
   __shared__ uint16_t lmask[2 * SCAN_TILE];  // head bits | FORCED
   __shared__ int wtot[4];
   __shared__ int hcnt[GM];
-  __shared__ float hm[GM];  // running maximum of the log-weights per head
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
   const int j16 = lane & 15, grp = tid >> 4;
-  const int64_t u = blockIdx.y;
-  // Tiles run in reverse order within a unit, so that the short last tile is
-  // dispatched first and the blocks left over for a second round start early.
-  const int64_t c = nchunks - 1 - blockIdx.x;
+  // Blocks run tile-major: consecutive blocks take the same tile of
+  // consecutive units, so the units' short last tiles are dispatched last and
+  // are what a grid slightly larger than one round of blocks leaves over.
+  const int64_t U = (int64_t)gridDim.x / nchunks;
+  const int64_t u = blockIdx.x % U;
+  const int64_t c = blockIdx.x / U;
   const int64_t b = u / Hkv, kvh = u % Hkv;
   const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
   const int64_t tbase = c * SCAN_TILE;
@@ -257,7 +300,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
   const int64_t rstride = 8 * cap;  // bytes between this wave's consecutive tables
   const char *rows0 = (const char *)(codes + u * (int64_t)L * cap + (int64_t)wave * cap + tbase);
   uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
-#define MP_ROW(j) (*(const uint4 *)(rows0 + (int64_t)min((j), jlast) * rstride + lo))
+  // the code store is streamed once: non-temporal loads keep it from evicting
+  // the caches' reused lines (query codes, keys and values of the list)
+#define MP_ROW(j) \
+  __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)(rows0 + (int64_t)min((j), jlast) * rstride + lo)))
   uint4 cw[MP_SB];
   if (ntw > 0) {
 #pragma unroll
@@ -275,10 +321,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     qsh[h][t] = h < G ? (float)q[(qrow0 + h) * D + t] : 0.0f;
   }
   if (tid < D) msh[tid] = kmean[u * D + tid];
-  if (tid < GM) {
-    hcnt[tid] = 0;
-    hm[tid] = -INFINITY;
-  }
+  if (tid < GM) hcnt[tid] = 0;
   __syncthreads();
 
   for (int h = wave; h < GM; h += 4) {  // |q_h| and q_h . mu
@@ -436,81 +479,59 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     const int ne = min(ATT_E, nu - e0);
     static_assert(ATT_E == 32, "two entries per 16-lane group");
     const int el0 = grp, el1 = grp + 16;
-    {  // (a) both of a group's entries are loaded before either is used
+    if (el0 < ne) {  // (a) gather both entries, then dots and log-weights
+      const bool ok1 = el1 < ne;
       Raw8<T> k0, v0, k1, v1;
-      if (el0 < ne) {
-        const int64_t key = lkey[e0 + el0];
-        k0.load(Ku + key * D);
-        v0.load(Vu + key * D);
+      const int64_t key0 = lkey[e0 + el0];
+      k0.load(Ku + key0 * D);
+      v0.load(Vu + key0 * D);
+      uint32_t mk1 = 0;
+      if (ok1) {
+        const int64_t key1 = lkey[e0 + el1];
+        k1.load(Ku + key1 * D);
+        v1.load(Vu + key1 * D);
+        mk1 = lmask[e0 + el1];
+      } else {
+        k1.zero();
       }
-      if (el1 < ne) {
-        const int64_t key = lkey[e0 + el1];
-        k1.load(Ku + key * D);
-        v1.load(Vu + key * D);
-      }
-      if (el0 < ne) entry_dots<T, GM>(k0, v0, el0, j16, G, qsh, msh, sm.a.v[el0], sm.a.dk[el0], sm.a.nc2);
-      if (el1 < ne) entry_dots<T, GM>(k1, v1, el1, j16, G, qsh, msh, sm.a.v[el1], sm.a.dk[el1], sm.a.nc2);
+      entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[e0 + el0], mk1, j16, G, K, L, cf, scale, qsh, msh,
+                        qn_sh, qmu_sh, sm.a.v, sm.a.lw);
     }
     __syncthreads();
-    // (b) log-weights, one thread per (entry, head) (ATT_E * GM <= 256), and
-    // this round's maximum per head (lanes of one head are GM apart)
-    const int pel = tid / GM, ph = tid % GM;
-    float lw = -INFINITY;
-    if (pel < ne && ph < G) {
-      const uint32_t mk = lmask[e0 + pel];
-      if ((mk >> ph) & 1u) {
-        const float dk = sm.a.dk[pel][ph];
-        float lnP = 0.0f;
-        if (!(mk & FORCED)) {
-          const float den = qn_sh[ph] * sqrtf(sm.a.nc2[pel]);
-          const float cosv = den > 0.0f ? (dk - qmu_sh[ph]) / den : 0.0f;
-          lnP = log_sampling_prob(cosv, K, L);
-        }
-        lw = dk * scale - lnP;
-      }
-    }
-    {
-      float m = lw;
-#pragma unroll
-      for (int o = GM; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
-      if (lane < GM) sm.a.rmax[wave][lane] = m;
-    }
-    __syncthreads();
-    // new running maximum per head; probabilities relative to it
-    if (pel < ne && ph < G) {
-      const float M = fmaxf(fmaxf(hm[ph], fmaxf(sm.a.rmax[0][ph], sm.a.rmax[1][ph])),
-                            fmaxf(sm.a.rmax[2][ph], sm.a.rmax[3][ph]));
-      sm.a.pw[ph][pel] = lw > -INFINITY ? __expf(lw - M) : 0.0f;
-    }
-    float Mo = -INFINITY;
+    // (b) each output thread folds the round into its head's running maximum
+    // m, normaliser l and output slice o (online softmax over the round)
     if (othread) {
-      const float mold = hm[oh];
-      Mo = fmaxf(fmaxf(mold, fmaxf(sm.a.rmax[0][oh], sm.a.rmax[1][oh])), fmaxf(sm.a.rmax[2][oh], sm.a.rmax[3][oh]));
-      const float alpha = mold > -INFINITY ? __expf(mold - Mo) : 0.0f;
-      ol *= alpha;
-#pragma unroll
-      for (int i = 0; i < DPT; ++i) oacc[i] *= alpha;
-    }
-    __syncthreads();
-    // (c) fold the round into (l, o), four entries per vector read of pw
-    if (othread) {
+      float mr = -INFINITY;
       for (int el = 0; el < ne; el += 4) {
-        const f32x4 p4 = *(const f32x4 *)&sm.a.pw[oh][el];
+        const f32x4 w4 = *(const f32x4 *)&sm.a.lw[oh][el];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (el + k < ne) {
-            ol += p4[k];
-            float vv[DPT];
-            ldv<T, DPT>(&sm.a.v[el + k][od], vv);
+        for (int k = 0; k < 4; ++k)
+          if (el + k < ne) mr = fmaxf(mr, w4[k]);
+      }
+      const float mn = fmaxf(om, mr);
+      if (mn > -INFINITY) {
+        const float alpha = __expf(om - mn);  // 0 while om = -inf
+        ol *= alpha;
 #pragma unroll
-            for (int i = 0; i < DPT; ++i) oacc[i] += p4[k] * vv[i];
+        for (int i = 0; i < DPT; ++i) oacc[i] *= alpha;
+        for (int el = 0; el < ne; el += 4) {
+          const f32x4 w4 = *(const f32x4 *)&sm.a.lw[oh][el];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (el + k < ne) {
+              const float pk = __expf(w4[k] - mn);  // 0 for -inf
+              ol += pk;
+              float vv[DPT];
+              ldv<T, DPT>(&sm.a.v[el + k][od], vv);
+#pragma unroll
+              for (int i = 0; i < DPT; ++i) oacc[i] += pk * vv[i];
+            }
           }
         }
+        om = mn;
       }
-      om = Mo;
-      if (tid % TPH == 0) hm[oh] = Mo;
     }
-    __syncthreads();
+    if (e0 + ATT_E < nu) __syncthreads();  // the next round reuses the staging
   }
   if (othread) {
     float *rec = part + ((u * nchunks + c) * G + oh) * PSTRIDE;
@@ -530,15 +551,16 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
                          int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int G = Hq / Hkv;
-  const dim3 grid((unsigned)geo.nchunks, (unsigned)geo.U);
+  const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
   const uint32_t one2 = 0x00010001u;
+  const LnPCoef cf = lnp_coef(L);
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
 #define MP_SAMPLE(T, GMV)                                                                                    \
   hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
-                        nsh, nst, geo.nchunks, scale, one2, ws.part, ent, ent_cnt)
+                        nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \

@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;          // supported head dimension
 constexpr int KSTEPS = D / 16;  // k-steps of one 32x32x16 bf16 matrix-core op over d
@@ -30,6 +31,15 @@ constexpr int SCAN_TILE = 512;  // keys per scan tile: 64 lanes x 8 keys (16 B o
 constexpr int PSTRIDE = 132;    // floats per partial record: m, l, count, pad, o[128]
 constexpr int MAX_G = 8;        // query heads per KV head handled by one pass
 constexpr int MAX_L = 512;
+
+// Series coefficients of the sampling probability for one L: a[i] =
+// C(L, 2+i) / C(L, 2) and lnc2 = ln C(L, 2) (filled on the host).
+constexpr int LNP_TERMS = 12;
+struct LnPCoef {
+  float a[LNP_TERMS];
+  float lnc2;
+};
+LnPCoef lnp_coef(int L);
 
 struct DecodeGeom {
   int64_t U;          // units = B * Hkv
