@@ -241,12 +241,6 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
       float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       if (ok) {
         load_row8<T>(in + u * in_su + r * in_si + d0, v);
-        if (kcopy && copy_rows) store_row8<T>(kcopy + u * kc_su + r * kc_si + d0, v);
-        if (vcopy && copy_rows) {
-          float w[8];
-          load_row8<T>(vin + u * in_su + r * in_si + d0, w);
-          store_row8<T>(vcopy + u * kc_su + r * kc_si + d0, w);
-        }
         if (mu) {
           float m[8];
           load8<float>(mu + u * mu_su + r * mu_si + d0, m);
@@ -256,6 +250,23 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) xb[nt][s][e] = (__bf16)v[e];  // round to nearest even
+    }
+  }
+
+  // appends: the first table block of each row block copies the raw key and
+  // value rows into the caches (16 bytes per thread and step; both loads
+  // before both stores, after the operand loads so those are not held up)
+  if (kcopy && vcopy && copy_rows) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    const int64_t r0 = rb * ENC_ROWS;
+    const int nr = (int)min((int64_t)ENC_ROWS, rows - r0);
+    for (int c = threadIdx.x; c < nr * CPR; c += 256) {
+      const int64_t r = r0 + c / CPR;
+      const int pc = c % CPR;
+      const uint4 kx = *(const uint4 *)((const char *)(in + u * in_su + r * in_si) + 16 * pc);
+      const uint4 vx = *(const uint4 *)((const char *)(vin + u * in_su + r * in_si) + 16 * pc);
+      *(uint4 *)((char *)(kcopy + u * kc_su + r * kc_si) + 16 * pc) = kx;
+      *(uint4 *)((char *)(vcopy + u * kc_su + r * kc_si) + 16 * pc) = vx;
     }
   }
 
@@ -313,6 +324,114 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
 #undef MP_COMMIT
 }
 
+// ---------------------------------------------------------------------------
+// Encoder for small jobs (at most 64 rows in all, e.g. the key appended per
+// unit and the queries of a decode step).  A block takes SM_TABLES tables of
+// one job; each of its 4 waves computes one of the (at most 3) tiles
+// covering those tables.  A wave reads its tile's A operands straight from
+// the packed projections (no LDS staging), holds all rows as the two 32-row
+// B operands, and writes the 32 sign bits of every row for the tile to LDS;
+// after one barrier each code is cut out of its row's bit string.  One memory
+// round trip for the rows and projections, one for the codes.
+constexpr int SM_TABLES = 4;                                   // tables per block
+constexpr int SM_MAXT = (SM_TABLES * 16 + 31 + 31) / 32;       // tiles a block touches (K <= 16)
+static_assert(SM_MAXT <= 4, "one tile per wave");
+
+template <typename T>
+__global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1, int njobs, int blocks0,
+                                                           const uint4 *__restrict__ wp, int K, int L) {
+  __shared__ uint32_t bits[64][SM_MAXT + 2];  // [row][tile - t0]
+  const bool second = njobs > 1 && (int)blockIdx.x >= blocks0;
+  const EncJob &jb = second ? j1 : j0;
+  const int lb = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int l0 = lb * SM_TABLES, l1 = min(L, l0 + SM_TABLES);
+  const int t0 = (l0 * K) >> 5, t1 = (l1 * K + 31) >> 5;
+  const int R = (int)(jb.units * jb.rows);  // rows of the job, flattened (<= 64)
+  const T *__restrict__ in = (const T *)jb.in;
+  T *__restrict__ kcopy = (T *)jb.kcopy;
+  const T *__restrict__ vin = (const T *)jb.vin;
+  T *__restrict__ vcopy = (T *)jb.vcopy;
+  // this wave's tile: its A operands are loaded first, so that their latency
+  // overlaps the row loads
+  const int t = t0 + wave;
+  const bool has_tile = t < t1;
+  uint4 a[KSTEPS];
+  if (has_tile) {
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) a[s] = wp[((int64_t)t * KSTEPS + s) * 64 + lane];
+  }
+
+  // B operands: row r = 32 nt + lane % 32 (unit r / rows, row r % rows), dims 16 s + 8 half + e
+  bf16x8 xb[2][KSTEPS];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = 32 * nt + (lane & 31);
+    const bool ok = r < R;
+    const int rows = (int)jb.rows;  // rows of a small job fit an int
+    const int64_t u = ok ? r / rows : 0, i = ok ? r % rows : 0;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+      const int d0 = 16 * s + 8 * half;
+      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok) {
+        load_row8<T>(in + u * jb.in_su + i * jb.in_si + d0, v);
+        if (jb.mu) {
+          float m[8];
+          load8<float>(jb.mu + u * jb.mu_su + i * jb.mu_si + d0, m);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] - m[e];  // fp32 subtraction
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[nt][s][e] = (__bf16)v[e];  // round to nearest even
+    }
+  }
+
+  // appends: block 0 copies the raw key and value rows into the caches (16
+  // bytes per thread and step; both loads before both stores)
+  if (kcopy && vcopy && lb == 0) {
+    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+    for (int c = threadIdx.x; c < R * CPR; c += 256) {
+      const int r = c / CPR, pc = c % CPR;
+      const int64_t u = r / (int)jb.rows, i = r % (int)jb.rows;
+      const uint4 kx = *(const uint4 *)((const char *)(in + u * jb.in_su + i * jb.in_si) + 16 * pc);
+      const uint4 vx = *(const uint4 *)((const char *)(vin + u * jb.in_su + i * jb.in_si) + 16 * pc);
+      *(uint4 *)((char *)(kcopy + u * jb.kc_su + i * jb.kc_si) + 16 * pc) = kx;
+      *(uint4 *)((char *)(vcopy + u * jb.kc_su + i * jb.kc_si) + 16 * pc) = vx;
+    }
+  }
+
+  const bool two = R > 32;
+  if (has_tile) {
+    f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]), xb[0][s], acc0, 0, 0, 0);
+    if (two) {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]), xb[1][s], acc1, 0, 0, 0);
+    }
+    const uint32_t m0 = sign_bits16(acc0), m1 = two ? sign_bits16(acc1) : 0u;
+    // lane l ends with the tile's 32 bits of row l (as in the large encoder)
+    const uint32_t send = half ? m0 : m1;
+    const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+    bits[lane][t - t0] = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+  }
+  __syncthreads();
+
+  // codes: table l of row r is bits [l K, l K + K) of the row's bit string
+  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
+  const int ntab = l1 - l0;
+  for (int idx = threadIdx.x; idx < R * ntab; idx += 256) {
+    const int r = idx / ntab, l = l0 + idx % ntab;
+    const int cb = l * K - 32 * t0;
+    const int w = cb >> 5, sh = cb & 31;
+    const uint64_t v = (uint64_t)bits[r][w] | ((uint64_t)bits[r][w + 1] << 32);
+    const int64_t u = r / (int)jb.rows, i = r % (int)jb.rows;
+    jb.out[u * jb.out_su + (int64_t)l * jb.out_sl + i * jb.out_si] = (uint16_t)((v >> sh) & kmask);
+  }
+}
+
 // Grid shape of one job.  Few rows: the tables are split over blocks so that
 // the projection pass runs on many compute units instead of one.
 static void plan_job(EncJob &j, int L, int64_t first_block) {
@@ -340,6 +459,17 @@ hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp
   }
   if (nj == 0) return hipSuccess;
   if (nj == 1) j[1] = j[0];
+  bool small = true;
+  for (int i = 0; i < nj; ++i) small = small && j[i].units * j[i].rows <= 64;
+  if (small) {
+    const int bpj = (L + SM_TABLES - 1) / SM_TABLES;
+    const dim3 g((unsigned)(bpj * nj));
+    if (dtype == 0)
+      encode_small_kernel<__bf16><<<g, 256, 0, s>>>(j[0], j[1], nj, bpj, (const uint4 *)Wp, K, L);
+    else
+      encode_small_kernel<float><<<g, 256, 0, s>>>(j[0], j[1], nj, bpj, (const uint4 *)Wp, K, L);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)total);
   if (dtype == 0)
     encode_kernel<__bf16><<<grid, 256, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
