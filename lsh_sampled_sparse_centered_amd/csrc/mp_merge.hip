@@ -15,9 +15,7 @@ namespace mp {
 // One block of 1024 threads per head: thread (phase, j) owns dims 4j..4j+3 of
 // chunks phase, phase + 32, ...; it loads 8 of its chunk records at once (so
 // every load of a pass is in flight together), then folds them in with a
-// running maximum.  The partial results are transposed through LDS so that
-// the phase becomes the low 5 lane bits, and the 32 phases are combined by a
-// butterfly of cross-lane shuffles.  When idx is
+// running maximum.  The 32 phases are combined through LDS.  When idx is
 // requested the block then assembles the ascending sampled-index list from
 // the chunks' union entries.
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
@@ -44,8 +42,7 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
   // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...
   // A pass loads MERGE_CPT records at once (independent loads), then merges
   // them online (running maximum, rescaled sums).
-  static_assert(MERGE_PH == 32, "32 phases x 32 dim groups");
-  const int ph = t >> 5, j = t & 31;  // a wave reads two whole records' output slices
+  const int ph = t >> 5, j = t & 31;
   float m = -INFINITY, l = 0.0f;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int cnt = 0;
@@ -77,8 +74,6 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
       }
     }
   }
-  // transpose through LDS so that the phase is the low 5 lane bits, then
-  // combine the 32 phases with a butterfly of cross-lane shuffles
   red_o[ph][j] = acc;
   if (j == 0) {
     red_m[ph] = m;
@@ -86,34 +81,25 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
     red_c[ph] = cnt;
   }
   __syncthreads();
-  {
-    const int q = t & 31, jj = t >> 5;  // phase q, dims 4jj..4jj+3
-    acc = red_o[q][jj];
-    m = red_m[q];
-    l = red_l[q];
-    cnt = red_c[q];
-  }
+  if (t < 32) {
+    float M = -INFINITY;
 #pragma unroll
-  for (int off = 1; off < MERGE_PH; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
-    f32x4 o2;
+    for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ls = 0.0f;
+    int cs_ = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) o2[e] = __shfl_xor(acc[e], off);
-    cnt += __shfl_xor(cnt, off);
-    const float mn = fmaxf(m, m2);
-    if (mn > -INFINITY) {
-      const float a = __expf(m - mn), bsc = __expf(m2 - mn);
-      l = l * a + l2 * bsc;
-      acc = acc * a + o2 * bsc;
-      m = mn;
+    for (int p = 0; p < MERGE_PH; ++p) {
+      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
+      o += red_o[p][t] * sc;
+      ls += red_l[p] * sc;
+      cs_ += red_c[p];
     }
-  }
-  if ((t & 31) == 0) {
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-    *(f32x4 *)(out + bh * D + 4 * (t >> 5)) = acc * inv;
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+    *(f32x4 *)(out + bh * D + 4 * t) = o * inv;
     if (t == 0) {
-      if (lse) lse[bh] = l > 0.0f ? m + logf(l) : -INFINITY;
-      if (count) count[bh] = cnt;
+      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
+      if (count) count[bh] = cs_;
     }
   }
   if (!idx) return;
