@@ -38,9 +38,12 @@ hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t 
 // ---------------------------------------------------------------------------
 // Key mean k_avg = (1/n) sum_i k_i per unit, accumulated in fp64 and rounded
 // once to fp32.  Stage 1: each block sums KM_ROWS rows of one unit
-// (16 lanes x 8 dims cover a row; 16 rows in flight per pass).  Stage 2: one
-// block per unit adds the stage-1 sums in block order (deterministic).
-constexpr int KM_ROWS = 2048;
+// (16 lanes x 8 dims cover a row; 16 x KM_UNR rows in flight per pass).
+// Stage 2: one block per unit adds the stage-1 sums in a fixed order
+// (deterministic).
+constexpr int KM_ROWS = 512;   // rows per block
+constexpr int KM_UNR = 4;      // rows a 16-lane group has in flight
+constexpr int KM_SLICES = 8;   // threads per dimension in the final sum
 
 int kmean_parts(int64_t n) { return (int)((n + KM_ROWS - 1) / KM_ROWS); }
 
@@ -69,11 +72,22 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict_
   const int64_t r0 = (int64_t)p * KM_ROWS, r1 = min(n, r0 + KM_ROWS);
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const T *base = Kc + u * cap * D + 8 * j16;
-  for (int64_t r = r0 + rsub; r < r1; r += 16) {
-    float v[8];
-    load8<T>(base + r * D, v);
+  for (int64_t r = r0 + rsub; r < r1; r += 16 * KM_UNR) {
+    float v[KM_UNR][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += (double)v[e];
+    for (int k = 0; k < KM_UNR; ++k) {  // independent loads first
+      const int64_t rk = r + 16 * k;
+      if (rk < r1) {
+        load8<T>(base + rk * D, v[k]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[k][e] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < KM_UNR; ++k)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (double)v[k][e];
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rsub][8 * j16 + e] = acc[e];
@@ -86,12 +100,30 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict_
   }
 }
 
-__global__ __launch_bounds__(D) void kmean_final_kernel(const double *__restrict__ partial, int nparts, int64_t n,
-                                                        float *__restrict__ kmean) {
+__global__ __launch_bounds__(D * KM_SLICES) void kmean_final_kernel(const double *__restrict__ partial, int nparts,
+                                                                   int64_t n, float *__restrict__ kmean) {
+  // thread (slice, dim) adds parts slice, slice + KM_SLICES, ... (four loads
+  // in flight), then the slices are added in slice order: a fixed order
+  __shared__ double red[KM_SLICES][D];
   const int64_t u = blockIdx.x;
-  double s = 0.0;
-  for (int p = 0; p < nparts; ++p) s += partial[(u * nparts + p) * D + threadIdx.x];
-  kmean[u * D + threadIdx.x] = (float)(s / (double)n);
+  const int dim = threadIdx.x % D, slice = threadIdx.x / D;
+  const double *p0 = partial + u * (int64_t)nparts * D + dim;
+  double s4[4] = {0, 0, 0, 0};
+  for (int p = slice; p < nparts; p += 4 * KM_SLICES) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int pk = p + k * KM_SLICES;
+      if (pk < nparts) s4[k] += p0[(int64_t)pk * D];
+    }
+  }
+  red[slice][dim] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  __syncthreads();
+  if (slice == 0) {
+    double s = 0.0;
+#pragma unroll
+    for (int k = 0; k < KM_SLICES; ++k) s += red[k][dim];
+    kmean[u * D + dim] = (float)(s / (double)n);
+  }
 }
 
 hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, double *partial,
@@ -101,7 +133,7 @@ hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int6
     kmean_partial_kernel<__bf16><<<g1, 256, 0, s>>>((const __bf16 *)Kc, n, cap, nparts, partial);
   else
     kmean_partial_kernel<float><<<g1, 256, 0, s>>>((const float *)Kc, n, cap, nparts, partial);
-  kmean_final_kernel<<<dim3((unsigned)U), D, 0, s>>>(partial, nparts, n, kmean);
+  kmean_final_kernel<<<dim3((unsigned)U), D * KM_SLICES, 0, s>>>(partial, nparts, n, kmean);
   return hipGetLastError();
 }
 
