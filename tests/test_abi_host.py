@@ -46,7 +46,7 @@ def test_size_queries():
     assert mp.mp_proj_bytes(64, 8, 75) == 0
     assert mp.mp_proj_bytes(128, 17, 75) == 0
     assert mp.mp_proj_bytes(128, 10, 1) == 0
-    assert mp.mp_build_ws_bytes(8, 16384) == 8 * 8 * 128 * 8
+    assert mp.mp_build_ws_bytes(8, 16384) == 8 * (16384 // 512) * 128 * 8  # fp64 partial sums per 512 keys
     a = mp.mp_decode_ws_bytes(1, 32, 8, 98368, 150)
     b = mp.mp_decode_ws_bytes(1, 32, 8, 2 * 98368, 150)
     assert 0 < a < b
