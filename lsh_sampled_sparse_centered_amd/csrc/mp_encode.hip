@@ -172,19 +172,37 @@ __device__ inline void store_row8<__bf16>(__bf16 *p, const float (&v)[8]) {
   *(bf16x8 *)p = a;
 }
 
-// Bit r of the result is (a[r] > 0): the fp32 pattern read as a signed
-// integer is positive exactly for positive, non-zero values (+0, -0 and
-// negatives give 0).  Each element is copied to a scalar before the bit cast.
+// Bit r of the result is (a[r] > 0) for every non-zero a[r]: the sign bits
+// are shifted in one per element (a funnel shift of (word, element) by 31,
+// from element 15 down to 0) and inverted.  Negative values and -0 give 0; +0 gives 1, which differs from
+// (a[r] > 0) only where the projection is exactly zero.  That is inside the
+// rounding band unless the projected row itself is zero, which the caller
+// handles (a zero row encodes to all-zero codes).  Each element is copied
+// to a scalar before the bit cast.
 __device__ inline uint32_t sign_bits16(const f32x16 &a) {
-  uint32_t m = 0;
+  uint32_t neg = 0;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 15; r >= 0; --r) {
     const float z = a[r];
-    const int32_t i = __builtin_bit_cast(int32_t, z);
-    const int32_t bit = __builtin_elementwise_min(__builtin_elementwise_max(i, 0), 1);
-    m |= (uint32_t)bit << r;
+    neg = __builtin_amdgcn_alignbit(neg, __builtin_bit_cast(uint32_t, z), 31u);  // (neg << 1) | sign(z)
   }
-  return m;
+  return ~neg & 0xffffu;
+}
+
+// 1 when the row held as B operands (xb[nt], this lane's half of the dims)
+// together with the partner lane's half has a non-zero element, per lane's
+// final row: lane l < 32 owns row l (nt = 0), lane l >= 32 owns row l (nt = 1).
+__device__ inline bool row_nonzero(const bf16x8 (&xb)[2][KSTEPS], int half) {
+  uint32_t nz0 = 0, nz1 = 0;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const uint4 a = __builtin_bit_cast(uint4, xb[0][s]), b = __builtin_bit_cast(uint4, xb[1][s]);
+    nz0 |= (a.x | a.y | a.z | a.w) & 0x7fff7fffu;  // -0 counts as zero
+    nz1 |= (b.x | b.y | b.z | b.w) & 0x7fff7fffu;
+  }
+  const uint32_t send = half ? nz0 : nz1;
+  const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
+  return ((half ? nz1 : nz0) | recv) != 0u;
 }
 
 // The kernel takes up to two independent row sets ("jobs", e.g. the keys to
@@ -303,6 +321,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
   }
 
   const int64_t my_row = row_w + lane;  // row whose 32-bit words this lane assembles
+  const bool my_nz = row_nonzero(xb, half);
   const bool my_ok = my_row < rows;
   uint16_t *my_out = out + u * out_su + my_row * out_si;
   int lt = l0;  // next table to emit
@@ -334,6 +353,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
       const uint32_t send = half ? m0 : m1;
       const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
       uint32_t word = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+      if (!my_nz) word = 0u;
       int nw = 32;
       if (tg + tt == t0 && skip) {
         word >>= skip;
@@ -435,6 +455,7 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
   }
 
   const bool two = R > 32;
+  const bool my_nz = row_nonzero(xb, half);
   if (has_tile) {
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -447,7 +468,8 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
     // lane l ends with the tile's 32 bits of row l (as in the large encoder)
     const uint32_t send = half ? m0 : m1;
     const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-    bits[lane][t - t0] = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+    const uint32_t word = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+    bits[lane][t - t0] = my_nz ? word : 0u;
   }
   __syncthreads();
 
