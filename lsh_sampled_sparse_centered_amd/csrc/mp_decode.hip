@@ -493,6 +493,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
         mk1 = lmask[e0 + el1];
       } else {
         k1.zero();
+        v1.zero();
       }
       entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[e0 + el0], mk1, j16, G, K, L, cf, scale, qsh, msh,
                         qn_sh, qmu_sh, sm.a.v, sm.a.lw);
