@@ -89,6 +89,34 @@ def test_query_codes(name):
     assert nbad == 0
 
 
+@pytest.mark.parametrize("rows", [5, 100])
+def test_zero_rows_encode_to_zero_codes(rows):
+    """A zero row projects to exactly 0 in every column, and (z > 0) is false:
+    all its codes are 0 (the oracle agrees), for the small-job (<= 64 rows)
+    and the large encoder alike.  An appended key equal to the frozen mean
+    (fp32 cache) is such a row after centring."""
+    w = variant("tiny", K=10, L=30)
+    lay = layer(w, seed=5)
+    Wp = mp.mp_proj_pack(lay["W"], w.K, w.L)
+    q = torch.randn(1, rows, w.d, generator=torch.Generator().manual_seed(3)).cuda()
+    q[0, 1] = 0.0
+    q[0, rows - 1] = -0.0
+    got = mp.mp_encode_queries(q, Wp, w.K, w.L).cpu().numpy().reshape(rows, w.L)
+    ref = oracle.encode(host_f32(q).reshape(rows, w.d), lay["host"]["W"], w.K, w.L)
+    assert np.all(ref[1] == 0) and np.all(ref[rows - 1] == 0)
+    assert np.all(got[1] == 0) and np.all(got[rows - 1] == 0)
+    _, nbad = code_mismatches_outside_band(got, ref, oracle.encode(host_f32(q).reshape(rows, w.d), lay["host"]["W"],
+                                                                   w.K, w.L, with_margin=True)[1])
+    assert nbad == 0
+    # append a key equal to the frozen mean: centred row = 0 -> codes 0
+    kmean, gcodes = mp.mp_build_codes(lay["Kc"], lay["n"], Wp, w.K, w.L)
+    n = lay["n"]
+    kn = kmean.clone()
+    mp.mp_append(kn, torch.zeros_like(kn), lay["Kc"], lay["Vc"], n, kmean, Wp, w.K, w.L, gcodes)
+    torch.cuda.synchronize()
+    assert int(np.abs(gcodes.view(torch.int16)[0, :, n].cpu().numpy().astype(np.int64)).sum()) == 0
+
+
 def _inject(w, lay, km, codes, qc):
     U = w.batch * w.hkv
     kmean = torch.from_numpy(km).cuda()
