@@ -156,7 +156,8 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
  *   count      nullable [B][Hq] int32: |S_h|
  *   ws         device workspace of mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)
  *              bytes (the same size for every n <= cap)
- * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_CAPACITY (n > cap or n < 1),
+ * Errors: MP_ERR_ARG, MP_ERR_UNSUPPORTED, MP_ERR_CAPACITY (n < 0 or n > cap; n = 0 is
+ * an empty cache),
  * MP_ERR_WORKSPACE, MP_ERR_HIP.
  */
 size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L);

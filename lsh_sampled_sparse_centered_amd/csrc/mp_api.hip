@@ -38,7 +38,7 @@ const char *mp_strerror(int status) {
     case MP_ERR_ARG: return "invalid argument (null pointer or inconsistent sizes)";
     case MP_ERR_UNSUPPORTED: return "unsupported shape (need d = 128, 0 <= K <= 16, 2 <= L <= 512, K*L <= 4096, "
                                     "Hq/Hkv <= 8, B*Hkv <= 65535, B*Hkv*ceil(cap/512) <= 2^23)";
-    case MP_ERR_CAPACITY: return "capacity exceeded (n outside [1, cap], or n >= cap on append)";
+    case MP_ERR_CAPACITY: return "capacity exceeded (n > cap, n < 1 for a build, n < 0 for a decode, or n >= cap on an append)";
     case MP_ERR_WORKSPACE: return "workspace missing or too small";
     case MP_ERR_HIP: return "HIP kernel launch failed";
     default: return "unknown status";

@@ -225,22 +225,27 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 // keeps several per compute unit and balances them dynamically.
 //
 // Scan: lane l of wave w reads 16 bytes (8 keys) of the codes of tables w,
-// w+4, w+8, ... and counts, for every head, the tables whose code differs
-// from the query's (xor, packed min with 1, add: two keys per 32-bit word,
-// two tables per add).  The four waves' counts are added through LDS; key i
-// is sampled for head h when L - mismatches >= 2.  Forced keys (the static
-// head/tail ranges) are sampled for every head with P = 1.
+// w+4, w+8, ... (non-temporal loads, eight rows in flight) and counts, for
+// every head, the tables whose code differs from the query's (xor, packed
+// min with 1, add: two keys per 32-bit word, two tables per add).  Each wave
+// turns its counts into "at least one" / "at least two of my tables
+// matched" flags; combined through LDS, key i is sampled for head h when some
+// wave has two matches or two waves have one (at least two of L tables).
+// Forced keys (the static head/tail ranges) are sampled for every head with
+// P = 1.
 //
 // Compaction: wave ballots + popcounts rank the keys, giving the tile's
 // union list (key, head mask) in LDS in ascending key order.
 //
 // Attention (Equations 9-11), in rounds of up to ATT_E list entries:
-//  (a) 16-lane groups gather an entry's key and value rows (8 elements per
-//      lane), reduce q_h.k and |k - mu|^2 and stage the value row in LDS;
-//  (b) one thread per (entry, head) forms the log-weight s - ln P, or -inf
-//      when the head did not sample the key;
-//  (c) one thread per (head, dims) folds the round into its running
-//      maximum m, normaliser l and unnormalised output o.
+//  (a) each 16-lane group gathers two entries' key and value rows (8
+//      elements per lane, all four loads in flight), stages the value rows in
+//      LDS, reduces q_h.k and |k - mu|^2, and its lanes form the log-weights
+//      s - ln P per (entry, head), or -inf where the head did not sample the
+//      key;
+//  (b) after one barrier, one thread per (head, dims) folds the round into
+//      its running maximum m, normaliser l and unnormalised output o (online
+//      softmax).
 // The query codes, queries and key mean are fetched while the first batch
 // of codes is in flight.  One partial record (m, l, count, o) per head.
 template <typename T, int GM>

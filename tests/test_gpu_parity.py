@@ -329,3 +329,35 @@ def test_decode_step_equals_separate_calls(name):
                      for t in (lay["Kc"], lay["Vc"], gcodes, out, lse, idx, cnt)])
     for a, b in zip(*outs):
         assert np.array_equal(a, b)
+
+
+def test_two_streams_with_own_workspaces_match_sequential():
+    """The library keeps no state: two decodes enqueued on two streams at
+    once, each with its own workspace, give the bytes of running them one
+    after the other."""
+    runs = []
+    for name in ("llama8b_layer", "g8_ragged"):
+        w, lay, km, codes, margin, qc = case(name)
+        kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+        runs.append((w, lay, kmean, gcodes, qcodes))
+
+    def launch(w, lay, kmean, gcodes, qcodes, stream):
+        out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+        cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+        idx = torch.full((w.batch, w.hq, lay["cap"]), -1, dtype=torch.int32, device="cuda")
+        ws = mp.decode_workspace(w.batch, w.hq, w.hkv, lay["cap"], w.L, "cuda")
+        torch.cuda.synchronize()
+        mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K,
+                          qcodes_in=qcodes, out=out, idx=idx, count=cnt, ws=ws, stream=stream)
+        return out, idx, cnt
+
+    seq = []
+    for r in runs:
+        seq.append(launch(*r, stream=torch.cuda.current_stream()))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    par = [launch(*r, stream=st) for r, st in zip(runs, streams)]
+    torch.cuda.synchronize()
+    for a, b in zip(seq, par):
+        for x, y in zip(a, b):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
