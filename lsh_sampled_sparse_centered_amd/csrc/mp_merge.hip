@@ -31,10 +31,14 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
   __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
   __shared__ int red_c[MERGE_PH];
   __shared__ int wsum[16];
-  const int64_t bh = blockIdx.x;
-  const int64_t b = bh / Hq, h = bh % Hq;
-  const int64_t u = b * Hkv + h / G;
-  const int hg = (int)(h % G);
+  // unit-minor order, as the sampling kernel's grid: block i serves unit
+  // i % U, so it runs on the same XCD as the blocks that wrote its partials
+  const int64_t U = (int64_t)gridDim.x / G;
+  const int64_t u = blockIdx.x % U;
+  const int hg = (int)(blockIdx.x / U);
+  const int64_t b = u / Hkv;
+  const int64_t h = (u % Hkv) * G + hg;
+  const int64_t bh = b * Hq + h;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;

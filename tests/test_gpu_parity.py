@@ -349,7 +349,7 @@ def test_two_streams_with_own_workspaces_match_sequential():
         torch.cuda.synchronize()
         mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K,
                           qcodes_in=qcodes, out=out, idx=idx, count=cnt, ws=ws, stream=stream)
-        return out, idx, cnt
+        return out, idx, cnt, ws  # ws stays referenced until the streams are synchronised
 
     seq = []
     for r in runs:
@@ -359,5 +359,5 @@ def test_two_streams_with_own_workspaces_match_sequential():
     par = [launch(*r, stream=st) for r, st in zip(runs, streams)]
     torch.cuda.synchronize()
     for a, b in zip(seq, par):
-        for x, y in zip(a, b):
+        for x, y in zip(a[:3], b[:3]):
             assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
