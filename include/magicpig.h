@@ -29,6 +29,11 @@
  *    once the stream has reached the point after the call.
  *  - Arguments are validated before anything is enqueued: a call that
  *    returns an error has written nothing.  No call aborts or prints.
+ *  - The kernels move data in 16-byte vectors: the K/V caches, new key and
+ *    value rows, queries, codes, kmean, the packed projection, out and the
+ *    workspace must start on a 16-byte boundary (every hipMalloc and torch
+ *    allocation does); a misaligned one is MP_ERR_ARG.  qcodes, lse, idx and
+ *    count need only their element alignment.
  *  - Shapes: d (head dimension) must be 128.  0 <= K <= 16 bits per table,
  *    2 <= L <= 512 tables, K*L <= 4096.  Query heads per KV head
  *    G = Hq / Hkv must divide exactly and be at most 8.  Cache capacities
@@ -60,7 +65,7 @@ extern "C" {
 
 /* Status codes returned by every int-returning entry point. */
 #define MP_OK 0
-#define MP_ERR_ARG (-1)         /* null or inconsistent argument            */
+#define MP_ERR_ARG (-1)         /* null, misaligned or inconsistent argument */
 #define MP_ERR_UNSUPPORTED (-2) /* shape outside the supported set          */
 #define MP_ERR_CAPACITY (-3)    /* n >= cap on append, or n > cap           */
 #define MP_ERR_WORKSPACE (-4)   /* workspace missing or smaller than needed */

@@ -28,6 +28,14 @@ int check_heads(int B, int Hq, int Hkv) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MP_OK : MP_ERR_HIP; }
 
+// The kernels move rows, code words, means and partials in 16-byte vectors.
+// Null passes (each entry point checks the pointers it requires separately).
+bool a16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+template <typename... P>
+bool all_a16(const P *...p) {
+  return (a16(p) && ...);
+}
+
 }  // namespace
 
 extern "C" {
@@ -35,7 +43,7 @@ extern "C" {
 const char *mp_strerror(int status) {
   switch (status) {
     case MP_OK: return "success";
-    case MP_ERR_ARG: return "invalid argument (null pointer or inconsistent sizes)";
+    case MP_ERR_ARG: return "invalid argument (null or misaligned pointer, or inconsistent sizes)";
     case MP_ERR_UNSUPPORTED: return "unsupported shape (need d = 128, 0 <= K <= 16, 2 <= L <= 512, K*L <= 4096, "
                                     "Hq/Hkv <= 8, B*Hkv <= 65535, B*Hkv*ceil(cap/512) <= 2^23)";
     case MP_ERR_CAPACITY: return "capacity exceeded (n > cap, n < 1 for a build, n < 0 for a decode, or n >= cap on an append)";
@@ -56,6 +64,7 @@ int mp_proj_pack(const float *W, int d, int K, int L, void *Wp, void *stream) {
   int st = check_shape(d, K, L);
   if (st) return st;
   if (K > 0 && (!W || !Wp)) return MP_ERR_ARG;
+  if (!all_a16(Wp)) return MP_ERR_ARG;
   return hip_status(launch_proj_pack(W, K, L, Wp, as_stream(stream)));
 }
 
@@ -70,6 +79,7 @@ int mp_build_codes(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t c
   if (st) return st;
   if ((st = check_dtype(kv_dtype))) return st;
   if (!Kc || !kmean || !codes || (K > 0 && !Wp) || U < 1 || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (!all_a16(Kc, Wp, kmean, codes, ws)) return MP_ERR_ARG;
   if (U > 65535) return MP_ERR_UNSUPPORTED;
   if (n < 1 || n > cap) return MP_ERR_CAPACITY;
   if (!ws || ws_bytes < mp_build_ws_bytes(U, n, d)) return MP_ERR_WORKSPACE;
@@ -89,6 +99,7 @@ int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_d
   if (!k_new || !v_new || !Kc || !Vc || !kmean || !codes || (K > 0 && !Wp) || U < 1 || cap < 1 || cap % 8 ||
       n < 0)
     return MP_ERR_ARG;
+  if (!all_a16(k_new, v_new, Kc, Vc, kmean, Wp, codes)) return MP_ERR_ARG;
   if (n >= cap) return MP_ERR_CAPACITY;
   const size_t es = kv_dtype == MP_BF16 ? 2 : 4;
   // one "unit" of U rows; row u has its own mean, cache row and code column
@@ -104,6 +115,7 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
   if (st) return st;
   if ((st = check_dtype(q_dtype))) return st;
   if (!q || !qcodes || (K > 0 && !Wp) || nq < 1) return MP_ERR_ARG;
+  if (!all_a16(q, Wp)) return MP_ERR_ARG;
   hipError_t e = launch_encode(q_dtype, q, 0, D, nullptr, 0, 0, 1, nq, Wp, K, L, qcodes, 0, L, 1, nullptr, 0, 0,
                                nullptr, nullptr, as_stream(stream));
   return hip_status(e);
@@ -122,6 +134,7 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
   if ((st = check_dtype(kv_dtype))) return st;
   if ((st = check_heads(B, Hq, Hkv))) return st;
   if (!q || !Kc || !Vc || !codes || !kmean || cap < 1 || cap % 8 || nsh < 0 || nst < 0) return MP_ERR_ARG;
+  if (!all_a16(q, Kc, Vc, codes, kmean, ws)) return MP_ERR_ARG;
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
   // one sampling block per 512-key tile per unit, in a 1-D grid of < 2^31 threads
   if ((int64_t)B * Hkv * ((cap + SCAN_TILE - 1) / SCAN_TILE) > ((int64_t)1 << 23)) return MP_ERR_UNSUPPORTED;
@@ -150,6 +163,7 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
   if (st) return st;
   if (d != D || L < 2 || L > MAX_L) return MP_ERR_UNSUPPORTED;
   if (!out || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (!all_a16(out, ws)) return MP_ERR_ARG;
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
   if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
@@ -166,6 +180,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
+  if (!all_a16(out, Wp)) return MP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
@@ -197,6 +212,7 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
+  if (!all_a16(out, Wp, k_new, v_new)) return MP_ERR_ARG;
   hipStream_t s = as_stream(stream);
   const int64_t U = (int64_t)B * Hkv;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, nd, cap);

@@ -75,6 +75,8 @@ def test_build_rejects_invalid_arguments():
     assert _build(n=129) == CAP
     assert _build(ws=None) == WS
     assert _build(wsb=16) == WS
+    for arg in ("Kc", "Wp", "km", "codes", "ws"):  # 16-byte vector loads and stores
+        assert _build(**{arg: FAKE + 8}) == ARG, arg
 
 
 def _append(**kw):
@@ -92,6 +94,8 @@ def test_append_rejects_invalid_arguments():
     assert _append(v=None) == ARG
     assert _append(d=256) == UNSUP
     assert _append(cap=129) == ARG
+    for arg in ("k", "v", "Kc", "Vc", "km", "Wp", "codes"):
+        assert _append(**{arg: FAKE + 4}) == ARG, arg
 
 
 def _decode(**kw):
@@ -117,6 +121,8 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(wsb=100) == WS
     assert _decode(d=96) == UNSUP
     assert _decode(B=70000, Hq=8, Hkv=8) == UNSUP
+    for arg in ("q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
+        assert _decode(**{arg: FAKE + 2}) == ARG, arg
 
 
 def test_decode_stages_reject_invalid_arguments():
@@ -133,3 +139,26 @@ def test_encode_queries_rejects_invalid_arguments():
     assert L.mp_encode_queries(FAKE, 3, 4, 128, FAKE, 8, 75, FAKE, None) == ARG
     assert L.mp_encode_queries(FAKE, 0, 4, 128, FAKE, 8, 513, FAKE, None) == UNSUP
     assert L.mp_proj_pack(None, 128, 8, 75, FAKE, None) == ARG
+    assert L.mp_proj_pack(FAKE, 128, 8, 75, FAKE + 8, None) == ARG
+    assert L.mp_encode_queries(FAKE + 8, 0, 4, 128, FAKE, 8, 75, FAKE, None) == ARG
+
+
+def _step(**kw):
+    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100,
+             cap=128, d=128, K=8, L=75, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return mp.lib().mp_decode_step(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"],
+                                   a["B"], a["Hq"], a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["nsh"],
+                                   a["nst"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None, None)
+
+
+def test_step_rejects_invalid_arguments():
+    assert _step(v=None) == ARG
+    assert _step(n=128) == CAP  # no room for the appended row
+    assert _step(n=-1) == CAP
+    assert _step(Wp=None) == ARG
+    assert _step(out=None) == ARG
+    assert _step(Hkv=3) == ARG
+    assert _step(ws=None) == WS
+    for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
+        assert _step(**{arg: FAKE + 4}) == ARG, arg
