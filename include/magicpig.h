@@ -86,8 +86,8 @@ int mp_version(void);
  * W in R^{d x (K*L)} (Section 4.3 "Hash function selection"): float32,
  * row-major [d][K*L], column l*K + b being hyperplane b of table l.  It is
  * rounded to bf16 (round to nearest even) and rearranged into the operand
- * order of the encoder's matrix-core tiles.  Wp receives mp_proj_bytes(d,K,L)
- * bytes.  Both pointers are device pointers.  One packed W serves every
+ * order of the encoder's matrix-core tiles (8 KB per tile of floor(32/K)
+ * whole tables).  Wp receives mp_proj_bytes(d,K,L) bytes.  Both pointers are device pointers.  One packed W serves every
  * unit of a layer (the paper shares projectors across heads, Section 4.4).
  * Errors: MP_ERR_ARG (null pointers), MP_ERR_UNSUPPORTED (d, K, L limits).
  */

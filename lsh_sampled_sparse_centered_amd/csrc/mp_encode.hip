@@ -11,19 +11,25 @@ namespace mp {
 // ---------------------------------------------------------------------------
 // Projection packing: W[d][K*L] fp32 -> bf16 tiles in matrix-core A-operand
 // order.  Element e of lane l in k-step s of tile t is
-//   W[16 s + 8 (l / 32) + e][32 t + enc_row_col(l % 32)]   (0 past K*L).
+//   W[16 s + 8 (l / 32) + e][K (t tpt + j) + b],  K j + b = enc_row_col(l % 32),
+// and 0 where j >= tpt or t tpt + j >= L.
 // One thread per (tile, k-step, lane) writes 16 bytes.
-__global__ void proj_pack_kernel(const float *__restrict__ W, int ncol, int ntiles, uint4 *__restrict__ Wp) {
+__global__ void proj_pack_kernel(const float *__restrict__ W, int K, int L, int ntiles, uint4 *__restrict__ Wp) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)ntiles * KSTEPS * 64) return;
   const int lane = (int)(gid & 63);
   const int s = (int)((gid >> 6) % KSTEPS);
   const int t = (int)(gid / (64 * KSTEPS));
-  const int col = 32 * t + enc_row_col(lane & 31);
+  const int tpt = enc_tpt(K);
+  const int p = enc_row_col(lane & 31);  // bit of the tile's word
+  const int j = p / K, b = p % K, l = t * tpt + j;
+  const bool live = j < tpt && l < L;
+  const int col = l * K + b;
+  const int ncol = K * L;
   const int d0 = 16 * s + 8 * (lane >> 5);
   bf16x8 v;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (__bf16)(col < ncol ? W[(int64_t)(d0 + e) * ncol + col] : 0.0f);
+  for (int e = 0; e < 8; ++e) v[e] = (__bf16)(live ? W[(int64_t)(d0 + e) * ncol + col] : 0.0f);
   Wp[gid] = __builtin_bit_cast(uint4, v);
 }
 
@@ -31,7 +37,7 @@ hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t 
   const int ntiles = enc_ntiles(K, L);
   const int64_t total = (int64_t)ntiles * KSTEPS * 64;
   if (total == 0) return hipSuccess;
-  proj_pack_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(W, K * L, ntiles, (uint4 *)Wp);
+  proj_pack_kernel<<<dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s>>>(W, K, L, ntiles, (uint4 *)Wp);
   return hipGetLastError();
 }
 
@@ -139,15 +145,14 @@ hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int6
 
 // ---------------------------------------------------------------------------
 // Encoder.  Each block encodes ENC_ROWS rows of one unit for the tables
-// [l0, l1) assigned to blockIdx.z.  Wave w owns rows w*64 .. w*64+63 as two
+// [l0, l1) of its table group.  Wave w owns rows w*64 .. w*64+63 as two
 // 32-row B operands held in registers (x = bf16(row - mu) for the 128 dims).
-// Packed projection tiles stream through LDS (double buffered, ENC_TG tiles
-// per stage); per tile a wave issues 2 x 8 matrix-core ops (32x32x16 bf16,
-// fp32 accumulate).  Each accumulator's sign gives one bit (z > 0); the
-// 16-bit masks of the two lane halves are exchanged so that lane l holds all
-// 32 bits of row w*64 + l, which are appended to a 64-bit bit queue; every
-// complete group of K bits is one table code, stored to
-// out[u*out_su + l*out_sl + row*out_si].
+// Packed projection tiles are copied global -> LDS (double buffered, ENC_TG
+// tiles per stage); per tile a wave issues 2 x 8 matrix-core ops (32x32x16
+// bf16, fp32 accumulate).  Each accumulator's sign gives one bit (z > 0);
+// the 16-bit masks of the two lane halves are swapped so that lane l holds
+// the tile's 32-bit word of row w*64 + l, whose bit fields are the codes of
+// the tile's tables, stored to out[u*out_su + l*out_sl + row*out_si].
 //
 // For appends the same pass copies the raw key row (and value row) into the
 // cache when kcopy / vcopy are given.
@@ -209,9 +214,10 @@ __device__ inline bool row_nonzero(const bf16x8 (&xb)[2][KSTEPS], int half) {
 // append and the queries of a decode step) and maps its linear block index
 // onto (job, row block, unit, table group).
 template <typename T>
-__global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
+__global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
                                                         int K, int L) {
   __shared__ uint4 wsh[2][ENC_TG * KSTEPS * 64];
+  __shared__ uint16_t cst[ENC_NW][ENC_CST][64];  // a wave's codes of one stage, [table][row]
   const bool second = njobs > 1 && (int64_t)blockIdx.x >= j1.first_block;
   const EncJob &jb = second ? j1 : j0;
   const T *__restrict__ in = (const T *)jb.in;
@@ -237,70 +243,62 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
   const int l1 = min(L, l0 + tables_per_block);
   const bool copy_rows = zt == 0;  // table-split blocks share rows
 
-  const int c0 = l0 * K, c1 = l1 * K;
-  const int t0 = c0 >> 5, t1 = (c1 + 31) >> 5;
-  const int skip = c0 - 32 * t0;
-  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
-  uint64_t q = 0;  // bit queue
-  int nb = 0;
+  // tiles [t0, t1) hold tables [l0, l1) (l0 is a multiple of tpt)
+  const int tpt = enc_tpt(K);
+  const int t0 = K > 0 ? l0 / tpt : 0, t1 = K > 0 ? (l1 + tpt - 1) / tpt : 0;
 
-  // Projection tiles [tg, tg + ENC_TG) are staged global -> registers -> LDS.
-  uint4 st0, st1, st2, st3, st4, st5, st6, st7;
-#define MP_FETCH(tg_)                                                        \
-  do {                                                                       \
-    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
-    const uint4 *src_ = wp + (int64_t)(tg_)*KSTEPS * 64 + threadIdx.x;       \
-    const int i_ = threadIdx.x;                                              \
-    if (i_ + 0 * 256 < cnt_) st0 = src_[0 * 256];                            \
-    if (i_ + 1 * 256 < cnt_) st1 = src_[1 * 256];                            \
-    if (i_ + 2 * 256 < cnt_) st2 = src_[2 * 256];                            \
-    if (i_ + 3 * 256 < cnt_) st3 = src_[3 * 256];                            \
-    if (i_ + 4 * 256 < cnt_) st4 = src_[4 * 256];                            \
-    if (i_ + 5 * 256 < cnt_) st5 = src_[5 * 256];                            \
-    if (i_ + 6 * 256 < cnt_) st6 = src_[6 * 256];                            \
-    if (i_ + 7 * 256 < cnt_) st7 = src_[7 * 256];                            \
-  } while (0)
-#define MP_COMMIT(buf_, tg_)                                                 \
-  do {                                                                       \
-    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                  \
-    uint4 *dst_ = &wsh[buf_][threadIdx.x];                                   \
-    const int i_ = threadIdx.x;                                              \
-    if (i_ + 0 * 256 < cnt_) dst_[0 * 256] = st0;                            \
-    if (i_ + 1 * 256 < cnt_) dst_[1 * 256] = st1;                            \
-    if (i_ + 2 * 256 < cnt_) dst_[2 * 256] = st2;                            \
-    if (i_ + 3 * 256 < cnt_) dst_[3 * 256] = st3;                            \
-    if (i_ + 4 * 256 < cnt_) dst_[4 * 256] = st4;                            \
-    if (i_ + 5 * 256 < cnt_) dst_[5 * 256] = st5;                            \
-    if (i_ + 6 * 256 < cnt_) dst_[6 * 256] = st6;                            \
-    if (i_ + 7 * 256 < cnt_) dst_[7 * 256] = st7;                            \
+  // Projection tiles [tg, tg + ENC_TG) are copied global -> LDS directly
+  // (no registers): each wave moves whole 1 KB pieces, so the condition is
+  // uniform per wave.  The barrier that ends a stage waits for them.
+  constexpr int NT = 64 * ENC_NW;
+#define MP_FETCH(buf_, tg_)                                                                        \
+  do {                                                                                             \
+    const int cnt_ = min(ENC_TG, t1 - (tg_)) * KSTEPS * 64;                                        \
+    const uint4 *src_ = wp + (int64_t)(tg_)*KSTEPS * 64 + threadIdx.x;                             \
+    _Pragma("unroll") for (int k_ = 0; k_ < (ENC_TG * KSTEPS * 64 + NT - 1) / NT; ++k_) {          \
+      const int base_ = wave * 64 + k_ * NT;                                                       \
+      if (base_ < cnt_)                                                                            \
+        __builtin_amdgcn_global_load_lds((const void *)(src_ + k_ * NT),                           \
+                                         (__attribute__((address_space(3))) void *)&wsh[buf_][base_], \
+                                         16, 0, 0);                                                \
+    }                                                                                              \
   } while (0)
 
   // the first stage's loads are issued before the rows are read, so the two
   // latencies overlap (this is what bounds small jobs)
-  if (K > 0) MP_FETCH(t0);
+  if (K > 0) MP_FETCH(0, t0);
 
-  // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.
+  // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.  All
+  // loads of a 32-row set are issued before any is used (one memory round
+  // trip per set): rows past the end read the last row and are zeroed after.
   bf16x8 xb[2][KSTEPS];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int64_t r = row_w + 32 * nt + (lane & 31);
     const bool ok = r < rows;
+    const int64_t rc = ok ? r : rows - 1;
+    const T *rp = in + u * in_su + rc * in_si + 8 * half;
+    float v[KSTEPS][8];
+    if (mu) {  // the row and mean loads go out together
+      const float *mp = mu + u * mu_su + rc * mu_si + 8 * half;
+      float m[KSTEPS][8];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int d0 = 16 * s + 8 * half;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok) {
-        load_row8<T>(in + u * in_su + r * in_si + d0, v);
-        if (mu) {
-          float m[8];
-          load8<float>(mu + u * mu_su + r * mu_si + d0, m);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = v[e] - m[e];  // fp32 subtraction
-        }
+      for (int s = 0; s < KSTEPS; ++s) {
+        load_row8<T>(rp + 16 * s, v[s]);
+        load8<float>(mp + 16 * s, m[s]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xb[nt][s][e] = (__bf16)v[e];  // round to nearest even
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[s][e] = v[s][e] - m[s][e];  // fp32 subtraction
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) load_row8<T>(rp + 16 * s, v[s]);
     }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[nt][s][e] = ok ? (__bf16)v[s][e] : (__bf16)0.0f;  // round to nearest even
   }
 
   // appends: the first table block of each row block copies the raw key and
@@ -310,7 +308,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
     const int64_t r0 = rb * ENC_ROWS;
     const int nr = (int)min((int64_t)ENC_ROWS, rows - r0);
-    for (int c = threadIdx.x; c < nr * CPR; c += 256) {
+    for (int c = threadIdx.x; c < nr * CPR; c += NT) {
       const int64_t r = r0 + c / CPR;
       const int pc = c % CPR;
       const uint4 kx = *(const uint4 *)((const char *)(in + u * in_su + r * in_si) + 16 * pc);
@@ -324,22 +322,70 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
   const bool my_nz = row_nonzero(xb, half);
   const bool my_ok = my_row < rows;
   uint16_t *my_out = out + u * out_su + my_row * out_si;
-  int lt = l0;  // next table to emit
 
   if (K == 0) {
-    for (; lt < l1; ++lt)
-      if (my_ok) my_out[(int64_t)lt * out_sl] = 0;
+    for (int l = l0; l < l1; ++l)
+      if (my_ok) my_out[(int64_t)l * out_sl] = 0;
     return;
   }
 
-  MP_COMMIT(0, t0);
   __syncthreads();
+  // A stage's sign words are cut into codes and stored at the start of the
+  // next stage, so the stores complete while that stage's tiles run (the
+  // wait for the next projection stage then does not wait for them).  Table
+  // t*tpt + j of a tile is the bit field [K j, K j + K) of its word.
+  uint32_t wd[ENC_TG];
+  int tpend = 0, npend = 0;  // first tile and number of tiles pending
+  // Key-major code rows (out_si = 1, the code store) with at most ENC_CST
+  // tables per stage go out as 16-byte stores of 8 rows of one table: the
+  // wave's codes are transposed through LDS.  Otherwise each lane stores its
+  // own 2-byte codes.
+  const bool vec_out = out_si == 1 && ENC_TG * tpt <= ENC_CST;
+  auto emit_stage = [&]() {
+    const int lb = tpend * tpt, le = min(l1, (tpend + npend) * tpt);
+    if (vec_out) {
+#pragma unroll
+      for (int i = 0; i < ENC_TG; ++i)
+        if (i < npend)
+          for (int j = 0; j < tpt; ++j) {
+            const int l = (tpend + i) * tpt + j;
+            if (l < le) cst[wave][l - lb][lane] = (uint16_t)__builtin_amdgcn_ubfe(wd[i], (uint32_t)(K * j), (uint32_t)K);
+          }
+      uint16_t *o = out + u * out_su + (int64_t)lb * out_sl + row_w;
+      for (int k = lane; k < (le - lb) * 8; k += 64) {
+        const int t = k >> 3, g = k & 7;
+        const uint4 v = *(const uint4 *)&cst[wave][t][8 * g];
+        uint16_t *dst = o + (int64_t)t * out_sl + 8 * g;
+        const int64_t r0 = row_w + 8 * g;
+        if (r0 + 8 <= rows) {
+          *(uint4 *)dst = v;
+        } else {  // the unit's last rows: columns past them are not touched
+          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+          for (int e = 0; e < 8; ++e)
+            if (r0 + e < rows) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < ENC_TG; ++i)
+        if (i < npend) {
+          const int lt = (tpend + i) * tpt;
+          uint16_t *o = my_out + (int64_t)lt * out_sl;
+          for (int j = 0; j < min(tpt, l1 - lt); ++j)
+            if (my_ok) o[(int64_t)j * out_sl] = (uint16_t)__builtin_amdgcn_ubfe(wd[i], (uint32_t)(K * j), (uint32_t)K);
+        }
+    }
+  };
   int buf = 0;
   for (int tg = t0; tg < t1; tg += ENC_TG) {
+    if (npend) emit_stage();
     const int tnext = tg + ENC_TG;
-    if (tnext < t1) MP_FETCH(tnext);
-    const int ntile = min(ENC_TG, t1 - tg);
-    for (int tt = 0; tt < ntile; ++tt) {
+    if (tnext < t1) MP_FETCH(buf ^ 1, tnext);
+    // every stage runs ENC_TG tiles (one straight block of matrix-core and
+    // vector work for the scheduler); tiles past t1 read stale LDS and are
+    // dropped
+#pragma unroll
+    for (int tt = 0; tt < ENC_TG; ++tt) {
       f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) {
@@ -347,33 +393,21 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[0][s], acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[1][s], acc1, 0, 0, 0);
       }
-      const uint32_t m0 = sign_bits16(acc0), m1 = sign_bits16(acc1);
-      // lane half 0 keeps row lane (tile 0) and needs the partner's upper 16
-      // columns of it; lane half 1 keeps row 32 + lane%32 (tile 1).
-      const uint32_t send = half ? m0 : m1;
-      const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-      uint32_t word = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
-      if (!my_nz) word = 0u;
-      int nw = 32;
-      if (tg + tt == t0 && skip) {
-        word >>= skip;
-        nw = 32 - skip;
-      }
-      q |= (uint64_t)word << nb;
-      nb += nw;
-      while (nb >= K && lt < l1) {
-        if (my_ok) my_out[(int64_t)lt * out_sl] = (uint16_t)(q & kmask);
-        q >>= K;
-        nb -= K;
-        ++lt;
-      }
+      // lane l < 32 holds bits 0-15 of row l in m0 and bits 0-15 of row
+      // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
+      // cross-half swap leaves lane l with row l's halves and lane 32 + l
+      // with row 32 + l's.
+      const auto sw = __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), sign_bits16(acc1), false, false);
+      const uint32_t word = sw[0] | (sw[1] << 16);
+      wd[tt] = my_nz ? word : 0u;
     }
-    if (tnext < t1) MP_COMMIT(buf ^ 1, tnext);
+    tpend = tg;
+    npend = min(ENC_TG, t1 - tg);
     __syncthreads();
     buf ^= 1;
   }
+  if (npend) emit_stage();
 #undef MP_FETCH
-#undef MP_COMMIT
 }
 
 // ---------------------------------------------------------------------------
@@ -386,7 +420,7 @@ __global__ __launch_bounds__(256, 2) void encode_kernel(EncJob j0, EncJob j1, in
 // after one barrier each code is cut out of its row's bit string.  One memory
 // round trip for the rows and projections, one for the codes.
 constexpr int SM_TABLES = 4;                                   // tables per block
-constexpr int SM_MAXT = (SM_TABLES * 16 + 31 + 31) / 32;       // tiles a block touches (K <= 16)
+constexpr int SM_MAXT = 3;  // tiles a block touches: K <= 16 gives tpt >= 2, and 4 tables span <= 3 tiles
 static_assert(SM_MAXT <= 4, "one tile per wave");
 
 template <typename T>
@@ -398,7 +432,8 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
   const int lb = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
   const int l0 = lb * SM_TABLES, l1 = min(L, l0 + SM_TABLES);
-  const int t0 = (l0 * K) >> 5, t1 = (l1 * K + 31) >> 5;
+  const int tpt = enc_tpt(K);
+  const int t0 = K > 0 ? l0 / tpt : 0, t1 = K > 0 ? (l1 + tpt - 1) / tpt : 0;
   const int R = (int)(jb.units * jb.rows);  // rows of the job, flattened (<= 64)
   const T *__restrict__ in = (const T *)jb.in;
   T *__restrict__ kcopy = (T *)jb.kcopy;
@@ -464,36 +499,35 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]), xb[1][s], acc1, 0, 0, 0);
     }
-    const uint32_t m0 = sign_bits16(acc0), m1 = two ? sign_bits16(acc1) : 0u;
     // lane l ends with the tile's 32 bits of row l (as in the large encoder)
-    const uint32_t send = half ? m0 : m1;
-    const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-    const uint32_t word = half ? (recv | (m1 << 16)) : (m0 | (recv << 16));
+    const auto sw =
+        __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), two ? sign_bits16(acc1) : 0u, false, false);
+    const uint32_t word = sw[0] | (sw[1] << 16);
     bits[lane][t - t0] = my_nz ? word : 0u;
   }
   __syncthreads();
 
-  // codes: table l of row r is bits [l K, l K + K) of the row's bit string
-  const uint32_t kmask = (K >= 16) ? 0xffffu : ((1u << K) - 1u);
+  // codes: table l of row r is the bit field [K (l % tpt), + K) of the row's
+  // word of tile l / tpt (all zero when K = 0)
   const int ntab = l1 - l0;
   for (int idx = threadIdx.x; idx < R * ntab; idx += 256) {
     const int r = idx / ntab, l = l0 + idx % ntab;
-    const int cb = l * K - 32 * t0;
-    const int w = cb >> 5, sh = cb & 31;
-    const uint64_t v = (uint64_t)bits[r][w] | ((uint64_t)bits[r][w + 1] << 32);
+    const uint32_t c = K > 0 ? __builtin_amdgcn_ubfe(bits[r][l / tpt - t0], (uint32_t)(K * (l % tpt)), (uint32_t)K) : 0u;
     const int64_t u = r / (int)jb.rows, i = r % (int)jb.rows;
-    jb.out[u * jb.out_su + (int64_t)l * jb.out_sl + i * jb.out_si] = (uint16_t)((v >> sh) & kmask);
+    jb.out[u * jb.out_su + (int64_t)l * jb.out_sl + i * jb.out_si] = (uint16_t)c;
   }
 }
 
 // Grid shape of one job.  Few rows: the tables are split over blocks so that
 // the projection pass runs on many compute units instead of one.
-static void plan_job(EncJob &j, int L, int64_t first_block) {
+static void plan_job(EncJob &j, int K, int L, int64_t first_block) {
   j.rblocks = (j.rows + ENC_ROWS - 1) / ENC_ROWS;
   const int64_t blocks = j.rblocks * j.units;
   int tsplit = 1;
   if (blocks < 512) tsplit = (int)std::min<int64_t>((512 + blocks - 1) / blocks, (int64_t)L);
+  const int tpt = std::max(enc_tpt(K), 1);  // a block's tables start on a tile
   j.tpb = (L + tsplit - 1) / tsplit;
+  j.tpb = (j.tpb + tpt - 1) / tpt * tpt;
   j.tsplit = (L + j.tpb - 1) / j.tpb;
   j.first_block = first_block;
 }
@@ -507,7 +541,7 @@ hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp
   for (int i = 0; i < njobs; ++i) {
     if (jobs[i].units == 0 || jobs[i].rows == 0) continue;
     j[nj] = jobs[i];
-    plan_job(j[nj], L, total);
+    plan_job(j[nj], K, L, total);
     total += job_blocks(j[nj]);
     ++nj;
   }
@@ -526,9 +560,9 @@ hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp
   }
   const dim3 grid((unsigned)total);
   if (dtype == 0)
-    encode_kernel<__bf16><<<grid, 256, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
+    encode_kernel<__bf16><<<grid, 64 * ENC_NW, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
   else
-    encode_kernel<float><<<grid, 256, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
+    encode_kernel<float><<<grid, 64 * ENC_NW, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
   return hipGetLastError();
 }
 

@@ -17,13 +17,18 @@ constexpr int KSTEPS = D / 16;  // k-steps of one 32x32x16 bf16 matrix-core op o
 
 // ---------------------------------------------------------------- encoder
 // Packed projections: [ntiles][KSTEPS][64 lanes][8 bf16], one 32-column tile
-// = 8 KB.  Within a tile, matrix row i (the A-operand row that lane i % 32
-// supplies) carries projection column 32*t + enc_row_col(i); the column order
-// is chosen so that accumulator register r of lane half a holds column
-// 16*a + r, i.e. each lane's 16 sign bits come out in column order.
-constexpr int ENC_ROWS = 256;   // rows (keys or queries) per encoder block
+// = 8 KB.  A tile holds whole tables: tpt = floor(32 / K) tables per tile,
+// table t*tpt + j in bits K*j .. K*j + K-1 of the tile's 32-bit word (the
+// bits past tpt*K are zero columns).  Within a tile, matrix row i (the
+// A-operand row that lane i % 32 supplies) carries word bit enc_row_col(i);
+// the order is chosen so that accumulator register r of lane half a holds
+// bit 16*a + r, i.e. each lane's 16 sign bits come out in bit order.
+constexpr int ENC_NW = 4;       // waves per encoder block (64 rows each)
+constexpr int ENC_ROWS = 64 * ENC_NW;  // rows (keys or queries) per encoder block
 constexpr int ENC_TG = 4;       // tiles staged in LDS per step (32 KB)
-__host__ __device__ inline int enc_ntiles(int K, int L) { return (K * L + 31) / 32; }
+constexpr int ENC_CST = 32;     // tables per stage whose codes are transposed through LDS
+__host__ __device__ inline int enc_tpt(int K) { return K > 0 ? 32 / K : 0; }
+__host__ __device__ inline int enc_ntiles(int K, int L) { return K > 0 ? (L + enc_tpt(K) - 1) / enc_tpt(K) : 0; }
 __host__ __device__ inline int enc_row_col(int i) { return 16 * ((i >> 2) & 1) + (i & 3) + 4 * (i >> 3); }
 
 // ---------------------------------------------------------------- decode

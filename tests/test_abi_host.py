@@ -41,7 +41,7 @@ def test_strerror_and_version():
 
 
 def test_size_queries():
-    assert mp.mp_proj_bytes(128, 10, 150) == 47 * 8 * 64 * 16
+    assert mp.mp_proj_bytes(128, 10, 150) == 50 * 8 * 64 * 16  # 3 tables of 10 bits per 32-column tile
     assert mp.mp_proj_bytes(128, 8, 75) == 19 * 8 * 64 * 16
     assert mp.mp_proj_bytes(64, 8, 75) == 0
     assert mp.mp_proj_bytes(128, 17, 75) == 0
