@@ -336,33 +336,37 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
   // t*tpt + j of a tile is the bit field [K j, K j + K) of its word.
   uint32_t wd[ENC_TG];
   int tpend = 0, npend = 0;  // first tile and number of tiles pending
-  // Key-major code rows (out_si = 1, the code store) with at most ENC_CST
-  // tables per stage go out as 16-byte stores of 8 rows of one table: the
-  // wave's codes are transposed through LDS.  Otherwise each lane stores its
-  // own 2-byte codes.
-  const bool vec_out = out_si == 1 && ENC_TG * tpt <= ENC_CST;
+  // Key-major code rows (out_si = 1, the code store) with at most 8 tables
+  // per tile go out as 16-byte stores of 8 rows of one table: the wave's
+  // codes are transposed through LDS ([table][row]).  Each tile writes 8
+  // slots without branches, in tile order, so the slots past a tile's tpt
+  // codes are overwritten by the next tile's.  Otherwise each lane stores
+  // its own 2-byte codes.
+  const bool vec_out = out_si == 1 && tpt <= 8;
   auto emit_stage = [&]() {
     const int lb = tpend * tpt, le = min(l1, (tpend + npend) * tpt);
     if (vec_out) {
 #pragma unroll
       for (int i = 0; i < ENC_TG; ++i)
-        if (i < npend)
-          for (int j = 0; j < tpt; ++j) {
-            const int l = (tpend + i) * tpt + j;
-            if (l < le) cst[wave][l - lb][lane] = (uint16_t)__builtin_amdgcn_ubfe(wd[i], (uint32_t)(K * j), (uint32_t)K);
-          }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          cst[wave][i * tpt + j][lane] = (uint16_t)__builtin_amdgcn_ubfe(wd[i], (uint32_t)(K * j), (uint32_t)K);
+      const int nv = (le - lb) * 8;  // 16-byte pieces
       uint16_t *o = out + u * out_su + (int64_t)lb * out_sl + row_w;
-      for (int k = lane; k < (le - lb) * 8; k += 64) {
-        const int t = k >> 3, g = k & 7;
-        const uint4 v = *(const uint4 *)&cst[wave][t][8 * g];
-        uint16_t *dst = o + (int64_t)t * out_sl + 8 * g;
-        const int64_t r0 = row_w + 8 * g;
-        if (r0 + 8 <= rows) {
-          *(uint4 *)dst = v;
-        } else {  // the unit's last rows: columns past them are not touched
-          const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-          for (int e = 0; e < 8; ++e)
-            if (r0 + e < rows) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+#pragma unroll
+      for (int k0 = 0; k0 < ENC_CST * 8; k0 += 64) {
+        const int k = k0 + lane, t = k >> 3, g = k & 7;
+        if (k < nv) {
+          const uint4 v = *(const uint4 *)&cst[wave][t][8 * g];
+          uint16_t *dst = o + (int64_t)t * out_sl + 8 * g;
+          const int64_t r0 = row_w + 8 * g;
+          if (r0 + 8 <= rows) {
+            *(uint4 *)dst = v;
+          } else {  // the unit's last rows: columns past them are not touched
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+            for (int e = 0; e < 8; ++e)
+              if (r0 + e < rows) dst[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+          }
         }
       }
     } else {
