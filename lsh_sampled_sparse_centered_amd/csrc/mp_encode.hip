@@ -453,30 +453,46 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
     for (int s = 0; s < KSTEPS; ++s) a[s] = wp[((int64_t)t * KSTEPS + s) * 64 + lane];
   }
 
-  // B operands: row r = 32 nt + lane % 32 (unit r / rows, row r % rows), dims 16 s + 8 half + e
+  // B operands: row r = 32 nt + lane % 32 (unit r / rows, row r % rows), dims
+  // 16 s + 8 half + e.  All loads of a 32-row set go out before any is used;
+  // rows past the job's last read its last row and are zeroed after.
   bf16x8 xb[2][KSTEPS];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
+    if (nt == 1 && R <= 32) {  // no second row set
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xb[1][s][e] = (__bf16)0.0f;
+      break;
+    }
     const int r = 32 * nt + (lane & 31);
     const bool ok = r < R;
     const int rows = (int)jb.rows;  // rows of a small job fit an int
-    const int64_t u = ok ? r / rows : 0, i = ok ? r % rows : 0;
+    const int rc = ok ? r : R - 1;
+    const int64_t u = rc / rows, i = rc % rows;
+    const T *rp = in + u * jb.in_su + i * jb.in_si + 8 * half;
+    float v[KSTEPS][8];
+    if (jb.mu) {
+      const float *mp = jb.mu + u * jb.mu_su + i * jb.mu_si + 8 * half;
+      float m[KSTEPS][8];
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      const int d0 = 16 * s + 8 * half;
-      float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok) {
-        load_row8<T>(in + u * jb.in_su + i * jb.in_si + d0, v);
-        if (jb.mu) {
-          float m[8];
-          load8<float>(jb.mu + u * jb.mu_su + i * jb.mu_si + d0, m);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = v[e] - m[e];  // fp32 subtraction
-        }
+      for (int s = 0; s < KSTEPS; ++s) {
+        load_row8<T>(rp + 16 * s, v[s]);
+        load8<float>(mp + 16 * s, m[s]);
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xb[nt][s][e] = (__bf16)v[e];  // round to nearest even
+      for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[s][e] = v[s][e] - m[s][e];  // fp32 subtraction
+    } else {
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) load_row8<T>(rp + 16 * s, v[s]);
     }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xb[nt][s][e] = ok ? (__bf16)v[s][e] : (__bf16)0.0f;  // round to nearest even
   }
 
   // appends: block 0 copies the raw key and value rows into the caches (16

@@ -21,7 +21,7 @@ namespace mp {
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
 constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
 
-__global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                      int64_t nchunks, int64_t chunk, float *__restrict__ out,
                                                      float *__restrict__ lse, int32_t *__restrict__ count,
                                                      int32_t *__restrict__ idx, int64_t cap,
@@ -51,31 +51,38 @@ __global__ __launch_bounds__(1024) void merge_kernel(const float *__restrict__ p
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   int cnt = 0;
   for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
-    float mc[MERGE_CPT], lc[MERGE_CPT];
+    // loads are unconditional (chunks past the last re-read the last one and
+    // are dropped), so all of them are in flight at once
+    f32x2 ml[MERGE_CPT];
+    int cn[MERGE_CPT];
     f32x4 oc[MERGE_CPT];
 #pragma unroll
     for (int k = 0; k < MERGE_CPT; ++k) {
-      const int64_t ci = c0 + (int64_t)k * MERGE_PH;
-      mc[k] = -INFINITY;
-      lc[k] = 0.0f;
-      oc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if (ci < nchunks) {
-        const float *r = p0 + ci * cs;
-        mc[k] = r[0];
-        lc[k] = r[1];
-        oc[k] = *(const f32x4 *)(r + 4 + 4 * j);
-        cnt += __builtin_bit_cast(int, r[2]);
-      }
+      const int64_t ci = min(c0 + (int64_t)k * MERGE_PH, nchunks - 1);
+      const float *r = p0 + ci * cs;
+      ml[k] = *(const f32x2 *)r;  // m, l
+      cn[k] = __builtin_bit_cast(int, r[2]);
+      oc[k] = *(const f32x4 *)(r + 4 + 4 * j);
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pass is issued before any result is used
+    float mc[MERGE_CPT], lc[MERGE_CPT];
 #pragma unroll
     for (int k = 0; k < MERGE_CPT; ++k) {
-      if (mc[k] > -INFINITY) {
-        const float mn = fmaxf(m, mc[k]);
-        const float a = __expf(m - mn), bsc = __expf(mc[k] - mn);  // a = 0 while m = -inf
-        l = l * a + lc[k] * bsc;
-        acc = acc * a + oc[k] * bsc;
-        m = mn;
-      }
+      const bool live = c0 + (int64_t)k * MERGE_PH < nchunks;
+      mc[k] = live ? ml[k][0] : -INFINITY;
+      lc[k] = ml[k][1];
+      cnt += live ? cn[k] : 0;
+    }
+    // branch-free fold (a branch would let the compiler sink the loads into
+    // it, one round trip each); an empty side gets weight 0
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const float mn = fmaxf(m, mc[k]);
+      const float a = m > -INFINITY ? __expf(m - mn) : 0.0f;
+      const float bsc = mc[k] > -INFINITY ? __expf(mc[k] - mn) : 0.0f;
+      l = l * a + lc[k] * bsc;
+      acc = acc * a + oc[k] * bsc;
+      m = mn;
     }
   }
   red_o[ph][j] = acc;
