@@ -89,6 +89,40 @@ def test_query_codes(name):
     assert nbad == 0
 
 
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 7, 11, 12, 15])
+def test_codes_every_table_width(K):
+    """Codes of every table width the encoders handle differently: a 32-bit
+    tile word holds floor(32/K) tables (32 for K = 1 down to 2 for K >= 11),
+    K <= 3 stores each code from its lane, K >= 4 transposes a stage's codes
+    through LDS.  L = 37 leaves a partial last tile; n = 700 a ragged last
+    row block.  Build (large encoder), 8 query rows and one append (small
+    encoder), all against the oracle."""
+    w = variant("llama8b_layer", hq=4, hkv=2, n=700, K=K, L=37)
+    lay = layer(w, seed=40 + K)
+    km, codes, margin, qc = oracle_codes(w, lay)
+    Wp, kmean, gcodes = gpu_build(w, lay)
+    n = lay["n"]
+    torch.cuda.synchronize()
+    assert np.array_equal(kmean.cpu().numpy().view(np.uint32), km.view(np.uint32))
+    g = gcodes.cpu().numpy()[:, :, :n].transpose(0, 2, 1).reshape(-1, w.L)
+    r = codes[:, :, :n].transpose(0, 2, 1).reshape(-1, w.L)
+    assert code_mismatches_outside_band(g, r, margin.reshape(-1, w.L))[1] == 0
+    assert int(gcodes[:, :, n:].cpu().numpy().astype(np.int64).sum()) == 0  # columns >= n untouched
+    h = lay["host"]
+    q = lay["q"].reshape(-1, w.d)[:8]
+    gq = mp.mp_encode_queries(q, Wp, w.K, w.L).cpu().numpy().reshape(-1, w.L)
+    ref, mg = oracle.encode(h["q"].reshape(-1, w.d)[:8], h["W"], w.K, w.L, with_margin=True)
+    assert code_mismatches_outside_band(gq, ref, mg)[1] == 0
+    kn = lay["Kc"][:, n - 1].clone()
+    mp.mp_append(kn, torch.zeros_like(kn), lay["Kc"], lay["Vc"], n, kmean, Wp, w.K, w.L, gcodes)
+    torch.cuda.synchronize()
+    got = gcodes.cpu().numpy()[:, :, n]
+    U = w.batch * w.hkv
+    for u in range(U):
+        ref, mg = oracle.encode(host_f32(kn)[u][None], h["W"], w.K, w.L, mu=km[u], with_margin=True)
+        assert code_mismatches_outside_band(got[u][None], ref, mg)[1] == 0, u
+
+
 @pytest.mark.parametrize("rows", [5, 100])
 def test_zero_rows_encode_to_zero_codes(rows):
     """A zero row projects to exactly 0 in every column, and (z > 0) is false:
