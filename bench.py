@@ -261,6 +261,26 @@ def main() -> int:
         del flush
         log("calibration copy of %d MiB done" % args.calib_copy_mib)
 
+    # ------------------------------------------------------------------ achievable HBM rate (context)
+    # a 1 GiB device-to-device copy (reads and writes 1 GiB each), best of 3, sources flushed
+    nb = 1 << 30
+    src = torch.empty(nb, dtype=torch.uint8, device=dev)
+    src.fill_(3)
+    dst = torch.empty_like(src)
+    flush = torch.empty(nb, dtype=torch.uint8, device=dev)
+    copy_ms = []
+    for _ in range(3):
+        flush.fill_(4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_ms.append(e0.elapsed_time(e1))
+    copy_gbs = 2.0 * nb / (min(copy_ms) * 1e-3) / 1e9
+    del src, dst, flush
+    log("device copy: %.0f GB/s (read + write)" % copy_gbs)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(w, args.seed, args.cpu_seconds)
@@ -283,7 +303,8 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "sample_kernel (mp_decode_step / mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
-                     "algorithmic_bytes_per_launch": bytes_launch},
+                     "algorithmic_bytes_per_launch": bytes_launch, "device_copy_GBs": copy_gbs,
+                     "frac_of_device_copy": achieved / copy_gbs},
         "step": {"latency_ms": wall_ms, "latency_ms_events": ev_ms, "bytes_per_step": step_bytes,
                  "frac_hbm_step": step_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "sampled_frac_per_head": head_frac, "union_keys_per_unit": union_per_unit},
@@ -337,11 +358,26 @@ def cpu_baseline(w, seed: int, budget_s: float):
         if el >= budget_s:
             break
     keys_done = reps * nunits * n
+    # the same decode on one thread, on one KV head's query heads, for a quarter of the budget
+    oracle.set_threads(1)
+    reps1 = 0
+    t = time.perf_counter()
+    while True:
+        q1 = synth.unit_queries(seed, 0, 0, 0, G, d, w.torch_dtype, "cpu", step=reps1 + 1).float().numpy()[None]
+        oracle.decode(q1, keys[:, :1], vals[:, :1], codes[:1].reshape(1, 1, w.L, cap), km[:1].reshape(1, 1, d), W,
+                      w.K, w.L, n)
+        reps1 += 1
+        el1 = time.perf_counter() - t
+        if el1 >= budget_s / 4:
+            break
+    oracle.set_threads(threads)
     return {"value": keys_done / el, "unit": "keys/s", "cores": min(threads, nunits * G), "kind": "oracle",
             "sample": "%d decode passes over %d KV heads x %d keys (%d query heads each), layer 0; "
-                      "oracle build of their codes %.1fs untimed" % (reps, nunits, n, G, build_s),
+                      "oracle build of their codes %.1fs untimed; one-thread figure: %d passes over KV head 0"
+                      % (reps, nunits, n, G, build_s, reps1),
+            "value_1thread": reps1 * n / el1,
             "cpu_model": platform.processor() or platform.machine(), "host_threads": threads,
-            "seconds": el}
+            "seconds": el + el1}
 
 
 if __name__ == "__main__":

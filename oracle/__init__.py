@@ -46,6 +46,8 @@ def lib():
     if _lib is None:
         build()
         L = ctypes.CDLL(_LIB)
+        L.orc_set_threads.argtypes = [_int]
+        L.orc_set_threads.restype = None
         L.orc_bf16.argtypes = [ctypes.c_float]
         L.orc_bf16.restype = ctypes.c_float
         L.orc_key_mean.argtypes = [_f32p, _i64, _int, _i64, _f32p]
@@ -72,6 +74,11 @@ def lib():
         L.orc_decode.restype = None
         _lib = L
     return _lib
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's OpenMP loops (timing only)."""
+    lib().orc_set_threads(int(n))
 
 
 def _f32(a) -> np.ndarray:

@@ -31,6 +31,7 @@
  *   - an empty sampled set gives out = 0 and lse = -inf.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -338,3 +339,7 @@ void orc_decode(const float *q, const float *keys, const float *vals, const uint
         free(qc);
     }
 }
+
+/* Threads the oracle's parallel loops use from now on (timing only; the
+ * results do not depend on it). */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
