@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--workload", default="llama8b_96k")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--policy", choices=("sampled", "pages"), default="sampled",
+                    help="sampled: every layer sampled; pages: the pages' decoding policy (layers 0 and 16 "
+                         "dense, i.e. K = 0, and 4 sink + 64 local keys forced into every sampled layer's set)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle baseline budget (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
@@ -129,8 +132,14 @@ def main() -> int:
     total_steps = args.warmup + args.steps
     cap = (n0 + total_steps + 8 + 63) // 64 * 64
     dt = w.torch_dtype
-    log("workload %s: %d layers, B=%d Hq=%d Hkv=%d d=%d n=%d cap=%d (K,L)=(%d,%d)" %
-        (w.name, nlayers, w.batch, w.hq, w.hkv, d, n0, cap, K, L))
+    log("workload %s: %d layers, B=%d Hq=%d Hkv=%d d=%d n=%d cap=%d (K,L)=(%d,%d) policy %s" %
+        (w.name, nlayers, w.batch, w.hq, w.hkv, d, n0, cap, K, L, args.policy))
+    # per layer: (K, L, forced head, forced tail); a dense layer has K = 0 (every key collides in
+    # every table, P = 1: exact attention) and the smallest table count
+    pages = args.policy == "pages"
+    lcfg = [((0, 2, 0, 0) if pages and l in (0, 16) else (K, L, 4 if pages else 0, 64 if pages else 0))
+            for l in range(nlayers)]
+    sampled_layers = [l for l in range(nlayers) if lcfg[l][0] > 0]
 
     # ------------------------------------------------------------------ inputs + code-store build
     layers = []
@@ -142,13 +151,14 @@ def main() -> int:
         for u in range(U):
             b, h = divmod(u, w.hkv)
             synth.unit_kv(args.seed, l, b, h, n0, d, dt, dev, out_k=Kc[u, :n0], out_v=Vc[u, :n0])
-        W = synth.projections(args.seed, l, d, K, L, dev)
-        Wp = mp.mp_proj_pack(W, K, L)
+        Kl, Ll = lcfg[l][0], lcfg[l][1]
+        W = synth.projections(args.seed, l, d, Kl, Ll, dev)
+        Wp = mp.mp_proj_pack(W, Kl, Ll)
         kmean = torch.empty(U, d, dtype=torch.float32, device=dev)
-        codes = torch.zeros(U, L, cap, dtype=torch.uint16, device=dev)
+        codes = torch.zeros(U, Ll, cap, dtype=torch.uint16, device=dev)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        mp.mp_build_codes(Kc, n0, Wp, K, L, kmean=kmean, codes=codes, ws=ws_build)
+        mp.mp_build_codes(Kc, n0, Wp, Kl, Ll, kmean=kmean, codes=codes, ws=ws_build)
         e1.record()
         kn = torch.empty(total_steps, U, d, dtype=dt)
         vn = torch.empty(total_steps, U, d, dtype=dt)
@@ -161,7 +171,7 @@ def main() -> int:
         kn, vn, qs = kn.to(dev), vn.to(dev), qs.to(dev)
         layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1)))
     torch.cuda.synchronize()
-    build_ms = [lay["ev"][0].elapsed_time(lay["ev"][1]) for lay in layers]
+    build_ms = [layers[l]["ev"][0].elapsed_time(layers[l]["ev"][1]) for l in sampled_layers]
     log("built %d layers; build %.3f ms/layer (median)" % (nlayers, float(np.median(build_ms))))
 
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
@@ -193,7 +203,8 @@ def main() -> int:
             k = s - (total_steps - ev_steps)
             ev = kev[k * nlayers + l] if k >= 0 else None
             mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
-                              lay["kmean"], lay["Wp"], w.hkv, n_cur, K, ws, out=outs[l], lse=lses[l], sample_events=ev)
+                              lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
+                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev)
         if timed:
             n_timed.append(n_cur + 1)
         n_cur += 1
@@ -202,7 +213,8 @@ def main() -> int:
     t1 = time.perf_counter()
     wall_ms = (t1 - t0) * 1e3 / args.steps
     ev_ms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
-    kern_ms = np.array([a.elapsed_time(b) for a, b in kev])
+    kern_all = np.array([a.elapsed_time(b) for a, b in kev])
+    kern_ms = kern_all[sampled_layers]  # the roofline is the sampled layers' kernel
     log("step %.3f ms (wall) / %.3f ms (events); sample kernel %.2f us avg over %d launches" %
         (wall_ms, ev_ms, kern_ms.mean() * 1e3, len(kern_ms)))
     keys_per_step = float(np.mean(n_timed)) * U * nlayers
@@ -214,9 +226,10 @@ def main() -> int:
     idx = torch.empty(w.batch, w.hq, cap, dtype=torch.int32, device=dev)
     cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device=dev)
     s_last = total_steps - 1
-    for lay in layers:
+    for l in sampled_layers:
+        lay = layers[l]
         mp.mp_decode_attn(lay["qs"][s_last], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], lay["Wp"], w.hkv,
-                          n_cur, K, idx=idx, count=cnt, ws=ws)
+                          n_cur, K, lcfg[l][2], lcfg[l][3], idx=idx, count=cnt, ws=ws)
         for b in range(w.batch):
             for h in range(w.hkv):
                 mask = torch.zeros(n_cur, dtype=torch.bool, device=dev)
@@ -225,8 +238,8 @@ def main() -> int:
                     mask[idx[b, h * G + g, :c].long()] = True
                 union_sum += int(mask.sum())
         head_sum += int(cnt.sum())
-    union_per_unit = union_sum / (nlayers * U)
-    head_frac = head_sum / (nlayers * w.batch * w.hq * n_cur)
+    union_per_unit = union_sum / (len(sampled_layers) * U)
+    head_frac = head_sum / (len(sampled_layers) * w.batch * w.hq * n_cur)
     e = 2 if w.dtype == "bf16" else 4
     n_dec = float(np.mean(n_timed))
     # algorithmic bytes of one sample launch (one layer): codes of every key once, each distinct sampled
@@ -237,9 +250,11 @@ def main() -> int:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name:
+        if tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages:
             traffic = tr.get("bytes_per_launch")
-    step_bytes = nlayers * bytes_launch
+    # a dense layer reads its (two-table) codes and every key's K and V row
+    dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
+    step_bytes = len(sampled_layers) * bytes_launch + (nlayers - len(sampled_layers)) * dense_bytes
     log("|S_h|/n = %.4f, union per unit %.0f keys (%.4f of n); %.1f MB algorithmic per launch" %
         (head_frac, union_per_unit, union_per_unit / n_dec, bytes_launch / 1e6))
 
@@ -299,7 +314,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
         "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
-                   "head_dim": d, "context": n0, "K": K, "L": L, "parallelism": "single GPU"},
+                   "head_dim": d, "context": n0, "K": K, "L": L, "parallelism": "single GPU",
+                   "policy": ("every layer sampled" if not pages else
+                              "pages: layers 0 and 16 dense (K = 0), 4 sink + 64 local keys forced elsewhere")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "sample_kernel (mp_decode_step / mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,

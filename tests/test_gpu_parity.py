@@ -241,6 +241,36 @@ def test_decode_K0_is_exact_attention():
     assert np.max(np.abs(out.cpu().numpy()[0, 0] - ref)) <= OUT_TOL
 
 
+def test_dense_layer_step_is_exact_attention():
+    """A dense layer of the pages' policy runs as K = 0 (one 0-bit code per
+    table, every key sampled with P = 1) through mp_decode_step: append, then
+    exact softmax attention over all n + 1 keys for every query head."""
+    w = variant("llama8b_layer", K=0, L=2, n=3000)
+    lay = layer(w, seed=91)
+    Wp = mp.mp_proj_pack(lay["W"], 0, w.L)
+    kmean, gcodes = mp.mp_build_codes(lay["Kc"], lay["n"], Wp, 0, w.L)
+    n, U, G = lay["n"], w.batch * w.hkv, w.group
+    kn = torch.randn(U, w.d, generator=torch.Generator().manual_seed(5)).to(w.torch_dtype).cuda()
+    vn = torch.randn(U, w.d, generator=torch.Generator().manual_seed(6)).to(w.torch_dtype).cuda()
+    ws = mp.decode_workspace(w.batch, w.hq, w.hkv, lay["cap"], w.L, "cuda")
+    out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_step(kn, vn, lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, n, 0, ws, out=out, count=cnt)
+    torch.cuda.synchronize()
+    Kh = host_f32(lay["Kc"]).astype(np.float64)
+    Vh = host_f32(lay["Vc"]).astype(np.float64)
+    qh = lay["host"]["q"].reshape(w.batch, w.hq, w.d).astype(np.float64)
+    o = out.cpu().numpy()
+    assert np.all(cnt.cpu().numpy() == n + 1)
+    for b in range(w.batch):
+        for h in range(w.hq):
+            u = b * w.hkv + h // G
+            s = Kh[u, :n + 1] @ qh[b, h] / math.sqrt(w.d)
+            p = np.exp(s - s.max())
+            ref = (p / p.sum()) @ Vh[u, :n + 1]
+            assert np.max(np.abs(o[b, h] - ref)) <= OUT_TOL, (b, h)
+
+
 def test_end_to_end_gpu_codes():
     """The whole GPU path (its own means, codes and query codes).  Where every
     code of a unit equals the oracle's, the sets must be identical."""
