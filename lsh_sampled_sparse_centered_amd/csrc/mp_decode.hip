@@ -38,7 +38,6 @@ DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap) {
   (void)Hq;
   DecodeGeom g;
   g.U = (int64_t)B * Hkv;
-  g.chunk_tiles = 1;
   g.chunk = SCAN_TILE;
   g.nchunks = (n + SCAN_TILE - 1) / SCAN_TILE;
   g.nchunks_max = (cap + SCAN_TILE - 1) / SCAN_TILE;
@@ -291,20 +290,19 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
   const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
   const int64_t tbase = c * SCAN_TILE;
   const int64_t tend = min(n, tbase + SCAN_TILE);
-  const int nsub = 1;
   const uint16_t headbits = (uint16_t)((1u << G) - 1u);
   const u16x2 one = __builtin_bit_cast(u16x2, one2);
 
   // This wave's tables are wave, wave+4, ...  A lane reads 16 bytes (8 keys)
   // at a scalar row base plus its own byte offset.  Loads are unconditional:
-  // lanes past the last key re-read the sub-tile's first 8 keys and tables
+  // lanes past the last key re-read the tile's first 8 keys and tables
   // past the wave's last re-read its last table (all inside the code store;
   // their counts are discarded).
   const int ntw = (L - wave + 3) / 4;
   const int jlast = ntw - 1;
   const int64_t rstride = 8 * cap;  // bytes between this wave's consecutive tables
   const char *rows0 = (const char *)(codes + u * (int64_t)L * cap + (int64_t)wave * cap + tbase);
-  uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
+  const uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
   // the code store is streamed once: non-temporal loads keep it from evicting
   // the caches' reused lines (query codes, keys and values of the list)
 #define MP_ROW(j) \
@@ -345,16 +343,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
 
   int nu = 0;  // entries in the union list so far
   uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
-  for (int st = 0; st < nsub; ++st) {
-    const int64_t sbase = tbase + (int64_t)st * SCAN_TILE;
-    if (st > 0) {
-      rows0 += 2 * SCAN_TILE;  // 512 keys further along every row
-      lo = (sbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
-      if (ntw > 0) {
-#pragma unroll
-        for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(jj);
-      }
-    }
+  {
+    const int64_t sbase = tbase;
     // ---- scan
     uint32_t acc[GM][4];
 #pragma unroll
@@ -465,7 +455,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
       lmask[p2] = (uint16_t)mhi;
       if (uent) uent[p2] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
     }
-    __syncthreads();  // list complete; red and wtot free for the next sub-tile
+    __syncthreads();  // list complete
   }
 #undef MP_ROW
   if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;

@@ -49,7 +49,6 @@ LnPCoef lnp_coef(int L);
 
 struct DecodeGeom {
   int64_t U;          // units = B * Hkv
-  int chunk_tiles;    // scan tiles per block
   int64_t chunk;      // keys per block = chunk_tiles * SCAN_TILE
   int64_t nchunks;    // blocks per unit for this n
   int64_t nchunks_max;  // for n = cap (workspace sizing)
