@@ -3,6 +3,7 @@
 // the table-major code store (Section 2.2 "Locality sensitive hashing";
 // Section 4.3 "Hash function selection" and "Data pre-processing").
 #include <algorithm>
+#include <type_traits>
 
 #include "mp_internal.h"
 
@@ -380,37 +381,113 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
         }
     }
   };
-  int buf = 0;
-  for (int tg = t0; tg < t1; tg += ENC_TG) {
-    if (npend) emit_stage();
-    const int tnext = tg + ENC_TG;
-    if (tnext < t1) MP_FETCH(buf ^ 1, tnext);
-    // every stage runs ENC_TG tiles (one straight block of matrix-core and
-    // vector work for the scheduler); tiles past t1 read stale LDS and are
-    // dropped
+  // Fast path (2, 3 or 4 tables per tile, code region of the unit below
+  // 2 GB): the next stage's projection copy is issued before this stage's
+  // code stores, and a stage ends with a wait for all but the last
+  // ENC_TG * TPT vector-memory operations (the code stores) and a barrier
+  // without a memory fence, so no wave waits for its own code stores to be
+  // written.  Each lane stores its row's codes directly (one 2-byte store per
+  // table: a wave writes 128 contiguous bytes of a table row), and every lane
+  // issues exactly ENC_TG * TPT stores per stage: codes of tables past l1,
+  // of tiles past the stage's last and of rows past the end get an offset
+  // past the buffer's end, which the hardware drops.  No LDS is written
+  // between the copy's issue and the barrier.  The wait relies on the vector
+  // memory counter retiring loads and stores in issue order, so "all but the
+  // last NST" includes every projection-copy load issued before the stores.
+  const int64_t oreach = 2 * ((int64_t)(L - 1) * out_sl + (rows - 1) * out_si + 1);  // bytes of the unit's codes
+  const int ftpt = (oreach <= 0x7fffffffLL && tpt >= 2 && tpt <= 4) ? tpt : 0;
+  const __amdgpu_buffer_rsrc_t orsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(out + u * out_su), 0, (int)min(oreach, (int64_t)0x7fffffff), 0x00020000);
+  const int64_t my_off = my_row * out_si;
+  auto emit_direct = [&](auto tptc) {
+    constexpr int TPT = decltype(tptc)::value;
 #pragma unroll
-    for (int tt = 0; tt < ENC_TG; ++tt) {
-      f32x16 acc0 = {}, acc1 = {};
+    for (int i = 0; i < ENC_TG; ++i)
 #pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, wsh[buf][(tt * KSTEPS + s) * 64 + lane]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[0][s], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xb[1][s], acc1, 0, 0, 0);
+      for (int j = 0; j < TPT; ++j) {
+        const int l = (tpend + i) * TPT + j;
+        const bool ok = i < npend && l < l1 && my_ok;
+        const uint32_t off = ok ? (uint32_t)(2 * ((int64_t)l * out_sl + my_off)) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b16((unsigned short)__builtin_amdgcn_ubfe(wd[i], (uint32_t)(K * j), (uint32_t)K),
+                                              orsrc, off, 0, 0);
       }
-      // lane l < 32 holds bits 0-15 of row l in m0 and bits 0-15 of row
-      // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
-      // cross-half swap leaves lane l with row l's halves and lane 32 + l
-      // with row 32 + l's.
-      const auto sw = __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), sign_bits16(acc1), false, false);
-      const uint32_t word = sw[0] | (sw[1] << 16);
-      wd[tt] = my_nz ? word : 0u;
+  };
+  // The stage loop is instantiated per path (general, and fast for each
+  // tables-per-tile count), so that the compiler's wait analysis of one never
+  // merges with another's.
+  auto run_stages = [&](auto tptc) {
+    constexpr int TPT = decltype(tptc)::value;  // 0: general path
+    constexpr int NST = ENC_TG * (TPT > 0 ? TPT : 1);
+    int buf = 0;
+    for (int tg = t0; tg < t1; tg += ENC_TG) {
+      const int tnext = tg + ENC_TG;
+      const bool stores = TPT > 0 && npend;
+      if constexpr (TPT > 0) {
+        if (tnext < t1) MP_FETCH(buf ^ 1, tnext);
+        asm volatile("" ::: "memory");
+        if (npend) emit_direct(tptc);
+        asm volatile("" ::: "memory");
+      } else {
+        if (npend) emit_stage();
+        if (tnext < t1) MP_FETCH(buf ^ 1, tnext);
+      }
+      // every stage runs ENC_TG tiles (one straight block of matrix-core and
+      // vector work for the scheduler; tiles past t1 read stale LDS and are
+      // dropped).  The next tile's A operands are read from LDS while the
+      // current tile's matrix-core ops run.
+      bf16x8 ap[2][KSTEPS];
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s) ap[0][s] = __builtin_bit_cast(bf16x8, wsh[buf][s * 64 + lane]);
+#pragma unroll
+      for (int tt = 0; tt < ENC_TG; ++tt) {
+        f32x16 acc0 = {}, acc1 = {};
+        if (tt + 1 < ENC_TG) {
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s)
+            ap[(tt + 1) & 1][s] = __builtin_bit_cast(bf16x8, wsh[buf][((tt + 1) * KSTEPS + s) * 64 + lane]);
+        }
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[0][s], acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[1][s], acc1, 0, 0, 0);
+        }
+        // lane l < 32 holds bits 0-15 of row l in m0 and bits 0-15 of row
+        // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
+        // cross-half swap leaves lane l with row l's halves and lane 32 + l
+        // with row 32 + l's.
+        const auto sw = __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), sign_bits16(acc1), false, false);
+        const uint32_t word = sw[0] | (sw[1] << 16);
+        wd[tt] = my_nz ? word : 0u;
+      }
+      tpend = tg;
+      npend = min(ENC_TG, t1 - tg);
+      if (stores) {
+        // vmcnt(NST) lgkmcnt(0): this wave's projection copy (issued before
+        // its NST code stores) has landed in LDS and its LDS reads are done
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt((NST & 15) | (7 << 4) | ((NST >> 4) << 14));
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      } else {
+        __syncthreads();
+      }
+      buf ^= 1;
     }
-    tpend = tg;
-    npend = min(ENC_TG, t1 - tg);
-    __syncthreads();
-    buf ^= 1;
-  }
-  if (npend) emit_stage();
+    if (npend) {
+      if constexpr (TPT > 0)
+        emit_direct(tptc);
+      else
+        emit_stage();
+    }
+  };
+  if (ftpt == 3)
+    run_stages(std::integral_constant<int, 3>{});
+  else if (ftpt == 4)
+    run_stages(std::integral_constant<int, 4>{});
+  else if (ftpt == 2)
+    run_stages(std::integral_constant<int, 2>{});
+  else
+    run_stages(std::integral_constant<int, 0>{});
 #undef MP_FETCH
 }
 
