@@ -138,6 +138,7 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
   // one sampling block per 512-key tile per unit, in a 1-D grid of < 2^31 threads
   if ((int64_t)B * Hkv * ((cap + SCAN_TILE - 1) / SCAN_TILE) > ((int64_t)1 << 23)) return MP_ERR_UNSUPPORTED;
+  if (cap >= ((int64_t)1 << 26)) return MP_ERR_UNSUPPORTED;  // a scan batch's row offsets fit 32 bits
   if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
   return MP_OK;
 }

@@ -268,7 +268,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     ScanLds s;
     AttnLds a;
   } sm;  // scan and attention phases never overlap in time
-  extern __shared__ uint32_t qpk[];  // [L][GM] query codes, each twice per word
+  extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
+  uint32_t *qpk = (uint32_t *)qpk4;
   __shared__ float qsh[GM][D];
   __shared__ float msh[D];
   __shared__ float qn_sh[GM], qmu_sh[GM];
@@ -294,24 +295,30 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
   const u16x2 one = __builtin_bit_cast(u16x2, one2);
 
   // This wave's tables are wave, wave+4, ...  A lane reads 16 bytes (8 keys)
-  // at a scalar row base plus its own byte offset.  Loads are unconditional:
-  // lanes past the last key re-read the tile's first 8 keys and tables
-  // past the wave's last re-read its last table (all inside the code store;
-  // their counts are discarded).
+  // per table row: a batch of MP_SB rows is read through a buffer resource
+  // based at the batch's first row, with the row's offset in a scalar and the
+  // lane's in a vector register (no per-row address arithmetic).  Loads are
+  // unconditional: lanes past the last key re-read the tile's first 8 keys
+  // and tables past the wave's last re-read its last table (all inside the
+  // code store; their counts are discarded).  The code store is streamed
+  // once: non-temporal loads keep it from evicting the caches' reused lines
+  // (query codes, keys and values of the list).
   const int ntw = (L - wave + 3) / 4;
   const int jlast = ntw - 1;
   const int64_t rstride = 8 * cap;  // bytes between this wave's consecutive tables
+  const uint32_t rstride32 = (uint32_t)rstride;  // MP_SB rows span < 2^32 bytes (cap < 2^26)
   const char *rows0 = (const char *)(codes + u * (int64_t)L * cap + (int64_t)wave * cap + tbase);
   const uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
-  // the code store is streamed once: non-temporal loads keep it from evicting
-  // the caches' reused lines (query codes, keys and values of the list)
-#define MP_ROW(j) \
-  __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4 *)(rows0 + (int64_t)min((j), jlast) * rstride + lo)))
   uint4 cw[MP_SB];
-  if (ntw > 0) {
+  auto load_batch = [&](int j0) {  // j0 <= jlast
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(rows0 + (int64_t)j0 * rstride), 0, -1, 0x00020000);
 #pragma unroll
-    for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(jj);
-  }
+    for (int jj = 0; jj < MP_SB; ++jj)
+      cw[jj] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (uint32_t)(min(j0 + jj, jlast) - j0) * rstride32, 2));
+  };
+  if (ntw > 0) load_batch(0);
 
   // ---- prologue: query codes (packed twice per word), queries, key mean
   for (int i = tid; i < L * GM; i += 256) {
@@ -353,28 +360,62 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
       for (int w = 0; w < 4; ++w) acc[h][w] = 0;
 #define MP_MIS(word, Q) \
   __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, (word) ^ (Q)), one))
-    for (int j0 = 0; j0 < ntw; j0 += MP_SB) {
-      if (j0 > 0) {
+    // query codes of table l for every head (GM >= 4: 16-byte LDS reads)
+    auto qcodes_of = [&](int l, uint32_t (&Q)[GM]) {
+      if constexpr (GM >= 4) {
 #pragma unroll
-        for (int jj = 0; jj < MP_SB; ++jj) cw[jj] = MP_ROW(j0 + jj);
+        for (int k = 0; k < GM / 4; ++k) {
+          const u32x4 v = qpk4[l * (GM / 4) + k];
+          Q[4 * k] = v[0];
+          Q[4 * k + 1] = v[1];
+          Q[4 * k + 2] = v[2];
+          Q[4 * k + 3] = v[3];
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < GM; ++h) Q[h] = qpk[l * GM + h];
       }
+    };
+    // two tables (rows ra, rb: tables l and l + 4) into the mismatch counts
+    auto scan_pair = [&](const uint4 &ra, const uint4 &rb, int l) {
+      uint32_t Qa[GM], Qb[GM];
+      qcodes_of(l, Qa);
+      qcodes_of(l + 4, Qb);
+      const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w};
+      const uint32_t b4[4] = {rb.x, rb.y, rb.z, rb.w};
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa[h]) + MP_MIS(b4[w], Qb[h]);
+        __builtin_amdgcn_sched_barrier(0);  // few temporaries live at once
+      }
+    };
+    // whole batches (branch-free pairs), then the wave's last, partial batch
+    // outside the loop (one code path per loop body keeps the counts in one
+    // set of registers)
+    int j0 = 0;
+    for (; j0 + MP_SB <= ntw; j0 += MP_SB) {
+      if (j0 > 0) load_batch(j0);
 #pragma unroll
       for (int jj = 0; jj < MP_SB; jj += 2) {
-        if (j0 + jj < ntw) {
-          const int l = wave + 4 * (j0 + jj);
-          const uint32_t a4[4] = {cw[jj].x, cw[jj].y, cw[jj].z, cw[jj].w};
-          const uint32_t b4[4] = {cw[jj + 1].x, cw[jj + 1].y, cw[jj + 1].z, cw[jj + 1].w};
-          const bool two = j0 + jj + 1 < ntw;
+        scan_pair(cw[jj], cw[jj + 1], wave + 4 * (j0 + jj));
+        // one pair's query codes live at a time
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (j0 < ntw) {  // tables past the wave's last add no mismatch (selects, no branches)
+      if (j0 > 0) load_batch(j0);
 #pragma unroll
-          for (int h = 0; h < GM; ++h) {
-            const uint32_t Qa = qpk[l * GM + h];
-            const uint32_t Qb = two ? qpk[(l + 4) * GM + h] : 0u;
+      for (int jj = 0; jj < MP_SB; ++jj) {
+        const bool live = j0 + jj < ntw;
+        uint32_t Qa[GM];
+        qcodes_of(min(wave + 4 * (j0 + jj), L - 1), Qa);
+        const uint32_t a4[4] = {cw[jj].x, cw[jj].y, cw[jj].z, cw[jj].w};
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const uint32_t mb = two ? MP_MIS(b4[w], Qb) : 0u;  // a missing second table adds 0
-              acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa) + mb;
-            }
-          }
+        for (int h = 0; h < GM; ++h) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[h][w] += live ? MP_MIS(a4[w], Qa[h]) : 0u;
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -457,7 +498,6 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     }
     __syncthreads();  // list complete
   }
-#undef MP_ROW
   if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;
 
   // ---- attention over the union list
