@@ -38,7 +38,8 @@
  *    2 <= L <= 512 tables, K*L <= 4096.  Query heads per KV head
  *    G = Hq / Hkv must divide exactly and be at most 8.  Cache capacities
  *    `cap` must be multiples of 8 (16-byte code rows).  Units U = B * Hkv
- *    at most 65535, and U * ceil(cap / 512) at most 2^23 for the decode.
+ *    at most 65535; for the decode U * ceil(cap / 512) at most 2^23 and
+ *    cap below 2^26 (MP_ERR_UNSUPPORTED otherwise).
  *  - Element types: MP_BF16 (bfloat16) or MP_F32 (float32) for keys, values
  *    and queries; codes are uint16; means, outputs and lse are float32.
  *  - Layouts (row-major, innermost last):

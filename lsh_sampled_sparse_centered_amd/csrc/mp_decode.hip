@@ -310,15 +310,21 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
   const char *rows0 = (const char *)(codes + u * (int64_t)L * cap + (int64_t)wave * cap + tbase);
   const uint32_t lo = (tbase + 8 * lane < tend) ? 16u * (uint32_t)lane : 0u;
   uint4 cw[MP_SB];
-  auto load_batch = [&](int j0) {  // j0 <= jlast
+  // rows j0 + hf*MP_SB/2 .. + MP_SB/2 - 1 (clamped to the last) into cw's half hf
+  auto load_half = [&](int j0, int hf) {
+    const int jb = min(j0 + hf * (MP_SB / 2), jlast);
     const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(rows0 + (int64_t)j0 * rstride), 0, -1, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void *)(rows0 + (int64_t)jb * rstride), 0, -1, 0x00020000);
 #pragma unroll
-    for (int jj = 0; jj < MP_SB; ++jj)
-      cw[jj] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lo, (uint32_t)(min(j0 + jj, jlast) - j0) * rstride32, 2));
+    for (int r = 0; r < MP_SB / 2; ++r)
+      cw[hf * (MP_SB / 2) + r] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rs, lo, (uint32_t)(min(j0 + hf * (MP_SB / 2) + r, jlast) - jb) * rstride32, 2));
   };
-  if (ntw > 0) load_batch(0);
+  if (ntw > 0) {
+    load_half(0, 0);
+    load_half(0, 1);
+  }
 
   // ---- prologue: query codes (packed twice per word), queries, key mean
   for (int i = tid; i < L * GM; i += 256) {
@@ -393,18 +399,23 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     // whole batches (branch-free pairs), then the wave's last, partial batch
     // outside the loop (one code path per loop body keeps the counts in one
     // set of registers)
+    // Two halves per batch: the next batch's half is issued as soon as this
+    // half's rows have been counted, so a wave keeps loads in flight while
+    // it computes.
     int j0 = 0;
     for (; j0 + MP_SB <= ntw; j0 += MP_SB) {
-      if (j0 > 0) load_batch(j0);
 #pragma unroll
-      for (int jj = 0; jj < MP_SB; jj += 2) {
-        scan_pair(cw[jj], cw[jj + 1], wave + 4 * (j0 + jj));
-        // one pair's query codes live at a time
-        __builtin_amdgcn_sched_barrier(0);
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int jj = hf * (MP_SB / 2); jj < (hf + 1) * (MP_SB / 2); jj += 2) {
+          scan_pair(cw[jj], cw[jj + 1], wave + 4 * (j0 + jj));
+          // one pair's query codes live at a time
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        load_half(j0 + MP_SB, hf);
       }
     }
-    if (j0 < ntw) {  // tables past the wave's last add no mismatch (selects, no branches)
-      if (j0 > 0) load_batch(j0);
+    if (j0 < ntw) {  // rows already loaded; tables past the wave's last add no mismatch (selects)
 #pragma unroll
       for (int jj = 0; jj < MP_SB; ++jj) {
         const bool live = j0 + jj < ntw;
