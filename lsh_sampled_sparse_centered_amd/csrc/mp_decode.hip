@@ -326,17 +326,53 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     load_half(0, 1);
   }
 
-  // ---- prologue: query codes (packed twice per word), queries, key mean
-  for (int i = tid; i < L * GM; i += 256) {
-    const int l = i / GM, h = i % GM;
-    const uint32_t code = h < G ? qcodes[(qrow0 + h) * L + l] : 0u;
-    qpk[i] = code | (code << 16);
+  // ---- prologue: query codes (packed twice per word), queries, key mean.
+  // Every load of a pass is issued before any is used (one memory round trip
+  // instead of one per element); indices past the end re-read a valid
+  // element and are not stored.
+  constexpr int QPASS = 4;                     // query-code loads per thread and pass
+  constexpr int QV = (GM * D + 255) / 256;     // query elements per thread
+  {
+    const int nq = L * GM;
+    int i0 = tid;
+    do {
+      uint16_t cq[QPASS];
+      T qv[QV];
+      float mv = 0.0f;
+#pragma unroll
+      for (int k = 0; k < QPASS; ++k) {
+        const int i = min(i0 + 256 * k, nq - 1), l = i / GM, h = min(i % GM, G - 1);
+        cq[k] = qcodes[(qrow0 + h) * L + l];
+      }
+      const bool first = i0 == tid;
+      if (first) {
+#pragma unroll
+        for (int k = 0; k < QV; ++k) {
+          const int i = min(tid + 256 * k, GM * D - 1), h = min(i / D, G - 1);
+          qv[k] = q[(qrow0 + h) * D + i % D];
+        }
+        mv = kmean[u * D + (tid & (D - 1))];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keeps the loads ahead of every use
+#pragma unroll
+      for (int k = 0; k < QPASS; ++k) {
+        const int i = i0 + 256 * k;
+        if (i < nq) {
+          const uint32_t code = i % GM < G ? (uint32_t)cq[k] : 0u;
+          qpk[i] = code | (code << 16);
+        }
+      }
+      if (first) {
+#pragma unroll
+        for (int k = 0; k < QV; ++k) {
+          const int i = tid + 256 * k;
+          if (i < GM * D) qsh[i / D][i % D] = i / D < G ? (float)qv[k] : 0.0f;
+        }
+        if (tid < D) msh[tid] = mv;
+      }
+      i0 += 256 * QPASS;
+    } while (i0 < nq);
   }
-  for (int i = tid; i < GM * D; i += 256) {
-    const int h = i / D, t = i % D;
-    qsh[h][t] = h < G ? (float)q[(qrow0 + h) * D + t] : 0.0f;
-  }
-  if (tid < D) msh[tid] = kmean[u * D + tid];
   if (tid < GM) hcnt[tid] = 0;
   __syncthreads();
 

@@ -45,11 +45,12 @@ hipError_t launch_proj_pack(const float *W, int K, int L, void *Wp, hipStream_t 
 // ---------------------------------------------------------------------------
 // Key mean k_avg = (1/n) sum_i k_i per unit, accumulated in fp64 and rounded
 // once to fp32.  Stage 1: each block sums KM_ROWS rows of one unit
-// (16 lanes x 8 dims cover a row; 16 x KM_UNR rows in flight per pass).
+// (16 lanes x 8 dims cover a row; 16 x KM_UNR rows in flight per pass, all
+// loads of a pass issued together).
 // Stage 2: one block per unit adds the stage-1 sums in a fixed order
 // (deterministic).
 constexpr int KM_ROWS = 512;   // rows per block
-constexpr int KM_UNR = 4;      // rows a 16-lane group has in flight
+constexpr int KM_UNR = 8;      // rows a 16-lane group has in flight
 constexpr int KM_SLICES = 8;   // threads per dimension in the final sum
 
 int kmean_parts(int64_t n) { return (int)((n + KM_ROWS - 1) / KM_ROWS); }
@@ -69,6 +70,37 @@ __device__ inline void load8<__bf16>(const __bf16 *p, float (&v)[8]) {
   for (int e = 0; e < 8; ++e) v[e] = (float)a[e];
 }
 
+// A row slice of 8 elements as raw 16-byte words (so the loads can all be
+// issued before any is converted).
+template <typename T>
+struct KRow;
+template <>
+struct KRow<__bf16> {
+  uint4 a;
+  __device__ void load(const __bf16 *p) { a = *(const uint4 *)p; }
+  __device__ void add_to(double (&acc)[8], bool live) const {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += live ? (double)(float)b[e] : 0.0;
+  }
+};
+template <>
+struct KRow<float> {
+  uint4 a, b;
+  __device__ void load(const float *p) {
+    a = *(const uint4 *)p;
+    b = *(const uint4 *)(p + 4);
+  }
+  __device__ void add_to(double (&acc)[8], bool live) const {
+    const f32x4 x = __builtin_bit_cast(f32x4, a), y = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += live ? (double)x[e] : 0.0;
+      acc[e + 4] += live ? (double)y[e] : 0.0;
+    }
+  }
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict__ Kc, int64_t n, int64_t cap,
                                                             int nparts, double *__restrict__ partial) {
@@ -80,21 +112,14 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict_
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   const T *base = Kc + u * cap * D + 8 * j16;
   for (int64_t r = r0 + rsub; r < r1; r += 16 * KM_UNR) {
-    float v[KM_UNR][8];
+    // every load of the pass is issued before any is used: rows past the
+    // block's last re-read its last row and add nothing
+    KRow<T> v[KM_UNR];
 #pragma unroll
-    for (int k = 0; k < KM_UNR; ++k) {  // independent loads first
-      const int64_t rk = r + 16 * k;
-      if (rk < r1) {
-        load8<T>(base + rk * D, v[k]);
-      } else {
+    for (int k = 0; k < KM_UNR; ++k) v[k].load(base + min(r + 16 * k, r1 - 1) * D);
+    __builtin_amdgcn_sched_barrier(0);  // keeps the loads ahead of every use
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[k][e] = 0.0f;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < KM_UNR; ++k)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += (double)v[k][e];
+    for (int k = 0; k < KM_UNR; ++k) v[k].add_to(acc, r + 16 * k < r1);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) red[rsub][8 * j16 + e] = acc[e];
@@ -109,21 +134,23 @@ __global__ __launch_bounds__(256) void kmean_partial_kernel(const T *__restrict_
 
 __global__ __launch_bounds__(D * KM_SLICES) void kmean_final_kernel(const double *__restrict__ partial, int nparts,
                                                                    int64_t n, float *__restrict__ kmean) {
-  // thread (slice, dim) adds parts slice, slice + KM_SLICES, ... (four loads
-  // in flight), then the slices are added in slice order: a fixed order
+  // thread (slice, dim) adds parts slice, slice + KM_SLICES, ... (eight
+  // loads in flight: unconditional, parts past the last re-read it and add
+  // nothing), then the slices are added in slice order: a fixed order
   __shared__ double red[KM_SLICES][D];
   const int64_t u = blockIdx.x;
   const int dim = threadIdx.x % D, slice = threadIdx.x / D;
   const double *p0 = partial + u * (int64_t)nparts * D + dim;
-  double s4[4] = {0, 0, 0, 0};
-  for (int p = slice; p < nparts; p += 4 * KM_SLICES) {
+  double s8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int p = slice; p < nparts; p += 8 * KM_SLICES) {
+    double v[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int pk = p + k * KM_SLICES;
-      if (pk < nparts) s4[k] += p0[(int64_t)pk * D];
-    }
+    for (int k = 0; k < 8; ++k) v[k] = p0[(int64_t)min(p + k * KM_SLICES, nparts - 1) * D];
+    __builtin_amdgcn_sched_barrier(0);  // keeps the loads ahead of every use
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s8[k] += p + k * KM_SLICES < nparts ? v[k] : 0.0;
   }
-  red[slice][dim] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  red[slice][dim] = ((s8[0] + s8[1]) + (s8[2] + s8[3])) + ((s8[4] + s8[5]) + (s8[6] + s8[7]));
   __syncthreads();
   if (slice == 0) {
     double s = 0.0;
