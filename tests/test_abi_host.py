@@ -121,6 +121,8 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(wsb=100) == WS
     assert _decode(d=96) == UNSUP
     assert _decode(B=70000, Hq=8, Hkv=8) == UNSUP
+    assert _decode(cap=1 << 26) == UNSUP  # a scan batch's row offsets must fit 32 bits
+    assert _decode(cap=(1 << 26) - 8) != UNSUP
     for arg in ("q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _decode(**{arg: FAKE + 2}) == ARG, arg
 

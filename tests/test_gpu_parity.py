@@ -89,14 +89,17 @@ def test_query_codes(name):
     assert nbad == 0
 
 
-@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 7, 11, 12, 15])
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 6, 7, 8, 11, 12, 15, 16])
 def test_codes_every_table_width(K):
     """Codes of every table width the encoders handle differently: a 32-bit
-    tile word holds floor(32/K) tables (32 for K = 1 down to 2 for K >= 11),
-    K <= 3 stores each code from its lane, K >= 4 transposes a stage's codes
-    through LDS.  L = 37 leaves a partial last tile; n = 700 a ragged last
-    row block.  Build (large encoder), 8 query rows and one append (small
-    encoder), all against the oracle."""
+    tile word holds floor(32/K) tables (32 for K = 1 down to 2 for K >= 11).
+    In the build encoder, 2 to 4 tables per tile (K = 7 to 16) take the path
+    whose lanes store their codes directly with a fixed number of buffer
+    stores per stage (dropped past the row or table range); 5 to 8 tables
+    (K = 4 to 6) transpose a stage's codes through LDS; K <= 3 store each
+    code from its lane.  L = 37 leaves a partial last tile; n = 700 a ragged
+    last row block.  Build (large encoder), 8 query rows and one append
+    (small encoder), all against the oracle."""
     w = variant("llama8b_layer", hq=4, hkv=2, n=700, K=K, L=37)
     lay = layer(w, seed=40 + K)
     km, codes, margin, qc = oracle_codes(w, lay)
