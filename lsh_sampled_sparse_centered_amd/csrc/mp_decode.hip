@@ -14,6 +14,9 @@ namespace mp {
 #ifndef MP_OCC
 #define MP_OCC 6  // waves per SIMD the G <= 4 kernels are compiled for
 #endif
+#ifndef MP_OCC8
+#define MP_OCC8 5  // waves per SIMD the G = 8 kernels are compiled for (96 VGPRs)
+#endif
 #ifndef MP_SB
 #define MP_SB 8  // code-store rows per load batch of a wave
 #endif
@@ -248,7 +251,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 // The query codes, queries and key mean are fetched while the first batch
 // of codes is in flight.  One partial record (m, l, count, o) per head.
 template <typename T, int GM>
-__global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
+__global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
@@ -420,16 +423,26 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
     };
     // two tables (rows ra, rb: tables l and l + 4) into the mismatch counts
     auto scan_pair = [&](const uint4 &ra, const uint4 &rb, int l) {
-      uint32_t Qa[GM], Qb[GM];
-      qcodes_of(l, Qa);
-      qcodes_of(l + 4, Qb);
       const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w};
       const uint32_t b4[4] = {rb.x, rb.y, rb.z, rb.w};
+      if constexpr (GM == 8) {  // eight heads: one head's two codes live at a time (register budget)
 #pragma unroll
-      for (int h = 0; h < GM; ++h) {
+        for (int h = 0; h < GM; ++h) {
+          const uint32_t Qa = qpk[l * GM + h], Qb = qpk[(l + 4) * GM + h];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa[h]) + MP_MIS(b4[w], Qb[h]);
-        __builtin_amdgcn_sched_barrier(0);  // few temporaries live at once
+          for (int w = 0; w < 4; ++w) acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa) + MP_MIS(b4[w], Qb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        uint32_t Qa[GM], Qb[GM];
+        qcodes_of(l, Qa);
+        qcodes_of(l + 4, Qb);
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[h][w] = acc[h][w] + MP_MIS(a4[w], Qa[h]) + MP_MIS(b4[w], Qb[h]);
+          __builtin_amdgcn_sched_barrier(0);  // few temporaries live at once
+        }
       }
     };
     // whole batches (branch-free pairs), then the wave's last, partial batch
@@ -455,13 +468,15 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : 4)) void sample_kernel(
 #pragma unroll
       for (int jj = 0; jj < MP_SB; ++jj) {
         const bool live = j0 + jj < ntw;
+        const int l = min(wave + 4 * (j0 + jj), L - 1);
         uint32_t Qa[GM];
-        qcodes_of(min(wave + 4 * (j0 + jj), L - 1), Qa);
+        if constexpr (GM != 8) qcodes_of(l, Qa);
         const uint32_t a4[4] = {cw[jj].x, cw[jj].y, cw[jj].z, cw[jj].w};
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
+          const uint32_t Q = GM == 8 ? qpk[l * GM + h] : Qa[h];
 #pragma unroll
-          for (int w = 0; w < 4; ++w) acc[h][w] += live ? MP_MIS(a4[w], Qa[h]) : 0u;
+          for (int w = 0; w < 4; ++w) acc[h][w] += live ? MP_MIS(a4[w], Q) : 0u;
           __builtin_amdgcn_sched_barrier(0);
         }
       }
