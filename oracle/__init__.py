@@ -60,18 +60,22 @@ def lib():
         L.orc_sampling_prob_p.restype = ctypes.c_double
         L.orc_sampling_prob.argtypes = [ctypes.c_double, _int, _int]
         L.orc_sampling_prob.restype = ctypes.c_double
-        L.orc_scan.argtypes = [_u16p, _i64, _i64, _int, _u16p, _i64, _i64, _vp, _vp]
-        L.orc_scan.restype = _i64
+        L.orc_sampling_prob_pt.argtypes = [ctypes.c_double, _int, _int]
+        L.orc_sampling_prob_pt.restype = ctypes.c_double
+        L.orc_sampling_prob_t.argtypes = [ctypes.c_double, _int, _int, _int]
+        L.orc_sampling_prob_t.restype = ctypes.c_double
+        L.orc_scan_t.argtypes = [_u16p, _i64, _i64, _int, _int, _u16p, _i64, _i64, _vp, _vp]
+        L.orc_scan_t.restype = _i64
         L.orc_match_counts.argtypes = [_u16p, _i64, _i64, _int, _u16p, _i32p]
         L.orc_match_counts.restype = None
-        L.orc_attend.argtypes = [_f32p, _f32p, _f32p, _i64, _int, _vp, _int, _int, _i32p, _vp, _i64, _f64p,
-                                 _f64p, _vp]
-        L.orc_attend.restype = None
+        L.orc_attend_t.argtypes = [_f32p, _f32p, _f32p, _i64, _int, _vp, _int, _int, _int, _i32p, _vp, _i64,
+                                   _f64p, _f64p, _vp]
+        L.orc_attend_t.restype = None
         L.orc_build.argtypes = [_f32p, _i64, _i64, _i64, _int, _f32p, _int, _int, _f32p, _u16p, _vp]
         L.orc_build.restype = None
-        L.orc_decode.argtypes = [_f32p, _f32p, _f32p, _u16p, _f32p, _f32p, _vp, _int, _int, _int, _i64, _i64,
-                                 _int, _int, _int, _i64, _i64, _vp, _f32p, _f32p, _vp, _i32p]
-        L.orc_decode.restype = None
+        L.orc_decode_t.argtypes = [_f32p, _f32p, _f32p, _u16p, _f32p, _f32p, _vp, _int, _int, _int, _i64, _i64,
+                                   _int, _int, _int, _int, _i64, _i64, _vp, _f32p, _f32p, _vp, _i32p]
+        L.orc_decode_t.restype = None
         _lib = L
     return _lib
 
@@ -129,27 +133,28 @@ def table_collision_prob(cos_qk: float, K: int) -> float:
     return lib().orc_table_collision_prob(float(cos_qk), int(K))
 
 
-def sampling_prob_p(p: float, L: int) -> float:
-    """P(at least 2 of L tables collide) for per-table probability p (Equation 10)."""
-    return lib().orc_sampling_prob_p(float(p), int(L))
+def sampling_prob_p(p: float, L: int, T: int = 2) -> float:
+    """P(at least T of L tables collide) for per-table probability p (Equation 10 for T = 2)."""
+    return lib().orc_sampling_prob_pt(float(p), int(L), int(T))
 
 
-def sampling_prob(cos_qk: float, K: int, L: int) -> float:
-    """Sampling probability of a key at cosine ``cos_qk`` from the query (Equation 10)."""
-    return lib().orc_sampling_prob(float(cos_qk), int(K), int(L))
+def sampling_prob(cos_qk: float, K: int, L: int, T: int = 2) -> float:
+    """Sampling probability of a key at cosine ``cos_qk`` from the query (Equation 10 for T = 2)."""
+    return lib().orc_sampling_prob_t(float(cos_qk), int(K), int(L), int(T))
 
 
-def scan(codes_tn, qcode, n_static_head: int = 0, n_static_tail: int = 0):
+def scan(codes_tn, qcode, n_static_head: int = 0, n_static_tail: int = 0, T: int = 2):
     """Sampled set of one query head: ascending indices and forced flags.
 
-    ``codes_tn`` is table-major ``[L][n]``; Section 4.3 (at least 2 tables).
+    ``codes_tn`` is table-major ``[L][n]``; Section 4.3 (at least T tables,
+    the pages' T = 2).
     """
     codes_tn = np.ascontiguousarray(codes_tn, dtype=np.uint16)
     L, n = codes_tn.shape
     qcode = np.ascontiguousarray(qcode, dtype=np.uint16)
     idx = np.zeros(max(n, 1), np.int32)
     forced = np.zeros(max(n, 1), np.uint8)
-    cnt = lib().orc_scan(codes_tn, n, n, L, qcode, n_static_head, n_static_tail, _ptr(idx), _ptr(forced))
+    cnt = lib().orc_scan_t(codes_tn, n, n, L, T, qcode, n_static_head, n_static_tail, _ptr(idx), _ptr(forced))
     return idx[:cnt].copy(), forced[:cnt].astype(bool)
 
 
@@ -161,7 +166,7 @@ def match_counts(codes_tn, qcode) -> np.ndarray:
     return m
 
 
-def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool = False):
+def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool = False, T: int = 2):
     """Estimator of one head over its sampled set (Equations 9 and 11).
 
     Returns ``(out[d] fp64, lse)`` (and the per-sample log-weights).
@@ -175,8 +180,8 @@ def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool 
     lse = np.zeros(1, np.float64)
     logw = np.zeros(max(cnt, 1), np.float64) if with_logw else None
     mu_a = None if mu is None else _f32(mu)
-    lib().orc_attend(q, keys, vals, d, d, _ptr(mu_a), K, L, idx if cnt else np.zeros(1, np.int32), _ptr(forced_a),
-                     cnt, out, lse, _ptr(logw))
+    lib().orc_attend_t(q, keys, vals, d, d, _ptr(mu_a), K, L, T, idx if cnt else np.zeros(1, np.int32),
+                       _ptr(forced_a), cnt, out, lse, _ptr(logw))
     if with_logw:
         return out, float(lse[0]), logw[:cnt]
     return out, float(lse[0])
@@ -199,8 +204,9 @@ def build_codes(keys, n: int, W, K: int, L: int, with_margin: bool = False):
 
 
 def decode(q, keys, vals, codes, kmean, W, K: int, L: int, n: int, qcodes=None, n_static_head: int = 0,
-           n_static_tail: int = 0, want_idx: bool = False):
-    """Decode of one layer (Algorithm 1 for every query head).
+           n_static_tail: int = 0, want_idx: bool = False, T: int = 2):
+    """Decode of one layer (Algorithm 1 for every query head; a key is sampled
+    when it collides in at least T tables, the pages' T = 2).
 
     Shapes: q ``[B][Hq][d]``, keys/vals ``[B][Hkv][cap][d]``, codes
     ``[B][Hkv][L][cap]``, kmean ``[B][Hkv][d]``, qcodes ``[B][Hq][L]`` or None.
@@ -218,8 +224,8 @@ def decode(q, keys, vals, codes, kmean, W, K: int, L: int, n: int, qcodes=None, 
     lse = np.zeros((B, Hq), np.float32)
     count = np.zeros((B, Hq), np.int32)
     idx = np.full((B, Hq, cap), -1, np.int32) if want_idx else None
-    lib().orc_decode(q, keys, vals, codes, kmean, W, _ptr(qc_in), B, Hq, Hkv, n, cap, d, K, L, n_static_head,
-                     n_static_tail, _ptr(qc_out), out, lse, _ptr(idx), count)
+    lib().orc_decode_t(q, keys, vals, codes, kmean, W, _ptr(qc_in), B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
+                       n_static_tail, _ptr(qc_out), out, lse, _ptr(idx), count)
     res = {"out": out, "lse": lse, "count": count, "qcodes": qc_out}
     if want_idx:
         res["idx"] = [[idx[b, h, :count[b, h]].copy() for h in range(Hq)] for b in range(B)]

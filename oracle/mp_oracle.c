@@ -156,39 +156,44 @@ double orc_table_collision_prob(double cos_qk, int K)
 
 /* ---------------------------------------------------------------------------
  * Sampling probability (Section 4.3, Equation 10): a key is sampled when it
- * shares its code with the query in at least two of the L independent
- * tables, each matching with probability p.  Written as the binomial tail
- * P = sum_{j=2}^{L} C(L,j) p^j (1-p)^(L-j), which is the quantity
- * Equation 10 states in closed form; the tail sum has no cancellation.
+ * shares its code with the query in at least T of the L independent tables,
+ * each matching with probability p.  Written as the binomial tail
+ * P = sum_{j=T}^{L} C(L,j) p^j (1-p)^(L-j); for the pages' threshold T = 2
+ * this is the quantity Equation 10 states in closed form.  The tail sum has
+ * no cancellation.
  * ------------------------------------------------------------------------- */
-double orc_sampling_prob_p(double p, int L)
+double orc_sampling_prob_pt(double p, int L, int T)
 {
     double P = 0.0, c = 1.0; /* c = C(L, j) */
-    for (int j = 1; j <= L; ++j) {
-        c = c * (double)(L - j + 1) / (double)j;
-        if (j >= 2)
+    for (int j = 0; j <= L; ++j) {
+        if (j > 0) c = c * (double)(L - j + 1) / (double)j;
+        if (j >= T)
             P += c * pow(p, (double)j) * pow(1.0 - p, (double)(L - j));
     }
     return P;
 }
 
-double orc_sampling_prob(double cos_qk, int K, int L)
+double orc_sampling_prob_p(double p, int L) { return orc_sampling_prob_pt(p, L, 2); }
+
+double orc_sampling_prob_t(double cos_qk, int K, int L, int T)
 {
-    return orc_sampling_prob_p(orc_table_collision_prob(cos_qk, K), L);
+    return orc_sampling_prob_pt(orc_table_collision_prob(cos_qk, K), L, T);
 }
+
+double orc_sampling_prob(double cos_qk, int K, int L) { return orc_sampling_prob_t(cos_qk, K, L, 2); }
 
 /* ---------------------------------------------------------------------------
  * Sampled set of one query head (Section 4.3 "Hash function selection",
  * Algorithm 1 "Query hash tables"): key i is sampled when its code equals
- * the query's code in at least 2 of the L tables.  Keys i < n_static_head
+ * the query's code in at least T of the L tables (the pages use T = 2).  Keys i < n_static_head
  * and i >= n - n_static_tail are always included and flagged as forced
  * (Algorithm 1's static cache K_T, V_T; the authors' reply on sink tokens).
  * codes: table l of key i at codes[l * table_stride + i].
  * Writes the ascending index list (nullable) and forced flags (nullable);
  * returns its length.
  * ------------------------------------------------------------------------- */
-int64_t orc_scan(const uint16_t *codes, int64_t table_stride, int64_t n, int L, const uint16_t *qcode,
-                 int64_t n_static_head, int64_t n_static_tail, int32_t *idx, uint8_t *forced)
+int64_t orc_scan_t(const uint16_t *codes, int64_t table_stride, int64_t n, int L, int T, const uint16_t *qcode,
+                   int64_t n_static_head, int64_t n_static_tail, int32_t *idx, uint8_t *forced)
 {
     int64_t cnt = 0;
     for (int64_t i = 0; i < n; ++i) {
@@ -196,13 +201,19 @@ int64_t orc_scan(const uint16_t *codes, int64_t table_stride, int64_t n, int L, 
         int matches = 0;
         for (int l = 0; l < L; ++l)
             matches += codes[(int64_t)l * table_stride + i] == qcode[l];
-        if (is_forced || matches >= 2) {
+        if (is_forced || matches >= T) {
             if (idx) idx[cnt] = (int32_t)i;
             if (forced) forced[cnt] = (uint8_t)is_forced;
             ++cnt;
         }
     }
     return cnt;
+}
+
+int64_t orc_scan(const uint16_t *codes, int64_t table_stride, int64_t n, int L, const uint16_t *qcode,
+                 int64_t n_static_head, int64_t n_static_tail, int32_t *idx, uint8_t *forced)
+{
+    return orc_scan_t(codes, table_stride, n, L, 2, qcode, n_static_head, n_static_tail, idx, forced);
 }
 
 /* Per-key match counts for one query head (diagnostics for the tests). */
@@ -222,14 +233,14 @@ void orc_match_counts(const uint16_t *codes, int64_t table_stride, int64_t n, in
  * Algorithm 1 "Compute attention output estimation"):
  *   s_i   = q.k_i / sqrt(d)                      (raw key)
  *   cos_i = q.(k_i - mu) / (|q| |k_i - mu|)      (0 if a norm is 0)
- *   lnP_i = ln P(cos_i)                          (0 for forced keys)
+ *   lnP_i = ln P(cos_i), tail from T             (0 for forced keys)
  *   out   = sum_i softmax(s - lnP)_i v_i,  lse = logsumexp(s - lnP)
  * An empty set gives out = 0, lse = -inf.  mu may be NULL (no centring).
  * logw (nullable, [cnt]) receives s_i - lnP_i.
  * ------------------------------------------------------------------------- */
-void orc_attend(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
-                const float *mu, int K, int L, const int32_t *idx, const uint8_t *forced, int64_t cnt,
-                double *out, double *lse, double *logw)
+void orc_attend_t(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
+                  const float *mu, int K, int L, int T, const int32_t *idx, const uint8_t *forced, int64_t cnt,
+                  double *out, double *lse, double *logw)
 {
     for (int t = 0; t < d; ++t)
         out[t] = 0.0;
@@ -258,7 +269,7 @@ void orc_attend(const float *q, const float *keys, const float *vals, int64_t ro
         double lnP = 0.0;
         if (!(forced && forced[s])) {
             double cosv = (qn > 0.0 && cn > 0.0) ? qc / (qn * cn) : 0.0;
-            lnP = log(orc_sampling_prob(cosv, K, L));
+            lnP = log(orc_sampling_prob_t(cosv, K, L, T));
         }
         lw[s] = qk * inv_sqrt_d - lnP;
         if (lw[s] > M) M = lw[s];
@@ -279,6 +290,13 @@ void orc_attend(const float *q, const float *keys, const float *vals, int64_t ro
     free(lw);
 }
 
+void orc_attend(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
+                const float *mu, int K, int L, const int32_t *idx, const uint8_t *forced, int64_t cnt,
+                double *out, double *lse, double *logw)
+{
+    orc_attend_t(q, keys, vals, row_stride, d, mu, K, L, 2, idx, forced, cnt, out, lse, logw);
+}
+
 /* ---------------------------------------------------------------------------
  * Code-store build of one layer: per unit u (batch x KV head) the key mean
  * over its n keys, then the centred codes of every key.
@@ -296,16 +314,16 @@ void orc_build(const float *keys, int64_t U, int64_t n, int64_t cap, int d, cons
 }
 
 /* ---------------------------------------------------------------------------
- * Decode of one layer (Algorithm 1 for every query head).  Query head h
- * reads KV head h / (Hq / Hkv).
+ * Decode of one layer (Algorithm 1 for every query head, threshold T).
+ * Query head h reads KV head h / (Hq / Hkv).
  *   q [B][Hq][d]; keys, vals [B][Hkv][cap][d]; codes [B][Hkv][L][cap];
  *   kmean [B][Hkv][d]; qcodes [B][Hq][L] (NULL: encode q here, uncentred);
  *   out [B][Hq][d]; lse [B][Hq]; idx [B][Hq][cap] (nullable); count [B][Hq].
  * ------------------------------------------------------------------------- */
-void orc_decode(const float *q, const float *keys, const float *vals, const uint16_t *codes,
-                const float *kmean, const float *W, const uint16_t *qcodes_in, int B, int Hq, int Hkv,
-                int64_t n, int64_t cap, int d, int K, int L, int64_t n_static_head, int64_t n_static_tail,
-                uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count)
+void orc_decode_t(const float *q, const float *keys, const float *vals, const uint16_t *codes,
+                  const float *kmean, const float *W, const uint16_t *qcodes_in, int B, int Hq, int Hkv,
+                  int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                  uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count)
 {
     const int G = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -321,12 +339,12 @@ void orc_decode(const float *q, const float *keys, const float *vals, const uint
             memcpy(qcodes_out + bh * L, qc, sizeof(uint16_t) * (size_t)L);
         int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
         uint8_t *forced = (uint8_t *)malloc((size_t)(n > 0 ? n : 1));
-        int64_t cnt = orc_scan(codes + u * (int64_t)L * cap, cap, n, L, qc, n_static_head, n_static_tail,
-                               list, forced);
+        int64_t cnt = orc_scan_t(codes + u * (int64_t)L * cap, cap, n, L, T, qc, n_static_head, n_static_tail,
+                                 list, forced);
         double *o = (double *)malloc(sizeof(double) * (size_t)d);
         double l;
-        orc_attend(qh, keys + u * cap * d, vals + u * cap * d, d, d, kmean + u * d, K, L, list, forced, cnt,
-                   o, &l, NULL);
+        orc_attend_t(qh, keys + u * cap * d, vals + u * cap * d, d, d, kmean + u * d, K, L, T, list, forced, cnt,
+                     o, &l, NULL);
         for (int t = 0; t < d; ++t)
             out[bh * d + t] = (float)o[t];
         if (lse) lse[bh] = (float)l;
@@ -338,6 +356,15 @@ void orc_decode(const float *q, const float *keys, const float *vals, const uint
         free(list);
         free(qc);
     }
+}
+
+void orc_decode(const float *q, const float *keys, const float *vals, const uint16_t *codes,
+                const float *kmean, const float *W, const uint16_t *qcodes_in, int B, int Hq, int Hkv,
+                int64_t n, int64_t cap, int d, int K, int L, int64_t n_static_head, int64_t n_static_tail,
+                uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count)
+{
+    orc_decode_t(q, keys, vals, codes, kmean, W, qcodes_in, B, Hq, Hkv, n, cap, d, K, L, 2, n_static_head,
+                 n_static_tail, qcodes_out, out, lse, idx, count);
 }
 
 /* Threads the oracle's parallel loops use from now on (timing only; the

@@ -4,7 +4,7 @@ Pure Python loops, written separately from the C oracle to pin it:
   * bf16 rounding comes from torch's cast, not the oracle's bit routine;
   * each code bit is sign(x . w) with a Python float dot product;
   * the sampling probability enumerates every subset of the L tables
-    (P = sum over subsets with at least two members of
+    (P = sum over subsets with at least T members, the pages' T = 2, of
      prod p * prod (1 - p)), instead of a binomial formula;
   * the estimator is Equation 9 literally: sum (w_i / u_i) v_i / sum (w_i / u_i)
     with w_i = exp(q.k_i / sqrt(d)).
@@ -47,10 +47,10 @@ def code_of(vec, mu, W, K, L):
     return codes
 
 
-def prob_at_least_two(p: float, L: int) -> float:
+def prob_at_least(p: float, L: int, T: int = 2) -> float:
     total = 0.0
     for hits in itertools.product([0, 1], repeat=L):
-        if sum(hits) >= 2:
+        if sum(hits) >= T:
             term = 1.0
             for h in hits:
                 term *= p if h else (1.0 - p)
@@ -58,8 +58,13 @@ def prob_at_least_two(p: float, L: int) -> float:
     return total
 
 
-def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0):
-    """Returns (sampled index list, out vector, lse) for one query head."""
+def prob_at_least_two(p: float, L: int) -> float:
+    return prob_at_least(p, L, 2)
+
+
+def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0, T=2):
+    """Returns (sampled index list, out vector, lse) for one query head; a key
+    is sampled when it collides in at least T tables."""
     n, d = len(keys), len(q)
     mu = mean_f32(keys)
     kc = [code_of(k, mu, W, K, L) for k in keys]
@@ -68,7 +73,7 @@ def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0):
     for i in range(n):
         f = i < n_static_head or i >= n - n_static_tail
         m = sum(1 for l in range(L) if kc[i][l] == qc[l])
-        if f or m >= 2:
+        if f or m >= T:
             S.append(i)
             forced.append(f)
     qn = math.sqrt(sum(float(a) * float(a) for a in q))
@@ -84,7 +89,7 @@ def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0):
             cosv = sum(float(q[t]) * c[t] for t in range(d)) / (qn * cn) if qn > 0 and cn > 0 else 0.0
             cosv = max(-1.0, min(1.0, cosv))
             p = (1.0 - math.acos(cosv) / math.pi) ** K
-            u = prob_at_least_two(p, L)
+            u = prob_at_least(p, L, T)
         w = math.exp(sum(float(q[t]) * k[t] for t in range(d)) / math.sqrt(d))
         den += w / u
         for t in range(d):

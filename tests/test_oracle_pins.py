@@ -154,6 +154,55 @@ def test_sampling_probability_equals_equation_10_closed_form(K, L):
         assert oracle.sampling_prob(cosv, K, L) == pytest.approx(closed, rel=1e-10)
 
 
+def test_threshold_sampling_probability_closed_forms():
+    """Collision threshold T: T = 1 gives 1 - (1-p)^L, T = L gives p^L, the
+    pages' T = 2 is Equation 10, consecutive thresholds differ by the binomial
+    term C(L,T) p^T (1-p)^(L-T), and P falls as T rises."""
+    for L in [2, 5, 75, 150]:
+        for p in [0.0, 1e-6, 0.013, 0.3, 0.97, 1.0]:
+            ref1 = -math.expm1(L * math.log1p(-p)) if p < 1 else 1.0  # 1 - (1-p)^L without cancellation
+            assert oracle.sampling_prob_p(p, L, 1) == pytest.approx(ref1, rel=1e-12, abs=1e-300)
+            assert oracle.sampling_prob_p(p, L, L) == pytest.approx(p ** L, rel=1e-12, abs=1e-300)
+            assert oracle.sampling_prob_p(p, L, 2) == oracle.sampling_prob_p(p, L)
+            prev = 1.0 + 1e-12
+            for T in range(1, min(L, 8) + 1):
+                P = oracle.sampling_prob_p(p, L, T)
+                assert P <= prev
+                prev = P
+                if T < L and L <= 75:
+                    term = math.comb(L, T) * p ** T * (1 - p) ** (L - T)
+                    diff = P - oracle.sampling_prob_p(p, L, T + 1)
+                    assert diff == pytest.approx(term, rel=1e-9, abs=1e-15)
+
+
+def test_threshold_inclusion_frequency_matches_sampling_probability():
+    """With threshold T = 3 the per-key inclusion frequency over random
+    projections converges to the tail from 3 at the centred angle."""
+    K, L, T, d, n, draws = 2, 7, 3, 16, 20, 2500
+    rng = np.random.default_rng(13)
+    mu_dir = rng.standard_normal(d)
+    mu_dir /= np.linalg.norm(mu_dir)
+    keys = (rng.standard_normal((n, d)) + 2 * mu_dir).astype(np.float32)
+    q = oracle.bf16((rng.standard_normal(d) - 2 * mu_dir).astype(np.float32))
+    mu = oracle.key_mean(keys)
+    c = keys.astype(np.float64) - mu
+    cos_c = c @ q / (np.linalg.norm(c, axis=1) * np.linalg.norm(q))
+    P = np.array([oracle.sampling_prob(v, K, L, T) for v in cos_c])
+    hits = np.zeros(n)
+    for _ in range(draws):
+        W = rng.standard_normal((d, K * L)).astype(np.float32)
+        kc = oracle.encode(keys, W, K, L, mu)
+        qc = oracle.encode(q, W, K, L)[0]
+        idx, _ = oracle.scan(kc.T, qc, T=T)
+        hits[idx] += 1
+    freq = hits / draws
+    sig = np.sqrt(P * (1 - P) / draws)
+    assert np.all(np.abs(freq - P) <= 4.5 * sig + 0.01), np.max(np.abs(freq - P) / (sig + 1e-9))
+    # the pages' threshold predicts visibly higher rates: the threshold matters
+    P2 = np.array([oracle.sampling_prob(v, K, L, 2) for v in cos_c])
+    assert np.max(np.abs(freq - P2)) > 0.1
+
+
 def test_sampling_probability_small_p_asymptote():
     """For p -> 0 the tail is dominated by C(L,2) p^2."""
     for L in [75, 150, 240]:
@@ -338,24 +387,26 @@ def test_translation_of_keys_leaves_the_estimate_unchanged():
     assert np.max(np.abs(out - out2)) < 1e-5
 
 
-@pytest.mark.parametrize("seed,d,n,K,L,nsh,nst", [(20, 4, 12, 2, 3, 0, 0), (21, 8, 16, 3, 4, 0, 0),
-                                                   (22, 8, 16, 1, 4, 1, 2), (23, 4, 9, 3, 2, 0, 0),
-                                                   (24, 8, 16, 0, 3, 0, 0)])
-def test_matches_independent_brute_force(seed, d, n, K, L, nsh, nst):
+@pytest.mark.parametrize("seed,d,n,K,L,nsh,nst,T", [(20, 4, 12, 2, 3, 0, 0, 2), (21, 8, 16, 3, 4, 0, 0, 2),
+                                                     (22, 8, 16, 1, 4, 1, 2, 2), (23, 4, 9, 3, 2, 0, 0, 2),
+                                                     (24, 8, 16, 0, 3, 0, 0, 2), (25, 8, 16, 1, 5, 0, 0, 1),
+                                                     (26, 8, 16, 1, 5, 1, 1, 3), (27, 4, 12, 1, 4, 0, 0, 4)])
+def test_matches_independent_brute_force(seed, d, n, K, L, nsh, nst, T):
     """Tiny inputs: the oracle and an independent pure-Python statement of
-    Section 2.2 + Equations 9-11 agree exactly on sets and to 1e-12 on outputs."""
+    Section 2.2 + Equations 9-11 agree exactly on sets and to 1e-12 on outputs
+    (collision threshold T, the pages' T = 2, and T = 1, 3, L)."""
     rng = np.random.default_rng(seed)
     keys = (rng.standard_normal((n, d)) + 0.7).astype(np.float32)
     vals = rng.standard_normal((n, d)).astype(np.float32)
     q = (rng.standard_normal(d) - 0.7).astype(np.float32)
     W = rng.standard_normal((d, K * L)).astype(np.float32)
-    S, bout, blse = brute.decode_head(q.tolist(), keys.tolist(), vals.tolist(), W.tolist(), K, L, nsh, nst)
+    S, bout, blse = brute.decode_head(q.tolist(), keys.tolist(), vals.tolist(), W.tolist(), K, L, nsh, nst, T)
     mu = oracle.key_mean(keys)
     kc = oracle.encode(keys, W, K, L, mu)
     qc = oracle.encode(q, W, K, L)[0]
-    idx, forced = oracle.scan(kc.T, qc, nsh, nst)
+    idx, forced = oracle.scan(kc.T, qc, nsh, nst, T=T)
     assert idx.tolist() == S
-    out, lse = oracle.attend(q, keys, vals, idx, forced, K, L, mu)
+    out, lse = oracle.attend(q, keys, vals, idx, forced, K, L, mu, T=T)
     assert np.max(np.abs(out - np.array(bout))) < 1e-12
     assert (lse == blse) or abs(lse - blse) < 1e-12
 
