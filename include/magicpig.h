@@ -140,14 +140,19 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
 /*
  * Sampled decode attention of one layer (Algorithm 1 for every query head;
  * Equations 9-11).  For query head h of batch b (KV unit u = b*Hkv + h/G):
- *   S_h   = { i < n : #{l : codes[u][l][i] == qcode_h[l]} >= 2 }
+ *   S_h   = { i < n : #{l : codes[u][l][i] == qcode_h[l]} >= T }
  *           plus the forced ranges i < n_static_head and
  *           i >= n - n_static_tail (probability 1; Algorithm 1's static
  *           cache K_T, V_T and the authors' reply on sink tokens),
  *   cos_i = q_h.(K_i - kmean_u) / (|q_h| |K_i - kmean_u|),
- *   lnP_i = ln(1 - (1-p)^L - L p (1-p)^(L-1)), p = (1 - acos(cos_i)/pi)^K,
+ *   lnP_i = ln sum_{j>=T} C(L,j) p^j (1-p)^(L-j), p = (1 - acos(cos_i)/pi)^K
+ *           (for the pages' threshold T = 2: ln(1 - (1-p)^L - L p (1-p)^(L-1)),
+ *           Equation 10),
  *   s_i   = q_h.K_i / sqrt(d) - lnP_i,
  *   out   = sum_{S_h} e^{s_i} V_i / sum_{S_h} e^{s_i},  lse = ln sum e^{s_i}.
+ * T is the collision threshold, 1 <= T <= L (MP_ERR_UNSUPPORTED otherwise);
+ * the pages use T = 2 (a key colliding with the query in at least two
+ * tables, Section 4.3), and the benchmarked workloads do too.
  * All G query heads of a KV head share one pass over its codes; each head
  * keeps its own set and probabilities.  An empty set gives out = 0,
  * lse = -inf, count = 0.
@@ -169,7 +174,7 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
 size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L);
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                    const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
-                   int L, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
+                   int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream);
 
@@ -186,7 +191,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
  */
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                      const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                     int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
+                     int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream);
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
                     int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream);
@@ -207,7 +212,7 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  */
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
                    uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                   int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
+                   int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream);
 
 #ifdef __cplusplus

@@ -39,13 +39,13 @@ _SIGS = {
     "mp_encode_queries": ([_vp, _c_int, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp], _c_int),
     "mp_decode_ws_bytes": ([_c_int, _c_int, _c_int, _c_i64, _c_int, _c_int], _c_sz),
     "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
-                        _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
+                        _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
-                          _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
+                          _c_int, _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
     "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                         _c_int),
     "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
-                        _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
+                        _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
 }
 
 _lib = None
@@ -221,8 +221,12 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
                    n_static_tail: int = 0, qcodes_in: Optional[torch.Tensor] = None,
                    qcodes_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
-                   count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
-    """Sampled decode attention of one layer.  q [B][Hq][d]; caches [B*Hkv][cap][d]."""
+                   count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None,
+                   T: int = 2):
+    """Sampled decode attention of one layer.  q [B][Hq][d]; caches [B*Hkv][cap][d].
+
+    ``T`` is the collision threshold (a key is sampled when it collides with
+    the query in at least T of the L tables; the pages use 2)."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     dev = q.device
     if out is None:
@@ -240,19 +244,20 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
     if ws is None:
         ws = decode_workspace(B, Hq, Hkv, cap, L, dev)
     st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp), B, Hq, Hkv, n, cap,
-                              d, K, L, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
+                              d, K, L, T, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
                               _p(idx), _p(count), _p(ws), ws.numel(), _stream(stream))
     _check("mp_decode_attn", st)
     return out
 
 
 def mp_decode_sample(q, Kc, Vc, codes, kmean, qcodes, Hkv: int, n: int, K: int, ws: torch.Tensor,
-                     n_static_head: int = 0, n_static_tail: int = 0, want_idx: bool = False, stream=None) -> None:
+                     n_static_head: int = 0, n_static_tail: int = 0, want_idx: bool = False, stream=None,
+                     T: int = 2) -> None:
     """Scan + weighting + split attention into the workspace (first stage of mp_decode_attn)."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     _need(qcodes, torch.uint16, (B, Hq, L), "qcodes")
     st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(qcodes), B, Hq, Hkv,
-                                n, cap, d, K, L, n_static_head, n_static_tail, int(bool(want_idx)), _p(ws), ws.numel(),
+                                n, cap, d, K, L, T, n_static_head, n_static_tail, int(bool(want_idx)), _p(ws), ws.numel(),
                                 _stream(stream))
     _check("mp_decode_sample", st)
 
@@ -271,7 +276,7 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
                    Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor, Wp: torch.Tensor, Hkv: int, n: int,
                    K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
-                   n_static_tail: int = 0, sample_events=None, stream=None) -> torch.Tensor:
+                   n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2) -> torch.Tensor:
     """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
 
     ``sample_events``: optional pair of torch.cuda.Event objects (created with
@@ -291,7 +296,7 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
     if idx is not None:
         _need(idx, torch.int32, (B, Hq, cap), "idx")
     st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp),
-                              B, Hq, Hkv, n, cap, d, K, L, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),
+                              B, Hq, Hkv, n, cap, d, K, L, T, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),
                               _p(count), _p(ws), ws.numel(), _event_pair(sample_events), _stream(stream))
     _check("mp_decode_step", st)
     return out

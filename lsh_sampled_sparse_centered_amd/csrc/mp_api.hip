@@ -128,9 +128,10 @@ size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L) {
 
 static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                         const float *kmean, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L,
-                        int64_t nsh, int64_t nst, void *ws, size_t ws_bytes) {
+                        int T, int64_t nsh, int64_t nst, void *ws, size_t ws_bytes) {
   int st = check_shape(d, K, L);
   if (st) return st;
+  if (T < 1 || T > L) return MP_ERR_UNSUPPORTED;
   if ((st = check_dtype(kv_dtype))) return st;
   if ((st = check_heads(B, Hq, Hkv))) return st;
   if (!q || !Kc || !Vc || !codes || !kmean || cap < 1 || cap % 8 || nsh < 0 || nst < 0) return MP_ERR_ARG;
@@ -145,16 +146,16 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
 
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                      const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                     int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
+                     int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream) {
-  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, n_static_head,
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!qcodes) return MP_ERR_ARG;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   if (geo.nchunks == 0) return MP_OK;
-  return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L,
+  return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T,
                                   n_static_head, n_static_tail, geo, w, want_idx != 0, as_stream(stream)));
 }
 
@@ -174,10 +175,10 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
 
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                    const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
-                   int L, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
+                   int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream) {
-  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, n_static_head,
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
@@ -194,7 +195,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
     qc = dst;
   }
   if (geo.nchunks > 0) {
-    hipError_t e = launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, n_static_head,
+    hipError_t e = launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head,
                                  n_static_tail, geo, w, idx != nullptr, s);
     if (e != hipSuccess) return MP_ERR_HIP;
   }
@@ -203,13 +204,13 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
 
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
                    uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                   int d, int K, int L, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
+                   int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
   const bool app = k_new != nullptr;
   if (app && !v_new) return MP_ERR_ARG;
   if (app && (n < 0 || n >= cap)) return MP_ERR_CAPACITY;
   const int64_t nd = app ? n + 1 : n;  // keys the decode sees
-  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, nd, cap, d, K, L, n_static_head,
+  int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, nd, cap, d, K, L, T, n_static_head,
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
@@ -232,7 +233,7 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
   // the events ride on the sampling kernel's dispatch (its own start and end)
   hipEvent_t *ev = (hipEvent_t *)sample_events;
   if (geo.nchunks > 0) {
-    if (launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, n_static_head,
+    if (launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, T, n_static_head,
                       n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) !=
         hipSuccess)
       return MP_ERR_HIP;

@@ -24,8 +24,10 @@ namespace mp {
 constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
 constexpr int ATT_E = 32;  // list entries per attention round
 
-LnPCoef lnp_coef(int L) {
+LnPCoef lnp_coef(int L, int T) {
   LnPCoef c{};
+  c.T = T;
+  c.lnct = (float)(std::lgamma((double)L + 1.0) - std::lgamma((double)T + 1.0) - std::lgamma((double)(L - T) + 1.0));
   double a = 1.0;  // C(L, 2+i) / C(L, 2), by the ratio C(L, k+1) / C(L, k) = (L-k)/(k+1)
   for (int i = 0; i < LNP_TERMS; ++i) {
     c.a[i] = (float)a;
@@ -81,12 +83,38 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
 // with L p < 1 the terms from i = 12 on are below 3e-11 of the sum.  For
 // L p >= 1 the closed form is evaluated as
 // ln(-expm1((L-1) ln(1-p) + ln(1 + (L-1) p))).
+// Any other threshold T (at least T of L tables): with r = p/(1-p),
+//   L p <= T: P = C(L,T) p^T (1-p)^(L-T) * sum_{j>=T} t_j / t_T, where
+//             t_{j+1}/t_j = (L-j)/(j+1) r; past the mode (<= T) the terms
+//             only fall, and the sum stops once a term is below 1e-8 of it;
+//   L p >  T: P = 1 - sum_{j<T} C(L,j) p^j (1-p)^(L-j) (P is not small there).
+__device__ inline float log_sampling_prob_t(float lnp, float p, int L, int T, float lnct) {
+  if (p >= 1.0f) return 0.0f;
+  const float l1p = log1pf(-p), r = p / (1.0f - p);
+  if ((float)L * p <= (float)T) {
+    float sum = 1.0f, term = 1.0f;
+    for (int j = T; j < L; ++j) {
+      term *= (float)(L - j) / (float)(j + 1) * r;
+      sum += term;
+      if (term < 1e-8f * sum) break;
+    }
+    return lnct + (float)T * lnp + (float)(L - T) * l1p + __logf(sum);
+  }
+  float term = __expf((float)L * l1p), below = term;  // j = 0
+  for (int j = 0; j + 1 < T; ++j) {
+    term *= (float)(L - j) / (float)(j + 1) * r;
+    below += term;
+  }
+  return log1pf(-fminf(below, 1.0f));
+}
+
 __device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &cf) {
   if (K == 0) return 0.0f;  // p = 1: every table collides, P = 1
   c = fminf(1.0f, fmaxf(-1.0f, c));
   const float u = acosf(-c) * 0.318309886183790671538f;
   const float lnp = (float)K * __logf(u);
   const float p = __expf(lnp);
+  if (cf.T != 2) return log_sampling_prob_t(lnp, p, L, cf.T, cf.lnct);
   const float Lf = (float)L;
   if (Lf * p < 1.0f) {
     const float r = p * __frcp_rn(1.0f - p);
@@ -263,12 +291,16 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
   struct ScanLds {
     uint32_t flg[4][64][2 * FW];
   };
+  struct CntLds {  // thresholds other than 2: per-wave match counts [wave][lane][key][head]
+    uint8_t c[4][64][8][GM];
+  };
   struct AttnLds {
     T v[ATT_E][D];                         // staged value rows of this round's entries
     alignas(16) float lw[GM][ATT_E];       // log-weights s - ln P (or -inf), head-major
   };
   __shared__ union {
     ScanLds s;
+    CntLds c;
     AttnLds a;
   } sm;  // scan and attention phases never overlap in time
   extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
@@ -496,20 +528,43 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
           g2[bit >> 5] |= ((uint32_t)(mlo >= 2) | ((uint32_t)(mhi >= 2) << 1)) << (bit & 31);
         }
       }
+      if (cf.T == 2) {
 #pragma unroll
-      for (int f = 0; f < FW; ++f) {
-        sm.s.flg[wave][lane][f] = g1[f];
-        sm.s.flg[wave][lane][FW + f] = g2[f];
+        for (int f = 0; f < FW; ++f) {
+          sm.s.flg[wave][lane][f] = g1[f];
+          sm.s.flg[wave][lane][FW + f] = g2[f];
+        }
+      } else {  // other thresholds: this wave's match counts (<= 128 tables per wave)
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            sm.c.c[wave][lane][2 * w][h] = (uint8_t)(ntw - (int)(acc[h][w] & 0xffffu));
+            sm.c.c[wave][lane][2 * w + 1][h] = (uint8_t)(ntw - (int)(acc[h][w] >> 16));
+          }
       }
     }
     __syncthreads();
 
     // ---- threshold + compaction: thread tid owns sub-tile keys 2*tid, 2*tid+1
     // (scan lane tid/4, key slots k0 = 2*(tid%4) and k0+1).  At least two
-    // matching tables overall <=> some wave has two, or two waves have one.
+    // matching tables overall <=> some wave has two, or two waves have one;
+    // any other threshold adds the four waves' counts.
     const int64_t klo = sbase + 2 * tid;
     uint32_t mlo = 0, mhi = 0;
-    {
+    if (cf.T != 2) {
+      const int sl = tid >> 2, k0 = 2 * (tid & 3);
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const int s0 = sm.c.c[0][sl][k0][h] + sm.c.c[1][sl][k0][h] + sm.c.c[2][sl][k0][h] + sm.c.c[3][sl][k0][h];
+          const int s1 = sm.c.c[0][sl][k0 + 1][h] + sm.c.c[1][sl][k0 + 1][h] + sm.c.c[2][sl][k0 + 1][h] +
+                         sm.c.c[3][sl][k0 + 1][h];
+          mlo |= (uint32_t)(s0 >= cf.T) << h;
+          mhi |= (uint32_t)(s1 >= cf.T) << h;
+        }
+      }
+    } else {
       const int sl = tid >> 2, k0 = 2 * (tid & 3);
 #pragma unroll
       for (int f = 0; f < FW; ++f) {
@@ -646,13 +701,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
 
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                         int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
+                         int K, int L, int Tthr, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
   const int G = Hq / Hkv;
   const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
   const uint32_t one2 = 0x00010001u;
-  const LnPCoef cf = lnp_coef(L);
+  const LnPCoef cf = lnp_coef(L, Tthr);
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
 #define MP_SAMPLE(T, GMV)                                                                                    \

@@ -38,14 +38,17 @@ constexpr int PSTRIDE = 132;    // floats per partial record: m, l, count, pad, 
 constexpr int MAX_G = 8;        // query heads per KV head handled by one pass
 constexpr int MAX_L = 512;
 
-// Series coefficients of the sampling probability for one L: a[i] =
-// C(L, 2+i) / C(L, 2) and lnc2 = ln C(L, 2) (filled on the host).
+// Sampling-probability constants for one (L, T), filled on the host: series
+// coefficients a[i] = C(L, 2+i) / C(L, 2) and lnc2 = ln C(L, 2) for the
+// pages' threshold T = 2, and lnct = ln C(L, T) for other thresholds.
 constexpr int LNP_TERMS = 12;
 struct LnPCoef {
   float a[LNP_TERMS];
   float lnc2;
+  float lnct;
+  int T;  // collision threshold: a key is sampled in at least T of L tables
 };
-LnPCoef lnp_coef(int L);
+LnPCoef lnp_coef(int L, int T);
 
 struct DecodeGeom {
   int64_t U;          // units = B * Hkv
@@ -128,7 +131,7 @@ hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si
 // dispatch, so they time exactly this launch (no queue gap before it).
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                         int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
+                         int K, int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr);
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,

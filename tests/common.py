@@ -42,11 +42,11 @@ def oracle_codes(w: synth.Workload, lay, with_margin=True):
     return km, codes, margin, qc
 
 
-def oracle_decode(w: synth.Workload, lay, km, codes, qc, n=None, nsh=0, nst=0):
+def oracle_decode(w: synth.Workload, lay, km, codes, qc, n=None, nsh=0, nst=0, T=2):
     h = lay["host"]
     return oracle.decode(h["q"], h["K"], h["V"], codes.reshape(w.batch, w.hkv, w.L, lay["cap"]),
                          km.reshape(w.batch, w.hkv, w.d), h["W"], w.K, w.L, lay["n"] if n is None else n,
-                         qcodes=qc, n_static_head=nsh, n_static_tail=nst, want_idx=True)
+                         qcodes=qc, n_static_head=nsh, n_static_tail=nst, want_idx=True, T=T)
 
 
 def code_mismatches_outside_band(gpu_codes: np.ndarray, ref_codes: np.ndarray, margin: np.ndarray):

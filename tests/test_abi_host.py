@@ -100,11 +100,11 @@ def test_append_rejects_invalid_arguments():
 
 def _decode(**kw):
     a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100, cap=128,
-             d=128, K=8, L=75, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
+             d=128, K=8, L=75, T=2, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
              wsb=1 << 30)
     a.update(kw)
     return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"], a["B"], a["Hq"],
-                                   a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["nsh"], a["nst"], a["qin"],
+                                   a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"], a["nst"], a["qin"],
                                    a["qout"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
 
 
@@ -123,14 +123,19 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(B=70000, Hq=8, Hkv=8) == UNSUP
     assert _decode(cap=1 << 26) == UNSUP  # a scan batch's row offsets must fit 32 bits
     assert _decode(cap=(1 << 26) - 8) != UNSUP
+    assert _decode(T=0) == UNSUP  # collision threshold outside [1, L]
+    assert _decode(T=76) == UNSUP
+    assert _decode(T=1) != UNSUP and _decode(T=75) != UNSUP
     for arg in ("q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _decode(**{arg: FAKE + 2}) == ARG, arg
 
 
 def test_decode_stages_reject_invalid_arguments():
     L = mp.lib()
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0, FAKE,
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0, 0, 0, FAKE,
                               1 << 30, None) == ARG  # qcodes required
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0, 0, FAKE,
+                              1 << 30, None) == UNSUP  # threshold 0
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, None, None, None, None, FAKE, 1 << 30, None) == ARG
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, FAKE, None, None, None, FAKE, 10, None) == WS
 
@@ -147,10 +152,11 @@ def test_encode_queries_rejects_invalid_arguments():
 
 def _step(**kw):
     a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100,
-             cap=128, d=128, K=8, L=75, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE, wsb=1 << 30)
+             cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
+             wsb=1 << 30)
     a.update(kw)
     return mp.lib().mp_decode_step(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"],
-                                   a["B"], a["Hq"], a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["nsh"],
+                                   a["B"], a["Hq"], a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"],
                                    a["nst"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None, None)
 
 
@@ -162,5 +168,6 @@ def test_step_rejects_invalid_arguments():
     assert _step(out=None) == ARG
     assert _step(Hkv=3) == ARG
     assert _step(ws=None) == WS
+    assert _step(T=0) == UNSUP
     for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _step(**{arg: FAKE + 4}) == ARG, arg

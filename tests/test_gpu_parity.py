@@ -163,7 +163,7 @@ def _inject(w, lay, km, codes, qc):
     return kmean, gcodes, qcodes
 
 
-def _run_decode(w, lay, kmean, gcodes, qcodes, n=None, nsh=0, nst=0, Wp=None):
+def _run_decode(w, lay, kmean, gcodes, qcodes, n=None, nsh=0, nst=0, Wp=None, T=2):
     n = lay["n"] if n is None else n
     B, Hq, cap = w.batch, w.hq, lay["cap"]
     out = torch.empty(B, Hq, w.d, dtype=torch.float32, device="cuda")
@@ -171,7 +171,7 @@ def _run_decode(w, lay, kmean, gcodes, qcodes, n=None, nsh=0, nst=0, Wp=None):
     idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
     cnt = torch.empty(B, Hq, dtype=torch.int32, device="cuda")
     mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, n, w.K, nsh, nst, qcodes_in=qcodes,
-                      out=out, lse=lse, idx=idx, count=cnt)
+                      out=out, lse=lse, idx=idx, count=cnt, T=T)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
 
@@ -202,6 +202,24 @@ def test_decode_with_oracle_codes(name):
     out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes)
     ref = oracle_decode(w, lay, km, codes, qc)
     _compare(w, ref, out, lse, idx, cnt, name)
+
+
+@pytest.mark.parametrize("name,T", [("llama8b_layer", 1), ("llama8b_layer", 3), ("llama8b_layer", 5),
+                                    ("g8_ragged", 1), ("g8_ragged", 3), ("tiny", 4), ("tiny", 75)])
+def test_decode_collision_threshold(name, T):
+    """Collision threshold T other than the pages' 2 (a key is sampled in at
+    least T of L tables, P the binomial tail from T): with the oracle's codes
+    injected, sets and counts are equal and outputs within tolerance.  T = 1
+    takes the complement of the tail wherever L p > 1, T = L leaves only keys
+    that collide everywhere (often none: out = 0, lse = -inf)."""
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes, T=T)
+    ref = oracle_decode(w, lay, km, codes, qc, T=T)
+    _compare(w, ref, out, lse, idx, cnt, "%s T=%d" % (name, T))
+    if T == 1:
+        ref2 = oracle_decode(w, lay, km, codes, qc)
+        assert np.all(ref["count"] >= ref2["count"])  # T = 1 samples a superset of T = 2
 
 
 @pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged"])
