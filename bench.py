@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--workload", default="llama8b_96k")
     ap.add_argument("--seed", type=int, default=2024)
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--threshold", type=int, default=2,
+                    help="collision threshold T: a key is sampled in at least T of the L tables (the pages' 2)")
     ap.add_argument("--policy", choices=("sampled", "pages"), default="sampled",
                     help="sampled: every layer sampled; pages: the pages' decoding policy (layers 0 and 16 "
                          "dense, i.e. K = 0, and 4 sink + 64 local keys forced into every sampled layer's set)")
@@ -204,7 +206,7 @@ def main() -> int:
             ev = kev[k * nlayers + l] if k >= 0 else None
             mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
                               lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
-                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev)
+                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev, T=args.threshold)
         if timed:
             n_timed.append(n_cur + 1)
         n_cur += 1
@@ -229,7 +231,7 @@ def main() -> int:
     for l in sampled_layers:
         lay = layers[l]
         mp.mp_decode_attn(lay["qs"][s_last], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], lay["Wp"], w.hkv,
-                          n_cur, K, lcfg[l][2], lcfg[l][3], idx=idx, count=cnt, ws=ws)
+                          n_cur, K, lcfg[l][2], lcfg[l][3], idx=idx, count=cnt, ws=ws, T=args.threshold)
         for b in range(w.batch):
             for h in range(w.hkv):
                 mask = torch.zeros(n_cur, dtype=torch.bool, device=dev)
@@ -250,7 +252,8 @@ def main() -> int:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages:
+        if (tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages and
+                args.threshold == 2):
             traffic = tr.get("bytes_per_launch")
     # a dense layer reads its (two-table) codes and every key's K and V row
     dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
@@ -298,7 +301,7 @@ def main() -> int:
 
     cpu = None
     if args.cpu_seconds > 0:
-        cpu = cpu_baseline(w, args.seed, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.seed, args.cpu_seconds, args.threshold)
 
     res = {
         "metric": METRIC,
@@ -314,7 +317,8 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
         "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
-                   "head_dim": d, "context": n0, "K": K, "L": L, "parallelism": "single GPU",
+                   "head_dim": d, "context": n0, "K": K, "L": L, "threshold": args.threshold,
+                   "parallelism": "single GPU",
                    "policy": ("every layer sampled" if not pages else
                               "pages: layers 0 and 16 dense (K = 0), 4 sink + 64 local keys forced elsewhere")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -334,7 +338,7 @@ def main() -> int:
     return 0
 
 
-def cpu_baseline(w, seed: int, budget_s: float):
+def cpu_baseline(w, seed: int, budget_s: float, T: int = 2):
     """The CPU oracle timed on the host on a bounded sample of the same workload.
 
     Sample: KV heads 0..3 of layer 0 (batch 0) at the full context, with their
@@ -369,7 +373,8 @@ def cpu_baseline(w, seed: int, budget_s: float):
         for h in range(nunits):
             q[0, h * G:(h + 1) * G] = synth.unit_queries(seed, 0, 0, h, G, d, w.torch_dtype, "cpu",
                                                          step=reps + 1).float().numpy()
-        oracle.decode(q, keys, vals, codes.reshape(1, nunits, w.L, cap), km.reshape(1, nunits, d), W, w.K, w.L, n)
+        oracle.decode(q, keys, vals, codes.reshape(1, nunits, w.L, cap), km.reshape(1, nunits, d), W, w.K, w.L, n,
+                      T=T)
         reps += 1
         el = time.perf_counter() - t
         if el >= budget_s:
@@ -382,7 +387,7 @@ def cpu_baseline(w, seed: int, budget_s: float):
     while True:
         q1 = synth.unit_queries(seed, 0, 0, 0, G, d, w.torch_dtype, "cpu", step=reps1 + 1).float().numpy()[None]
         oracle.decode(q1, keys[:, :1], vals[:, :1], codes[:1].reshape(1, 1, w.L, cap), km[:1].reshape(1, 1, d), W,
-                      w.K, w.L, n)
+                      w.K, w.L, n, T=T)
         reps1 += 1
         el1 = time.perf_counter() - t
         if el1 >= budget_s / 4:
