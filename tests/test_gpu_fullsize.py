@@ -64,8 +64,8 @@ def code_subset(w, layers):
 class LayerRun:
     """One layer on the device, decoded step by step, checked against the oracle."""
 
-    def __init__(self, w, layer_idx, code_units):
-        self.w, self.li = w, layer_idx
+    def __init__(self, w, layer_idx, code_units, T=2):
+        self.w, self.li, self.T = w, layer_idx, T
         self.code_units = sorted(code_units)
         lay = synth.layer_inputs(w, SEED, layer_idx, device="cuda")
         self.U, self.cap, self.n0 = w.batch * w.hkv, lay["cap"], lay["n"]
@@ -158,7 +158,7 @@ class LayerRun:
         lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
         cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
         mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, self.ws,
-                          out=out, lse=lse, count=cnt)
+                          out=out, lse=lse, count=cnt, T=self.T)
         torch.cuda.synchronize()
         assert torch.equal(self.Kc[:, n], kn) and torch.equal(self.Vc[:, n], vn)
         # appended codes (frozen means) of every unit
@@ -192,7 +192,7 @@ class LayerRun:
         cnt2 = torch.empty_like(cnt)
         idx = torch.full((w.batch, w.hq, self.cap), -1, dtype=torch.int32, device="cuda")
         mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K,
-                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws)
+                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws, T=self.T)
         torch.cuda.synchronize()
         o1, l1, c1 = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
         o2, c2, ix = out2.cpu().numpy(), cnt2.cpu().numpy(), idx.cpu().numpy()
@@ -205,7 +205,7 @@ class LayerRun:
                                 np.stack([k for k, _ in kv])[:, None], np.stack([v for _, v in kv])[:, None],
                                 np.stack([self.host_codes(u) for u in us])[:, None], self.km_o[us][:, None],
                                 self.Wh, w.K, w.L, self.n, qcodes=np.stack([qref[b, h * G:(h + 1) * G] for b, h in bh]),
-                                want_idx=True)
+                                want_idx=True, T=self.T)
             for j, (u, (b, h)) in enumerate(zip(us, bh)):
                 own = app_same[u] and not nd_q[b, h * G:(h + 1) * G].any()
                 direct += int(own)
@@ -226,15 +226,15 @@ class LayerRun:
                     if own:
                         assert np.max(np.abs(o1[b, hh] - ref["out"][j, g])) <= OUT_TOL, (s, u, g)
                         assert abs(float(l1[b, hh]) - float(ref["lse"][j, g])) <= LSE_TOL, (s, u, g)
-        _say("layer %d step %d (n=%d): %d units checked (%d on the step's own outputs); sets exact; worst "
-             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, len(check_units), direct, worst,
+        _say("layer %d step %d (n=%d, T=%d): %d units checked (%d on the step's own outputs); sets exact; worst "
+             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, self.T, len(check_units), direct, worst,
                                                      float(np.mean(sizes))))
 
 
-def _run_layers(w, layers, steps=1, check_every=None):
+def _run_layers(w, layers, steps=1, check_every=None, T=2):
     subset = code_subset(w, layers)
     for li in layers:
-        run = LayerRun(w, li, [u for l, u in subset if l == li])
+        run = LayerRun(w, li, [u for l, u in subset if l == li], T=T)
         run.check_build_and_inject()
         allu = list(range(run.U))
         sub = run.code_units
@@ -251,6 +251,13 @@ def test_llama8b_96k_all_layers(part):
     every unit of 8 of the 32 layers, one appending step."""
     w = synth.WORKLOADS["llama8b_96k"]
     _run_layers(w, list(range(8 * part, 8 * part + 8)))
+
+
+@pytest.mark.parametrize("T", [1, 3])
+def test_llama8b_96k_threshold(T):
+    """The 96K layer shape with collision thresholds 1 and 3 (the step and the
+    index-list decode both take T): every unit of one layer, one appending step."""
+    _run_layers(synth.WORKLOADS["llama8b_96k"], [5], T=T)
 
 
 @pytest.mark.parametrize("layer_idx", [0, 39])
