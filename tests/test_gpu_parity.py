@@ -250,7 +250,11 @@ def test_decode_K0_is_exact_attention():
     lay = layer(w, seed=77)
     Wp = mp.mp_proj_pack(lay["W"], 0, w.L)
     kmean, gcodes = mp.mp_build_codes(lay["Kc"], lay["n"], Wp, 0, w.L)
-    out = mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, w.n, 0)
+    idx = torch.full((1, 1, lay["cap"]), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(1, 1, dtype=torch.int32, device="cuda")
+    lse = torch.empty(1, 1, dtype=torch.float32, device="cuda")
+    out = mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, Wp, w.hkv, w.n, 0, idx=idx, count=cnt,
+                            lse=lse)
     torch.cuda.synchronize()
     h = lay["host"]
     q = h["q"][0, 0].astype(np.float64)
@@ -260,6 +264,10 @@ def test_decode_K0_is_exact_attention():
     p = np.exp(s - s.max())
     ref = (p / p.sum()) @ V
     assert np.max(np.abs(out.cpu().numpy()[0, 0] - ref)) <= OUT_TOL
+    assert int(cnt[0, 0]) == w.n
+    assert np.array_equal(idx.cpu().numpy()[0, 0, :w.n], np.arange(w.n))  # every key, ascending
+    lse_ref = s.max() + math.log(np.exp(s - s.max()).sum())
+    assert abs(float(lse[0, 0]) - lse_ref) <= LSE_TOL
 
 
 def test_dense_layer_step_is_exact_attention():
