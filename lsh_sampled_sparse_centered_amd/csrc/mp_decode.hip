@@ -312,6 +312,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
   __shared__ uint16_t lmask[2 * SCAN_TILE];  // head bits | FORCED
   __shared__ int wtot[4];
   __shared__ int hcnt[GM];
+  __shared__ float mrun[GM], alpha_sh[GM];  // per head: running maximum, this round's rescale factor
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
@@ -408,7 +409,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
       i0 += 256 * QPASS;
     } while (i0 < nq);
   }
-  if (tid < GM) hcnt[tid] = 0;
+  if (tid < GM) {
+    hcnt[tid] = 0;
+    mrun[tid] = -INFINITY;
+  }
   __syncthreads();
 
   for (int h = wave; h < GM; h += 4) {  // |q_h| and q_h . mu
@@ -622,7 +626,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
   constexpr int DPT = D / TPH;                              // dims per output thread
   const int oh = tid / TPH, od = (tid % TPH) * DPT;
   const bool othread = oh < G && tid < GM * TPH;
-  float om = -INFINITY, ol = 0.0f, oacc[DPT];
+  float ol = 0.0f, oacc[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) oacc[i] = 0.0f;
   const T *Ku = Kc + (u * cap + tbase) * D + 8 * j16;
@@ -651,37 +655,45 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
                         qn_sh, qmu_sh, sm.a.v, sm.a.lw);
     }
     __syncthreads();
-    // (b) each output thread folds the round into its head's running maximum
-    // m, normaliser l and output slice o (online softmax over the round)
-    if (othread) {
-      float mr = -INFINITY;
-      for (int el = 0; el < ne; el += 4) {
-        const f32x4 w4 = *(const f32x4 *)&sm.a.lw[oh][el];
+    // (b) one thread per (head, entry) turns the log-weights into
+    // exp(w - m) against the head's new running maximum m (a 32-lane max),
+    // in place, and one per head records m and the rescale factor of the
+    // head's earlier rounds
+    if (tid < GM * ATT_E) {
+      const int h = tid / ATT_E, e = tid % ATT_E;
+      const float x = (h < G && e < ne) ? sm.a.lw[h][e] : -INFINITY;
+      float mr = x;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (el + k < ne) mr = fmaxf(mr, w4[k]);
+      for (int sh = ATT_E / 2; sh > 0; sh >>= 1) mr = fmaxf(mr, __shfl_xor(mr, sh));  // within the 32 lanes of h
+      const float mo = mrun[h];
+      const float mn = fmaxf(mo, mr);
+      if (h < G && e < ne) sm.a.lw[h][e] = mn > -INFINITY ? __expf(x - mn) : 0.0f;  // 0 for -inf
+      if (e == 0) {
+        alpha_sh[h] = mn > -INFINITY ? __expf(mo - mn) : 1.0f;  // 0 while mo = -inf
+        mrun[h] = mn;
       }
-      const float mn = fmaxf(om, mr);
-      if (mn > -INFINITY) {
-        const float alpha = __expf(om - mn);  // 0 while om = -inf
-        ol *= alpha;
+    }
+    __syncthreads();
+    // (c) each output thread folds the round into its head's normaliser l and
+    // output slice o
+    if (othread) {
+      const float alpha = alpha_sh[oh];
+      ol *= alpha;
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) oacc[i] *= alpha;
-        for (int el = 0; el < ne; el += 4) {
-          const f32x4 w4 = *(const f32x4 *)&sm.a.lw[oh][el];
+      for (int i = 0; i < DPT; ++i) oacc[i] *= alpha;
+      for (int el = 0; el < ne; el += 4) {
+        const f32x4 p4 = *(const f32x4 *)&sm.a.lw[oh][el];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (el + k < ne) {
-              const float pk = __expf(w4[k] - mn);  // 0 for -inf
-              ol += pk;
-              float vv[DPT];
-              ldv<T, DPT>(&sm.a.v[el + k][od], vv);
+        for (int k = 0; k < 4; ++k) {
+          if (el + k < ne) {
+            const float pk = p4[k];
+            ol += pk;
+            float vv[DPT];
+            ldv<T, DPT>(&sm.a.v[el + k][od], vv);
 #pragma unroll
-              for (int i = 0; i < DPT; ++i) oacc[i] += pk * vv[i];
-            }
+            for (int i = 0; i < DPT; ++i) oacc[i] += pk * vv[i];
           }
         }
-        om = mn;
       }
     }
     if (e0 + ATT_E < nu) __syncthreads();  // the next round reuses the staging
@@ -691,7 +703,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
 #pragma unroll
     for (int i = 0; i < DPT; ++i) rec[4 + od + i] = oacc[i];
     if (tid % TPH == 0) {
-      rec[0] = om;
+      rec[0] = mrun[oh];
       rec[1] = ol;
       rec[2] = __builtin_bit_cast(float, hcnt[oh]);
       rec[3] = 0.0f;
