@@ -128,6 +128,25 @@ int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_d
               int64_t cap, int d, const float *kmean, const void *Wp, int K, int L, uint16_t *codes, void *stream);
 
 /*
+ * Bit-plane index of the code store: the same codes, packed as K bit planes
+ * per table (K bits per key and table instead of 16), so the collision scan
+ * reads K/16 of the bytes.  Layout [U][ceil(cap/512)][K][L][16] uint32: word
+ * j of row (b, l) of tile t holds bit b of codes[u][l][i] for keys
+ * i = 512 t + 32 j + e at bit e (e < 32); a tile's rows are contiguous.
+ * mp_build_planes fills tiles [n0/512, n1/512) of every unit from codes
+ * (their keys must have been written); n0 and n1 multiples of 512 with
+ * 0 <= n0 <= n1 <= cap.  Appends do not update it: a decode scans the
+ * planes only for tiles below its n_planes and the 16-bit codes elsewhere,
+ * so the caller rebuilds the newest tile once it is full.
+ *   codes  [U][L][cap] (mp_build_codes);  planes out, mp_planes_bytes bytes
+ * Errors: MP_ERR_ARG (null or misaligned pointers, n0 / n1 not multiples of
+ * 512 or out of range, K = 0), MP_ERR_UNSUPPORTED (shape), MP_ERR_HIP.
+ */
+size_t mp_planes_bytes(int64_t U, int64_t cap, int K, int L);
+int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, int64_t cap, int K, int L,
+                    uint32_t *planes, void *stream);
+
+/*
  * Query encoding (Algorithm 1, "Compute hash code for new query"):
  * qcodes[r][l] = code of table l of y_r = bf16(q[r]); queries are NOT
  * centred (centring shifts keys only; softmax is translation invariant).
@@ -158,6 +177,11 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
  * lse = -inf, count = 0.
  *   q          [B][Hq][d] (kv_dtype)
  *   Kc, Vc     [B*Hkv][cap][d];  codes [B*Hkv][L][cap];  kmean [B*Hkv][d]
+ *   planes     nullable bit-plane index (mp_build_planes) valid for tiles
+ *              below n_planes (a multiple of 512, 0 <= n_planes <= n): with
+ *              T = 2 those tiles are scanned from it; the sets and outputs
+ *              are the same as from codes.  n_planes is ignored when planes
+ *              is NULL.
  *   Wp         packed projections (read only when qcodes_in is NULL)
  *   qcodes_in  nullable [B][Hq][L]: use these query codes instead of
  *              encoding q
@@ -173,7 +197,7 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
  */
 size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L);
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
                    int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream);
@@ -190,7 +214,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
  * qcodes is required here ([B][Hq][L]).
  */
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     const uint32_t *planes, int64_t n_planes, const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                      int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream);
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
@@ -202,7 +226,8 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  * k_new is NULL), encode the queries (as mp_encode_queries, into ws) -- both
  * in one launch -- then sample and merge (as mp_decode_attn) over n + 1 keys
  * (n keys without an append).  Arguments as in mp_append and
- * mp_decode_attn; q codes are kept in ws.  sample_events is NULL or points
+ * mp_decode_attn; q codes are kept in ws.  The appended key is not added to
+ * planes (n_planes <= n, the keys before the append).  sample_events is NULL or points
  * to two host hipEvent_t handles that are attached to the sampling kernel's
  * dispatch, so they record its own start and end (for callers that time it;
  * with no keys to decode there is no such kernel and both are recorded back to
@@ -211,7 +236,8 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  * with n >= cap.
  */
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                   uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
+                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
                    int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream);
 

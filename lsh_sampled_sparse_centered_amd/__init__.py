@@ -38,13 +38,15 @@ _SIGS = {
                   _c_int),
     "mp_encode_queries": ([_vp, _c_int, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp], _c_int),
     "mp_decode_ws_bytes": ([_c_int, _c_int, _c_int, _c_i64, _c_int, _c_int], _c_sz),
-    "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
+    "mp_planes_bytes": ([_c_i64, _c_i64, _c_int, _c_int], _c_sz),
+    "mp_build_planes": ([_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp], _c_int),
+    "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
                         _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
-    "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
+    "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
                           _c_int, _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
     "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                         _c_int),
-    "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
+    "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
                         _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
 }
 
@@ -190,6 +192,24 @@ def mp_encode_queries(q: torch.Tensor, Wp: torch.Tensor, K: int, L: int, qcodes:
     return qcodes
 
 
+def mp_planes_bytes(U: int, cap: int, K: int, L: int) -> int:
+    return lib().mp_planes_bytes(U, cap, K, L)
+
+
+def mp_build_planes(codes: torch.Tensor, K: int, n1: int, n0: int = 0, planes: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Bit-plane index of ``codes`` ([U][L][cap] uint16) for keys [n0, n1) (multiples of 512).
+
+    Returns (or fills) ``planes``: uint32 [U][ceil(cap/512)][K][L][16]."""
+    U, L, cap = codes.shape
+    shape = (U, (cap + 511) // 512, K, L, 16)
+    if planes is None:
+        planes = torch.empty(shape, dtype=torch.int32, device=codes.device)
+    _need(planes, torch.int32, shape, "planes")
+    _check("mp_build_planes", lib().mp_build_planes(_p(codes), U, n0, n1, cap, K, L, _p(planes), _stream(stream)))
+    return planes
+
+
 # ----------------------------------------------------------------------------- decode
 def mp_decode_ws_bytes(B: int, Hq: int, Hkv: int, cap: int, L: int, d: int = D) -> int:
     return lib().mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)
@@ -216,17 +236,25 @@ def _decode_shapes(q, Kc, Vc, codes, kmean, Hkv):
     return B, Hq, d, U, cap, L
 
 
+def _planes_ok(planes, codes, K):
+    if planes is not None:
+        U, L, cap = codes.shape
+        _need(planes, torch.int32, (U, (cap + 511) // 512, K, L, 16), "planes")
+
+
 def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor,
                    Wp: Optional[torch.Tensor], Hkv: int, n: int, K: int, n_static_head: int = 0,
                    n_static_tail: int = 0, qcodes_in: Optional[torch.Tensor] = None,
                    qcodes_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                    count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None,
-                   T: int = 2):
+                   T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0):
     """Sampled decode attention of one layer.  q [B][Hq][d]; caches [B*Hkv][cap][d].
 
     ``T`` is the collision threshold (a key is sampled when it collides with
-    the query in at least T of the L tables; the pages use 2)."""
+    the query in at least T of the L tables; the pages use 2).  ``planes``
+    (from mp_build_planes, valid below ``n_planes``) lets the T = 2 scan read
+    the bit-plane index for those tiles."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     dev = q.device
     if out is None:
@@ -243,7 +271,9 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
             _need(t, torch.uint16, (B, Hq, L), name)
     if ws is None:
         ws = decode_workspace(B, Hq, Hkv, cap, L, dev)
-    st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp), B, Hq, Hkv, n, cap,
+    _planes_ok(planes, codes, K)
+    st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(kmean), _p(Wp),
+                              B, Hq, Hkv, n, cap,
                               d, K, L, T, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
                               _p(idx), _p(count), _p(ws), ws.numel(), _stream(stream))
     _check("mp_decode_attn", st)
@@ -252,11 +282,13 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
 
 def mp_decode_sample(q, Kc, Vc, codes, kmean, qcodes, Hkv: int, n: int, K: int, ws: torch.Tensor,
                      n_static_head: int = 0, n_static_tail: int = 0, want_idx: bool = False, stream=None,
-                     T: int = 2) -> None:
+                     T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> None:
     """Scan + weighting + split attention into the workspace (first stage of mp_decode_attn)."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     _need(qcodes, torch.uint16, (B, Hq, L), "qcodes")
-    st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(qcodes), B, Hq, Hkv,
+    _planes_ok(planes, codes, K)
+    st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(kmean),
+                                _p(qcodes), B, Hq, Hkv,
                                 n, cap, d, K, L, T, n_static_head, n_static_tail, int(bool(want_idx)), _p(ws), ws.numel(),
                                 _stream(stream))
     _check("mp_decode_sample", st)
@@ -276,7 +308,8 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
                    Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor, Wp: torch.Tensor, Hkv: int, n: int,
                    K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
-                   n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2) -> torch.Tensor:
+                   n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2,
+                   planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> torch.Tensor:
     """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
 
     ``sample_events``: optional pair of torch.cuda.Event objects (created with
@@ -295,7 +328,9 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
         _need(count, torch.int32, (B, Hq), "count")
     if idx is not None:
         _need(idx, torch.int32, (B, Hq, cap), "idx")
-    st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(kmean), _p(Wp),
+    _planes_ok(planes, codes, K)
+    st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes),
+                              n_planes, _p(kmean), _p(Wp),
                               B, Hq, Hkv, n, cap, d, K, L, T, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),
                               _p(count), _p(ws), ws.numel(), _event_pair(sample_events), _stream(stream))
     _check("mp_decode_step", st)

@@ -53,7 +53,7 @@ const char *mp_strerror(int status) {
   }
 }
 
-int mp_version(void) { return 1; }
+int mp_version(void) { return 2; }
 
 size_t mp_proj_bytes(int d, int K, int L) {
   if (check_shape(d, K, L) != MP_OK) return 0;
@@ -109,6 +109,28 @@ int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_d
   return hip_status(e);
 }
 
+size_t mp_planes_bytes(int64_t U, int64_t cap, int K, int L) {
+  if (U < 1 || cap < 1 || K < 1 || K > 16 || L < 2 || L > MAX_L || K * L > 4096) return 0;
+  return (size_t)U * (size_t)((cap + SCAN_TILE - 1) / SCAN_TILE) * (size_t)K * (size_t)L * 16 * sizeof(uint32_t);
+}
+
+int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, int64_t cap, int K, int L,
+                    uint32_t *planes, void *stream) {
+  if (L < 2 || L > MAX_L || K > 16 || K * L > 4096) return MP_ERR_UNSUPPORTED;
+  if (!codes || !planes || U < 1 || cap < 1 || cap % 8 || K < 1) return MP_ERR_ARG;
+  if (!all_a16(codes, planes)) return MP_ERR_ARG;
+  if (n0 < 0 || n0 > n1 || n1 > cap || n0 % SCAN_TILE || n1 % SCAN_TILE) return MP_ERR_ARG;
+  const int64_t nt = (n1 - n0) / SCAN_TILE;
+  if (U * nt * L >= ((int64_t)1 << 31)) return MP_ERR_UNSUPPORTED;  // one block per (unit, tile, table)
+  return hip_status(launch_plane_build(codes, U, cap, K, L, n0 / SCAN_TILE, nt, planes, as_stream(stream)));
+}
+
+static int check_planes(const uint32_t *planes, int64_t n_planes, int64_t n) {
+  if (!planes) return MP_OK;
+  if (!a16(planes) || n_planes < 0 || n_planes > n || n_planes % SCAN_TILE) return MP_ERR_ARG;
+  return MP_OK;
+}
+
 int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void *Wp, int K, int L, uint16_t *qcodes,
                       void *stream) {
   int st = check_shape(d, K, L);
@@ -145,18 +167,20 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
 }
 
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     const uint32_t *planes, int64_t n_planes, const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                      int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream) {
   int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
   if (!qcodes) return MP_ERR_ARG;
+  if ((st = check_planes(planes, n_planes, n))) return st;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   if (geo.nchunks == 0) return MP_OK;
   return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T,
-                                  n_static_head, n_static_tail, geo, w, want_idx != 0, as_stream(stream)));
+                                  n_static_head, n_static_tail, geo, w, want_idx != 0, as_stream(stream), nullptr,
+                                  nullptr, planes, n_planes));
 }
 
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
@@ -174,7 +198,7 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
 }
 
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
                    int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream) {
@@ -183,6 +207,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   if (st) return st;
   if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
   if (!all_a16(out, Wp)) return MP_ERR_ARG;
+  if ((st = check_planes(planes, n_planes, n))) return st;
   hipStream_t s = as_stream(stream);
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
@@ -196,14 +221,15 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   }
   if (geo.nchunks > 0) {
     hipError_t e = launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head,
-                                 n_static_tail, geo, w, idx != nullptr, s);
+                                 n_static_tail, geo, w, idx != nullptr, s, nullptr, nullptr, planes, n_planes);
     if (e != hipSuccess) return MP_ERR_HIP;
   }
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
 }
 
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                   uint16_t *codes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
+                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
                    int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
   const bool app = k_new != nullptr;
@@ -215,6 +241,7 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
   if (st) return st;
   if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
   if (!all_a16(out, Wp, k_new, v_new)) return MP_ERR_ARG;
+  if ((st = check_planes(planes, n_planes, n))) return st;  // the keys before the append
   hipStream_t s = as_stream(stream);
   const int64_t U = (int64_t)B * Hkv;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, nd, cap);
@@ -234,7 +261,8 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
   hipEvent_t *ev = (hipEvent_t *)sample_events;
   if (geo.nchunks > 0) {
     if (launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, T, n_static_head,
-                      n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr) !=
+                      n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, planes,
+                      n_planes) !=
         hipSuccess)
       return MP_ERR_HIP;
   } else if (ev && (hipEventRecord(ev[0], s) != hipSuccess || hipEventRecord(ev[1], s) != hipSuccess)) {

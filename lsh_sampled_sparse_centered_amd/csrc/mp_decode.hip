@@ -7,6 +7,8 @@
 
 #include <cmath>
 
+#include <type_traits>
+
 #include "mp_internal.h"
 
 namespace mp {
@@ -283,7 +285,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
-    float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt) {
+    float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt,
+    const uint32_t *__restrict__ planes, int64_t npt, int64_t ptiles) {
   // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
   // words [0, FW) says "at least one of this wave's tables matched", of
   // words [FW, 2FW) "at least two".
@@ -298,11 +301,17 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
     T v[ATT_E][D];                         // staged value rows of this round's entries
     alignas(16) float lw[GM][ATT_E];       // log-weights s - ln P (or -inf), head-major
   };
+  struct PlaneLds {  // per table stream: "at least one" / "at least two" words [stream][head][word]
+    uint32_t c1[16][GM][16];
+    uint32_t c2[16][GM][16];
+  };
   __shared__ union {
     ScanLds s;
     CntLds c;
     AttnLds a;
+    PlaneLds p;
   } sm;  // scan and attention phases never overlap in time
+  __shared__ uint32_t pw2[GM][16];  // plane scan: per head, the tile's sampled-key words
   extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
   uint32_t *qpk = (uint32_t *)qpk4;
   __shared__ float qsh[GM][D];
@@ -357,7 +366,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
                      rs, lo, (uint32_t)(min(j0 + hf * (MP_SB / 2) + r, jlast) - jb) * rstride32, 2));
   };
-  if (ntw > 0) {
+  // Tiles the bit-plane index covers are scanned there (threshold 2 only).
+  const bool use_pl = planes != nullptr && K > 0 && cf.T == 2 && c < npt;
+  if (!use_pl && ntw > 0) {
     load_half(0, 0);
     load_half(0, 1);
   }
@@ -433,14 +444,6 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
   uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
   {
     const int64_t sbase = tbase;
-    // ---- scan
-    uint32_t acc[GM][4];
-#pragma unroll
-    for (int h = 0; h < GM; ++h)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) acc[h][w] = 0;
-#define MP_MIS(word, Q) \
-  __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, (word) ^ (Q)), one))
     // query codes of table l for every head (GM >= 4: 16-byte LDS reads)
     auto qcodes_of = [&](int l, uint32_t (&Q)[GM]) {
       if constexpr (GM >= 4) {
@@ -457,6 +460,83 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
         for (int h = 0; h < GM; ++h) Q[h] = qpk[l * GM + h];
       }
     };
+    const int64_t klo = sbase + 2 * tid;
+    uint32_t mlo = 0, mhi = 0;
+    if (use_pl) {
+      // Bit-plane scan: the tile's planes are one contiguous region, row
+      // (b, l) = bit b of table l's codes for the tile's 512 keys (16 words).
+      // Lane j of a 16-lane group holds word j (32 keys); the wave's four
+      // groups take four consecutive tables (one contiguous 256-byte read per
+      // plane).  Per head, the 32 keys' mismatch word of a table is the OR over
+      // b of the plane XOR the query's bit b (sign-extended); "at least one" /
+      // "at least two" matching tables are kept as bit masks.
+      const int pj = lane & 15, sg = (wave << 2) | (lane >> 4);  // word, table stream
+      const uint32_t *pt = planes + (u * ptiles + c) * (int64_t)K * L * 16 + pj;
+      uint32_t c1[GM], c2[GM];
+#pragma unroll
+      for (int h = 0; h < GM; ++h) c1[h] = c2[h] = 0u;
+      // KB >= K planes per table; planes past K repeat plane K-1 (same word,
+      // same query bit), which leaves the OR unchanged
+      auto pscan = [&](auto kbc) {
+        constexpr int KB = decltype(kbc)::value;
+        for (int l = sg; l < L; l += 16) {
+          uint32_t pw[KB];
+#pragma unroll
+          for (int b = 0; b < KB; ++b) pw[b] = __builtin_nontemporal_load(pt + ((int64_t)min(b, K - 1) * L + l) * 16);
+          uint32_t Q[GM];
+          qcodes_of(l, Q);
+#pragma unroll
+          for (int h = 0; h < GM; ++h) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int b = 0; b < KB; ++b) m |= pw[b] ^ (uint32_t)__builtin_amdgcn_sbfe((int)Q[h], min(b, K - 1), 1);
+            c2[h] |= c1[h] & ~m;
+            c1[h] |= ~m;
+          }
+        }
+      };
+      if (K <= 8)
+        pscan(std::integral_constant<int, 8>{});
+      else if (K <= 10)
+        pscan(std::integral_constant<int, 10>{});
+      else if (K <= 12)
+        pscan(std::integral_constant<int, 12>{});
+      else
+        pscan(std::integral_constant<int, 16>{});
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        sm.p.c1[sg][h][pj] = c1[h];
+        sm.p.c2[sg][h][pj] = c2[h];
+      }
+      __syncthreads();
+      if (tid < GM * 16) {  // fold the 16 streams: at least two overall
+        const int h = tid >> 4, jj = tid & 15;
+        uint32_t a1 = 0u, a2 = 0u;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t b1 = sm.p.c1[v][h][jj], b2 = sm.p.c2[v][h][jj];
+          a2 |= b2 | (a1 & b1);
+          a1 |= b1;
+        }
+        pw2[h][jj] = h < G ? a2 : 0u;
+      }
+      __syncthreads();
+      const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        const uint32_t wv = pw2[h][wj];
+        mlo |= ((wv >> k0) & 1u) << h;
+        mhi |= ((wv >> (k0 + 1)) & 1u) << h;
+      }
+    } else {
+    // ---- scan
+    uint32_t acc[GM][4];
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc[h][w] = 0;
+#define MP_MIS(word, Q) \
+  __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, (word) ^ (Q)), one))
     // two tables (rows ra, rb: tables l and l + 4) into the mismatch counts
     auto scan_pair = [&](const uint4 &ra, const uint4 &rb, int l) {
       const uint32_t a4[4] = {ra.x, ra.y, ra.z, ra.w};
@@ -554,8 +634,6 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
     // (scan lane tid/4, key slots k0 = 2*(tid%4) and k0+1).  At least two
     // matching tables overall <=> some wave has two, or two waves have one;
     // any other threshold adds the four waves' counts.
-    const int64_t klo = sbase + 2 * tid;
-    uint32_t mlo = 0, mhi = 0;
     if (cf.T != 2) {
       const int sl = tid >> 2, k0 = 2 * (tid & 3);
 #pragma unroll
@@ -584,6 +662,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
           }
         }
       }
+    }
     }
     if (klo < nsh || klo >= n - nst) mlo = headbits | FORCED;
     if (klo + 1 < nsh || klo + 1 >= n - nst) mhi = headbits | FORCED;
@@ -711,10 +790,44 @@ __global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kern
   }
 }
 
+// --------------------------------------------------------------------------
+// Bit-plane index of the code store (the same codes, K bits per key and table
+// instead of 16): one block of 8 waves per (unit, tile, table).  Lane i of
+// wave w holds the code of key 512 t + 64 w + i; the ballot of its bit b is
+// bit b's plane for those 64 keys (two 32-key words), and lane b (b < K) of
+// each lane half stores its half's word.
+__global__ __launch_bounds__(512) void plane_build_kernel(const uint16_t *__restrict__ codes, int64_t cap, int K,
+                                                          int L, int64_t t0, int64_t nt, int64_t ptiles,
+                                                          uint32_t *__restrict__ planes) {
+  const int64_t bid = blockIdx.x;
+  const int l = (int)(bid % L);
+  const int64_t r = bid / L;
+  const int64_t t = t0 + r % nt, u = r / nt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t code = codes[(u * L + l) * cap + t * SCAN_TILE + 64 * wave + lane];
+  uint32_t val = 0u;
+  for (int b = 0; b < K; ++b) {
+    const uint64_t bal = __ballot((code >> b) & 1u);
+    if ((lane & 31) == b) val = (uint32_t)(lane < 32 ? bal : bal >> 32);
+  }
+  const int b = lane & 31;
+  if (b < K) planes[(((u * ptiles + t) * K + b) * L + l) * 16 + 2 * wave + (lane >> 5)] = val;
+}
+
+hipError_t launch_plane_build(const uint16_t *codes, int64_t U, int64_t cap, int K, int L, int64_t t0, int64_t nt,
+                              uint32_t *planes, hipStream_t s) {
+  if (nt <= 0 || U <= 0) return hipSuccess;
+  const int64_t ptiles = (cap + SCAN_TILE - 1) / SCAN_TILE;
+  const int64_t nb = U * nt * L;
+  plane_build_kernel<<<dim3((unsigned)nb), 512, 0, s>>>(codes, cap, K, L, t0, nt, ptiles, planes);
+  return hipGetLastError();
+}
+
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int Tthr, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
-                         bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop) {
+                         bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
+                         const uint32_t *planes, int64_t n_planes) {
   const int G = Hq / Hkv;
   const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
@@ -722,10 +835,12 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   const LnPCoef cf = lnp_coef(L, Tthr);
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
+  const int64_t npt = planes ? n_planes / SCAN_TILE : 0;  // tiles the plane index covers
+  const int64_t ptiles = (cap + SCAN_TILE - 1) / SCAN_TILE;
 #define MP_SAMPLE(T, GMV)                                                                                    \
   hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
-                        nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt)
+                        nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \

@@ -133,7 +133,12 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start = nullptr,
-                         hipEvent_t ev_stop = nullptr);
+                         hipEvent_t ev_stop = nullptr, const uint32_t *planes = nullptr, int64_t n_planes = 0);
+// Bit-plane index of the code store: tiles [t0, t0 + nt) of every unit,
+// planes [U][ptiles][K][L][16] u32 (word j of row (b, l) of tile t = bit b of
+// table l's codes for keys 512 t + 32 j .. + 31).
+hipError_t launch_plane_build(const uint16_t *codes, int64_t U, int64_t cap, int K, int L, int64_t t0, int64_t nt,
+                              uint32_t *planes, hipStream_t s);
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
                         float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s);
 

@@ -37,7 +37,7 @@ def test_strerror_and_version():
     for code in (OK, ARG, UNSUP, CAP, WS, -5):
         assert len(mp.strerror(code)) > 5
     assert mp.strerror(12345) == "unknown status"
-    assert mp.lib().mp_version() == 1
+    assert mp.lib().mp_version() == 2
 
 
 def test_size_queries():
@@ -99,11 +99,12 @@ def test_append_rejects_invalid_arguments():
 
 
 def _decode(**kw):
-    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100, cap=128,
-             d=128, K=8, L=75, T=2, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
-             wsb=1 << 30)
+    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8,
+             n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None,
+             cnt=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"], a["B"], a["Hq"],
+    return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["planes"], a["np"], a["km"],
+                                   a["Wp"], a["B"], a["Hq"],
                                    a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"], a["nst"], a["qin"],
                                    a["qout"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
 
@@ -128,14 +129,47 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(T=1) != UNSUP and _decode(T=75) != UNSUP
     for arg in ("q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _decode(**{arg: FAKE + 2}) == ARG, arg
+    # bit-plane index: whole 512-key tiles at or below n, 16-byte aligned
+    assert _decode(planes=FAKE, np=100, n=1000, cap=1024) == ARG
+    assert _decode(planes=FAKE, np=1024, n=1000, cap=1024) == ARG
+    assert _decode(planes=FAKE + 4, np=512, n=1000, cap=1024) == ARG
+    assert _decode(planes=FAKE, np=-512, n=1000, cap=1024) == ARG
+    assert _decode(planes=None, np=12345) != ARG  # ignored without planes
+
+
+def test_build_planes_rejects_invalid_arguments():
+    L = mp.lib()
+    assert L.mp_planes_bytes(8, 98304, 10, 150) == 8 * 192 * 10 * 150 * 64
+    assert L.mp_planes_bytes(2, 1000, 8, 75) == 2 * 2 * 8 * 75 * 64  # the last tile is partial
+    assert L.mp_planes_bytes(2, 1024, 0, 75) == 0
+    ok = dict(codes=FAKE, U=2, n0=0, n1=1024, cap=1024, K=8, L=75, planes=FAKE)
+
+    def b(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mp_build_planes(a["codes"], a["U"], a["n0"], a["n1"], a["cap"], a["K"], a["L"], a["planes"], None)
+
+    assert b(codes=None) == ARG
+    assert b(planes=None) == ARG
+    assert b(planes=FAKE + 4) == ARG
+    assert b(n0=100) == ARG
+    assert b(n1=1000) == ARG
+    assert b(n1=1536) == ARG  # past cap
+    assert b(n0=1024, n1=512) == ARG
+    assert b(K=0) == ARG
+    assert b(L=513) == UNSUP
+    assert b(cap=1020) == ARG
+    assert b(n0=512, n1=512) == OK  # nothing to do
 
 
 def test_decode_stages_reject_invalid_arguments():
     L = mp.lib()
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0, 0, 0, FAKE,
-                              1 << 30, None) == ARG  # qcodes required
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0, 0, FAKE,
-                              1 << 30, None) == UNSUP  # threshold 0
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0, 0,
+                              0, FAKE, 1 << 30, None) == ARG  # qcodes required
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0,
+                              0, FAKE, 1 << 30, None) == UNSUP  # threshold 0
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 512, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0,
+                              0, 0, FAKE, 1 << 30, None) == ARG  # planes past n
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, None, None, None, None, FAKE, 1 << 30, None) == ARG
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, FAKE, None, None, None, FAKE, 10, None) == WS
 
@@ -151,11 +185,12 @@ def test_encode_queries_rejects_invalid_arguments():
 
 
 def _step(**kw):
-    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8, n=100,
-             cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None, ws=FAKE,
-             wsb=1 << 30)
+    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1,
+             Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None,
+             ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return mp.lib().mp_decode_step(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["km"], a["Wp"],
+    return mp.lib().mp_decode_step(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["planes"],
+                                   a["np"], a["km"], a["Wp"],
                                    a["B"], a["Hq"], a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"],
                                    a["nst"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None, None)
 
@@ -169,5 +204,7 @@ def test_step_rejects_invalid_arguments():
     assert _step(Hkv=3) == ARG
     assert _step(ws=None) == WS
     assert _step(T=0) == UNSUP
+    assert _step(planes=FAKE, np=512, n=511, cap=1024) == ARG  # the appended key is not in the index
+    assert _step(planes=FAKE, np=512, n=512, cap=1024) != ARG
     for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _step(**{arg: FAKE + 4}) == ARG, arg
