@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--threshold", type=int, default=2,
                     help="collision threshold T: a key is sampled in at least T of the L tables (the pages' 2)")
+    ap.add_argument("--planes", choices=("on", "off"), default="on",
+                    help="on: build the bit-plane index of the code store at set-up (whole 512-key tiles of the "
+                         "prefill keys) and let the threshold-2 scan read it; off: scan the 16-bit codes only")
     ap.add_argument("--policy", choices=("sampled", "pages"), default="sampled",
                     help="sampled: every layer sampled; pages: the pages' decoding policy (layers 0 and 16 "
                          "dense, i.e. K = 0, and 4 sink + 64 local keys forced into every sampled layer's set)")
@@ -70,7 +73,7 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str) -> dict:
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, planes: bool) -> dict:
     """HBM bytes per sampling-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
     copy of calib_mib MiB (the largest __amd_rocclr_copyBuffer dispatch)."""
@@ -98,7 +101,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, worklo
     write_scale = calib_bytes / (w_c * 1024.0)
     fetch_b = f_s * 1024.0 * fetch_scale
     write_b = w_s * 1024.0 * write_scale
-    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "bytes_per_launch": fetch_b + write_b,
+    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "planes": planes,
+            "bytes_per_launch": fetch_b + write_b,
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
             "fetch_size_kib_per_launch": f_s, "write_size_kib_per_launch": w_s, "dispatches": [nf, nw],
             "calibration": {"copy_mib": calib_mib, "fetch_size_kib": f_c, "write_size_kib": w_c,
@@ -108,7 +112,8 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, worklo
 def main() -> int:
     args = parse()
     if args.traffic:
-        tr = traffic_from_counters(args.traffic[0], args.traffic[1], args.calib_copy_mib, args.workload)
+        tr = traffic_from_counters(args.traffic[0], args.traffic[1], args.calib_copy_mib, args.workload,
+                                   args.planes == "on" and args.threshold == 2)
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(tr, f, indent=1)
         print(json.dumps(tr))
@@ -142,6 +147,9 @@ def main() -> int:
     lcfg = [((0, 2, 0, 0) if pages and l in (0, 16) else (K, L, 4 if pages else 0, 64 if pages else 0))
             for l in range(nlayers)]
     sampled_layers = [l for l in range(nlayers) if lcfg[l][0] > 0]
+    use_planes = args.planes == "on"
+    n_planes = (n0 // 512) * 512  # appended keys stay in the 16-bit codes (tiles past the index)
+    scan_planes = use_planes and args.threshold == 2
 
     # ------------------------------------------------------------------ inputs + code-store build
     layers = []
@@ -171,10 +179,22 @@ def main() -> int:
                 kn[s, u], vn[s, u] = synth.step_kv(args.seed, l, b, h, d, dt, step=s + 1)
                 qs[s, b, h * G:(h + 1) * G] = synth.unit_queries(args.seed, l, b, h, G, d, dt, step=s + 1)
         kn, vn, qs = kn.to(dev), vn.to(dev), qs.to(dev)
-        layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1)))
+        planes, pev = None, None
+        if use_planes and Kl > 0:  # the index of the prefill keys' whole tiles
+            planes = torch.empty(U, (cap + 511) // 512, Kl, Ll, 16, dtype=torch.int32, device=dev)
+            pev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            pev[0].record()
+            mp.mp_build_planes(codes, Kl, n_planes, planes=planes)
+            pev[1].record()
+        layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1),
+                           planes=planes, pev=pev))
     torch.cuda.synchronize()
     build_ms = [layers[l]["ev"][0].elapsed_time(layers[l]["ev"][1]) for l in sampled_layers]
-    log("built %d layers; build %.3f ms/layer (median)" % (nlayers, float(np.median(build_ms))))
+    planes_ms = [layers[l]["pev"][0].elapsed_time(layers[l]["pev"][1]) for l in sampled_layers
+                 if layers[l]["pev"] is not None]
+    log("built %d layers; build %.3f ms/layer (median)%s" %
+        (nlayers, float(np.median(build_ms)),
+         "; bit-plane index %.3f ms/layer" % float(np.median(planes_ms)) if planes_ms else ""))
 
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
     outs = [torch.empty(w.batch, w.hq, d, dtype=torch.float32, device=dev) for _ in range(nlayers)]
@@ -206,7 +226,8 @@ def main() -> int:
             ev = kev[k * nlayers + l] if k >= 0 else None
             mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
                               lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
-                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev, T=args.threshold)
+                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev, T=args.threshold,
+                              planes=lay["planes"], n_planes=n_planes if lay["planes"] is not None else 0)
         if timed:
             n_timed.append(n_cur + 1)
         n_cur += 1
@@ -246,14 +267,16 @@ def main() -> int:
     n_dec = float(np.mean(n_timed))
     # algorithmic bytes of one sample launch (one layer): codes of every key once, each distinct sampled
     # K and V row once, the queries, their codes and the key means
-    bytes_launch = U * (2 * L * n_dec + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
+    # (with the bit-plane index, K bits per key and table for the tiles it covers)
+    code_bytes = (K * L * n_planes / 8 + 2 * L * (n_dec - n_planes)) if scan_planes else 2 * L * n_dec
+    bytes_launch = U * (code_bytes + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
     achieved = bytes_launch / (kern_ms.mean() * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages and
-                args.threshold == 2):
+                args.threshold == 2 and bool(tr.get("planes", False)) == scan_planes):
             traffic = tr.get("bytes_per_launch")
     # a dense layer reads its (two-table) codes and every key's K and V row
     dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
@@ -318,6 +341,8 @@ def main() -> int:
         "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
         "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": d, "context": n0, "K": K, "L": L, "threshold": args.threshold,
+                   "code_scan": ("bit-plane index below key %d, 16-bit codes above" % n_planes if scan_planes
+                                 else "16-bit codes"),
                    "parallelism": "single GPU",
                    "policy": ("every layer sampled" if not pages else
                               "pages: layers 0 and 16 dense (K = 0), 4 sink + 64 local keys forced elsewhere")},
@@ -331,7 +356,8 @@ def main() -> int:
                  "sampled_frac_per_head": head_frac, "union_keys_per_unit": union_per_unit},
         "encoder": {"build_ms_per_layer": float(np.median(build_ms)), "tflops": enc_tflops,
                     "frac_mfma_bf16": enc_tflops / BF16_MFMA_PEAK_TFLOPS,
-                    "note": "build = key mean + projection GEMM + sign pack, per layer"},
+                    "note": "build = key mean + projection GEMM + sign pack, per layer",
+                    "planes_ms_per_layer": float(np.median(planes_ms)) if planes_ms else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
