@@ -64,8 +64,9 @@ def code_subset(w, layers):
 class LayerRun:
     """One layer on the device, decoded step by step, checked against the oracle."""
 
-    def __init__(self, w, layer_idx, code_units, T=2):
+    def __init__(self, w, layer_idx, code_units, T=2, planes=False):
         self.w, self.li, self.T = w, layer_idx, T
+        self.use_planes, self.planes, self.n_planes = planes, None, 0
         self.code_units = sorted(code_units)
         lay = synth.layer_inputs(w, SEED, layer_idx, device="cuda")
         self.U, self.cap, self.n0 = w.batch * w.hkv, lay["cap"], lay["n"]
@@ -141,6 +142,14 @@ class LayerRun:
         _say("layer %d: %d key means bitwise; %d of %d subset codes differ, all inside the band" %
              (self.li, self.U, ndiff, total))
 
+    def build_planes(self):
+        """Bit-plane index of the (injected) codes for the prefill keys' whole
+        tiles, as the benchmark builds it; appended keys stay past it."""
+        self.n_planes = (self.n0 // 512) * 512
+        self.planes = mp.mp_build_planes(self.codes, self.w.K, self.n_planes)
+        torch.cuda.synchronize()
+        _say("layer %d: bit-plane index of keys [0, %d)" % (self.li, self.n_planes))
+
     # ------------------------------------------------------------ one step
     def step(self, s, check_units):
         w, G = self.w, self.w.group
@@ -158,7 +167,7 @@ class LayerRun:
         lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
         cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
         mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, self.ws,
-                          out=out, lse=lse, count=cnt, T=self.T)
+                          out=out, lse=lse, count=cnt, T=self.T, planes=self.planes, n_planes=self.n_planes)
         torch.cuda.synchronize()
         assert torch.equal(self.Kc[:, n], kn) and torch.equal(self.Vc[:, n], vn)
         # appended codes (frozen means) of every unit
@@ -192,7 +201,8 @@ class LayerRun:
         cnt2 = torch.empty_like(cnt)
         idx = torch.full((w.batch, w.hq, self.cap), -1, dtype=torch.int32, device="cuda")
         mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K,
-                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws, T=self.T)
+                          qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws, T=self.T,
+                          planes=self.planes, n_planes=self.n_planes)
         torch.cuda.synchronize()
         o1, l1, c1 = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
         o2, c2, ix = out2.cpu().numpy(), cnt2.cpu().numpy(), idx.cpu().numpy()
@@ -226,16 +236,19 @@ class LayerRun:
                     if own:
                         assert np.max(np.abs(o1[b, hh] - ref["out"][j, g])) <= OUT_TOL, (s, u, g)
                         assert abs(float(l1[b, hh]) - float(ref["lse"][j, g])) <= LSE_TOL, (s, u, g)
-        _say("layer %d step %d (n=%d, T=%d): %d units checked (%d on the step's own outputs); sets exact; worst "
-             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, self.T, len(check_units), direct, worst,
+        _say("layer %d step %d (n=%d, T=%d, index below %d): %d units checked (%d on the step's own outputs); sets exact; worst "
+             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, self.T, self.n_planes, len(check_units),
+                                                     direct, worst,
                                                      float(np.mean(sizes))))
 
 
-def _run_layers(w, layers, steps=1, check_every=None, T=2):
+def _run_layers(w, layers, steps=1, check_every=None, T=2, planes=True):
     subset = code_subset(w, layers)
     for li in layers:
-        run = LayerRun(w, li, [u for l, u in subset if l == li], T=T)
+        run = LayerRun(w, li, [u for l, u in subset if l == li], T=T, planes=planes)
         run.check_build_and_inject()
+        if planes:
+            run.build_planes()
         allu = list(range(run.U))
         sub = run.code_units
         for s in range(1, steps + 1):
@@ -248,9 +261,15 @@ def _run_layers(w, layers, steps=1, check_every=None, T=2):
 @pytest.mark.parametrize("part", range(4))
 def test_llama8b_96k_all_layers(part):
     """Llama-3.1-8B shape at 96K context (32 q / 8 KV heads, K=10, L=150):
-    every unit of 8 of the 32 layers, one appending step."""
+    every unit of 8 of the 32 layers, one appending step, scanning the
+    bit-plane index of the prefill keys as the benchmark does."""
     w = synth.WORKLOADS["llama8b_96k"]
     _run_layers(w, list(range(8 * part, 8 * part + 8)))
+
+
+def test_llama8b_96k_codes_only():
+    """The 96K layer shape scanning only the 16-bit codes (no index)."""
+    _run_layers(synth.WORKLOADS["llama8b_96k"], [7], planes=False)
 
 
 @pytest.mark.parametrize("T", [1, 3])
@@ -263,7 +282,7 @@ def test_llama8b_96k_threshold(T):
 @pytest.mark.parametrize("layer_idx", [0, 39])
 def test_codellama13b_b16_layer(layer_idx):
     """CodeLlama-13B shape, batch 16, MHA (640 units per layer, K=9, L=120), one appending step."""
-    _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx])
+    _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx], planes=layer_idx == 0)
 
 
 def test_codellama34b_b4_64_steps():
