@@ -14,7 +14,10 @@
 namespace mp {
 
 #ifndef MP_OCC
-#define MP_OCC 6  // waves per SIMD the G <= 4 kernels are compiled for
+#define MP_OCC 7  // waves per SIMD the G <= 4 bf16 kernels are compiled for (72 VGPRs: one round at 96K)
+#endif
+#ifndef MP_OCC_F32
+#define MP_OCC_F32 6  // fp32 caches (more registers per gathered row)
 #endif
 #ifndef MP_OCC8
 #define MP_OCC8 5  // waves per SIMD the G = 8 kernels are compiled for (96 VGPRs)
@@ -281,7 +284,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 // The query codes, queries and key mean are fetched while the first batch
 // of codes is in flight.  One partial record (m, l, count, o) per head.
 template <typename T, int GM>
-__global__ __launch_bounds__(256, (GM <= 4 ? MP_OCC : MP_OCC8)) void sample_kernel(
+__global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F32) : MP_OCC8)) void sample_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
