@@ -795,34 +795,47 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
 
 // --------------------------------------------------------------------------
 // Bit-plane index of the code store (the same codes, K bits per key and table
-// instead of 16): one block of 8 waves per (unit, tile, table).  Lane i of
-// wave w holds the code of key 512 t + 64 w + i; the ballot of its bit b is
-// bit b's plane for those 64 keys (two 32-key words), and lane b (b < K) of
-// each lane half stores its half's word.
-__global__ __launch_bounds__(512) void plane_build_kernel(const uint16_t *__restrict__ codes, int64_t cap, int K,
-                                                          int L, int64_t t0, int64_t nt, int64_t ptiles,
-                                                          uint32_t *__restrict__ planes) {
+// instead of 16): one block of 8 waves per (unit, tile, group of 8 tables),
+// wave w taking table 8g + w.  Lane i holds the codes of keys 512 t + 64 c + i
+// (c < 8, all eight loads in flight); the ballot of their bit b is bit b's
+// plane for those 64 keys (two 32-key words), and lane b (b < K) of each lane
+// half stores its half's word.
+constexpr int PB_TABLES = 8;  // tables per plane-build block (one per wave)
+
+__global__ __launch_bounds__(64 * PB_TABLES) void plane_build_kernel(const uint16_t *__restrict__ codes, int64_t cap,
+                                                                     int K, int L, int64_t t0, int64_t nt,
+                                                                     int64_t ptiles, uint32_t *__restrict__ planes) {
+  const int ng = (L + PB_TABLES - 1) / PB_TABLES;
   const int64_t bid = blockIdx.x;
-  const int l = (int)(bid % L);
-  const int64_t r = bid / L;
+  const int g = (int)(bid % ng);
+  const int64_t r = bid / ng;
   const int64_t t = t0 + r % nt, u = r / nt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t code = codes[(u * L + l) * cap + t * SCAN_TILE + 64 * wave + lane];
-  uint32_t val = 0u;
-  for (int b = 0; b < K; ++b) {
-    const uint64_t bal = __ballot((code >> b) & 1u);
-    if ((lane & 31) == b) val = (uint32_t)(lane < 32 ? bal : bal >> 32);
+  const int l = g * PB_TABLES + wave;
+  if (l >= L) return;  // whole waves; the kernel has no barrier
+  const uint16_t *src = codes + (u * L + l) * cap + t * SCAN_TILE + lane;
+  uint32_t cd[SCAN_TILE / 64];
+#pragma unroll
+  for (int c = 0; c < SCAN_TILE / 64; ++c) cd[c] = src[64 * c];
+  uint32_t *dst = planes + ((u * ptiles + t) * K * L + l) * 16 + (lane >> 5);
+  const int bl = lane & 31;
+#pragma unroll
+  for (int c = 0; c < SCAN_TILE / 64; ++c) {
+    uint32_t val = 0u;
+    for (int b = 0; b < K; ++b) {
+      const uint64_t bal = __ballot((cd[c] >> b) & 1u);
+      if (bl == b) val = (uint32_t)(lane < 32 ? bal : bal >> 32);
+    }
+    if (bl < K) dst[(int64_t)bl * L * 16 + 2 * c] = val;
   }
-  const int b = lane & 31;
-  if (b < K) planes[(((u * ptiles + t) * K + b) * L + l) * 16 + 2 * wave + (lane >> 5)] = val;
 }
 
 hipError_t launch_plane_build(const uint16_t *codes, int64_t U, int64_t cap, int K, int L, int64_t t0, int64_t nt,
                               uint32_t *planes, hipStream_t s) {
   if (nt <= 0 || U <= 0) return hipSuccess;
   const int64_t ptiles = (cap + SCAN_TILE - 1) / SCAN_TILE;
-  const int64_t nb = U * nt * L;
-  plane_build_kernel<<<dim3((unsigned)nb), 512, 0, s>>>(codes, cap, K, L, t0, nt, ptiles, planes);
+  const int64_t nb = U * nt * ((L + PB_TABLES - 1) / PB_TABLES);
+  plane_build_kernel<<<dim3((unsigned)nb), 64 * PB_TABLES, 0, s>>>(codes, cap, K, L, t0, nt, ptiles, planes);
   return hipGetLastError();
 }
 
