@@ -269,6 +269,12 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 // Forced keys (the static head/tail ranges) are sampled for every head with
 // P = 1.
 //
+// Tiles covered by the bit-plane index (threshold 2) are scanned there
+// instead: lane j of each 16-lane group holds word j (32 keys) of one table
+// stream's planes, a table's mismatch word per head is the OR over its K
+// planes of the plane XOR the query's bit, and "at least one / two matching
+// tables" are bit masks, folded over the 16 streams through LDS.
+//
 // Compaction: wave ballots + popcounts rank the keys, giving the tile's
 // union list (key, head mask) in LDS in ascending key order.
 //
