@@ -205,37 +205,21 @@ __device__ inline void store_row8<__bf16>(__bf16 *p, const float (&v)[8]) {
   *(bf16x8 *)p = a;
 }
 
-// Bit r of the result is (a[r] > 0) for every non-zero a[r]: the sign bits
+// Bit r of the result is (a[r] > 0).  0 - a[r] has its sign bit set exactly
+// when a[r] > 0: a positive value turns negative, a negative one positive,
+// and both zeros give +0 (x - x rounds to +0).  The sign bits of 0 - a[r]
 // are shifted in one per element (a funnel shift of (word, element) by 31,
-// from element 15 down to 0) and inverted.  Negative values and -0 give 0; +0 gives 1, which differs from
-// (a[r] > 0) only where the projection is exactly zero.  That is inside the
-// rounding band unless the projected row itself is zero, which the caller
-// handles (a zero row encodes to all-zero codes).  Each element is copied
-// to a scalar before the bit cast.
+// from element 15 down to 0).  An exactly zero projection -- a zero row, a
+// zero projection column, or an exact cancellation -- therefore gives bit 0,
+// as (z > 0) does.  Each element is copied to a scalar before the bit cast.
 __device__ inline uint32_t sign_bits16(const f32x16 &a) {
-  uint32_t neg = 0;
+  uint32_t pos = 0;
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
-    const float z = a[r];
-    neg = __builtin_amdgcn_alignbit(neg, __builtin_bit_cast(uint32_t, z), 31u);  // (neg << 1) | sign(z)
+    const float nz = 0.0f - a[r];
+    pos = __builtin_amdgcn_alignbit(pos, __builtin_bit_cast(uint32_t, nz), 31u);  // (pos << 1) | (a[r] > 0)
   }
-  return ~neg & 0xffffu;
-}
-
-// 1 when the row held as B operands (xb[nt], this lane's half of the dims)
-// together with the partner lane's half has a non-zero element, per lane's
-// final row: lane l < 32 owns row l (nt = 0), lane l >= 32 owns row l (nt = 1).
-__device__ inline bool row_nonzero(const bf16x8 (&xb)[2][KSTEPS], int half) {
-  uint32_t nz0 = 0, nz1 = 0;
-#pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) {
-    const uint4 a = __builtin_bit_cast(uint4, xb[0][s]), b = __builtin_bit_cast(uint4, xb[1][s]);
-    nz0 |= (a.x | a.y | a.z | a.w) & 0x7fff7fffu;  // -0 counts as zero
-    nz1 |= (b.x | b.y | b.z | b.w) & 0x7fff7fffu;
-  }
-  const uint32_t send = half ? nz0 : nz1;
-  const uint32_t recv = (uint32_t)__shfl_xor((int)send, 32);
-  return ((half ? nz1 : nz0) | recv) != 0u;
+  return pos & 0xffffu;
 }
 
 // The kernel takes up to two independent row sets ("jobs", e.g. the keys to
@@ -347,7 +331,6 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
   }
 
   const int64_t my_row = row_w + lane;  // row whose 32-bit words this lane assembles
-  const bool my_nz = row_nonzero(xb, half);
   const bool my_ok = my_row < rows;
   uint16_t *my_out = out + u * out_su + my_row * out_si;
 
@@ -484,7 +467,7 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
         // with row 32 + l's.
         const auto sw = __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), sign_bits16(acc1), false, false);
         const uint32_t word = sw[0] | (sw[1] << 16);
-        wd[tt] = my_nz ? word : 0u;
+        wd[tt] = word;
       }
       tpend = tg;
       npend = min(ENC_TG, t1 - tg);
@@ -614,7 +597,6 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
   }
 
   const bool two = R > 32;
-  const bool my_nz = row_nonzero(xb, half);
   if (has_tile) {
     f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
@@ -627,7 +609,7 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
     const auto sw =
         __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), two ? sign_bits16(acc1) : 0u, false, false);
     const uint32_t word = sw[0] | (sw[1] << 16);
-    bits[lane][t - t0] = my_nz ? word : 0u;
+    bits[lane][t - t0] = word;
   }
   __syncthreads();
 

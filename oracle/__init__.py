@@ -52,7 +52,7 @@ def lib():
         L.orc_bf16.restype = ctypes.c_float
         L.orc_key_mean.argtypes = [_f32p, _i64, _int, _i64, _f32p]
         L.orc_key_mean.restype = None
-        L.orc_encode.argtypes = [_f32p, _i64, _int, _i64, _vp, _f32p, _int, _int, _u16p, _i64, _i64, _vp]
+        L.orc_encode.argtypes = [_f32p, _i64, _int, _i64, _vp, _i64, _f32p, _int, _int, _u16p, _i64, _i64, _vp]
         L.orc_encode.restype = None
         L.orc_table_collision_prob.argtypes = [ctypes.c_double, _int]
         L.orc_table_collision_prob.restype = ctypes.c_double
@@ -66,8 +66,6 @@ def lib():
         L.orc_sampling_prob_t.restype = ctypes.c_double
         L.orc_scan_t.argtypes = [_u16p, _i64, _i64, _int, _int, _u16p, _i64, _i64, _vp, _vp]
         L.orc_scan_t.restype = _i64
-        L.orc_match_counts.argtypes = [_u16p, _i64, _i64, _int, _u16p, _i32p]
-        L.orc_match_counts.restype = None
         L.orc_attend_t.argtypes = [_f32p, _f32p, _f32p, _i64, _int, _vp, _int, _int, _int, _i32p, _vp, _i64,
                                    _f64p, _f64p, _vp]
         L.orc_attend_t.restype = None
@@ -110,10 +108,13 @@ def key_mean(keys) -> np.ndarray:
 
 
 def encode(rows, W, K: int, L: int, mu=None, with_margin: bool = False):
-    """SimHash codes ``[nrows][L]`` of ``rows`` (centred by ``mu`` when given).
+    """SimHash codes ``[nrows][L]`` of ``rows`` (centred by ``mu`` when given:
+    one mean ``[d]`` for every row, or one per row ``[nrows][d]``).
 
     Section 2.2 and Section 4.3 'Hash function selection'.  With
-    ``with_margin`` also returns, per (row, table), min |z|/(|x||w|).
+    ``with_margin`` also returns, per (row, projection column j = l*K + b),
+    the relative projection size |z_j|/(|x||w_j|) (+inf where that norm
+    product is 0: the projection is exactly 0 and the bit exactly 0).
     """
     rows = _f32(rows)
     if rows.ndim == 1:
@@ -122,9 +123,13 @@ def encode(rows, W, K: int, L: int, mu=None, with_margin: bool = False):
     W = _f32(W)
     assert W.shape == (d, K * L)
     codes = np.zeros((nrows, L), np.uint16)
-    margin = np.zeros((nrows, L), np.float32) if with_margin else None
+    margin = np.zeros((nrows, K * L), np.float32) if with_margin else None
     mu_a = None if mu is None else _f32(mu)
-    lib().orc_encode(rows, nrows, d, d, _ptr(mu_a), W, K, L, codes, L, 1, _ptr(margin))
+    mu_stride = 0
+    if mu_a is not None and mu_a.ndim == 2:
+        assert mu_a.shape == (nrows, d)
+        mu_stride = d
+    lib().orc_encode(rows, nrows, d, d, _ptr(mu_a), mu_stride, W, K, L, codes, L, 1, _ptr(margin))
     return (codes, margin) if with_margin else codes
 
 
@@ -158,14 +163,6 @@ def scan(codes_tn, qcode, n_static_head: int = 0, n_static_tail: int = 0, T: int
     return idx[:cnt].copy(), forced[:cnt].astype(bool)
 
 
-def match_counts(codes_tn, qcode) -> np.ndarray:
-    codes_tn = np.ascontiguousarray(codes_tn, dtype=np.uint16)
-    L, n = codes_tn.shape
-    m = np.zeros(n, np.int32)
-    lib().orc_match_counts(codes_tn, n, n, L, np.ascontiguousarray(qcode, dtype=np.uint16), m)
-    return m
-
-
 def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool = False, T: int = 2):
     """Estimator of one head over its sampled set (Equations 9 and 11).
 
@@ -191,14 +188,14 @@ def build_codes(keys, n: int, W, K: int, L: int, with_margin: bool = False):
     """Code-store build of one layer.  ``keys`` is ``[U][cap][d]`` (any float dtype).
 
     Returns ``kmean [U][d]``, ``codes [U][L][cap]`` (columns >= n zero) and,
-    with ``with_margin``, ``margin [U][n][L]``.
+    with ``with_margin``, ``margin [U][n][K*L]`` (per key and projection column).
     """
     keys = _f32(keys)
     U, cap, d = keys.shape
     W = _f32(W)
     kmean = np.zeros((U, d), np.float32)
     codes = np.zeros((U, L, cap), np.uint16)
-    margin = np.zeros((U, n, L), np.float32) if with_margin else None
+    margin = np.zeros((U, n, K * L), np.float32) if with_margin else None
     lib().orc_build(keys, U, n, cap, d, W, K, L, kmean, codes, _ptr(margin))
     return (kmean, codes, margin) if with_margin else (kmean, codes)
 

@@ -79,18 +79,21 @@ void orc_key_mean(const float *keys, int64_t n, int d, int64_t stride, float *mu
 
 /* ---------------------------------------------------------------------------
  * SimHash codes (Section 2.2; Section 4.3 "Hash function selection").
- * For each row r: x = bf16(fp32(row - mu)) (mu may be NULL: no centring),
+ * For each row r: x = bf16(fp32(row - mu_r)) with mu_r = mu + r * mu_stride
+ * (mu may be NULL: no centring; mu_stride 0: one mean for every row),
  * z_j = sum_t x_t * bf16(W[t][j]) in fp64, bit_j = (z_j > 0), and
  * code_l = sum_{b<K} bit_{l*K+b} << b.
  *
  * W is d x (K*L), row-major (Algorithm 1's W in R^{d x (K x L)}).
  * codes[r * code_row_stride + l * code_table_stride] receives code_l.
- * margin (nullable, [nrows][L]) receives, per table, the smallest
- * |z_j| / (|x| |w_j|) over its K columns (+inf when that norm product is 0
- * or K = 0): bits whose margin is tiny depend on rounding order.
+ * margin (nullable, [nrows][K*L]) receives, per projection column j, the
+ * relative size |z_j| / (|x| |w_j|) of the projection that decides bit j:
+ * a bit whose margin is tiny depends on the rounding order of the sum.
+ * When |x| |w_j| = 0 the projection is exactly 0 and the bit exactly 0,
+ * whatever the order, so the margin is +inf.
  * ------------------------------------------------------------------------- */
 void orc_encode(const float *rows, int64_t nrows, int d, int64_t row_stride, const float *mu,
-                const float *W, int K, int L, uint16_t *codes, int64_t code_row_stride,
+                int64_t mu_stride, const float *W, int K, int L, uint16_t *codes, int64_t code_row_stride,
                 int64_t code_table_stride, float *margin)
 {
     const int ncol = K * L;
@@ -111,14 +114,13 @@ void orc_encode(const float *rows, int64_t nrows, int d, int64_t row_stride, con
         double xn = 0.0;
         for (int t = 0; t < d; ++t) {
             float k = rows[r * row_stride + t];
-            float c = mu ? k - mu[t] : k; /* fp32 subtraction */
+            float c = mu ? k - mu[r * mu_stride + t] : k; /* fp32 subtraction */
             x[t] = (double)orc_bf16(c);
             xn += x[t] * x[t];
         }
         xn = sqrt(xn);
         for (int l = 0; l < L; ++l) {
             unsigned code = 0;
-            double mg = INFINITY;
             for (int b = 0; b < K; ++b) {
                 const int j = l * K + b;
                 double z = 0.0;
@@ -126,13 +128,12 @@ void orc_encode(const float *rows, int64_t nrows, int d, int64_t row_stride, con
                     z += x[t] * wb[(int64_t)j * d + t];
                 if (z > 0.0)
                     code |= 1u << b;
-                double den = xn * wnorm[j];
-                if (den > 0.0 && fabs(z) / den < mg)
-                    mg = fabs(z) / den;
+                if (margin) {
+                    const double den = xn * wnorm[j];
+                    margin[r * ncol + j] = den > 0.0 ? (float)(fabs(z) / den) : INFINITY;
+                }
             }
             codes[r * code_row_stride + (int64_t)l * code_table_stride] = (uint16_t)code;
-            if (margin)
-                margin[r * L + l] = (float)mg;
         }
         free(x);
     }
@@ -216,18 +217,6 @@ int64_t orc_scan(const uint16_t *codes, int64_t table_stride, int64_t n, int L, 
     return orc_scan_t(codes, table_stride, n, L, 2, qcode, n_static_head, n_static_tail, idx, forced);
 }
 
-/* Per-key match counts for one query head (diagnostics for the tests). */
-void orc_match_counts(const uint16_t *codes, int64_t table_stride, int64_t n, int L, const uint16_t *qcode,
-                      int32_t *matches)
-{
-    for (int64_t i = 0; i < n; ++i) {
-        int m = 0;
-        for (int l = 0; l < L; ++l)
-            m += codes[(int64_t)l * table_stride + i] == qcode[l];
-        matches[i] = m;
-    }
-}
-
 /* ---------------------------------------------------------------------------
  * Estimator of one query head over its sampled set (Equations 9 and 11,
  * Algorithm 1 "Compute attention output estimation"):
@@ -303,13 +292,13 @@ void orc_attend(const float *q, const float *keys, const float *vals, int64_t ro
  *   keys  [U][cap][d] fp32       kmean [U][d]       codes [U][L][cap]
  * ------------------------------------------------------------------------- */
 void orc_build(const float *keys, int64_t U, int64_t n, int64_t cap, int d, const float *W, int K, int L,
-               float *kmean, uint16_t *codes, float *margin /* nullable [U][n][L] */)
+               float *kmean, uint16_t *codes, float *margin /* nullable [U][n][K*L] */)
 {
     for (int64_t u = 0; u < U; ++u) {
         const float *ku = keys + u * cap * d;
         orc_key_mean(ku, n, d, d, kmean + u * d);
-        orc_encode(ku, n, d, d, kmean + u * d, W, K, L, codes + u * (int64_t)L * cap, 1, cap,
-                   margin ? margin + u * n * L : NULL);
+        orc_encode(ku, n, d, d, kmean + u * d, 0, W, K, L, codes + u * (int64_t)L * cap, 1, cap,
+                   margin ? margin + u * n * (int64_t)K * L : NULL);
     }
 }
 
@@ -334,7 +323,7 @@ void orc_decode_t(const float *q, const float *keys, const float *vals, const ui
         if (qcodes_in)
             memcpy(qc, qcodes_in + bh * L, sizeof(uint16_t) * (size_t)L);
         else
-            orc_encode(qh, 1, d, d, NULL, W, K, L, qc, 0, 1, NULL);
+            orc_encode(qh, 1, d, d, NULL, 0, W, K, L, qc, 0, 1, NULL);
         if (qcodes_out)
             memcpy(qcodes_out + bh * L, qc, sizeof(uint16_t) * (size_t)L);
         int32_t *list = (int32_t *)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));

@@ -50,6 +50,19 @@ def oracle_decode(w: synth.Workload, lay, km, codes, qc, n=None, nsh=0, nst=0, T
 
 
 def code_mismatches_outside_band(gpu_codes: np.ndarray, ref_codes: np.ndarray, margin: np.ndarray):
-    """gpu/ref [rows][L] codes and margin [rows][L]; returns (#differing, #differing outside the band)."""
-    diff = gpu_codes != ref_codes
-    return int(diff.sum()), int((diff & (margin >= BAND)).sum())
+    """Bit-by-bit comparison of codes against the oracle's.
+
+    gpu/ref codes are ``[rows][L]`` uint16, margin ``[rows][K*L]`` (the
+    oracle's |z|/(|x||w|) per projection column j = l*K + b).  A bit may
+    differ only where its own projection is inside the rounding band.
+    Returns (#differing bits, #differing bits outside the band)."""
+    rows, L = ref_codes.shape
+    assert gpu_codes.shape == ref_codes.shape and margin.shape[0] == rows and margin.shape[1] % L == 0
+    K = margin.shape[1] // L
+    diff = (np.asarray(gpu_codes, np.uint16) ^ np.asarray(ref_codes, np.uint16)).astype(np.uint32)
+    # bit b of table l -> column l*K + b
+    bits = (diff[:, :, None] >> np.arange(K, dtype=np.uint32)[None, None, :]) & 1
+    bits = bits.reshape(rows, L * K).astype(bool)
+    # codes carry no bits above K
+    high = int(np.count_nonzero(diff >> np.uint32(K))) if K < 16 else 0
+    return int(bits.sum()) + high, int((bits & (margin >= BAND)).sum()) + high

@@ -21,6 +21,8 @@ reads comes from memory the HIP path writes.  Checked per layer:
 Which units are checked at which step: every unit at the first and last
 step; at the steps in between, the code subset.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -64,8 +66,8 @@ def code_subset(w, layers):
 class LayerRun:
     """One layer on the device, decoded step by step, checked against the oracle."""
 
-    def __init__(self, w, layer_idx, code_units, T=2, planes=False):
-        self.w, self.li, self.T = w, layer_idx, T
+    def __init__(self, w, layer_idx, code_units, T=2, planes=False, nsh=0, nst=0):
+        self.w, self.li, self.T, self.nsh, self.nst = w, layer_idx, T, nsh, nst
         self.use_planes, self.planes, self.n_planes = planes, None, 0
         self.code_units = sorted(code_units)
         lay = synth.layer_inputs(w, SEED, layer_idx, device="cuda")
@@ -82,8 +84,8 @@ class LayerRun:
         self.oracle_codes = {}  # unit -> oracle codes [L][cap] of the build (code subset)
         self.km_o = np.zeros((self.U, w.d), np.float32)
         self.ws = mp.decode_workspace(w.batch, w.hq, w.hkv, self.cap, w.L, "cuda")
-        _say("%s layer %d: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d; code subset %s" %
-             (w.name, layer_idx, w.batch, w.hq, w.hkv, w.n, w.K, w.L, self.code_units))
+        _say("%s layer %d: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d forced %d+%d; code subset %s" %
+             (w.name, layer_idx, w.batch, w.hq, w.hkv, w.n, w.K, w.L, nsh, nst, self.code_units))
 
     # ------------------------------------------------------------ host inputs
     def host_kv(self, u):
@@ -167,21 +169,21 @@ class LayerRun:
         lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
         cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
         mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, self.ws,
-                          out=out, lse=lse, count=cnt, T=self.T, planes=self.planes, n_planes=self.n_planes)
+                          out=out, lse=lse, count=cnt, T=self.T, planes=self.planes, n_planes=self.n_planes,
+                          n_static_head=self.nsh, n_static_tail=self.nst)
         torch.cuda.synchronize()
         assert torch.equal(self.Kc[:, n], kn) and torch.equal(self.Vc[:, n], vn)
         # appended codes (frozen means) of every unit
         knh, vnh = host_f32(kn), host_f32(vn)
         got = _u16(self.c16[:, :, n])
-        app = np.zeros((self.U, w.L), np.uint16)
+        app, amg = oracle.encode(knh, self.Wh, w.K, w.L, mu=self.km_o, with_margin=True)  # one mean per unit
         app_same = np.zeros(self.U, bool)
         for u in range(self.U):
-            ref, mg = oracle.encode(knh[u][None], self.Wh, w.K, w.L, mu=self.km_o[u], with_margin=True)
-            nd, nbad = code_mismatches_outside_band(got[u][None], ref, mg)
+            nd, nbad = code_mismatches_outside_band(got[u][None], app[u][None], amg[u][None])
             assert nbad == 0, (s, u)
-            app[u], app_same[u] = ref[0], nd == 0
+            app_same[u] = nd == 0
             if nd:  # keep the stores identical for the later steps
-                self.c16[u, :, n] = _i16(ref[0])
+                self.c16[u, :, n] = _i16(app[u])
         self.kn_h.append(knh)
         self.vn_h.append(vnh)
         self.app.append(app)
@@ -200,7 +202,7 @@ class LayerRun:
         out2 = torch.empty_like(out)
         cnt2 = torch.empty_like(cnt)
         idx = torch.full((w.batch, w.hq, self.cap), -1, dtype=torch.int32, device="cuda")
-        mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K,
+        mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K, self.nsh, self.nst,
                           qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws, T=self.T,
                           planes=self.planes, n_planes=self.n_planes)
         torch.cuda.synchronize()
@@ -215,7 +217,7 @@ class LayerRun:
                                 np.stack([k for k, _ in kv])[:, None], np.stack([v for _, v in kv])[:, None],
                                 np.stack([self.host_codes(u) for u in us])[:, None], self.km_o[us][:, None],
                                 self.Wh, w.K, w.L, self.n, qcodes=np.stack([qref[b, h * G:(h + 1) * G] for b, h in bh]),
-                                want_idx=True, T=self.T)
+                                n_static_head=self.nsh, n_static_tail=self.nst, want_idx=True, T=self.T)
             for j, (u, (b, h)) in enumerate(zip(us, bh)):
                 own = app_same[u] and not nd_q[b, h * G:(h + 1) * G].any()
                 direct += int(own)
@@ -236,18 +238,23 @@ class LayerRun:
                     if own:
                         assert np.max(np.abs(o1[b, hh] - ref["out"][j, g])) <= OUT_TOL, (s, u, g)
                         assert abs(float(l1[b, hh]) - float(ref["lse"][j, g])) <= LSE_TOL, (s, u, g)
-        _say("layer %d step %d (n=%d, T=%d, index below %d): %d units checked (%d on the step's own outputs); sets exact; worst "
-             "|out - oracle| %.3g; mean |S| %.0f" % (self.li, s, self.n, self.T, self.n_planes, len(check_units),
-                                                     direct, worst,
-                                                     float(np.mean(sizes))))
+        _say("layer %d step %d (n=%d, K=%d, T=%d, forced %d+%d, index below %d): %d units checked (%d on the step's "
+             "own outputs); sets exact; worst |out - oracle| %.3g; mean |S| %.0f" %
+             (self.li, s, self.n, w.K, self.T, self.nsh, self.nst, self.n_planes, len(check_units), direct, worst,
+              float(np.mean(sizes))))
 
 
-def _run_layers(w, layers, steps=1, check_every=None, T=2, planes=True):
+def _run_layers(w, layers, steps=1, check_every=None, T=2, planes=True, layer_cfg=None):
+    """Each layer: build, check and inject; then ``steps`` appending decode
+    steps.  ``layer_cfg(layer) -> (workload, forced head, forced tail)``
+    gives a layer its own table shape and forced ranges (the pages' policy)."""
     subset = code_subset(w, layers)
     for li in layers:
-        run = LayerRun(w, li, [u for l, u in subset if l == li], T=T, planes=planes)
+        wl, nsh, nst = layer_cfg(li) if layer_cfg else (w, 0, 0)
+        use_planes = planes and wl.K > 0
+        run = LayerRun(wl, li, [u for l, u in subset if l == li], T=T, planes=use_planes, nsh=nsh, nst=nst)
         run.check_build_and_inject()
-        if planes:
+        if use_planes:
             run.build_planes()
         allu = list(range(run.U))
         sub = run.code_units
@@ -285,7 +292,26 @@ def test_codellama13b_b16_layer(layer_idx):
     _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx], planes=layer_idx == 0)
 
 
-def test_codellama34b_b4_64_steps():
-    """CodeLlama-34B shape, batch 4, GQA 8 (K=10, L=240): build, then 64 appending steps; every unit
-    at steps 1 and 64, the code subset at every other step."""
-    _run_layers(synth.WORKLOADS["codellama34b_b4"], [0], steps=64, check_every=1)
+@pytest.mark.parametrize("part", range(6))
+def test_codellama34b_b4_64_steps(part):
+    """CodeLlama-34B shape, batch 4, GQA 8 (K=10, L=240), all 48 layers in six
+    parts: build, then 64 appending steps; every unit at steps 1 and 64, the
+    seeded 5% code subset at every step in between (every appended key and
+    every query's codes at every step)."""
+    w = synth.WORKLOADS["codellama34b_b4"]
+    _run_layers(w, list(range(8 * part, 8 * part + 8)), steps=64, check_every=1)
+
+
+@pytest.mark.parametrize("part", range(2))
+def test_llama8b_96k_pages_policy(part):
+    """The pages' decoding policy at 96K, one appending step over all 32
+    layers (two parts): layers 0 and 16 dense (K = 0: every key sampled with
+    P = 1), every other layer sampled with 4 sink and 64 local keys forced in
+    with P = 1; every unit of every layer against the oracle."""
+    w = synth.WORKLOADS["llama8b_96k"]
+    dense = dataclasses.replace(w, K=0, L=2)
+
+    def cfg(li):
+        return (dense, 0, 0) if li in (0, 16) else (w, 4, 64)
+
+    _run_layers(w, list(range(16 * part, 16 * part + 16)), layer_cfg=cfg)

@@ -93,17 +93,67 @@ def test_parallel_vectors_collide_in_every_table():
     assert np.array_equal(a, b)
 
 
-def test_margin_is_relative_projection_size():
-    K, L, d = 2, 3, 8
+def test_margin_of_identity_projections_is_coordinate_share():
+    """With w_j = e_j the projection deciding bit j is x_j itself, so the
+    per-column margin |z_j| / (|x| |w_j|) is |x_j| / |x| (a closed form, one
+    value per bit, not per table)."""
+    K, L = 4, 3
+    d = K * L
+    W = np.eye(d, dtype=np.float32)
     rng = np.random.default_rng(6)
+    rows = rng.standard_normal((25, d)).astype(np.float32)
+    _, mg = oracle.encode(rows, W, K, L, with_margin=True)
+    assert mg.shape == (25, K * L)
+    x = oracle.bf16(rows).astype(np.float64)
+    share = np.abs(x) / np.linalg.norm(x, axis=1, keepdims=True)
+    assert np.allclose(mg, share, rtol=1e-6, atol=0)
+
+
+def test_zero_projection_column_gives_bit_zero_with_infinite_margin():
+    """A zero projection column projects every row to exactly 0: its bit is
+    (0 > 0) = 0 for every row, no rounding order can change it (margin +inf),
+    and the other bits of the table are unaffected."""
+    K, L, d = 5, 4, 32
+    rng = np.random.default_rng(7)
     W = rng.standard_normal((d, K * L)).astype(np.float32)
-    row = rng.standard_normal(d).astype(np.float32)
-    _, mg = oracle.encode(row, W, K, L, with_margin=True)
-    x = oracle.bf16(row).astype(np.float64)
-    Wb = oracle.bf16(W).astype(np.float64)
-    z = x @ Wb
-    rel = np.abs(z) / (np.linalg.norm(x) * np.linalg.norm(Wb, axis=0))
-    assert np.allclose(mg[0], rel.reshape(L, K).min(1), rtol=1e-6)
+    rows = rng.standard_normal((50, d)).astype(np.float32)
+    base = oracle.encode(rows, W, K, L)
+    j = 2 * K + 3  # table 2, bit 3
+    W0 = W.copy()
+    W0[:, j] = 0.0
+    codes, mg = oracle.encode(rows, W0, K, L, with_margin=True)
+    assert np.all((codes[:, 2] >> 3) & 1 == 0)
+    assert np.all(np.isinf(mg[:, j]))
+    assert np.array_equal(codes[:, 2] | (base[:, 2] & (1 << 3)), base[:, 2])
+    assert np.array_equal(np.delete(codes, 2, axis=1), np.delete(base, 2, axis=1))
+
+
+def test_per_row_means_equal_one_row_at_a_time():
+    """Encoding rows with one mean each (appended keys of several units)
+    gives what encoding each row alone with its own mean gives."""
+    K, L, d = 6, 7, 16
+    rng = np.random.default_rng(8)
+    W = rng.standard_normal((d, K * L)).astype(np.float32)
+    rows = rng.standard_normal((9, d)).astype(np.float32)
+    mus = rng.standard_normal((9, d)).astype(np.float32)
+    codes, mg = oracle.encode(rows, W, K, L, mu=mus, with_margin=True)
+    for r in range(9):
+        c1, m1 = oracle.encode(rows[r], W, K, L, mu=mus[r], with_margin=True)
+        assert np.array_equal(codes[r], c1[0]) and np.array_equal(mg[r], m1[0])
+
+
+def test_per_bit_band_check_flags_a_wrong_bit_beside_a_tied_one():
+    """The parity rule is per bit: a differing bit passes only when its own
+    projection is inside the band.  A planted wrong bit (outside the band) in
+    a table whose other bit is tied must be reported."""
+    from tests.common import code_mismatches_outside_band
+    K, L = 3, 2
+    ref = np.array([[0b101, 0b010]], np.uint16)
+    margin = np.array([[0.5, 0.0, 0.5, 0.5, 0.5, 0.5]], np.float32)  # bit 1 of table 0 tied
+    assert code_mismatches_outside_band(ref ^ np.array([[0b010, 0]], np.uint16), ref, margin) == (1, 0)
+    assert code_mismatches_outside_band(ref ^ np.array([[0b011, 0]], np.uint16), ref, margin) == (2, 1)
+    assert code_mismatches_outside_band(ref ^ np.array([[0, 0b100]], np.uint16), ref, margin) == (1, 1)
+    assert code_mismatches_outside_band(ref ^ np.array([[0b1000, 0]], np.uint16), ref, margin)[1] == 1  # above K
 
 
 @pytest.mark.parametrize("theta_frac", [0.0, 1 / 6, 1 / 3, 1 / 2, 2 / 3, 5 / 6])
