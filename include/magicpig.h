@@ -23,7 +23,9 @@
  *  - Every pointer is a DEVICE pointer on the current HIP device.  The caller
  *    allocates and owns every buffer; the library never allocates, frees or
  *    keeps pointers after a call returns, and keeps no global state, so calls
- *    on different streams are independent when their workspaces differ.
+ *    on different streams are independent when their workspaces differ.  The
+ *    one exception is mp_decode_step_static (at the end of this file), whose
+ *    workspace is a fixed device array of the library, shared by its calls.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
  *    work is enqueued on it; nothing synchronises the host.  Results are valid
  *    once the stream has reached the point after the call.
@@ -71,6 +73,7 @@ extern "C" {
 #define MP_ERR_CAPACITY (-3)    /* n >= cap on append, or n > cap           */
 #define MP_ERR_WORKSPACE (-4)   /* workspace missing or smaller than needed */
 #define MP_ERR_HIP (-5)         /* a HIP launch failed                      */
+#define MP_ERR_SCRATCH (-6)     /* shape needs more than the static scratch  */
 
 /* Element types of keys, values and queries. */
 #define MP_BF16 0
@@ -240,6 +243,28 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
                    int B, int Hq, int Hkv, int64_t n, int64_t cap,
                    int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream);
+
+/*
+ * mp_decode_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, results and errors are those
+ * of mp_decode_step without ws / ws_bytes; the workspace is instead a fixed
+ * device array of MP_STATIC_SCRATCH_BYTES bytes inside the library, one per
+ * GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); its first call on a
+ * device looks up that device's array.  Shapes whose workspace
+ * (mp_decode_ws_bytes) exceeds MP_STATIC_SCRATCH_BYTES return
+ * MP_ERR_SCRATCH before anything is enqueued.  Every call on one GPU uses
+ * that GPU's array, which keeps the last call's contents (nothing in it
+ * needs to start at zero): calls that overlap on one GPU (other streams or
+ * threads) race on it, so the caller serialises them, e.g. on one stream.
+ */
+#define MP_STATIC_SCRATCH_BYTES (32u << 20)
+int mp_decode_step_static(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean,
+                          const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T,
+                          int64_t n_static_head, int64_t n_static_tail, float *out, float *lse, int32_t *idx,
+                          int32_t *count, void *sample_events, void *stream);
 
 #ifdef __cplusplus
 }

@@ -48,7 +48,12 @@ _SIGS = {
                         _c_int),
     "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
                         _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
+    "mp_decode_step_static": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int,
+                               _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
+                               _vp], _c_int),
 }
+
+MP_STATIC_SCRATCH_BYTES = 32 << 20  # size of the library's static scratch (include/magicpig.h)
 
 _lib = None
 
@@ -304,17 +309,7 @@ def mp_decode_merge(B: int, Hq: int, Hkv: int, n: int, cap: int, L: int, out: to
     _check("mp_decode_merge", st)
 
 
-def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor], q: torch.Tensor, Kc: torch.Tensor,
-                   Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor, Wp: torch.Tensor, Hkv: int, n: int,
-                   K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
-                   n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2,
-                   planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> torch.Tensor:
-    """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
-
-    ``sample_events``: optional pair of torch.cuda.Event objects (created with
-    timing and recorded once, so that their handles exist); they are attached
-    to the sampling kernel's dispatch and record its start and end."""
+def _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes):
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     if k_new is not None:
         _need(k_new, Kc.dtype, (U, d), "k_new")
@@ -329,6 +324,42 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
     if idx is not None:
         _need(idx, torch.int32, (B, Hq, cap), "idx")
     _planes_ok(planes, codes, K)
+    return B, Hq, d, cap, L, out
+
+
+def mp_decode_step_static(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor], q: torch.Tensor,
+                          Kc: torch.Tensor, Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor,
+                          Wp: torch.Tensor, Hkv: int, n: int, K: int, out: torch.Tensor,
+                          lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                          count: Optional[torch.Tensor] = None, n_static_head: int = 0, n_static_tail: int = 0,
+                          sample_events=None, stream=None, T: int = 2, planes: Optional[torch.Tensor] = None,
+                          n_planes: int = 0) -> torch.Tensor:
+    """mp_decode_step with the library's static scratch as its workspace: the
+    native call allocates nothing (``out`` must be given, so this wrapper
+    allocates nothing either).  Calls that overlap on one GPU race."""
+    if out is None:
+        raise ValueError("mp_decode_step_static: out must be given")
+    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes)
+    st = lib().mp_decode_step_static(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes),
+                                     _p(planes), n_planes, _p(kmean), _p(Wp), B, Hq, Hkv, n, cap, d, K, L, T,
+                                     n_static_head, n_static_tail, _p(out), _p(lse), _p(idx), _p(count),
+                                     _event_pair(sample_events), _stream(stream))
+    _check("mp_decode_step_static", st)
+    return out
+
+
+def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor], q: torch.Tensor, Kc: torch.Tensor,
+                   Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor, Wp: torch.Tensor, Hkv: int, n: int,
+                   K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
+                   n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2,
+                   planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> torch.Tensor:
+    """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
+
+    ``sample_events``: optional pair of torch.cuda.Event objects (created with
+    timing and recorded once, so that their handles exist); they are attached
+    to the sampling kernel's dispatch and record its start and end."""
+    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes)
     st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes),
                               n_planes, _p(kmean), _p(Wp),
                               B, Hq, Hkv, n, cap, d, K, L, T, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),

@@ -1,6 +1,9 @@
 // C ABI of libmagicpig.so: argument validation, workspace carving and kernel
 // launches.  Every check runs before the first enqueue, so a call that
 // returns an error has written nothing.
+#include <atomic>
+#include <mutex>
+
 #include "magicpig.h"
 #include "mp_internal.h"
 
@@ -49,6 +52,8 @@ const char *mp_strerror(int status) {
     case MP_ERR_CAPACITY: return "capacity exceeded (n > cap, n < 1 for a build, n < 0 for a decode, or n >= cap on an append)";
     case MP_ERR_WORKSPACE: return "workspace missing or too small";
     case MP_ERR_HIP: return "HIP kernel launch failed";
+    case MP_ERR_SCRATCH: return "workspace of this shape exceeds the static scratch of mp_decode_step_static "
+                                "(MP_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -150,7 +155,7 @@ size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L) {
 
 static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                         const float *kmean, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L,
-                        int T, int64_t nsh, int64_t nst, void *ws, size_t ws_bytes) {
+                        int T, int64_t nsh, int64_t nst, void *ws, size_t ws_bytes, bool caller_ws = true) {
   int st = check_shape(d, K, L);
   if (st) return st;
   if (T < 1 || T > L) return MP_ERR_UNSUPPORTED;
@@ -162,7 +167,7 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
   // one sampling block per 512-key tile per unit, in a 1-D grid of < 2^31 threads
   if ((int64_t)B * Hkv * ((cap + SCAN_TILE - 1) / SCAN_TILE) > ((int64_t)1 << 23)) return MP_ERR_UNSUPPORTED;
   if (cap >= ((int64_t)1 << 26)) return MP_ERR_UNSUPPORTED;  // a scan batch's row offsets fit 32 bits
-  if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
+  if (caller_ws && (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L))) return MP_ERR_WORKSPACE;
   return MP_OK;
 }
 
@@ -227,21 +232,63 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
 }
 
-int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
-                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
-                   int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
-                   int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Static scratch of mp_decode_step_static: a fixed device array in the code
+// object, one copy per GPU, used instead of a caller workspace.  Host code
+// never passes `scratch` itself to a kernel or a copy (on the host the name
+// only stands in for the symbol): it takes the array's device address once
+// per device from hipGetSymbolAddress and uses that.
+static __device__ __align__(256) unsigned char scratch[MP_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void *> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_mu;
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with the device current).
+int static_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return MP_ERR_HIP;
+  void *p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MP_ERR_HIP;
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MP_OK;
+}
+
+
+// mp_decode_step: the public step entry points differ only in where the
+// workspace comes from (the caller's ws, or with static_ws the library's
+// static scratch, looked up once every argument has been validated).
+int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B,
+                int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head,
+                int64_t n_static_tail, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                size_t ws_bytes, void *sample_events, void *stream, bool static_ws) {
   const bool app = k_new != nullptr;
   if (app && !v_new) return MP_ERR_ARG;
   if (app && (n < 0 || n >= cap)) return MP_ERR_CAPACITY;
   const int64_t nd = app ? n + 1 : n;  // keys the decode sees
   int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, nd, cap, d, K, L, T, n_static_head,
-                        n_static_tail, ws, ws_bytes);
+                        n_static_tail, ws, ws_bytes, !static_ws);
   if (st) return st;
   if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
   if (!all_a16(out, Wp, k_new, v_new)) return MP_ERR_ARG;
   if ((st = check_planes(planes, n_planes, n))) return st;  // the keys before the append
+  if (static_ws) {
+    if (mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L) > (size_t)MP_STATIC_SCRATCH_BYTES) return MP_ERR_SCRATCH;
+    if ((st = static_scratch(&ws))) return st;
+  }
   hipStream_t s = as_stream(stream);
   const int64_t U = (int64_t)B * Hkv;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, nd, cap);
@@ -269,6 +316,30 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
     return MP_ERR_HIP;
   }
   return hip_status(launch_merge(B, Hq, Hkv, nd, L, geo, w, out, lse, idx, cap, count, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
+                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
+                   int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
+  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, kmean, Wp, B, Hq, Hkv, n, cap, d,
+                     K, L, T, n_static_head, n_static_tail, out, lse, idx, count, ws, ws_bytes, sample_events,
+                     stream, false);
+}
+
+int mp_decode_step_static(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
+                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean,
+                          const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T,
+                          int64_t n_static_head, int64_t n_static_tail, float *out, float *lse, int32_t *idx,
+                          int32_t *count, void *sample_events, void *stream) {
+  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, kmean, Wp, B, Hq, Hkv, n, cap, d,
+                     K, L, T, n_static_head, n_static_tail, out, lse, idx, count, nullptr, 0, sample_events, stream,
+                     true);
 }
 
 }  // extern "C"

@@ -123,10 +123,8 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(d=96) == UNSUP
     assert _decode(B=70000, Hq=8, Hkv=8) == UNSUP
     assert _decode(cap=1 << 26) == UNSUP  # a scan batch's row offsets must fit 32 bits
-    assert _decode(cap=(1 << 26) - 8) != UNSUP
     assert _decode(T=0) == UNSUP  # collision threshold outside [1, L]
     assert _decode(T=76) == UNSUP
-    assert _decode(T=1) != UNSUP and _decode(T=75) != UNSUP
     for arg in ("q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _decode(**{arg: FAKE + 2}) == ARG, arg
     # bit-plane index: whole 512-key tiles at or below n, 16-byte aligned
@@ -134,7 +132,6 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(planes=FAKE, np=1024, n=1000, cap=1024) == ARG
     assert _decode(planes=FAKE + 4, np=512, n=1000, cap=1024) == ARG
     assert _decode(planes=FAKE, np=-512, n=1000, cap=1024) == ARG
-    assert _decode(planes=None, np=12345) != ARG  # ignored without planes
 
 
 def test_build_planes_rejects_invalid_arguments():
@@ -205,6 +202,47 @@ def test_step_rejects_invalid_arguments():
     assert _step(ws=None) == WS
     assert _step(T=0) == UNSUP
     assert _step(planes=FAKE, np=512, n=511, cap=1024) == ARG  # the appended key is not in the index
-    assert _step(planes=FAKE, np=512, n=512, cap=1024) != ARG
     for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _step(**{arg: FAKE + 4}) == ARG, arg
+
+
+def _static(**kw):
+    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1,
+             Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None)
+    a.update(kw)
+    return mp.lib().mp_decode_step_static(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"],
+                                          a["planes"], a["np"], a["km"], a["Wp"], a["B"], a["Hq"], a["Hkv"], a["n"],
+                                          a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"], a["nst"], a["out"],
+                                          a["lse"], a["idx"], a["cnt"], None, None)
+
+
+def test_static_step_rejects_invalid_arguments_and_oversized_shapes():
+    """The allocation-free step validates like mp_decode_step (no workspace
+    argument) and rejects a shape whose workspace exceeds its static scratch
+    with MP_ERR_SCRATCH, all before any HIP call."""
+    SCRATCH = -6
+    assert len(mp.strerror(SCRATCH)) > 5
+    assert _static(v=None) == ARG
+    assert _static(n=128) == CAP
+    assert _static(Wp=None) == ARG
+    assert _static(out=None) == ARG
+    assert _static(Hkv=3) == ARG
+    assert _static(T=0) == UNSUP
+    for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out"):
+        assert _static(**{arg: FAKE + 4}) == ARG, arg
+    # the CodeLlama-13B-shaped batch of 16 MHA sequences needs far more than the scratch
+    big = dict(B=16, Hq=40, Hkv=40, n=16384, cap=16448, K=9, L=120)
+    assert mp.mp_decode_ws_bytes(16, 40, 40, 16448, 120) > mp.MP_STATIC_SCRATCH_BYTES
+    assert _static(**big) == SCRATCH
+    assert mp.mp_decode_ws_bytes(1, 32, 8, 98368, 150) <= mp.MP_STATIC_SCRATCH_BYTES  # the 96K layer fits
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(),
+                    reason="these arguments pass validation and would launch kernels on fake pointers")
+def test_valid_arguments_pass_validation():
+    """Arguments at the documented limits pass validation (the calls then
+    fail to launch: there is no GPU here)."""
+    assert _decode(cap=(1 << 26) - 8, wsb=1 << 40) not in (ARG, UNSUP, CAP, WS)
+    assert _decode(T=1) not in (ARG, UNSUP) and _decode(T=75) not in (ARG, UNSUP)
+    assert _decode(planes=None, np=12345) not in (ARG, UNSUP)  # ignored without planes
+    assert _step(planes=FAKE, np=512, n=512, cap=1024) not in (ARG, UNSUP, CAP, WS)
