@@ -58,9 +58,10 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--threshold", type=int, default=2,
                     help="collision threshold T: a key is sampled in at least T of the L tables (the pages' 2)")
-    ap.add_argument("--planes", choices=("on", "off"), default="on",
-                    help="on: build the bit-plane index of the code store at set-up (whole 512-key tiles of the "
-                         "prefill keys) and let the threshold-2 scan read it; off: scan the 16-bit codes only")
+    ap.add_argument("--index", choices=("planes", "buckets", "codes"), default="planes",
+                    help="planes: build the bit-plane index of the code store at set-up (whole 512-key tiles of the "
+                         "prefill keys) and let the threshold-2 scan read it; buckets: build the bucketed hash "
+                         "tables and look the query's buckets up instead of scanning; codes: scan the 16-bit codes")
     ap.add_argument("--policy", choices=("sampled", "pages"), default="sampled",
                     help="sampled: every layer sampled; pages: the pages' decoding policy (layers 0 and 16 "
                          "dense, i.e. K = 0, and 4 sink + 64 local keys forced into every sampled layer's set)")
@@ -73,7 +74,7 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, planes: bool) -> dict:
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, index: str) -> dict:
     """HBM bytes per sampling-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
     dispatch), each scaled by what the same counter reads for the calibration
     copy of calib_mib MiB (the largest __amd_rocclr_copyBuffer dispatch)."""
@@ -101,7 +102,7 @@ def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, worklo
     write_scale = calib_bytes / (w_c * 1024.0)
     fetch_b = f_s * 1024.0 * fetch_scale
     write_b = w_s * 1024.0 * write_scale
-    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "planes": planes,
+    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "index": index,
             "bytes_per_launch": fetch_b + write_b,
             "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
             "fetch_size_kib_per_launch": f_s, "write_size_kib_per_launch": w_s, "dispatches": [nf, nw],
@@ -113,7 +114,7 @@ def main() -> int:
     args = parse()
     if args.traffic:
         tr = traffic_from_counters(args.traffic[0], args.traffic[1], args.calib_copy_mib, args.workload,
-                                   args.planes == "on" and args.threshold == 2)
+                                   args.index if args.threshold == 2 else "codes")
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(tr, f, indent=1)
         print(json.dumps(tr))
@@ -147,9 +148,11 @@ def main() -> int:
     lcfg = [((0, 2, 0, 0) if pages and l in (0, 16) else (K, L, 4 if pages else 0, 64 if pages else 0))
             for l in range(nlayers)]
     sampled_layers = [l for l in range(nlayers) if lcfg[l][0] > 0]
-    use_planes = args.planes == "on"
+    use_planes = args.index == "planes"
+    use_buckets = args.index == "buckets"
     n_planes = (n0 // 512) * 512  # appended keys stay in the 16-bit codes (tiles past the index)
     scan_planes = use_planes and args.threshold == 2
+    scan_buckets = use_buckets and args.threshold == 2
 
     # ------------------------------------------------------------------ inputs + code-store build
     layers = []
@@ -179,22 +182,25 @@ def main() -> int:
                 kn[s, u], vn[s, u] = synth.step_kv(args.seed, l, b, h, d, dt, step=s + 1)
                 qs[s, b, h * G:(h + 1) * G] = synth.unit_queries(args.seed, l, b, h, G, d, dt, step=s + 1)
         kn, vn, qs = kn.to(dev), vn.to(dev), qs.to(dev)
-        planes, pev = None, None
-        if use_planes and Kl > 0:  # the index of the prefill keys' whole tiles
-            planes = torch.empty(U, (cap + 511) // 512, Kl, Ll, 16, dtype=torch.int32, device=dev)
+        planes, buckets, pev = None, None, None
+        if (use_planes or use_buckets) and Kl > 0:  # the index of the prefill keys' whole tiles
             pev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
             pev[0].record()
-            mp.mp_build_planes(codes, Kl, n_planes, planes=planes)
+            if use_planes:
+                planes = torch.empty(U, (cap + 511) // 512, Kl, Ll, 16, dtype=torch.int32, device=dev)
+                mp.mp_build_planes(codes, Kl, n_planes, planes=planes)
+            else:
+                buckets = mp.mp_build_buckets(codes, Kl, n_planes)
             pev[1].record()
         layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1),
-                           planes=planes, pev=pev))
+                           planes=planes, buckets=buckets, pev=pev))
     torch.cuda.synchronize()
     build_ms = [layers[l]["ev"][0].elapsed_time(layers[l]["ev"][1]) for l in sampled_layers]
     planes_ms = [layers[l]["pev"][0].elapsed_time(layers[l]["pev"][1]) for l in sampled_layers
                  if layers[l]["pev"] is not None]
     log("built %d layers; build %.3f ms/layer (median)%s" %
         (nlayers, float(np.median(build_ms)),
-         "; bit-plane index %.3f ms/layer" % float(np.median(planes_ms)) if planes_ms else ""))
+         "; %s index %.3f ms/layer" % (args.index, float(np.median(planes_ms))) if planes_ms else ""))
 
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
     outs = [torch.empty(w.batch, w.hq, d, dtype=torch.float32, device=dev) for _ in range(nlayers)]
@@ -227,7 +233,8 @@ def main() -> int:
             mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
                               lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
                               n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev, T=args.threshold,
-                              planes=lay["planes"], n_planes=n_planes if lay["planes"] is not None else 0)
+                              planes=lay["planes"], n_planes=n_planes if lay["planes"] is not None else 0,
+                              buckets=lay["buckets"], n_buckets=n_planes if lay["buckets"] is not None else 0)
         if timed:
             n_timed.append(n_cur + 1)
         n_cur += 1
@@ -246,6 +253,7 @@ def main() -> int:
     # ------------------------------------------------------------------ sampled-set sizes (after timing)
     union_sum = 0
     head_sum = 0
+    bucket_entries = 0  # sum over heads and tables of the query's bucket sizes (keys below the index)
     idx = torch.empty(w.batch, w.hq, cap, dtype=torch.int32, device=dev)
     cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device=dev)
     s_last = total_steps - 1
@@ -253,12 +261,16 @@ def main() -> int:
         lay = layers[l]
         mp.mp_decode_attn(lay["qs"][s_last], lay["Kc"], lay["Vc"], lay["codes"], lay["kmean"], lay["Wp"], w.hkv,
                           n_cur, K, lcfg[l][2], lcfg[l][3], idx=idx, count=cnt, ws=ws, T=args.threshold)
+        qc_last = mp.mp_encode_queries(lay["qs"][s_last], lay["Wp"], K, L).view(torch.int16)
         for b in range(w.batch):
             for h in range(w.hkv):
                 mask = torch.zeros(n_cur, dtype=torch.bool, device=dev)
                 for g in range(G):
                     c = int(cnt[b, h * G + g])
                     mask[idx[b, h * G + g, :c].long()] = True
+                    if scan_buckets:
+                        cu = lay["codes"].view(torch.int16)[b * w.hkv + h, :, :n_planes]
+                        bucket_entries += int((cu == qc_last[b, h * G + g][:, None]).sum())
                 union_sum += int(mask.sum())
         head_sum += int(cnt.sum())
     union_per_unit = union_sum / (len(sampled_layers) * U)
@@ -268,7 +280,15 @@ def main() -> int:
     # algorithmic bytes of one sample launch (one layer): codes of every key once, each distinct sampled
     # K and V row once, the queries, their codes and the key means
     # (with the bit-plane index, K bits per key and table for the tiles it covers)
-    code_bytes = (K * L * n_planes / 8 + 2 * L * (n_dec - n_planes)) if scan_planes else 2 * L * n_dec
+    # (with the buckets: the query's bucket entries, 2 bytes each, and two 2-byte offsets per head, table and
+    # 4096-key chunk, for the keys below the index; 16-bit codes above)
+    if scan_buckets:
+        nbc = (n_planes + 4095) // 4096
+        code_bytes = (2 * bucket_entries / len(sampled_layers) / U + G * L * nbc * 4 + 2 * L * (n_dec - n_planes))
+    elif scan_planes:
+        code_bytes = K * L * n_planes / 8 + 2 * L * (n_dec - n_planes)
+    else:
+        code_bytes = 2 * L * n_dec
     bytes_launch = U * (code_bytes + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
     achieved = bytes_launch / (kern_ms.mean() * 1e-3) / 1e9
     traffic = None
@@ -276,7 +296,7 @@ def main() -> int:
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages and
-                args.threshold == 2 and bool(tr.get("planes", False)) == scan_planes):
+                args.threshold == 2 and tr.get("index") == args.index):
             traffic = tr.get("bytes_per_launch")
     # a dense layer reads its (two-table) codes and every key's K and V row
     dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
@@ -342,6 +362,7 @@ def main() -> int:
         "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": d, "context": n0, "K": K, "L": L, "threshold": args.threshold,
                    "code_scan": ("bit-plane index below key %d, 16-bit codes above" % n_planes if scan_planes
+                                 else "bucketed tables below key %d, 16-bit codes above" % n_planes if scan_buckets
                                  else "16-bit codes"),
                    "parallelism": "single GPU",
                    "policy": ("every layer sampled" if not pages else
@@ -357,7 +378,7 @@ def main() -> int:
         "encoder": {"build_ms_per_layer": float(np.median(build_ms)), "tflops": enc_tflops,
                     "frac_mfma_bf16": enc_tflops / BF16_MFMA_PEAK_TFLOPS,
                     "note": "build = key mean + projection GEMM + sign pack, per layer",
-                    "planes_ms_per_layer": float(np.median(planes_ms)) if planes_ms else None},
+                    "index_build_ms_per_layer": float(np.median(planes_ms)) if planes_ms else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

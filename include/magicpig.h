@@ -150,6 +150,38 @@ int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, in
                     uint32_t *planes, void *stream);
 
 /*
+ * Bucketed hash tables of the code store: the L hash tables of 2^K buckets
+ * that the method builds from the keys' codes (Section 2.2 "Locality
+ * sensitive hashing"; Section 4.4, the retrieval step that looks the query's
+ * codes up in pre-built tables; built per layer, authors' reply to Q2 on
+ * page 3).  A decode that uses them reads only the query's L buckets per
+ * head instead of every key's codes; the sampled sets are the same, since a
+ * key is in the query's bucket of table l exactly when codes[u][l][i] equals
+ * the query's code of table l.
+ * Layout (one buffer of mp_buckets_bytes(U, cap, K, L) bytes): keys are cut
+ * into chunks of 4096; per (unit, table, chunk) a CSR of the chunk's keys
+ * ordered by code --
+ *   off   [U][L][ceil(cap/4096)][2^K + 1] uint16 at the buffer's start:
+ *         bucket c of chunk r holds entries off[c] .. off[c+1] - 1;
+ *   keys  [U][L][cap] uint16, starting at the next 256-byte boundary:
+ *         entry j of chunk r of table l is keys[u][l][4096 r + j], the key's
+ *         offset from the chunk's first key (the order inside a bucket is
+ *         not fixed).
+ * mp_build_buckets (re)builds the chunks [n0/4096, ceil(n1/4096)) from the
+ * codes of keys below n1 (written by mp_build_codes / mp_append); n0 a
+ * multiple of 4096, n1 a multiple of 512, 0 <= n0 <= n1 <= cap.  Appends do
+ * not update it: a decode uses the buckets for the 512-key tiles below its
+ * n_buckets and the codes (or planes) above, so the caller rebuilds the
+ * newest chunk once a tile has filled.  1 <= K <= 12.
+ * Errors: MP_ERR_ARG (null or misaligned pointers, n0 / n1 out of range),
+ * MP_ERR_UNSUPPORTED (shape), MP_ERR_WORKSPACE (buffer smaller than
+ * mp_buckets_bytes), MP_ERR_HIP.
+ */
+size_t mp_buckets_bytes(int64_t U, int64_t cap, int K, int L);
+int mp_build_buckets(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, int64_t cap, int K, int L,
+                     void *buckets, size_t buckets_bytes, void *stream);
+
+/*
  * Query encoding (Algorithm 1, "Compute hash code for new query"):
  * qcodes[r][l] = code of table l of y_r = bf16(q[r]); queries are NOT
  * centred (centring shifts keys only; softmax is translation invariant).
@@ -185,6 +217,13 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
  *              T = 2 those tiles are scanned from it; the sets and outputs
  *              are the same as from codes.  n_planes is ignored when planes
  *              is NULL.
+ *   buckets    nullable bucketed tables (mp_build_buckets) valid for keys
+ *              below n_buckets (a multiple of 512, 0 <= n_buckets <= n):
+ *              with T = 2 the tiles below n_buckets take their sampled keys
+ *              from the query's buckets (one more kernel, before the
+ *              sampling kernel) and are not scanned; the sets and outputs
+ *              are the same.  Tiles below n_buckets take precedence over
+ *              planes.  Ignored for other thresholds.
  *   Wp         packed projections (read only when qcodes_in is NULL)
  *   qcodes_in  nullable [B][Hq][L]: use these query codes instead of
  *              encoding q
@@ -200,7 +239,8 @@ int mp_encode_queries(const void *q, int q_dtype, int64_t nq, int d, const void 
  */
 size_t mp_decode_ws_bytes(int B, int Hq, int Hkv, int64_t cap, int d, int L);
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                   const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
                    int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream);
@@ -217,7 +257,8 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
  * qcodes is required here ([B][Hq][L]).
  */
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                     const uint32_t *planes, int64_t n_planes, const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                      int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream);
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
@@ -230,7 +271,7 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  * in one launch -- then sample and merge (as mp_decode_attn) over n + 1 keys
  * (n keys without an append).  Arguments as in mp_append and
  * mp_decode_attn; q codes are kept in ws.  The appended key is not added to
- * planes (n_planes <= n, the keys before the append).  sample_events is NULL or points
+ * planes or buckets (n_planes, n_buckets <= n, the keys before the append).  sample_events is NULL or points
  * to two host hipEvent_t handles that are attached to the sampling kernel's
  * dispatch, so they record its own start and end (for callers that time it;
  * with no keys to decode there is no such kernel and both are recorded back to
@@ -239,8 +280,8 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
  * with n >= cap.
  */
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
-                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                    int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream);
 
@@ -261,10 +302,10 @@ int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc
  */
 #define MP_STATIC_SCRATCH_BYTES (32u << 20)
 int mp_decode_step_static(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean,
-                          const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T,
-                          int64_t n_static_head, int64_t n_static_tail, float *out, float *lse, int32_t *idx,
-                          int32_t *count, void *sample_events, void *stream);
+                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const void *buckets,
+                          int64_t n_buckets, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n,
+                          int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                          float *out, float *lse, int32_t *idx, int32_t *count, void *sample_events, void *stream);
 
 #ifdef __cplusplus
 }

@@ -40,17 +40,22 @@ _SIGS = {
     "mp_decode_ws_bytes": ([_c_int, _c_int, _c_int, _c_i64, _c_int, _c_int], _c_sz),
     "mp_planes_bytes": ([_c_i64, _c_i64, _c_int, _c_int], _c_sz),
     "mp_build_planes": ([_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp], _c_int),
-    "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
-                        _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
-    "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int,
-                          _c_int, _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp], _c_int),
+    "mp_buckets_bytes": ([_c_i64, _c_i64, _c_int, _c_int], _c_sz),
+    "mp_build_buckets": ([_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _vp, _c_sz, _vp], _c_int),
+    "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64,
+                        _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                        _c_sz, _vp], _c_int),
+    "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int,
+                          _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp],
+                         _c_int),
     "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
                         _c_int),
-    "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int,
-                        _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp, _vp], _c_int),
-    "mp_decode_step_static": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int,
-                               _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp,
-                               _vp], _c_int),
+    "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int,
+                        _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp,
+                        _vp, _c_sz, _vp, _vp], _c_int),
+    "mp_decode_step_static": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int,
+                               _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp,
+                               _vp, _vp, _vp, _vp, _vp], _c_int),
 }
 
 MP_STATIC_SCRATCH_BYTES = 32 << 20  # size of the library's static scratch (include/magicpig.h)
@@ -215,6 +220,29 @@ def mp_build_planes(codes: torch.Tensor, K: int, n1: int, n0: int = 0, planes: O
     return planes
 
 
+def mp_buckets_bytes(U: int, cap: int, K: int, L: int) -> int:
+    return lib().mp_buckets_bytes(U, cap, K, L)
+
+
+def mp_build_buckets(codes: torch.Tensor, K: int, n1: int, n0: int = 0, buckets: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Bucketed hash tables of ``codes`` ([U][L][cap] uint16) for the chunks
+    of 4096 keys from n0 (a multiple of 4096) up to n1 (a multiple of 512).
+
+    Returns (or fills) ``buckets``: a uint8 buffer of mp_buckets_bytes bytes."""
+    U, L, cap = codes.shape
+    nb = mp_buckets_bytes(U, cap, K, L)
+    if nb == 0:
+        raise MPError("mp_buckets_bytes", -2)
+    if buckets is None:
+        buckets = torch.empty(nb, dtype=torch.uint8, device=codes.device)
+    if buckets.dtype != torch.uint8 or buckets.dim() != 1:
+        raise ValueError("buckets: expected a 1-D uint8 buffer")
+    _check("mp_build_buckets", lib().mp_build_buckets(_p(codes), U, n0, n1, cap, K, L, _p(buckets), buckets.numel(),
+                                                      _stream(stream)))
+    return buckets
+
+
 # ----------------------------------------------------------------------------- decode
 def mp_decode_ws_bytes(B: int, Hq: int, Hkv: int, cap: int, L: int, d: int = D) -> int:
     return lib().mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)
@@ -241,10 +269,14 @@ def _decode_shapes(q, Kc, Vc, codes, kmean, Hkv):
     return B, Hq, d, U, cap, L
 
 
-def _planes_ok(planes, codes, K):
+def _planes_ok(planes, codes, K, buckets=None):
+    U, L, cap = codes.shape
     if planes is not None:
-        U, L, cap = codes.shape
         _need(planes, torch.int32, (U, (cap + 511) // 512, K, L, 16), "planes")
+    if buckets is not None:
+        nb = mp_buckets_bytes(U, cap, K, L)
+        if buckets.dtype != torch.uint8 or buckets.dim() != 1 or buckets.numel() < nb:
+            raise ValueError("buckets: expected a 1-D uint8 buffer of at least %d bytes" % nb)
 
 
 def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: torch.Tensor, kmean: torch.Tensor,
@@ -253,13 +285,16 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
                    qcodes_out: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                    count: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None,
-                   T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0):
+                   T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0,
+                   buckets: Optional[torch.Tensor] = None, n_buckets: int = 0):
     """Sampled decode attention of one layer.  q [B][Hq][d]; caches [B*Hkv][cap][d].
 
     ``T`` is the collision threshold (a key is sampled when it collides with
     the query in at least T of the L tables; the pages use 2).  ``planes``
     (from mp_build_planes, valid below ``n_planes``) lets the T = 2 scan read
-    the bit-plane index for those tiles."""
+    the bit-plane index for those tiles; ``buckets`` (from mp_build_buckets,
+    valid below ``n_buckets``) replaces the T = 2 scan of those tiles by a
+    lookup of the query's buckets."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     dev = q.device
     if out is None:
@@ -276,8 +311,9 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
             _need(t, torch.uint16, (B, Hq, L), name)
     if ws is None:
         ws = decode_workspace(B, Hq, Hkv, cap, L, dev)
-    _planes_ok(planes, codes, K)
-    st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(kmean), _p(Wp),
+    _planes_ok(planes, codes, K, buckets)
+    st = lib().mp_decode_attn(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(buckets),
+                              n_buckets, _p(kmean), _p(Wp),
                               B, Hq, Hkv, n, cap,
                               d, K, L, T, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
                               _p(idx), _p(count), _p(ws), ws.numel(), _stream(stream))
@@ -287,12 +323,14 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
 
 def mp_decode_sample(q, Kc, Vc, codes, kmean, qcodes, Hkv: int, n: int, K: int, ws: torch.Tensor,
                      n_static_head: int = 0, n_static_tail: int = 0, want_idx: bool = False, stream=None,
-                     T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> None:
-    """Scan + weighting + split attention into the workspace (first stage of mp_decode_attn)."""
+                     T: int = 2, planes: Optional[torch.Tensor] = None, n_planes: int = 0,
+                     buckets: Optional[torch.Tensor] = None, n_buckets: int = 0) -> None:
+    """Scan (or bucket lookup) + weighting + split attention into the workspace (first stage of mp_decode_attn)."""
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     _need(qcodes, torch.uint16, (B, Hq, L), "qcodes")
-    _planes_ok(planes, codes, K)
-    st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(kmean),
+    _planes_ok(planes, codes, K, buckets)
+    st = lib().mp_decode_sample(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes, _p(buckets),
+                                n_buckets, _p(kmean),
                                 _p(qcodes), B, Hq, Hkv,
                                 n, cap, d, K, L, T, n_static_head, n_static_tail, int(bool(want_idx)), _p(ws), ws.numel(),
                                 _stream(stream))
@@ -309,7 +347,7 @@ def mp_decode_merge(B: int, Hq: int, Hkv: int, n: int, cap: int, L: int, out: to
     _check("mp_decode_merge", st)
 
 
-def _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes):
+def _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes, buckets):
     B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
     if k_new is not None:
         _need(k_new, Kc.dtype, (U, d), "k_new")
@@ -323,7 +361,7 @@ def _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, cou
         _need(count, torch.int32, (B, Hq), "count")
     if idx is not None:
         _need(idx, torch.int32, (B, Hq, cap), "idx")
-    _planes_ok(planes, codes, K)
+    _planes_ok(planes, codes, K, buckets)
     return B, Hq, d, cap, L, out
 
 
@@ -333,15 +371,18 @@ def mp_decode_step_static(k_new: Optional[torch.Tensor], v_new: Optional[torch.T
                           lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
                           count: Optional[torch.Tensor] = None, n_static_head: int = 0, n_static_tail: int = 0,
                           sample_events=None, stream=None, T: int = 2, planes: Optional[torch.Tensor] = None,
-                          n_planes: int = 0) -> torch.Tensor:
+                          n_planes: int = 0, buckets: Optional[torch.Tensor] = None,
+                          n_buckets: int = 0) -> torch.Tensor:
     """mp_decode_step with the library's static scratch as its workspace: the
     native call allocates nothing (``out`` must be given, so this wrapper
     allocates nothing either).  Calls that overlap on one GPU race."""
     if out is None:
         raise ValueError("mp_decode_step_static: out must be given")
-    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes)
+    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes,
+                                       buckets)
     st = lib().mp_decode_step_static(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes),
-                                     _p(planes), n_planes, _p(kmean), _p(Wp), B, Hq, Hkv, n, cap, d, K, L, T,
+                                     _p(planes), n_planes, _p(buckets), n_buckets, _p(kmean), _p(Wp), B, Hq, Hkv, n,
+                                     cap, d, K, L, T,
                                      n_static_head, n_static_tail, _p(out), _p(lse), _p(idx), _p(count),
                                      _event_pair(sample_events), _stream(stream))
     _check("mp_decode_step_static", st)
@@ -353,15 +394,17 @@ def mp_decode_step(k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
                    K: int, ws: torch.Tensor, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                    idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None, n_static_head: int = 0,
                    n_static_tail: int = 0, sample_events=None, stream=None, T: int = 2,
-                   planes: Optional[torch.Tensor] = None, n_planes: int = 0) -> torch.Tensor:
+                   planes: Optional[torch.Tensor] = None, n_planes: int = 0, buckets: Optional[torch.Tensor] = None,
+                   n_buckets: int = 0) -> torch.Tensor:
     """Append (k_new, v_new) at row n (unless None), encode q, sample and merge over the keys.
 
     ``sample_events``: optional pair of torch.cuda.Event objects (created with
     timing and recorded once, so that their handles exist); they are attached
     to the sampling kernel's dispatch and record its start and end."""
-    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes)
+    B, Hq, d, cap, L, out = _step_args(k_new, v_new, q, Kc, Vc, codes, kmean, Hkv, K, out, lse, idx, count, planes,
+                                       buckets)
     st = lib().mp_decode_step(_p(k_new), _p(v_new), _p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes),
-                              n_planes, _p(kmean), _p(Wp),
+                              n_planes, _p(buckets), n_buckets, _p(kmean), _p(Wp),
                               B, Hq, Hkv, n, cap, d, K, L, T, n_static_head, n_static_tail, _p(out), _p(lse), _p(idx),
                               _p(count), _p(ws), ws.numel(), _event_pair(sample_events), _stream(stream))
     _check("mp_decode_step", st)

@@ -58,7 +58,7 @@ const char *mp_strerror(int status) {
   }
 }
 
-int mp_version(void) { return 2; }
+int mp_version(void) { return 3; }
 
 size_t mp_proj_bytes(int d, int K, int L) {
   if (check_shape(d, K, L) != MP_OK) return 0;
@@ -130,6 +130,35 @@ int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, in
   return hip_status(launch_plane_build(codes, U, cap, K, L, n0 / SCAN_TILE, nt, planes, as_stream(stream)));
 }
 
+size_t mp_buckets_bytes(int64_t U, int64_t cap, int K, int L) {
+  if (U < 1 || cap < 1 || K < 1 || K > MAX_BK_K || L < 2 || L > MAX_L || K * L > 4096) return 0;
+  return bucket_layout(nullptr, U, cap, K, L).bytes;
+}
+
+int mp_build_buckets(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, int64_t cap, int K, int L,
+                     void *buckets, size_t buckets_bytes, void *stream) {
+  if (L < 2 || L > MAX_L || K < 1 || K > MAX_BK_K || K * L > 4096) return MP_ERR_UNSUPPORTED;
+  if (!codes || !buckets || U < 1 || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (!all_a16(codes, buckets)) return MP_ERR_ARG;
+  if (n0 < 0 || n0 > n1 || n1 > cap || n0 % BK_R || n1 % SCAN_TILE) return MP_ERR_ARG;
+  if (buckets_bytes < mp_buckets_bytes(U, cap, K, L)) return MP_ERR_WORKSPACE;
+  const int64_t nc = (n1 + BK_R - 1) / BK_R - n0 / BK_R;
+  if (U * L * nc >= ((int64_t)1 << 31)) return MP_ERR_UNSUPPORTED;  // one block per (unit, table, chunk)
+  const BucketLayout bl = bucket_layout(buckets, U, cap, K, L);
+  return hip_status(launch_bucket_build(codes, U, cap, K, L, n0, n1, bl, as_stream(stream)));
+}
+
+// Bucketed tables passed to a decode: whole 512-key tiles below n_buckets,
+// used with threshold 2 (other thresholds scan the codes).
+static int check_buckets(const void *buckets, int64_t n_buckets, int64_t n, int K) {
+  if (!buckets) return MP_OK;
+  if (!a16(buckets) || n_buckets < 0 || n_buckets > n || n_buckets % SCAN_TILE) return MP_ERR_ARG;
+  if (K < 1 || K > MAX_BK_K) return MP_ERR_ARG;  // no bucketed table can exist for this K
+  return MP_OK;
+}
+
+static int64_t list_keys(const void *buckets, int64_t n_buckets, int T) { return buckets && T == 2 ? n_buckets : 0; }
+
 static int check_planes(const uint32_t *planes, int64_t n_planes, int64_t n) {
   if (!planes) return MP_OK;
   if (!a16(planes) || n_planes < 0 || n_planes > n || n_planes % SCAN_TILE) return MP_ERR_ARG;
@@ -171,8 +200,26 @@ static int check_decode(const void *q, const void *Kc, const void *Vc, int kv_dt
   return MP_OK;
 }
 
+// The sampling stage: the bucket lookup of the tiles below nl (when
+// buckets are given), then the sampling kernel.
+static int run_sample(int kv_dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
+                      const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap, int K,
+                      int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &w, bool want_idx,
+                      hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint32_t *planes, int64_t n_planes,
+                      const void *buckets, int64_t nl) {
+  if (nl > 0) {  // the events then span the lookup and the sampling kernel
+    const BucketLayout bl = bucket_layout((void *)buckets, (int64_t)B * Hkv, cap, K, L);
+    if (launch_bucket_lookup(qcodes, bl, B, Hq, Hkv, n, nl, cap, K, L, nsh, nst, geo, w, s, ev0) != hipSuccess)
+      return MP_ERR_HIP;
+    ev0 = nullptr;
+  }
+  return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T, nsh, nst,
+                                  geo, w, want_idx, s, ev0, ev1, planes, n_planes, nl));
+}
+
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                     const uint32_t *planes, int64_t n_planes, const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                     const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                     const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                      int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream) {
   int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
@@ -180,12 +227,13 @@ int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype
   if (st) return st;
   if (!qcodes) return MP_ERR_ARG;
   if ((st = check_planes(planes, n_planes, n))) return st;
+  if ((st = check_buckets(buckets, n_buckets, n, K))) return st;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
   if (geo.nchunks == 0) return MP_OK;
-  return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T,
-                                  n_static_head, n_static_tail, geo, w, want_idx != 0, as_stream(stream), nullptr,
-                                  nullptr, planes, n_planes));
+  return run_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T, n_static_head,
+                    n_static_tail, geo, w, want_idx != 0, as_stream(stream), nullptr, nullptr, planes, n_planes,
+                    buckets, list_keys(buckets, n_buckets, T));
 }
 
 int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
@@ -203,7 +251,8 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
 }
 
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                   const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
                    int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
                    uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                    size_t ws_bytes, void *stream) {
@@ -213,6 +262,7 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   if (!out || (!qcodes_in && K > 0 && !Wp)) return MP_ERR_ARG;
   if (!all_a16(out, Wp)) return MP_ERR_ARG;
   if ((st = check_planes(planes, n_planes, n))) return st;
+  if ((st = check_buckets(buckets, n_buckets, n, K))) return st;
   hipStream_t s = as_stream(stream);
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
@@ -225,9 +275,10 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
     qc = dst;
   }
   if (geo.nchunks > 0) {
-    hipError_t e = launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head,
-                                 n_static_tail, geo, w, idx != nullptr, s, nullptr, nullptr, planes, n_planes);
-    if (e != hipSuccess) return MP_ERR_HIP;
+    st = run_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head, n_static_tail,
+                    geo, w, idx != nullptr, s, nullptr, nullptr, planes, n_planes, buckets,
+                    list_keys(buckets, n_buckets, T));
+    if (st) return st;
   }
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
 }
@@ -271,7 +322,8 @@ int static_scratch(void **out) {
 // workspace comes from (the caller's ws, or with static_ws the library's
 // static scratch, looked up once every argument has been validated).
 int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp, int B,
+                uint16_t *codes, const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                const float *kmean, const void *Wp, int B,
                 int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head,
                 int64_t n_static_tail, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
                 size_t ws_bytes, void *sample_events, void *stream, bool static_ws) {
@@ -285,6 +337,7 @@ int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, v
   if (!out || (K > 0 && !Wp)) return MP_ERR_ARG;
   if (!all_a16(out, Wp, k_new, v_new)) return MP_ERR_ARG;
   if ((st = check_planes(planes, n_planes, n))) return st;  // the keys before the append
+  if ((st = check_buckets(buckets, n_buckets, n, K))) return st;
   if (static_ws) {
     if (mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L) > (size_t)MP_STATIC_SCRATCH_BYTES) return MP_ERR_SCRATCH;
     if ((st = static_scratch(&ws))) return st;
@@ -307,11 +360,10 @@ int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, v
   // the events ride on the sampling kernel's dispatch (its own start and end)
   hipEvent_t *ev = (hipEvent_t *)sample_events;
   if (geo.nchunks > 0) {
-    if (launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, T, n_static_head,
-                      n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, planes,
-                      n_planes) !=
-        hipSuccess)
-      return MP_ERR_HIP;
+    st = run_sample(kv_dtype, q, Kc, Vc, codes, kmean, w.qcodes, B, Hq, Hkv, nd, cap, K, L, T, n_static_head,
+                    n_static_tail, geo, w, idx != nullptr, s, ev ? ev[0] : nullptr, ev ? ev[1] : nullptr, planes,
+                    n_planes, buckets, list_keys(buckets, n_buckets, T));
+    if (st) return st;
   } else if (ev && (hipEventRecord(ev[0], s) != hipSuccess || hipEventRecord(ev[1], s) != hipSuccess)) {
     return MP_ERR_HIP;
   }
@@ -323,21 +375,23 @@ int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, v
 extern "C" {
 
 int mp_decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean, const void *Wp,
-                   int B, int Hq, int Hkv, int64_t n, int64_t cap,
+                   uint16_t *codes, const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                    int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, float *out, float *lse,
                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *sample_events, void *stream) {
-  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, kmean, Wp, B, Hq, Hkv, n, cap, d,
+  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, buckets, n_buckets, kmean, Wp, B,
+                     Hq, Hkv, n, cap, d,
                      K, L, T, n_static_head, n_static_tail, out, lse, idx, count, ws, ws_bytes, sample_events,
                      stream, false);
 }
 
 int mp_decode_step_static(const void *k_new, const void *v_new, const void *q, void *Kc, void *Vc, int kv_dtype,
-                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const float *kmean,
-                          const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T,
-                          int64_t n_static_head, int64_t n_static_tail, float *out, float *lse, int32_t *idx,
-                          int32_t *count, void *sample_events, void *stream) {
-  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, kmean, Wp, B, Hq, Hkv, n, cap, d,
+                          uint16_t *codes, const uint32_t *planes, int64_t n_planes, const void *buckets,
+                          int64_t n_buckets, const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n,
+                          int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                          float *out, float *lse, int32_t *idx, int32_t *count, void *sample_events, void *stream) {
+  return decode_step(k_new, v_new, q, Kc, Vc, kv_dtype, codes, planes, n_planes, buckets, n_buckets, kmean, Wp, B,
+                     Hq, Hkv, n, cap, d,
                      K, L, T, n_static_head, n_static_tail, out, lse, idx, count, nullptr, 0, sample_events, stream,
                      true);
 }

@@ -72,6 +72,8 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
   off = align256(off + sizeof(uint32_t) * (size_t)U * ent_per_unit);
   w.ent_cnt = (int32_t *)(p + off);
   off = align256(off + sizeof(int32_t) * (size_t)U * ncm);
+  w.bits = (uint32_t *)(p + off);
+  off = align256(off + sizeof(uint32_t) * (size_t)U * G * ncm * (SCAN_TILE / 32));
   w.bytes = off;
   return w;
 }
@@ -295,7 +297,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
     float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt,
-    const uint32_t *__restrict__ planes, int64_t npt, int64_t ptiles) {
+    const uint32_t *__restrict__ planes, int64_t npt, int64_t ptiles, const uint32_t *__restrict__ sbits,
+    int64_t bwords, int64_t nlt) {
   // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
   // words [0, FW) says "at least one of this wave's tables matched", of
   // words [FW, 2FW) "at least two".
@@ -375,9 +378,11 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
                      rs, lo, (uint32_t)(min(j0 + hf * (MP_SB / 2) + r, jlast) - jb) * rstride32, 2));
   };
-  // Tiles the bit-plane index covers are scanned there (threshold 2 only).
-  const bool use_pl = planes != nullptr && K > 0 && cf.T == 2 && c < npt;
-  if (!use_pl && ntw > 0) {
+  // Tiles below nlt take their sampled keys from the bucket lookup's bitmaps;
+  // tiles the bit-plane index covers are scanned there (threshold 2 only).
+  const bool use_bits = c < nlt;
+  const bool use_pl = !use_bits && planes != nullptr && K > 0 && cf.T == 2 && c < npt;
+  if (!use_bits && !use_pl && ntw > 0) {
     load_half(0, 0);
     load_half(0, 1);
   }
@@ -389,16 +394,18 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   constexpr int QPASS = 4;                     // query-code loads per thread and pass
   constexpr int QV = (GM * D + 255) / 256;     // query elements per thread
   {
-    const int nq = L * GM;
+    const int nq = use_bits ? 0 : L * GM;  // a tile with bitmaps needs no query codes
     int i0 = tid;
     do {
       uint16_t cq[QPASS];
       T qv[QV];
       float mv = 0.0f;
+      if (nq > 0) {
 #pragma unroll
-      for (int k = 0; k < QPASS; ++k) {
-        const int i = min(i0 + 256 * k, nq - 1), l = i / GM, h = min(i % GM, G - 1);
-        cq[k] = qcodes[(qrow0 + h) * L + l];
+        for (int k = 0; k < QPASS; ++k) {
+          const int i = min(i0 + 256 * k, nq - 1), l = i / GM, h = min(i % GM, G - 1);
+          cq[k] = qcodes[(qrow0 + h) * L + l];
+        }
       }
       const bool first = i0 == tid;
       if (first) {
@@ -471,7 +478,21 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     };
     const int64_t klo = sbase + 2 * tid;
     uint32_t mlo = 0, mhi = 0;
-    if (use_pl) {
+    if (use_bits) {
+      // the tile's sampled-key words of every head, as the bucket lookup wrote them
+      if (tid < GM * 16) {
+        const int h = tid >> 4, jj = tid & 15;
+        pw2[h][jj] = h < G ? sbits[(u * G + h) * bwords + c * 16 + jj] : 0u;
+      }
+      __syncthreads();
+      const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        const uint32_t wv = pw2[h][wj];
+        mlo |= ((wv >> k0) & 1u) << h;
+        mhi |= ((wv >> (k0 + 1)) & 1u) << h;
+      }
+    } else if (use_pl) {
       // Bit-plane scan: the tile's planes are one contiguous region, row
       // (b, l) = bit b of table l's codes for the tile's 512 keys (16 words).
       // Lane j of a 16-lane group holds word j (32 keys); the wave's four
@@ -849,7 +870,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int Tthr, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         const uint32_t *planes, int64_t n_planes) {
+                         const uint32_t *planes, int64_t n_planes, int64_t n_lists) {
   const int G = Hq / Hkv;
   const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
@@ -859,10 +880,12 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
   const int64_t npt = planes ? n_planes / SCAN_TILE : 0;  // tiles the plane index covers
   const int64_t ptiles = (cap + SCAN_TILE - 1) / SCAN_TILE;
+  const int64_t nlt = n_lists / SCAN_TILE;  // tiles whose sampled-key bitmaps the bucket lookup wrote
 #define MP_SAMPLE(T, GMV)                                                                                    \
   hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
-                        nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles)
+                        nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles, ws.bits, \
+                        geo.nchunks_max * (SCAN_TILE / 32), nlt)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \

@@ -59,12 +59,13 @@ struct DecodeGeom {
 
 // Workspace layout of the decode: [qcodes B*Hq*L u16, 256-aligned]
 // [partials U * nchunks_max * G * PSTRIDE f32] [entries U * nchunks_max * chunk u32]
-// [entry counts U * nchunks_max i32].
+// [entry counts U * nchunks_max i32] [sampled-key bitmaps U * G * nchunks_max * 16 u32].
 struct DecodeWs {
   uint16_t *qcodes;
   float *part;
   uint32_t *ent;
   int32_t *ent_cnt;
+  uint32_t *bits;  // per (unit, head) one bit per key: sampled (bucket lookup)
   size_t bytes;
 };
 
@@ -129,11 +130,14 @@ hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si
                          const void *vin, void *vcopy, hipStream_t s);
 // When ev_start / ev_stop are set they are attached to the kernel's own
 // dispatch, so they time exactly this launch (no queue gap before it).
+// Tiles below n_lists take their sampled keys from the workspace's bitmaps
+// (written by launch_bucket_lookup) instead of scanning.
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start = nullptr,
-                         hipEvent_t ev_stop = nullptr, const uint32_t *planes = nullptr, int64_t n_planes = 0);
+                         hipEvent_t ev_stop = nullptr, const uint32_t *planes = nullptr, int64_t n_planes = 0,
+                         int64_t n_lists = 0);
 // Bit-plane index of the code store: tiles [t0, t0 + nt) of every unit,
 // planes [U][ptiles][K][L][16] u32 (word j of row (b, l) of tile t = bit b of
 // table l's codes for keys 512 t + 32 j .. + 31).
@@ -141,5 +145,31 @@ hipError_t launch_plane_build(const uint16_t *codes, int64_t U, int64_t cap, int
                               uint32_t *planes, hipStream_t s);
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
                         float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s);
+
+// ---------------------------------------------------------------- bucketed tables
+// Per (unit, table, chunk of BK_R keys) a table of 2^K buckets: the chunk's
+// keys ordered by their code (CSR).  off [U][L][bchunks][2^K + 1] uint16
+// (bucket c of the chunk holds entries off[c] .. off[c+1] - 1), keys
+// [U][L][cap] uint16 (entry j of chunk r at keys[u][l][r * BK_R + j], the key's
+// offset from the chunk's first key).
+constexpr int BK_R = 4096;  // keys per bucket chunk (8 scan tiles)
+constexpr int MAX_BK_K = 12;  // bits per table the bucketed tables support (2^K buckets per chunk)
+struct BucketLayout {
+  uint16_t *off;
+  uint16_t *keys;
+  int64_t bchunks;  // chunks per unit for the capacity
+  int nbins;        // 2^K
+  size_t bytes;
+};
+BucketLayout bucket_layout(void *base, int64_t U, int64_t cap, int K, int L);
+// (Re)builds the chunks [n0 / BK_R, ceil(n1 / BK_R)) from the codes of keys [.., n1).
+hipError_t launch_bucket_build(const uint16_t *codes, int64_t U, int64_t cap, int K, int L, int64_t n0, int64_t n1,
+                               const BucketLayout &bl, hipStream_t s);
+// Sampled-key bitmaps (threshold 2) of the tiles below nb (a multiple of
+// SCAN_TILE), from the query codes' buckets, into the workspace's bitmaps.
+// ev_start, when set, is attached to the lookup's own dispatch (its start).
+hipError_t launch_bucket_lookup(const uint16_t *qcodes, const BucketLayout &bl, int B, int Hq, int Hkv, int64_t n,
+                                int64_t nb, int64_t cap, int K, int L, int64_t nsh, int64_t nst, const DecodeGeom &geo,
+                                const DecodeWs &ws, hipStream_t s, hipEvent_t ev_start = nullptr);
 
 }  // namespace mp

@@ -37,7 +37,7 @@ def test_strerror_and_version():
     for code in (OK, ARG, UNSUP, CAP, WS, -5):
         assert len(mp.strerror(code)) > 5
     assert mp.strerror(12345) == "unknown status"
-    assert mp.lib().mp_version() == 2
+    assert mp.lib().mp_version() == 3
 
 
 def test_size_queries():
@@ -99,11 +99,12 @@ def test_append_rejects_invalid_arguments():
 
 
 def _decode(**kw):
-    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1, Hq=32, Hkv=8,
-             n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, qin=None, qout=None, out=FAKE, lse=None, idx=None,
-             cnt=None, ws=FAKE, wsb=1 << 30)
+    a = dict(q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, bk=None, nb=0, km=FAKE, Wp=FAKE, B=1,
+             Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, qin=None, qout=None, out=FAKE,
+             lse=None, idx=None, cnt=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
-    return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["planes"], a["np"], a["km"],
+    return mp.lib().mp_decode_attn(a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["planes"], a["np"], a["bk"],
+                                   a["nb"], a["km"],
                                    a["Wp"], a["B"], a["Hq"],
                                    a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"], a["nst"], a["qin"],
                                    a["qout"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None)
@@ -132,6 +133,11 @@ def test_decode_rejects_invalid_arguments():
     assert _decode(planes=FAKE, np=1024, n=1000, cap=1024) == ARG
     assert _decode(planes=FAKE + 4, np=512, n=1000, cap=1024) == ARG
     assert _decode(planes=FAKE, np=-512, n=1000, cap=1024) == ARG
+    # bucketed tables: whole 512-key tiles at or below n, 16-byte aligned, a K they can exist for
+    assert _decode(bk=FAKE, nb=100, n=1000, cap=1024) == ARG
+    assert _decode(bk=FAKE, nb=1024, n=1000, cap=1024) == ARG
+    assert _decode(bk=FAKE + 4, nb=512, n=1000, cap=1024) == ARG
+    assert _decode(bk=FAKE, nb=512, n=1000, cap=1024, K=13) == ARG
 
 
 def test_build_planes_rejects_invalid_arguments():
@@ -159,14 +165,45 @@ def test_build_planes_rejects_invalid_arguments():
     assert b(n0=512, n1=512) == OK  # nothing to do
 
 
+def test_build_buckets_rejects_invalid_arguments():
+    L = mp.lib()
+    # offsets: 2^K + 1 per (unit, table, 4096-key chunk), then the keys, each part 256-byte aligned
+    off = 8 * 150 * 25 * 1025 * 2
+    assert L.mp_buckets_bytes(8, 98368, 10, 150) == (off + 255) // 256 * 256 + 8 * 150 * 98368 * 2
+    assert L.mp_buckets_bytes(2, 1024, 0, 75) == 0
+    assert L.mp_buckets_bytes(2, 1024, 13, 75) == 0
+    ok = dict(codes=FAKE, U=2, n0=0, n1=1024, cap=1024, K=8, L=75, bk=FAKE, nb=1 << 30)
+
+    def b(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return L.mp_build_buckets(a["codes"], a["U"], a["n0"], a["n1"], a["cap"], a["K"], a["L"], a["bk"], a["nb"],
+                                  None)
+
+    assert b(codes=None) == ARG
+    assert b(bk=None) == ARG
+    assert b(bk=FAKE + 4) == ARG
+    assert b(n0=512) == ARG  # chunk starts are multiples of 4096
+    assert b(n1=1000) == ARG
+    assert b(n1=1536) == ARG  # past cap
+    assert b(K=0) == UNSUP
+    assert b(K=13) == UNSUP
+    assert b(L=513) == UNSUP
+    assert b(cap=1020) == ARG
+    assert b(nb=100) == WS
+    assert b(n0=0, n1=0) == OK  # nothing to do
+
+
 def test_decode_stages_reject_invalid_arguments():
     L = mp.lib()
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0, 0,
-                              0, FAKE, 1 << 30, None) == ARG  # qcodes required
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 0, 0, 0,
-                              0, FAKE, 1 << 30, None) == UNSUP  # threshold 0
-    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 512, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75, 2, 0,
-                              0, 0, FAKE, 1 << 30, None) == ARG  # planes past n
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, None, 0, FAKE, None, 1, 32, 8, 100, 128, 128, 8, 75,
+                              2, 0, 0, 0, FAKE, 1 << 30, None) == ARG  # qcodes required
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, None, 0, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8, 75,
+                              0, 0, 0, 0, FAKE, 1 << 30, None) == UNSUP  # threshold 0
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, FAKE, 512, None, 0, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8,
+                              75, 2, 0, 0, 0, FAKE, 1 << 30, None) == ARG  # planes past n
+    assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, 512, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8,
+                              75, 2, 0, 0, 0, FAKE, 1 << 30, None) == ARG  # buckets past n
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, None, None, None, None, FAKE, 1 << 30, None) == ARG
     assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, FAKE, None, None, None, FAKE, 10, None) == WS
 
@@ -182,12 +219,12 @@ def test_encode_queries_rejects_invalid_arguments():
 
 
 def _step(**kw):
-    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1,
-             Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None,
-             ws=FAKE, wsb=1 << 30)
+    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, bk=None, nb=0, km=FAKE,
+             Wp=FAKE, B=1, Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None,
+             idx=None, cnt=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return mp.lib().mp_decode_step(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"], a["planes"],
-                                   a["np"], a["km"], a["Wp"],
+                                   a["np"], a["bk"], a["nb"], a["km"], a["Wp"],
                                    a["B"], a["Hq"], a["Hkv"], a["n"], a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"],
                                    a["nst"], a["out"], a["lse"], a["idx"], a["cnt"], a["ws"], a["wsb"], None, None)
 
@@ -202,16 +239,19 @@ def test_step_rejects_invalid_arguments():
     assert _step(ws=None) == WS
     assert _step(T=0) == UNSUP
     assert _step(planes=FAKE, np=512, n=511, cap=1024) == ARG  # the appended key is not in the index
+    assert _step(bk=FAKE, nb=512, n=511, cap=1024) == ARG  # nor in the buckets
     for arg in ("k", "v", "q", "Kc", "Vc", "codes", "km", "Wp", "out", "ws"):
         assert _step(**{arg: FAKE + 4}) == ARG, arg
 
 
 def _static(**kw):
-    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, km=FAKE, Wp=FAKE, B=1,
-             Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None, idx=None, cnt=None)
+    a = dict(k=FAKE, v=FAKE, q=FAKE, Kc=FAKE, Vc=FAKE, dt=0, codes=FAKE, planes=None, np=0, bk=None, nb=0, km=FAKE,
+             Wp=FAKE, B=1, Hq=32, Hkv=8, n=100, cap=128, d=128, K=8, L=75, T=2, nsh=0, nst=0, out=FAKE, lse=None,
+             idx=None, cnt=None)
     a.update(kw)
     return mp.lib().mp_decode_step_static(a["k"], a["v"], a["q"], a["Kc"], a["Vc"], a["dt"], a["codes"],
-                                          a["planes"], a["np"], a["km"], a["Wp"], a["B"], a["Hq"], a["Hkv"], a["n"],
+                                          a["planes"], a["np"], a["bk"], a["nb"], a["km"], a["Wp"], a["B"], a["Hq"],
+                                          a["Hkv"], a["n"],
                                           a["cap"], a["d"], a["K"], a["L"], a["T"], a["nsh"], a["nst"], a["out"],
                                           a["lse"], a["idx"], a["cnt"], None, None)
 

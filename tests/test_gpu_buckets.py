@@ -1,0 +1,211 @@
+"""GPU parity of the bucketed hash tables (mp_build_buckets) and of the
+decode that looks the query's buckets up instead of scanning.
+
+A key sits in bucket c of table l exactly when its code of table l is c, so:
+(1) unpacked on the host, every bucket of every (unit, table, 4096-key
+chunk) holds exactly the keys whose code is that bucket's; (2) a decode that
+takes the tiles below n_buckets from the buckets gives the same sampled index
+lists, counts and outputs as the decode that scans the codes, bit for bit,
+and therefore meets the oracle's bars; (3) across appends, with the newest
+chunk rebuilt whenever a 512-key tile fills, the step stays equal to the
+scan and to the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import lsh_sampled_sparse_centered_amd as mp
+import synth
+from tests.common import layer, oracle_decode, variant
+from tests.test_gpu_parity import CASES, _compare, _inject, case, gpu_build
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 4096
+
+
+def unpack_buckets(buf: np.ndarray, U: int, L: int, cap: int, K: int):
+    """Host view of the layout: off [U][L][chunks][2^K + 1], keys [U][L][cap] (uint16)."""
+    nb = 1 << K
+    chunks = (cap + CHUNK - 1) // CHUNK
+    noff = U * L * chunks * (nb + 1)
+    off_bytes = (2 * noff + 255) // 256 * 256
+    off = buf[:2 * noff].view(np.uint16).reshape(U, L, chunks, nb + 1)
+    keys = buf[off_bytes:off_bytes + 2 * U * L * cap].view(np.uint16).reshape(U, L, cap)
+    return off, keys
+
+
+def check_buckets_hold_their_codes(buf, codes, K, n1, n0=0):
+    """Every bucket of the chunks [n0/4096, ceil(n1/4096)) holds exactly the keys with its code."""
+    U, L, cap = codes.shape
+    off, keys = unpack_buckets(buf, U, L, cap, K)
+    nb = 1 << K
+    for ci in range(n0 // CHUNK, (n1 + CHUNK - 1) // CHUNK):
+        r0, r1 = ci * CHUNK, min((ci + 1) * CHUNK, n1)
+        o = off[:, :, ci].astype(np.int64)  # [U][L][nb + 1]
+        assert np.all(o[:, :, 0] == 0) and np.all(o[:, :, nb] == r1 - r0)
+        assert np.all(np.diff(o, axis=2) >= 0)
+        c = codes[:, :, r0:r1].astype(np.int64)
+        k = keys[:, :, r0:r1].astype(np.int64)  # entries of the chunk, ordered by bucket
+        assert np.all(k < r1 - r0)
+        # entry j lies in the bucket whose range contains j; its key's code must be that bucket
+        for u in range(U):
+            for l in range(L):
+                bucket_of_entry = np.repeat(np.arange(nb), np.diff(o[u, l]))
+                assert np.array_equal(c[u, l, k[u, l]], bucket_of_entry), (u, l, ci)
+                assert np.array_equal(np.sort(k[u, l]), np.arange(r1 - r0)), (u, l, ci)  # each key once
+
+
+@pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged", "mha_b3", "g2_small", "g4_f32", "tiny"])
+def test_buckets_hold_their_codes(name):
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    n1 = (lay["n"] // 512) * 512
+    buf = mp.mp_build_buckets(gcodes, w.K, n1)
+    torch.cuda.synchronize()
+    check_buckets_hold_their_codes(buf.cpu().numpy(), codes, w.K, n1)
+
+
+def _decode(w, lay, kmean, gcodes, qcodes, buckets=None, n_buckets=0, nsh=0, nst=0, T=2, planes=None, n_planes=0):
+    B, Hq, cap = w.batch, w.hq, lay["cap"]
+    out = torch.empty(B, Hq, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(B, Hq, dtype=torch.float32, device="cuda")
+    idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, Hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K, nsh, nst,
+                      qcodes_in=qcodes, out=out, lse=lse, idx=idx, count=cnt, T=T, buckets=buckets,
+                      n_buckets=n_buckets, planes=planes, n_planes=n_planes)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+@pytest.mark.parametrize("name,nsh,nst,part", [
+    ("llama8b_layer", 0, 0, 1.0),
+    ("llama8b_layer", 4, 64, 1.0),   # forced ranges inside bucket tiles
+    ("llama8b_layer", 0, 0, 0.3),    # the first tiles from the buckets, the rest scanned
+    ("g8_ragged", 0, 0, 1.0),
+    ("g8_ragged", 4, 64, 1.0),
+    ("mha_b3", 0, 0, 1.0),
+    ("g2_small", 0, 0, 1.0),
+    ("g4_f32", 0, 0, 1.0),
+    ("g5_f32", 0, 0, 1.0),
+    ("g6_bf16", 0, 0, 1.0),
+    ("g7_bf16", 0, 0, 1.0),
+    ("tiny", 0, 0, 1.0),
+])
+def test_decode_with_buckets(name, nsh, nst, part):
+    """Sets, counts, outputs and lse bit-identical to the code scan, and within the oracle's bars."""
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    n1 = (lay["n"] // 512) * 512
+    buf = mp.mp_build_buckets(gcodes, w.K, n1)
+    nb = max(512, int(n1 * part) // 512 * 512)
+    got = _decode(w, lay, kmean, gcodes, qcodes, buf, nb, nsh, nst)
+    base = _decode(w, lay, kmean, gcodes, qcodes, None, 0, nsh, nst)
+    for a, b, what in zip(got, base, ("out", "lse", "idx", "count")):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (name, what)
+    ref = oracle_decode(w, lay, km, codes, qc, nsh=nsh, nst=nst)
+    _compare(w, ref, *got, "%s buckets<%d nsh=%d nst=%d" % (name, nb, nsh, nst))
+
+
+def test_buckets_with_other_thresholds_scan_the_codes():
+    """The buckets serve threshold 2; with T = 3 they are ignored and the decode scans."""
+    w, lay, km, codes, margin, qc = case("llama8b_layer")
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    n1 = (lay["n"] // 512) * 512
+    buf = mp.mp_build_buckets(gcodes, w.K, n1)
+    got = _decode(w, lay, kmean, gcodes, qcodes, buf, n1, T=3)
+    base = _decode(w, lay, kmean, gcodes, qcodes, None, 0, T=3)
+    for a, b in zip(got, base):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def test_buckets_and_planes_together():
+    """Buckets below 2048 keys, bit planes from there to the last whole tile, codes above."""
+    w, lay, km, codes, margin, qc = case("llama8b_layer")
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    n1 = (lay["n"] // 512) * 512
+    buf = mp.mp_build_buckets(gcodes, w.K, 2048)
+    planes = mp.mp_build_planes(gcodes, w.K, n1)
+    got = _decode(w, lay, kmean, gcodes, qcodes, buf, 2048, planes=planes, n_planes=n1)
+    base = _decode(w, lay, kmean, gcodes, qcodes)
+    for a, b in zip(got, base):
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+@pytest.mark.parametrize("name", ["llama8b_layer", "g8_small"])
+def test_index_maintenance_across_tile_boundaries(name):
+    """A long appending decode with both indexes kept up to date by the
+    caller's rule: whenever a 512-key tile fills, its plane tile and its
+    bucket chunk are rebuilt (the appended keys are scanned until then).
+    The step with buckets, the step with planes and the plain scan stay
+    bit-identical at every step, and the oracle (decoding the GPU's own codes)
+    agrees at the first step, on both sides of each rebuild and at the last."""
+    w = variant("llama8b_layer", n=3500, steps=700) if name == "llama8b_layer" else \
+        variant("codellama34b_b4", layers=1, batch=1, n=3900, steps=700)
+    lay = layer(w, seed=808)
+    Wp, kmean, codes = gpu_build(w, lay)
+    U, cap, G = w.batch * w.hkv, lay["cap"], w.group
+    n = lay["n"]
+    runs = {}
+    for mode in ("scan", "planes", "buckets"):
+        runs[mode] = dict(Kc=lay["Kc"].clone(), Vc=lay["Vc"].clone(), codes=codes.clone(),
+                          ws=mp.decode_workspace(w.batch, w.hq, w.hkv, cap, w.L, "cuda"))
+    r = runs["planes"]
+    r["planes"] = mp.mp_build_planes(r["codes"], w.K, (n // 512) * 512)
+    r = runs["buckets"]
+    r["buckets"] = mp.mp_build_buckets(r["codes"], w.K, (n // 512) * 512)
+    n_idx = (n // 512) * 512
+    steps = w.steps
+    checks = {1, steps}
+    rebuilds = 0
+    for s in range(1, steps + 1):
+        kn = torch.stack([synth.step_kv(808, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=s)[0]
+                          for u in range(U)]).cuda()
+        vn = torch.stack([synth.step_kv(808, 0, u // w.hkv, u % w.hkv, w.d, w.torch_dtype, step=s)[1]
+                          for u in range(U)]).cuda()
+        q = torch.stack([synth.unit_queries(808, 0, u // w.hkv, u % w.hkv, G, w.d, w.torch_dtype, step=s)
+                         for u in range(U)]).reshape(w.batch, w.hq, w.d).cuda()
+        res = {}
+        for mode, r in runs.items():
+            out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+            lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
+            cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+            idx = torch.full((w.batch, w.hq, cap), -1, dtype=torch.int32, device="cuda")
+            kw = {}
+            if mode == "planes":
+                kw = dict(planes=r["planes"], n_planes=n_idx)
+            elif mode == "buckets":
+                kw = dict(buckets=r["buckets"], n_buckets=n_idx)
+            mp.mp_decode_step(kn, vn, q, r["Kc"], r["Vc"], r["codes"], kmean, Wp, w.hkv, n, w.K, r["ws"], out=out,
+                              lse=lse, idx=idx, count=cnt, **kw)
+            res[mode] = [t.cpu().numpy() for t in (out, lse, idx, cnt)]
+        torch.cuda.synchronize()
+        for mode in ("planes", "buckets"):
+            for a, b in zip(res[mode], res["scan"]):
+                assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), (s, mode)
+        n += 1
+        if n % 512 == 0:  # a tile filled: rebuild its plane tile and its bucket chunk
+            mp.mp_build_planes(runs["planes"]["codes"], w.K, n, n0=n - 512, planes=runs["planes"]["planes"])
+            mp.mp_build_buckets(runs["buckets"]["codes"], w.K, n, n0=(n - 512) // CHUNK * CHUNK,
+                                buckets=runs["buckets"]["buckets"])
+            n_idx = n
+            rebuilds += 1
+            checks |= {s, s + 1}
+        if s in checks:
+            gc = runs["scan"]["codes"]
+            torch.cuda.synchronize()
+            Kh = runs["scan"]["Kc"].float().cpu().numpy().reshape(w.batch, w.hkv, cap, w.d)
+            Vh = runs["scan"]["Vc"].float().cpu().numpy().reshape(w.batch, w.hkv, cap, w.d)
+            qh = q.float().cpu().numpy()
+            qc = mp.mp_encode_queries(q, Wp, w.K, w.L).cpu().numpy()
+            import oracle
+            ref = oracle.decode(qh, Kh, Vh, gc.cpu().numpy().reshape(w.batch, w.hkv, w.L, cap),
+                                kmean.cpu().numpy().reshape(w.batch, w.hkv, w.d), lay["host"]["W"], w.K, w.L, n,
+                                qcodes=qc, want_idx=True)
+            out, lse, idx, cnt = res["buckets"]
+            _compare(w, ref, out, lse, idx, cnt, "%s step %d n=%d index<%d" % (name, s, n, n_idx))
+    assert rebuilds >= 1
+    # the rebuilt buckets hold their codes
+    buf = runs["buckets"]["buckets"].cpu().numpy()
+    check_buckets_hold_their_codes(buf, runs["buckets"]["codes"].cpu().numpy(), w.K, n_idx)
