@@ -28,6 +28,7 @@ namespace mp {
 
 constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
 constexpr int ATT_E = 32;  // list entries per attention round
+constexpr int VT_STRIDE = 40;  // entries per row of the transposed value rows (32 + padding, 16-byte rows)
 
 LnPCoef lnp_coef(int L, int T) {
   LnPCoef c{};
@@ -131,6 +132,27 @@ __device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &
     return cf.lnc2 + 2.0f * lnp + (Lf - 2.0f) * log1pf(-p) + __logf(sum);
   }
   return logf(-expm1f((Lf - 1.0f) * log1pf(-p) + log1pf((Lf - 1.0f) * p)));
+}
+
+// Maximum and sum over each half (32 lanes) of the wave, every lane ending
+// with its half's result: lane-xor swizzles (no lane-index registers).
+template <int XM>
+__device__ inline float swz_xor(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (XM << 10) | 0x1f));
+}
+__device__ inline float xor32_max(float x) {
+  x = fmaxf(x, swz_xor<16>(x));
+  x = fmaxf(x, swz_xor<8>(x));
+  x = fmaxf(x, swz_xor<4>(x));
+  x = fmaxf(x, swz_xor<2>(x));
+  return fmaxf(x, swz_xor<1>(x));
+}
+__device__ inline float xor32_sum(float x) {
+  x += swz_xor<16>(x);
+  x += swz_xor<8>(x);
+  x += swz_xor<4>(x);
+  x += swz_xor<2>(x);
+  return x + swz_xor<1>(x);
 }
 
 // Sum over the 16 lanes of a DPP row (each lane ends with the row sum).
@@ -317,11 +339,18 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     uint32_t c1[16][GM][16];
     uint32_t c2[16][GM][16];
   };
+  struct MfmaLds {  // matrix-core rounds (bf16 caches)
+    alignas(16) __bf16 vT[D][VT_STRIDE];  // value rows transposed: [dim][entry]
+    alignas(16) float p[GM][ATT_E];       // exp(w - m) per head and entry
+    float sdot[2][GM][ATT_E];             // q_h . k per head and entry: dims 0-63, 64-127
+    float nrm[2][ATT_E];                  // |k - mu|^2 per entry: dims 0-63, 64-127
+  };
   __shared__ union {
     ScanLds s;
     CntLds c;
     AttnLds a;
     PlaneLds p;
+    MfmaLds m;
   } sm;  // scan and attention phases never overlap in time
   __shared__ uint32_t pw2[GM][16];  // plane scan: per head, the tile's sampled-key words
   extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
@@ -334,6 +363,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   __shared__ int wtot[4];
   __shared__ int hcnt[GM];
   __shared__ float mrun[GM], alpha_sh[GM];  // per head: running maximum, this round's rescale factor
+  __shared__ float lsum[GM];                 // per head: running normaliser (matrix-core rounds)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
@@ -341,9 +371,14 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // Blocks run tile-major: consecutive blocks take the same tile of
   // consecutive units, so the units' short last tiles are dispatched last and
   // are what a grid slightly larger than one round of blocks leaves over.
+  // With bitmaps for the tiles below nlt, the tiles that still scan (the
+  // appended keys past the bucketed tables: a few per unit, each a chain of
+  // dependent load batches) are dispatched first, so their scans overlap the
+  // other tiles' attention instead of trailing it.
   const int64_t U = (int64_t)gridDim.x / nchunks;
   const int64_t u = blockIdx.x % U;
-  const int64_t c = blockIdx.x / U;
+  const int64_t cr = blockIdx.x / U, nscan = nchunks - nlt;
+  const int64_t c = nlt > 0 ? (cr < nscan ? nlt + cr : cr - nscan) : cr;
   const int64_t b = u / Hkv, kvh = u % Hkv;
   const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
   const int64_t tbase = c * SCAN_TILE;
@@ -385,6 +420,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   if (!use_bits && !use_pl && ntw > 0) {
     load_half(0, 0);
     load_half(0, 1);
+  }
+  // a tile with bitmaps: its words of every head, loaded with the prologue's loads
+  uint32_t bword = 0u;
+  if (use_bits && tid < GM * 16) {
+    const int h = tid >> 4;
+    if (h < G) bword = sbits[(u * G + h) * bwords + c * 16 + (tid & 15)];
   }
 
   // ---- prologue: query codes (packed twice per word), queries, key mean.
@@ -439,6 +480,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   if (tid < GM) {
     hcnt[tid] = 0;
     mrun[tid] = -INFINITY;
+    lsum[tid] = 0.0f;
   }
   __syncthreads();
 
@@ -480,10 +522,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     uint32_t mlo = 0, mhi = 0;
     if (use_bits) {
       // the tile's sampled-key words of every head, as the bucket lookup wrote them
-      if (tid < GM * 16) {
-        const int h = tid >> 4, jj = tid & 15;
-        pw2[h][jj] = h < G ? sbits[(u * G + h) * bwords + c * 16 + jj] : 0u;
-      }
+      if (tid < GM * 16) pw2[tid >> 4][tid & 15] = bword;
       __syncthreads();
       const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
 #pragma unroll
@@ -731,6 +770,149 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;
 
   // ---- attention over the union list
+  if constexpr (std::is_same<T, __bf16>::value) {
+    // Matrix-core rounds of ATT_E entries (16x16x32 bf16 operations, fp32
+    // accumulation; heads padded to 16 columns):
+    //  (a) wave w gathers half of the rows of 16 entries: entries
+    //      16 (w & 1) + li, dims 64 (w >> 1) .. + 63, lane (qd, li) holding dims
+    //      32 s + 8 qd .. + 7 of its two 32-dim steps s -- the A-operand
+    //      layout -- so its half of S = K Q^T takes two operations; lanes also
+    //      sum |k - mu|^2 over their 16 dims (fp32) and stage the value rows
+    //      transposed ([dim][entry]) in LDS; the two halves meet in (b);
+    //  (b) one thread per (head, entry) forms the log-weight
+    //      s = q.k / sqrt(d) - ln P (or -inf where the head did not sample the
+    //      key), the head's new running maximum m (a 32-lane max), exp(s - m)
+    //      and the round's sum, and records m, the rescale factor and the
+    //      running normaliser;
+    //  (c) wave w accumulates the output dims 32 w .. 32 w + 31 of every head
+    //      as O = O * alpha + P V, with P split into two bf16 parts
+    //      (hi + lo, 16 significant bits) so the weights keep fp32-like
+    //      precision.
+    const int qd = lane >> 4, li = lane & 15;
+    f32x4 oacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};  // heads 4 qd + j, dim 16 (2 wave + b) + li
+    const __bf16 *Kb = (const __bf16 *)Kc + (u * cap + tbase) * D + 8 * qd;
+    const __bf16 *Vb = (const __bf16 *)Vc + (u * cap + tbase) * D + 8 * qd;
+    for (int e0 = 0; e0 < nu; e0 += ATT_E) {
+      const int ne = min(ATT_E, nu - e0);
+      {  // (a)
+        const int e = 16 * (wave & 1) + li, kh = wave >> 1;
+        const bool ok = e < ne;
+        const int64_t key = ok ? lkey[e0 + e] : 0;  // the tile's first key: a valid row, discarded
+        uint4 kr[2], vr[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
+          vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
+        }
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
+        float n2 = 0.0f;
+        const int hq = li < GM ? li : 0;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int d0 = 64 * kh + 32 * st + 8 * qd;
+          const bf16x8 kb = __builtin_bit_cast(bf16x8, kr[st]);
+          float mv[8], qv[8];
+          ld8<float>(msh + d0, mv);
+          ld8<float>(&qsh[hq][d0], qv);
+          bf16x8 qb;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float cj = (float)kb[j] - mv[j];
+            n2 += cj * cj;
+            qb[j] = li < G ? (__bf16)qv[j] : (__bf16)0.0f;  // exact: the queries are bf16
+          }
+          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, sacc, 0, 0, 0);
+        }
+        n2 += swz_xor<16>(n2);
+        n2 += __shfl_xor(n2, 32);
+        if (li < GM) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm.m.sdot[kh][li][16 * (wave & 1) + 4 * qd + j] = sacc[j];
+        }
+        if (qd == 0) sm.m.nrm[kh][e] = n2;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[st]);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sm.m.vT[64 * kh + 32 * st + 8 * qd + j][e] = ok ? vb[j] : (__bf16)0.0f;
+        }
+      }
+      __syncthreads();
+      if (tid < GM * ATT_E) {  // (b)
+        const int h = tid / ATT_E, e = tid % ATT_E;
+        float w = -INFINITY;
+        if (h < G && e < ne) {
+          const uint32_t mk = lmask[e0 + e];
+          if ((mk >> h) & 1u) {
+            const float dk = sm.m.sdot[0][h][e] + sm.m.sdot[1][h][e];
+            float lnP = 0.0f;
+            if (!(mk & FORCED)) {
+              const float den = qn_sh[h] * sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]);
+              const float cosv = den > 0.0f ? (dk - qmu_sh[h]) / den : 0.0f;
+              lnP = log_sampling_prob(cosv, K, L, cf);
+            }
+            w = dk * scale - lnP;
+          }
+        }
+        const float mr = xor32_max(w);  // within the 32 lanes of h
+        const float mo = mrun[h];
+        const float mn = fmaxf(mo, mr);
+        const float pe = mn > -INFINITY ? __expf(w - mn) : 0.0f;  // 0 for -inf
+        const float ps = xor32_sum(pe);
+        sm.m.p[h][e] = pe;
+        if (e == 0) {
+          const float alpha = mn > -INFINITY ? __expf(mo - mn) : 1.0f;  // 0 while mo = -inf
+          alpha_sh[h] = alpha;
+          mrun[h] = mn;
+          lsum[h] = lsum[h] * alpha + ps;
+        }
+      }
+      __syncthreads();
+      {  // (c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int h = 4 * qd + j;
+          const float a = h < GM ? alpha_sh[h < GM ? h : 0] : 1.0f;
+          oacc[0][j] *= a;
+          oacc[1][j] *= a;
+        }
+        float pv[8];
+        ld8<float>(&sm.m.p[li < GM ? li : 0][8 * qd], pv);
+        bf16x8 ph, pl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = li < GM ? pv[j] : 0.0f;
+          const __bf16 hi = (__bf16)x;
+          ph[j] = hi;
+          pl[j] = (__bf16)(x - (float)hi);
+        }
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          const bf16x8 vb = *(const bf16x8 *)&sm.m.vT[16 * (2 * wave + b2) + li][8 * qd];
+          oacc[b2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[b2], 0, 0, 0);
+          oacc[b2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[b2], 0, 0, 0);
+        }
+      }
+      if (e0 + ATT_E < nu) __syncthreads();  // the next round reuses the staging
+    }
+    float *rec0 = part + (u * nchunks + c) * G * PSTRIDE;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * qd + j;
+      if (h < G) {
+        rec0[h * PSTRIDE + 4 + 16 * (2 * wave) + li] = oacc[0][j];
+        rec0[h * PSTRIDE + 4 + 16 * (2 * wave + 1) + li] = oacc[1][j];
+      }
+    }
+    if (tid < G) {
+      float *rec = rec0 + tid * PSTRIDE;
+      rec[0] = mrun[tid];
+      rec[1] = lsum[tid];
+      rec[2] = __builtin_bit_cast(float, hcnt[tid]);
+      rec[3] = 0.0f;
+    }
+    return;
+  }
   constexpr int TPH = (256 / GM) < 128 ? (256 / GM) : 128;  // output threads per head
   constexpr int DPT = D / TPH;                              // dims per output thread
   const int oh = tid / TPH, od = (tid % TPH) * DPT;
