@@ -74,6 +74,17 @@ def lib():
         L.orc_decode_t.argtypes = [_f32p, _f32p, _f32p, _u16p, _f32p, _f32p, _vp, _int, _int, _int, _i64, _i64,
                                    _int, _int, _int, _int, _i64, _i64, _vp, _f32p, _f32p, _vp, _i32p]
         L.orc_decode_t.restype = None
+        L.orc_lift_radius.argtypes = [_f32p, _i64, _int, _i64, _f32p]
+        L.orc_lift_radius.restype = ctypes.c_float
+        L.orc_encode_lifted.argtypes = [_f32p, _i64, _int, _i64, _vp, _i64, _int, ctypes.c_float, _f32p, _int, _int,
+                                        _u16p, _i64, _i64, _vp]
+        L.orc_encode_lifted.restype = None
+        L.orc_attend_lt.argtypes = [_f32p, _f32p, _f32p, _i64, _int, _vp, ctypes.c_float, _int, _int, _int, _i32p,
+                                    _vp, _i64, _f64p, _f64p, _vp]
+        L.orc_attend_lt.restype = None
+        L.orc_decode_lt.argtypes = [_f32p, _f32p, _f32p, _u16p, _f32p, _vp, _f32p, _vp, _int, _int, _int, _i64, _i64,
+                                    _int, _int, _int, _int, _i64, _i64, _vp, _f32p, _f32p, _vp, _i32p]
+        L.orc_decode_lt.restype = None
         _lib = L
     return _lib
 
@@ -133,6 +144,55 @@ def encode(rows, W, K: int, L: int, mu=None, with_margin: bool = False):
     return (codes, margin) if with_margin else codes
 
 
+def lift_radius(keys, mu) -> float:
+    """Lift radius of Section 4.2, Equation 8: the largest |bf16(k - mu)| (fp64 sums, one fp32 rounding)."""
+    keys = _f32(keys)
+    n, d = keys.shape
+    return float(lib().orc_lift_radius(keys, n, d, d, _f32(mu)))
+
+
+def encode_lifted(rows, W, K: int, L: int, mu=None, R: float = 0.0, lift: bool = True, with_margin: bool = False):
+    """SimHash codes of lifted rows (Section 4.2, Equation 8): ``W`` is
+    ``[d + 1][K*L]``; keys (``lift``) get the extra coordinate
+    bf16(sqrt(R^2 - |x|^2)), queries (``lift=False``) get 0.  ``mu`` is one
+    mean ``[d]`` or one per row ``[nrows][d]``.  With ``with_margin`` also the
+    per-column margins ``[nrows][K*L]``."""
+    rows = _f32(rows)
+    if rows.ndim == 1:
+        rows = rows[None]
+    nrows, d = rows.shape
+    W = _f32(W)
+    assert W.shape == (d + 1, K * L)
+    codes = np.zeros((nrows, L), np.uint16)
+    margin = np.zeros((nrows, K * L), np.float32) if with_margin else None
+    mu_a = None if mu is None else _f32(mu)
+    mu_stride = d if (mu_a is not None and mu_a.ndim == 2) else 0
+    lib().orc_encode_lifted(rows, nrows, d, d, _ptr(mu_a), mu_stride, int(bool(lift)), float(R), W, K, L, codes, L,
+                            1, _ptr(margin))
+    return (codes, margin) if with_margin else codes
+
+
+def build_codes_lifted(keys, n: int, W, K: int, L: int, with_margin: bool = False):
+    """Lifted code-store build of one layer: per unit the key mean, the lift
+    radius and the codes of the lifted centred keys.  ``keys`` ``[U][cap][d]``,
+    ``W`` ``[d + 1][K*L]``.  Returns kmean ``[U][d]``, rlift ``[U]``, codes
+    ``[U][L][cap]`` and, with ``with_margin``, margins ``[U][n][K*L]``."""
+    keys = _f32(keys)
+    U, cap, d = keys.shape
+    kmean = np.zeros((U, d), np.float32)
+    rlift = np.zeros(U, np.float32)
+    codes = np.zeros((U, L, cap), np.uint16)
+    margin = np.zeros((U, n, K * L), np.float32) if with_margin else None
+    for u in range(U):
+        kmean[u] = key_mean(keys[u, :n])
+        rlift[u] = lift_radius(keys[u, :n], kmean[u])
+        c, m = encode_lifted(keys[u, :n], W, K, L, mu=kmean[u], R=rlift[u], with_margin=True)
+        codes[u][:, :n] = c.T
+        if with_margin:
+            margin[u] = m
+    return (kmean, rlift, codes, margin) if with_margin else (kmean, rlift, codes)
+
+
 def table_collision_prob(cos_qk: float, K: int) -> float:
     """(1 - theta/pi)^K: one table's collision probability (Section 2.2)."""
     return lib().orc_table_collision_prob(float(cos_qk), int(K))
@@ -163,10 +223,13 @@ def scan(codes_tn, qcode, n_static_head: int = 0, n_static_tail: int = 0, T: int
     return idx[:cnt].copy(), forced[:cnt].astype(bool)
 
 
-def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool = False, T: int = 2):
+def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool = False, T: int = 2,
+           rlift: float = 0.0):
     """Estimator of one head over its sampled set (Equations 9 and 11).
 
-    Returns ``(out[d] fp64, lse)`` (and the per-sample log-weights).
+    Returns ``(out[d] fp64, lse)`` (and the per-sample log-weights).  With
+    ``rlift`` > 0 the keys were hashed lifted (Equation 8) and the sampling
+    angle uses the lifted key's norm ``rlift``.
     """
     q, keys, vals = _f32(q), _f32(keys), _f32(vals)
     n, d = keys.shape
@@ -177,8 +240,8 @@ def attend(q, keys, vals, idx, forced, K: int, L: int, mu=None, with_logw: bool 
     lse = np.zeros(1, np.float64)
     logw = np.zeros(max(cnt, 1), np.float64) if with_logw else None
     mu_a = None if mu is None else _f32(mu)
-    lib().orc_attend_t(q, keys, vals, d, d, _ptr(mu_a), K, L, T, idx if cnt else np.zeros(1, np.int32),
-                       _ptr(forced_a), cnt, out, lse, _ptr(logw))
+    lib().orc_attend_lt(q, keys, vals, d, d, _ptr(mu_a), float(rlift), K, L, T,
+                        idx if cnt else np.zeros(1, np.int32), _ptr(forced_a), cnt, out, lse, _ptr(logw))
     if with_logw:
         return out, float(lse[0]), logw[:cnt]
     return out, float(lse[0])
@@ -201,12 +264,14 @@ def build_codes(keys, n: int, W, K: int, L: int, with_margin: bool = False):
 
 
 def decode(q, keys, vals, codes, kmean, W, K: int, L: int, n: int, qcodes=None, n_static_head: int = 0,
-           n_static_tail: int = 0, want_idx: bool = False, T: int = 2):
+           n_static_tail: int = 0, want_idx: bool = False, T: int = 2, rlift=None):
     """Decode of one layer (Algorithm 1 for every query head; a key is sampled
     when it collides in at least T tables, the pages' T = 2).
 
     Shapes: q ``[B][Hq][d]``, keys/vals ``[B][Hkv][cap][d]``, codes
     ``[B][Hkv][L][cap]``, kmean ``[B][Hkv][d]``, qcodes ``[B][Hq][L]`` or None.
+    ``rlift`` (``[B][Hkv]``, optional) gives the units' lift radii when the
+    keys were hashed lifted (Equation 8).
     Returns a dict with out, lse, count, qcodes and (optionally) idx lists.
     """
     q, keys, vals = _f32(q), _f32(keys), _f32(vals)
@@ -221,8 +286,9 @@ def decode(q, keys, vals, codes, kmean, W, K: int, L: int, n: int, qcodes=None, 
     lse = np.zeros((B, Hq), np.float32)
     count = np.zeros((B, Hq), np.int32)
     idx = np.full((B, Hq, cap), -1, np.int32) if want_idx else None
-    lib().orc_decode_t(q, keys, vals, codes, kmean, W, _ptr(qc_in), B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
-                       n_static_tail, _ptr(qc_out), out, lse, _ptr(idx), count)
+    rl = None if rlift is None else _f32(np.asarray(rlift).reshape(B, Hkv))
+    lib().orc_decode_lt(q, keys, vals, codes, kmean, _ptr(rl), W, _ptr(qc_in), B, Hq, Hkv, n, cap, d, K, L, T,
+                        n_static_head, n_static_tail, _ptr(qc_out), out, lse, _ptr(idx), count)
     res = {"out": out, "lse": lse, "count": count, "qcodes": qc_out}
     if want_idx:
         res["idx"] = [[idx[b, h, :count[b, h]].copy() for h in range(Hq)] for b in range(B)]

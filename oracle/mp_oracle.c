@@ -28,7 +28,14 @@
  *     which is what Equation 10's closed form equals;
  *   - forced ("static") keys take probability 1 (authors' reply on sink
  *     tokens, page 3);
- *   - an empty sampled set gives out = 0 and lse = -inf.
+ *   - an empty sampled set gives out = 0 and lse = -inf;
+ *   - the optional lift of Section 4.2, Equation 8 (not used by the authors,
+ *     Section 5.1) is applied to the vector that is hashed, the centred key
+ *     x = bf16(k - mu): with r the largest |x| of the build keys (fp64 sums,
+ *     rounded once to fp32 and frozen with mu), the lifted key is
+ *     [x, bf16(fp32(sqrt(max(0, r^2 - |x|^2))))] and the lifted query
+ *     [bf16(q), 0]; the sampling angle is that between [q, 0] and the lifted
+ *     key, whose norm is r, so cos = q.(k - mu) / (|q| r).
  */
 #include <math.h>
 #include <omp.h>
@@ -142,6 +149,91 @@ void orc_encode(const float *rows, int64_t nrows, int d, int64_t row_stride, con
 }
 
 /* ---------------------------------------------------------------------------
+ * Lift radius of Section 4.2, Equation 8 (r = max_i |k_i|), taken over the
+ * vectors that are hashed, x_i = bf16(fp32(k_i) - mu): |x_i|^2 summed in
+ * fp64, the largest of them, its square root rounded once to fp32.
+ * ------------------------------------------------------------------------- */
+float orc_lift_radius(const float *rows, int64_t n, int d, int64_t row_stride, const float *mu)
+{
+    double best = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) {
+            const double x = (double)orc_bf16(rows[i * row_stride + t] - mu[t]);
+            s += x * x;
+        }
+        if (s > best) best = s;
+    }
+    return (float)sqrt(best);
+}
+
+/* ---------------------------------------------------------------------------
+ * SimHash codes of lifted keys (Section 4.2, Equation 8, then Section 2.2):
+ * row r becomes x = bf16(fp32(row - mu_r)) (mu_r = mu + r * mu_stride, or no
+ * centring when mu is NULL) extended by the coordinate
+ * e = bf16(fp32(sqrt(max(0, R^2 - |x|^2)))) (fp64 inside the root; R the
+ * lift radius), so that every lifted key has norm R up to rounding.  A row
+ * with lift = 0 is a lifted query: its extra coordinate is 0.  W is
+ * (d + 1) x (K*L); z_j = sum_t x_t bf16(W[t][j]) + e bf16(W[d][j]) exactly
+ * (fp64); bit_j = (z_j > 0).  margin as in orc_encode, over the d + 1
+ * coordinates.
+ * ------------------------------------------------------------------------- */
+void orc_encode_lifted(const float *rows, int64_t nrows, int d, int64_t row_stride, const float *mu,
+                       int64_t mu_stride, int lift, float R, const float *W, int K, int L, uint16_t *codes,
+                       int64_t code_row_stride, int64_t code_table_stride, float *margin)
+{
+    const int ncol = K * L, d1 = d + 1;
+    double *wb = (double *)malloc(sizeof(double) * (size_t)d1 * (size_t)(ncol > 0 ? ncol : 1));
+    double *wnorm = (double *)malloc(sizeof(double) * (size_t)(ncol > 0 ? ncol : 1));
+    for (int j = 0; j < ncol; ++j) {
+        double s = 0.0;
+        for (int t = 0; t < d1; ++t) {
+            double w = (double)orc_bf16(W[(int64_t)t * ncol + j]);
+            wb[(int64_t)j * d1 + t] = w;
+            s += w * w;
+        }
+        wnorm[j] = sqrt(s);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        double *x = (double *)malloc(sizeof(double) * (size_t)d1);
+        double xx = 0.0;
+        for (int t = 0; t < d; ++t) {
+            float k = rows[r * row_stride + t];
+            float c = mu ? k - mu[r * mu_stride + t] : k; /* fp32 subtraction */
+            x[t] = (double)orc_bf16(c);
+            xx += x[t] * x[t];
+        }
+        double e = 0.0;
+        if (lift) {
+            double rem = (double)R * (double)R - xx;
+            e = (double)orc_bf16((float)sqrt(rem > 0.0 ? rem : 0.0));
+        }
+        x[d] = e;
+        const double xn = sqrt(xx + e * e);
+        for (int l = 0; l < L; ++l) {
+            unsigned code = 0;
+            for (int b = 0; b < K; ++b) {
+                const int j = l * K + b;
+                double z = 0.0;
+                for (int t = 0; t < d1; ++t)
+                    z += x[t] * wb[(int64_t)j * d1 + t];
+                if (z > 0.0)
+                    code |= 1u << b;
+                if (margin) {
+                    const double den = xn * wnorm[j];
+                    margin[r * ncol + j] = den > 0.0 ? (float)(fabs(z) / den) : INFINITY;
+                }
+            }
+            codes[r * code_row_stride + (int64_t)l * code_table_stride] = (uint16_t)code;
+        }
+        free(x);
+    }
+    free(wb);
+    free(wnorm);
+}
+
+/* ---------------------------------------------------------------------------
  * Per-table collision probability of SimHash (Section 2.2): one random
  * hyperplane separates two vectors at angle theta with probability
  * theta/pi, so K independent ones all agree with probability
@@ -227,9 +319,23 @@ int64_t orc_scan(const uint16_t *codes, int64_t table_stride, int64_t n, int L, 
  * An empty set gives out = 0, lse = -inf.  mu may be NULL (no centring).
  * logw (nullable, [cnt]) receives s_i - lnP_i.
  * ------------------------------------------------------------------------- */
+void orc_attend_lt(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
+                   const float *mu, float rlift, int K, int L, int T, const int32_t *idx, const uint8_t *forced,
+                   int64_t cnt, double *out, double *lse, double *logw);
+
 void orc_attend_t(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
                   const float *mu, int K, int L, int T, const int32_t *idx, const uint8_t *forced, int64_t cnt,
                   double *out, double *lse, double *logw)
+{
+    orc_attend_lt(q, keys, vals, row_stride, d, mu, 0.0f, K, L, T, idx, forced, cnt, out, lse, logw);
+}
+
+/* As orc_attend_t; with rlift > 0 the keys were hashed lifted (Equation 8)
+ * with radius rlift, and the sampling angle is that between [q, 0] and the
+ * lifted key (norm rlift): cos = q.(k - mu) / (|q| rlift). */
+void orc_attend_lt(const float *q, const float *keys, const float *vals, int64_t row_stride, int d,
+                   const float *mu, float rlift, int K, int L, int T, const int32_t *idx, const uint8_t *forced,
+                   int64_t cnt, double *out, double *lse, double *logw)
 {
     for (int t = 0; t < d; ++t)
         out[t] = 0.0;
@@ -254,7 +360,7 @@ void orc_attend_t(const float *q, const float *keys, const float *vals, int64_t 
             qc += (double)q[t] * ct;
             cn += ct * ct;
         }
-        cn = sqrt(cn);
+        cn = rlift > 0.0f ? (double)rlift : sqrt(cn);
         double lnP = 0.0;
         if (!(forced && forced[s])) {
             double cosv = (qn > 0.0 && cn > 0.0) ? qc / (qn * cn) : 0.0;
@@ -309,10 +415,29 @@ void orc_build(const float *keys, int64_t U, int64_t n, int64_t cap, int d, cons
  *   kmean [B][Hkv][d]; qcodes [B][Hq][L] (NULL: encode q here, uncentred);
  *   out [B][Hq][d]; lse [B][Hq]; idx [B][Hq][cap] (nullable); count [B][Hq].
  * ------------------------------------------------------------------------- */
+void orc_decode_lt(const float *q, const float *keys, const float *vals, const uint16_t *codes,
+                   const float *kmean, const float *rlift, const float *W, const uint16_t *qcodes_in, int B, int Hq,
+                   int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head,
+                   int64_t n_static_tail, uint16_t *qcodes_out, float *out, float *lse, int32_t *idx,
+                   int32_t *count);
+
 void orc_decode_t(const float *q, const float *keys, const float *vals, const uint16_t *codes,
                   const float *kmean, const float *W, const uint16_t *qcodes_in, int B, int Hq, int Hkv,
                   int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
                   uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count)
+{
+    orc_decode_lt(q, keys, vals, codes, kmean, NULL, W, qcodes_in, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
+                  n_static_tail, qcodes_out, out, lse, idx, count);
+}
+
+/* As orc_decode_t; rlift (nullable, [B][Hkv]) gives each unit's lift radius
+ * when its keys were hashed lifted (Equation 8).  Queries are encoded (when
+ * qcodes_in is NULL) with the first d rows of W: their extra coordinate is 0. */
+void orc_decode_lt(const float *q, const float *keys, const float *vals, const uint16_t *codes,
+                   const float *kmean, const float *rlift, const float *W, const uint16_t *qcodes_in, int B, int Hq,
+                   int Hkv, int64_t n, int64_t cap, int d, int K, int L, int T, int64_t n_static_head,
+                   int64_t n_static_tail, uint16_t *qcodes_out, float *out, float *lse, int32_t *idx,
+                   int32_t *count)
 {
     const int G = Hq / Hkv;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -332,8 +457,8 @@ void orc_decode_t(const float *q, const float *keys, const float *vals, const ui
                                  list, forced);
         double *o = (double *)malloc(sizeof(double) * (size_t)d);
         double l;
-        orc_attend_t(qh, keys + u * cap * d, vals + u * cap * d, d, d, kmean + u * d, K, L, T, list, forced, cnt,
-                     o, &l, NULL);
+        orc_attend_lt(qh, keys + u * cap * d, vals + u * cap * d, d, d, kmean + u * d, rlift ? rlift[u] : 0.0f, K,
+                      L, T, list, forced, cnt, o, &l, NULL);
         for (int t = 0; t < d; ++t)
             out[bh * d + t] = (float)o[t];
         if (lse) lse[bh] = (float)l;

@@ -27,12 +27,19 @@ def mean_f32(keys):
     return [float(np.float32(math.fsum(float(k[t]) for k in keys) / len(keys))) for t in range(d)]
 
 
-def code_of(vec, mu, W, K, L):
+def code_of(vec, mu, W, K, L, lift_r=None):
+    """Code bits of one vector; with ``lift_r`` (Equation 8) the vector gets the
+    extra coordinate sqrt(r^2 - |x|^2) (rounded to fp32, then bf16) and W has
+    d + 1 rows; a lifted query passes lift_r = 0.0 (extra coordinate 0)."""
     d = len(vec)
     if mu is None:
         x = [bf16(float(np.float32(vec[t]))) for t in range(d)]
     else:
         x = [bf16(float(np.float32(vec[t]) - np.float32(mu[t]))) for t in range(d)]
+    if lift_r is not None:
+        rem = float(lift_r) ** 2 - math.fsum(v * v for v in x) if lift_r else 0.0
+        x = x + [bf16(float(np.float32(math.sqrt(rem)))) if rem > 0 else 0.0]
+        d += 1
     codes = []
     for l in range(L):
         c = 0
@@ -62,13 +69,25 @@ def prob_at_least_two(p: float, L: int) -> float:
     return prob_at_least(p, L, 2)
 
 
-def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0, T=2):
+def lift_radius(keys, mu):
+    """Largest |bf16(k - mu)| over the keys, rounded to fp32 (Equation 8's r)."""
+    best = 0.0
+    for k in keys:
+        x = [bf16(float(np.float32(k[t]) - np.float32(mu[t]))) for t in range(len(k))]
+        best = max(best, math.fsum(v * v for v in x))
+    return float(np.float32(math.sqrt(best)))
+
+
+def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0, T=2, lift=False):
     """Returns (sampled index list, out vector, lse) for one query head; a key
-    is sampled when it collides in at least T tables."""
+    is sampled when it collides in at least T tables.  With ``lift`` the keys
+    are hashed lifted (Equation 8; W has d + 1 rows) and the sampling angle is
+    taken against the lifted key, whose norm is r."""
     n, d = len(keys), len(q)
     mu = mean_f32(keys)
-    kc = [code_of(k, mu, W, K, L) for k in keys]
-    qc = code_of(q, None, W, K, L)
+    R = lift_radius(keys, mu) if lift else None
+    kc = [code_of(k, mu, W, K, L, R) for k in keys]
+    qc = code_of(q, None, W, K, L, 0.0 if lift else None)
     S, forced = [], []
     for i in range(n):
         f = i < n_static_head or i >= n - n_static_tail
@@ -82,7 +101,7 @@ def decode_head(q, keys, vals, W, K, L, n_static_head=0, n_static_tail=0, T=2):
     for i, f in zip(S, forced):
         k = [float(a) for a in keys[i]]
         c = [k[t] - mu[t] for t in range(d)]
-        cn = math.sqrt(sum(a * a for a in c))
+        cn = R if lift else math.sqrt(sum(a * a for a in c))
         if f:
             u = 1.0
         else:

@@ -486,3 +486,107 @@ def test_decode_composite_matches_per_head_steps():
             out, lse = oracle.attend(q[b, h], keys[b, h // 2, :n], vals[b, h // 2, :n], idx, forced, K, L, mu)
             assert np.max(np.abs(res["out"][b, h] - out)) < 1e-6
             assert abs(res["lse"][b, h] - lse) < 1e-5
+
+
+# --------------------------------------------------------------------------- lift (Section 4.2, Equation 8)
+def _lift_inputs(seed, n=300, d=16):
+    rng = np.random.default_rng(seed)
+    # keys of very different norms, so that angle and inner product disagree
+    keys = (rng.standard_normal((n, d)) * rng.uniform(0.2, 3.0, (n, 1)) + 0.5).astype(np.float32)
+    q = (rng.standard_normal(d) - 0.5).astype(np.float32)
+    return rng, keys, q
+
+
+def test_lifted_query_codes_are_the_unlifted_codes():
+    """The lifted query [q, 0] projects exactly as q on the first d rows of W."""
+    rng, keys, q = _lift_inputs(30)
+    K, L, d = 4, 9, keys.shape[1]
+    W = rng.standard_normal((d + 1, K * L)).astype(np.float32)
+    a = oracle.encode_lifted(keys, W, K, L, lift=False)
+    b = oracle.encode(keys, W[:d], K, L)
+    assert np.array_equal(a, b)
+
+
+def test_lifted_probability_is_monotone_in_the_inner_product():
+    """Equation 8 turns the inner product into a cosine: with the lift, the
+    sampling probability of a key is a function of q.(k - mu) alone (the
+    lifted key's norm is the same r for every key), so ln P rises with
+    q.(k - mu); without the lift it follows the angle, which the spread of key
+    norms makes disagree with the inner product."""
+    rng, keys, q = _lift_inputs(31)
+    n, d = keys.shape
+    K, L = 6, 20
+    mu = oracle.key_mean(keys)
+    R = oracle.lift_radius(keys, mu)
+    idx = np.arange(n, dtype=np.int32)
+    vals = np.zeros_like(keys)
+    s = keys.astype(np.float64) @ q.astype(np.float64) / math.sqrt(d)
+    ip = (keys.astype(np.float64) - mu.astype(np.float64)) @ q.astype(np.float64)
+    order = np.argsort(ip)
+    _, _, lw = oracle.attend(q, keys, vals, idx, None, K, L, mu, with_logw=True, rlift=R)
+    lnP = s - lw
+    assert np.all(np.diff(lnP[order]) >= -1e-9)
+    _, _, lw0 = oracle.attend(q, keys, vals, idx, None, K, L, mu, with_logw=True)
+    assert np.any(np.diff((s - lw0)[order]) < -1e-3)  # the unlifted probability is not monotone in q.(k - mu)
+
+
+def test_lift_radius_is_the_largest_centred_norm():
+    """r = max |x_i| (Equation 8) over the hashed vectors x = bf16(k - mu):
+    the key of largest centred norm gets the extra coordinate 0, every
+    other key a positive one; keys equal to the mean give r = 0."""
+    rng, keys, q = _lift_inputs(32)
+    mu = oracle.key_mean(keys)
+    R = oracle.lift_radius(keys, mu)
+    x = oracle.bf16((keys - mu).astype(np.float32)).astype(np.float64)
+    norms = np.sqrt((x * x).sum(1))
+    assert R == np.float32(norms.max())
+    flat = np.tile(mu, (5, 1))
+    assert oracle.lift_radius(flat, mu) == 0.0
+
+
+@pytest.mark.slow
+def test_lifted_inclusion_frequency_matches_sampling_probability():
+    """Monte-Carlo over projections W ~ N(0, 1) of d + 1 rows: how often each
+    lifted key collides with the lifted query in at least two of L tables
+    equals the oracle's sampling probability for it (the angle between
+    [q, 0] and the lifted key), within 4 binomial standard deviations."""
+    rng, keys, q = _lift_inputs(33, n=8, d=16)
+    n, d = keys.shape
+    K, L, draws = 3, 6, 6000
+    mu = oracle.key_mean(keys)
+    R = oracle.lift_radius(keys, mu)
+    hits = np.zeros(n)
+    for _ in range(draws):
+        W = rng.standard_normal((d + 1, K * L)).astype(np.float32)
+        kc = oracle.encode_lifted(keys, W, K, L, mu=mu, R=R)
+        qc = oracle.encode_lifted(q, W, K, L, lift=False)[0]
+        hits += ((kc == qc[None, :]).sum(1) >= 2)
+    freq = hits / draws
+    idx = np.arange(n, dtype=np.int32)
+    s = keys.astype(np.float64) @ q.astype(np.float64) / math.sqrt(d)
+    _, _, lw = oracle.attend(q, keys, np.zeros_like(keys), idx, None, K, L, mu, with_logw=True, rlift=R)
+    P = np.exp(s - lw)
+    sd = np.sqrt(P * (1 - P) / draws)
+    assert np.all(np.abs(freq - P) <= 4 * sd + 2e-3), (freq, P)
+
+
+@pytest.mark.parametrize("seed,d,n,K,L,T", [(40, 4, 12, 2, 3, 2), (41, 8, 16, 3, 4, 2), (42, 8, 16, 1, 5, 1)])
+def test_lifted_decode_matches_independent_brute_force(seed, d, n, K, L, T):
+    """Tiny inputs, keys hashed lifted: the oracle and the independent
+    pure-Python statement agree exactly on sets and to 1e-12 on outputs."""
+    rng = np.random.default_rng(seed)
+    keys = (rng.standard_normal((n, d)) * rng.uniform(0.3, 2.0, (n, 1)) + 0.7).astype(np.float32)
+    vals = rng.standard_normal((n, d)).astype(np.float32)
+    q = (rng.standard_normal(d) - 0.7).astype(np.float32)
+    W = rng.standard_normal((d + 1, K * L)).astype(np.float32)
+    S, bout, blse = brute.decode_head(q.tolist(), keys.tolist(), vals.tolist(), W.tolist(), K, L, T=T, lift=True)
+    mu = oracle.key_mean(keys)
+    R = oracle.lift_radius(keys, mu)
+    kc = oracle.encode_lifted(keys, W, K, L, mu=mu, R=R)
+    qc = oracle.encode_lifted(q, W, K, L, lift=False)[0]
+    idx, forced = oracle.scan(kc.T, qc, T=T)
+    assert idx.tolist() == S
+    out, lse = oracle.attend(q, keys, vals, idx, forced, K, L, mu, T=T, rlift=R)
+    assert np.max(np.abs(out - np.array(bout))) < 1e-12
+    if S:
+        assert abs(lse - blse) < 1e-9
