@@ -131,6 +131,41 @@ int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_d
               int64_t cap, int d, const float *kmean, const void *Wp, int K, int L, uint16_t *codes, void *stream);
 
 /*
+ * The lift of Section 4.2, Equation 8, as an option (the pages describe it
+ * and do not use it, Section 5.1): r = max_i |x_i|, keys [x_i,
+ * sqrt(r^2 - |x_i|^2)], queries [q, 0], so that the angle the hash preserves
+ * follows the inner product.  It applies to the vectors that are hashed,
+ * x_i = bf16(fp32(K[u][i]) - kmean[u]); r (rlift[u], fp32) is the largest
+ * |x_i| of the build keys (fp64 sums) and is frozen with the mean; a key's
+ * extra coordinate is e = bf16(fp32(sqrt(max(0, r^2 - |x|^2)))) (an appended
+ * key longer than r gets 0), and bit j = (x . bf16(W[:d, j]) +
+ * e bf16(W[d][j]) > 0).
+ *   mp_proj_pack_lift: W is [d + 1][K*L] float32; Wp receives
+ *     mp_proj_bytes_lift(d, K, L) bytes: the packed first d rows (as
+ *     mp_proj_pack, so Wp also serves the query encoders) followed by the
+ *     extra row.
+ *   mp_build_codes_lift: as mp_build_codes, plus rlift out [U] float32.
+ *   mp_append_lift: as mp_append, with the frozen rlift [U].
+ *   mp_decode_attn_lift: as mp_decode_attn for keys hashed lifted; the
+ *     sampling angle is the one between [q, 0] and the lifted key, whose
+ *     norm is r: cos = q.(K_i - kmean) / (|q| rlift[u]) (rlift [B*Hkv]).
+ * K >= 1 (MP_ERR_UNSUPPORTED otherwise); other errors as the unlifted calls.
+ */
+size_t mp_proj_bytes_lift(int d, int K, int L);
+int mp_proj_pack_lift(const float *W, int d, int K, int L, void *Wp, void *stream);
+int mp_build_codes_lift(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, int d, const void *Wp, int K,
+                        int L, float *kmean, float *rlift, uint16_t *codes, void *ws, size_t ws_bytes, void *stream);
+int mp_append_lift(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_dtype, int64_t U, int64_t n,
+                   int64_t cap, int d, const float *kmean, const float *rlift, const void *Wp, int K, int L,
+                   uint16_t *codes, void *stream);
+int mp_decode_attn_lift(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                        const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                        const float *kmean, const float *rlift, const void *Wp, int B, int Hq, int Hkv, int64_t n,
+                        int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                        const uint16_t *qcodes_in, uint16_t *qcodes_out, float *out, float *lse, int32_t *idx,
+                        int32_t *count, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Bit-plane index of the code store: the same codes, packed as K bit planes
  * per table (K bits per key and table instead of 16), so the collision scan
  * reads K/16 of the bytes.  Layout [U][ceil(cap/512)][K][L][16] uint32: word

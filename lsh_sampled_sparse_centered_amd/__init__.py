@@ -40,6 +40,15 @@ _SIGS = {
     "mp_decode_ws_bytes": ([_c_int, _c_int, _c_int, _c_i64, _c_int, _c_int], _c_sz),
     "mp_planes_bytes": ([_c_i64, _c_i64, _c_int, _c_int], _c_sz),
     "mp_build_planes": ([_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp], _c_int),
+    "mp_proj_bytes_lift": ([_c_int, _c_int, _c_int], _c_sz),
+    "mp_proj_pack_lift": ([_vp, _c_int, _c_int, _c_int, _vp, _vp], _c_int),
+    "mp_build_codes_lift": ([_vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                             _c_sz, _vp], _c_int),
+    "mp_append_lift": ([_vp, _vp, _vp, _vp, _c_int, _c_i64, _c_i64, _c_i64, _c_int, _vp, _vp, _vp, _c_int, _c_int,
+                        _vp, _vp], _c_int),
+    "mp_decode_attn_lift": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _vp, _c_int, _c_int,
+                             _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _c_sz, _vp], _c_int),
     "mp_buckets_bytes": ([_c_i64, _c_i64, _c_int, _c_int], _c_sz),
     "mp_build_buckets": ([_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_int, _c_int, _vp, _c_sz, _vp], _c_int),
     "mp_decode_attn": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int, _c_i64,
@@ -202,6 +211,49 @@ def mp_encode_queries(q: torch.Tensor, Wp: torch.Tensor, K: int, L: int, qcodes:
     return qcodes
 
 
+# ----------------------------------------------------------------------------- lift (Equation 8)
+def mp_proj_bytes_lift(d: int, K: int, L: int) -> int:
+    return lib().mp_proj_bytes_lift(d, K, L)
+
+
+def mp_proj_pack_lift(W: torch.Tensor, K: int, L: int, Wp: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Pack W[d + 1][K*L] fp32 (the lifted projections); returns the uint8 buffer."""
+    d = W.shape[0] - 1
+    _need(W, torch.float32, (d + 1, K * L), "W")
+    nb = mp_proj_bytes_lift(d, K, L)
+    if nb == 0:
+        raise MPError("mp_proj_bytes_lift", -2)
+    if Wp is None:
+        Wp = torch.empty(nb, dtype=torch.uint8, device=W.device)
+    _check("mp_proj_pack_lift", lib().mp_proj_pack_lift(_p(W), d, K, L, _p(Wp), _stream(stream)))
+    return Wp
+
+
+def mp_build_codes_lift(Kc: torch.Tensor, n: int, Wp: torch.Tensor, K: int, L: int, stream=None):
+    """Key means, lift radii and codes of the lifted centred keys; returns (kmean, rlift, codes)."""
+    U, cap, d = Kc.shape
+    kmean = torch.empty(U, d, dtype=torch.float32, device=Kc.device)
+    rlift = torch.empty(U, dtype=torch.float32, device=Kc.device)
+    codes = torch.zeros(U, L, cap, dtype=torch.uint16, device=Kc.device)
+    nb = mp_build_ws_bytes(U, max(n, 1), d)
+    ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=Kc.device)
+    _check("mp_build_codes_lift", lib().mp_build_codes_lift(_p(Kc), _kv_dtype(Kc), U, n, cap, d, _p(Wp), K, L,
+                                                            _p(kmean), _p(rlift), _p(codes), _p(ws), ws.numel(),
+                                                            _stream(stream)))
+    return kmean, rlift, codes
+
+
+def mp_append_lift(k_new, v_new, Kc, Vc, n: int, kmean, rlift, Wp, K: int, L: int, codes, stream=None) -> None:
+    """Write row n of the caches and its lifted codes (frozen mean and radius)."""
+    U, cap, d = Kc.shape
+    _need(k_new, Kc.dtype, (U, d), "k_new")
+    _need(v_new, Kc.dtype, (U, d), "v_new")
+    _need(rlift, torch.float32, (U,), "rlift")
+    _need(codes, torch.uint16, (U, L, cap), "codes")
+    _check("mp_append_lift", lib().mp_append_lift(_p(k_new), _p(v_new), _p(Kc), _p(Vc), _kv_dtype(Kc), U, n, cap, d,
+                                                  _p(kmean), _p(rlift), _p(Wp), K, L, _p(codes), _stream(stream)))
+
+
 def mp_planes_bytes(U: int, cap: int, K: int, L: int) -> int:
     return lib().mp_planes_bytes(U, cap, K, L)
 
@@ -318,6 +370,35 @@ def mp_decode_attn(q: torch.Tensor, Kc: torch.Tensor, Vc: torch.Tensor, codes: t
                               d, K, L, T, n_static_head, n_static_tail, _p(qcodes_in), _p(qcodes_out), _p(out), _p(lse),
                               _p(idx), _p(count), _p(ws), ws.numel(), _stream(stream))
     _check("mp_decode_attn", st)
+    return out
+
+
+def mp_decode_attn_lift(q, Kc, Vc, codes, kmean, rlift, Wp, Hkv: int, n: int, K: int, qcodes_in=None, out=None,
+                        lse=None, idx=None, count=None, ws=None, stream=None, T: int = 2, n_static_head: int = 0,
+                        n_static_tail: int = 0, buckets=None, n_buckets: int = 0, planes=None, n_planes: int = 0):
+    """mp_decode_attn for keys hashed lifted (Equation 8), with the units' radii ``rlift`` [B*Hkv]."""
+    B, Hq, d, U, cap, L = _decode_shapes(q, Kc, Vc, codes, kmean, Hkv)
+    _need(rlift, torch.float32, (U,), "rlift")
+    dev = q.device
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=dev)
+    _need(out, torch.float32, (B, Hq, d), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (B, Hq), "lse")
+    if count is not None:
+        _need(count, torch.int32, (B, Hq), "count")
+    if idx is not None:
+        _need(idx, torch.int32, (B, Hq, cap), "idx")
+    if qcodes_in is not None:
+        _need(qcodes_in, torch.uint16, (B, Hq, L), "qcodes_in")
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, cap, L, dev)
+    _planes_ok(planes, codes, K, buckets)
+    st = lib().mp_decode_attn_lift(_p(q), _p(Kc), _p(Vc), _kv_dtype(Kc), _p(codes), _p(planes), n_planes,
+                                   _p(buckets), n_buckets, _p(kmean), _p(rlift), _p(Wp), B, Hq, Hkv, n, cap, d, K, L,
+                                   T, n_static_head, n_static_tail, _p(qcodes_in), None, _p(out), _p(lse), _p(idx),
+                                   _p(count), _p(ws), ws.numel(), _stream(stream))
+    _check("mp_decode_attn_lift", st)
     return out
 
 

@@ -114,6 +114,68 @@ int mp_append(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_d
   return hip_status(e);
 }
 
+size_t mp_proj_bytes_lift(int d, int K, int L) {
+  const size_t base = mp_proj_bytes(d, K, L);
+  if (base == 0 || K < 1) return 0;
+  return base + (size_t)enc_ntiles(K, L) * 32 * sizeof(uint16_t);
+}
+
+int mp_proj_pack_lift(const float *W, int d, int K, int L, void *Wp, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if (K < 1) return MP_ERR_UNSUPPORTED;  // the lift needs projections
+  if (!W || !Wp) return MP_ERR_ARG;
+  if (!all_a16(Wp)) return MP_ERR_ARG;
+  hipStream_t s = as_stream(stream);
+  if (launch_proj_pack(W, K, L, Wp, s) != hipSuccess) return MP_ERR_HIP;
+  return hip_status(launch_proj_pack_lift(W, K, L, (uint16_t *)((char *)Wp + mp_proj_bytes(d, K, L)), s));
+}
+
+int mp_build_codes_lift(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, int d, const void *Wp, int K,
+                        int L, float *kmean, float *rlift, uint16_t *codes, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if (K < 1) return MP_ERR_UNSUPPORTED;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if (!Kc || !kmean || !rlift || !codes || !Wp || U < 1 || cap < 1 || cap % 8) return MP_ERR_ARG;
+  if (!all_a16(Kc, Wp, kmean, codes, ws)) return MP_ERR_ARG;
+  if (U > 65535) return MP_ERR_UNSUPPORTED;
+  if (n < 1 || n > cap) return MP_ERR_CAPACITY;
+  if (!ws || ws_bytes < mp_build_ws_bytes(U, n, d)) return MP_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  const int np = kmean_parts(n);
+  if (launch_kmean(Kc, kv_dtype, U, n, cap, (double *)ws, np, kmean, s) != hipSuccess) return MP_ERR_HIP;
+  if (launch_lift_radius(Kc, kv_dtype, U, n, cap, kmean, (double *)ws, np, rlift, s) != hipSuccess) return MP_ERR_HIP;
+  EncJob j = make_job(Kc, cap * D, D, kmean, D, 0, U, n, codes, (int64_t)L * cap, 1, cap, nullptr, 0, 0, nullptr,
+                      nullptr);
+  j.rl = rlift;
+  j.rl_su = 1;
+  j.rl_si = 0;
+  return hip_status(launch_encode_jobs(kv_dtype, &j, 1, Wp, K, L, s,
+                                       (const uint16_t *)((const char *)Wp + mp_proj_bytes(d, K, L))));
+}
+
+int mp_append_lift(const void *k_new, const void *v_new, void *Kc, void *Vc, int kv_dtype, int64_t U, int64_t n,
+                   int64_t cap, int d, const float *kmean, const float *rlift, const void *Wp, int K, int L,
+                   uint16_t *codes, void *stream) {
+  int st = check_shape(d, K, L);
+  if (st) return st;
+  if (K < 1) return MP_ERR_UNSUPPORTED;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if (!k_new || !v_new || !Kc || !Vc || !kmean || !rlift || !codes || !Wp || U < 1 || cap < 1 || cap % 8 || n < 0)
+    return MP_ERR_ARG;
+  if (!all_a16(k_new, v_new, Kc, Vc, kmean, Wp, codes)) return MP_ERR_ARG;
+  if (n >= cap) return MP_ERR_CAPACITY;
+  const size_t es = kv_dtype == MP_BF16 ? 2 : 4;
+  EncJob j = make_job(k_new, 0, D, kmean, 0, D, 1, U, codes + n, 0, (int64_t)L * cap, cap,
+                      (char *)Kc + (size_t)n * D * es, 0, cap * D, v_new, (char *)Vc + (size_t)n * D * es);
+  j.rl = rlift;  // row i is unit i's new key
+  j.rl_su = 0;
+  j.rl_si = 1;
+  return hip_status(launch_encode_jobs(kv_dtype, &j, 1, Wp, K, L, as_stream(stream),
+                                       (const uint16_t *)((const char *)Wp + mp_proj_bytes(d, K, L))));
+}
+
 size_t mp_planes_bytes(int64_t U, int64_t cap, int K, int L) {
   if (U < 1 || cap < 1 || K < 1 || K > 16 || L < 2 || L > MAX_L || K * L > 4096) return 0;
   return (size_t)U * (size_t)((cap + SCAN_TILE - 1) / SCAN_TILE) * (size_t)K * (size_t)L * 16 * sizeof(uint32_t);
@@ -206,7 +268,7 @@ static int run_sample(int kv_dtype, const void *q, const void *Kc, const void *V
                       const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap, int K,
                       int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &w, bool want_idx,
                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint32_t *planes, int64_t n_planes,
-                      const void *buckets, int64_t nl) {
+                      const void *buckets, int64_t nl, const float *rlift = nullptr) {
   if (nl > 0) {  // the events then span the lookup and the sampling kernel
     const BucketLayout bl = bucket_layout((void *)buckets, (int64_t)B * Hkv, cap, K, L);
     if (launch_bucket_lookup(qcodes, bl, B, Hq, Hkv, n, nl, cap, K, L, nsh, nst, geo, w, s, ev0) != hipSuccess)
@@ -214,7 +276,7 @@ static int run_sample(int kv_dtype, const void *q, const void *Kc, const void *V
     ev0 = nullptr;
   }
   return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T, nsh, nst,
-                                  geo, w, want_idx, s, ev0, ev1, planes, n_planes, nl));
+                                  geo, w, want_idx, s, ev0, ev1, planes, n_planes, nl, rlift));
 }
 
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
@@ -250,12 +312,12 @@ int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, as_stream(stream)));
 }
 
-int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
-                   const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
-                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
-                   int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
-                   uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
-                   size_t ws_bytes, void *stream) {
+static int decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                       const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                       const float *kmean, const float *rlift, const void *Wp, int B, int Hq, int Hkv, int64_t n,
+                       int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                       const uint16_t *qcodes_in, uint16_t *qcodes_out, float *out, float *lse, int32_t *idx,
+                       int32_t *count, void *ws, size_t ws_bytes, void *stream) {
   int st = check_decode(q, Kc, Vc, kv_dtype, codes, kmean, B, Hq, Hkv, n, cap, d, K, L, T, n_static_head,
                         n_static_tail, ws, ws_bytes);
   if (st) return st;
@@ -277,10 +339,33 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
   if (geo.nchunks > 0) {
     st = run_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head, n_static_tail,
                     geo, w, idx != nullptr, s, nullptr, nullptr, planes, n_planes, buckets,
-                    list_keys(buckets, n_buckets, T));
+                    list_keys(buckets, n_buckets, T), rlift);
     if (st) return st;
   }
   return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
+}
+
+int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                   const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                   const float *kmean, const void *Wp, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int K,
+                   int L, int T, int64_t n_static_head, int64_t n_static_tail, const uint16_t *qcodes_in,
+                   uint16_t *qcodes_out, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                   size_t ws_bytes, void *stream) {
+  return decode_attn(q, Kc, Vc, kv_dtype, codes, planes, n_planes, buckets, n_buckets, kmean, nullptr, Wp, B, Hq, Hkv,
+                     n, cap, d, K, L, T, n_static_head, n_static_tail, qcodes_in, qcodes_out, out, lse, idx, count,
+                     ws, ws_bytes, stream);
+}
+
+int mp_decode_attn_lift(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
+                        const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
+                        const float *kmean, const float *rlift, const void *Wp, int B, int Hq, int Hkv, int64_t n,
+                        int64_t cap, int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail,
+                        const uint16_t *qcodes_in, uint16_t *qcodes_out, float *out, float *lse, int32_t *idx,
+                        int32_t *count, void *ws, size_t ws_bytes, void *stream) {
+  if (!rlift) return MP_ERR_ARG;
+  return decode_attn(q, Kc, Vc, kv_dtype, codes, planes, n_planes, buckets, n_buckets, kmean, rlift, Wp, B, Hq, Hkv,
+                     n, cap, d, K, L, T, n_static_head, n_static_tail, qcodes_in, qcodes_out, out, lse, idx, count,
+                     ws, ws_bytes, stream);
 }
 
 }  // extern "C"

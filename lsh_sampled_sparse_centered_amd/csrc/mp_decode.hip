@@ -227,7 +227,8 @@ template <typename T, int GM>
 __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Raw8<T> &k1, const Raw8<T> &v1,
                                   bool ok1, int e0, int e1, uint32_t mk0, uint32_t mk1, int j16, int G, int K, int L,
                                   const LnPCoef &cf, float scale, const float (*qsh)[D], const float *msh,
-                                  const float *qn_sh, const float *qmu_sh, T (*vrows)[D], float (*lw)[ATT_E]) {
+                                  const float *qn_sh, const float *qmu_sh, T (*vrows)[D], float (*lw)[ATT_E],
+                                  float rl) {
   float kv0[8], kv1[8], mv[8];
   k0.get(kv0);
   k1.get(kv1);
@@ -268,7 +269,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
     if ((mk >> hh) & 1u) {
       float lnP = 0.0f;
       if (!(mk & FORCED)) {
-        const float den = qn_sh[hh] * sqrtf(second ? n1 : n0);
+        const float den = qn_sh[hh] * (rl > 0.0f ? rl : sqrtf(second ? n1 : n0));
         const float cosv = den > 0.0f ? (dk - qmu_sh[hh]) / den : 0.0f;
         lnP = log_sampling_prob(cosv, K, L, cf);
       }
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
     float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt,
     const uint32_t *__restrict__ planes, int64_t npt, int64_t ptiles, const uint32_t *__restrict__ sbits,
-    int64_t bwords, int64_t nlt) {
+    int64_t bwords, int64_t nlt, const float *__restrict__ rlift) {
   // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
   // words [0, FW) says "at least one of this wave's tables matched", of
   // words [FW, 2FW) "at least two".
@@ -381,6 +382,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   const int64_t c = nlt > 0 ? (cr < nscan ? nlt + cr : cr - nscan) : cr;
   const int64_t b = u / Hkv, kvh = u % Hkv;
   const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
+  // keys hashed lifted (Equation 8): the sampling angle is taken against the
+  // lifted key, whose norm is the unit's radius (0: not lifted)
+  const float rl = rlift ? rlift[u] : 0.0f;
   const int64_t tbase = c * SCAN_TILE;
   const int64_t tend = min(n, tbase + SCAN_TILE);
   const uint16_t headbits = (uint16_t)((1u << G) - 1u);
@@ -847,7 +851,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
             const float dk = sm.m.sdot[0][h][e] + sm.m.sdot[1][h][e];
             float lnP = 0.0f;
             if (!(mk & FORCED)) {
-              const float den = qn_sh[h] * sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]);
+              const float den = qn_sh[h] * (rl > 0.0f ? rl : sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
               const float cosv = den > 0.0f ? (dk - qmu_sh[h]) / den : 0.0f;
               lnP = log_sampling_prob(cosv, K, L, cf);
             }
@@ -943,7 +947,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         v1.zero();
       }
       entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[e0 + el0], mk1, j16, G, K, L, cf, scale, qsh, msh,
-                        qn_sh, qmu_sh, sm.a.v, sm.a.lw);
+                        qn_sh, qmu_sh, sm.a.v, sm.a.lw, rl);
     }
     __syncthreads();
     // (b) one thread per (head, entry) turns the log-weights into
@@ -1052,7 +1056,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int Tthr, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
-                         const uint32_t *planes, int64_t n_planes, int64_t n_lists) {
+                         const uint32_t *planes, int64_t n_planes, int64_t n_lists, const float *rlift) {
   const int G = Hq / Hkv;
   const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
@@ -1067,7 +1071,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
                         nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles, ws.bits, \
-                        geo.nchunks_max * (SCAN_TILE / 32), nlt)
+                        geo.nchunks_max * (SCAN_TILE / 32), nlt, rlift)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \

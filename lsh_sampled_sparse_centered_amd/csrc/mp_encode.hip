@@ -172,6 +172,124 @@ hipError_t launch_kmean(const void *Kc, int kv_dtype, int64_t U, int64_t n, int6
 }
 
 // ---------------------------------------------------------------------------
+// Lift of Section 4.2, Equation 8 (an option; the pages do not use it).  The
+// projections' extra row W[d] is packed per tile in the order of the tile
+// word's bits (bf16, 0 past the tile's tables), so a lane reads the 16 values
+// of its accumulator elements contiguously.
+__global__ void proj_pack_lift_kernel(const float *__restrict__ W, int K, int L, int ntiles,
+                                      uint16_t *__restrict__ wlift) {
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= ntiles * 32) return;
+  const int t = gid >> 5, p = gid & 31, tpt = enc_tpt(K);
+  const int j = p / K, b = p % K, l = t * tpt + j;
+  const bool live = j < tpt && l < L;
+  const __bf16 v = (__bf16)(live ? W[(int64_t)D * K * L + l * K + b] : 0.0f);
+  wlift[gid] = __builtin_bit_cast(uint16_t, v);
+}
+
+hipError_t launch_proj_pack_lift(const float *W, int K, int L, uint16_t *wlift, hipStream_t s) {
+  const int ntiles = enc_ntiles(K, L);
+  if (ntiles == 0) return hipSuccess;
+  proj_pack_lift_kernel<<<dim3((unsigned)((ntiles * 32 + 255) / 256)), dim3(256), 0, s>>>(W, K, L, ntiles, wlift);
+  return hipGetLastError();
+}
+
+// Lift radius: the largest |x_i|^2 of x_i = bf16(fp32(k_i) - mu) per 512-row
+// block (16 lanes per row, fp64), then per unit the largest block value, its
+// square root rounded once to fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void lift_partial_kernel(const T *__restrict__ Kc, int64_t n, int64_t cap,
+                                                           const float *__restrict__ kmean, int nparts,
+                                                           double *__restrict__ partial) {
+  __shared__ double red[16];
+  const int64_t u = blockIdx.y;
+  const int p = blockIdx.x;
+  const int j16 = threadIdx.x & 15, rsub = threadIdx.x >> 4;
+  const int64_t r0 = (int64_t)p * KM_ROWS, r1 = min(n, r0 + KM_ROWS);
+  float mv[8];
+  load8<float>(kmean + u * D + 8 * j16, mv);
+  double best = 0.0;
+  for (int64_t r = r0 + rsub; r < r1; r += 16) {
+    float v[8];
+    load8<T>(Kc + (u * cap + r) * D + 8 * j16, v);
+    double s2 = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double x = (double)(float)(__bf16)(v[e] - mv[e]);  // fp32 subtraction, bf16 rounding
+      s2 += x * x;
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) s2 += __shfl_xor(s2, o);  // the row's 16 lanes
+    best = fmax(best, s2);
+  }
+  if (j16 == 0) red[rsub] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = 0.0;
+    for (int k = 0; k < 16; ++k) m = fmax(m, red[k]);
+    partial[u * nparts + p] = m;
+  }
+}
+
+__global__ __launch_bounds__(256) void lift_final_kernel(const double *__restrict__ partial, int nparts,
+                                                         float *__restrict__ rlift) {
+  __shared__ double red[256];
+  const int64_t u = blockIdx.x;
+  double m = 0.0;
+  for (int p = threadIdx.x; p < nparts; p += 256) m = fmax(m, partial[u * nparts + p]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) rlift[u] = (float)sqrt(red[0]);
+}
+
+hipError_t launch_lift_radius(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, const float *kmean,
+                              double *partial, int nparts, float *rlift, hipStream_t s) {
+  dim3 g1((unsigned)nparts, (unsigned)U);
+  if (kv_dtype == 0)
+    lift_partial_kernel<__bf16><<<g1, 256, 0, s>>>((const __bf16 *)Kc, n, cap, kmean, nparts, partial);
+  else
+    lift_partial_kernel<float><<<g1, 256, 0, s>>>((const float *)Kc, n, cap, kmean, nparts, partial);
+  lift_final_kernel<<<dim3((unsigned)U), 256, 0, s>>>(partial, nparts, rlift);
+  return hipGetLastError();
+}
+
+// The extra coordinate of lifted rows: with the row's B operands held by this
+// lane (half of its dims) and its partner lane l ^ 32 (the other half),
+// e = bf16(fp32(sqrt(max(0, r^2 - |x|^2)))) with |x|^2 summed in fp64.
+__device__ inline float lift_coord(const bf16x8 (&xr)[KSTEPS], float r) {
+  double s2 = 0.0;
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double x = (double)(float)xr[s][e];
+      s2 += x * x;
+    }
+  s2 += __shfl_xor(s2, 32);
+  const double rem = (double)r * (double)r - s2;
+  return (float)(__bf16)(float)sqrt(rem > 0.0 ? rem : 0.0);
+}
+
+// Sign bits of lifted projections: z = acc[r] + e * W[d][bit 16 half + r]
+// (one fp32 fma), then bit r = (z > 0) as in sign_bits16.  wl holds the 16
+// bf16 extra-row values of this lane half's bits.
+__device__ inline uint32_t sign_bits16_lift(const f32x16 &a, float e, const uint4 (&wl)[2]) {
+  const bf16x8 w0 = __builtin_bit_cast(bf16x8, wl[0]), w1 = __builtin_bit_cast(bf16x8, wl[1]);
+  uint32_t pos = 0;
+#pragma unroll
+  for (int r = 15; r >= 0; --r) {
+    const float w = r < 8 ? (float)w0[r & 7] : (float)w1[r & 7];
+    const float nz = 0.0f - fmaf(e, w, a[r]);
+    pos = __builtin_amdgcn_alignbit(pos, __builtin_bit_cast(uint32_t, nz), 31u);
+  }
+  return pos & 0xffffu;
+}
+
+// ---------------------------------------------------------------------------
 // Encoder.  Each block encodes ENC_ROWS rows of one unit for the tables
 // [l0, l1) of its table group.  Wave w owns rows w*64 .. w*64+63 as two
 // 32-row B operands held in registers (x = bf16(row - mu) for the 128 dims).
@@ -225,9 +343,9 @@ __device__ inline uint32_t sign_bits16(const f32x16 &a) {
 // The kernel takes up to two independent row sets ("jobs", e.g. the keys to
 // append and the queries of a decode step) and maps its linear block index
 // onto (job, row block, unit, table group).
-template <typename T>
+template <typename T, bool LIFT>
 __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
-                                                        int K, int L) {
+                                                        int K, int L, const uint4 *__restrict__ wlift) {
   __shared__ uint4 wsh[2][ENC_TG * KSTEPS * 64];
   __shared__ uint16_t cst[ENC_NW][ENC_CST][64];  // a wave's codes of one stage, [table][row]
   const bool second = njobs > 1 && (int64_t)blockIdx.x >= j1.first_block;
@@ -311,6 +429,17 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int e = 0; e < 8; ++e) xb[nt][s][e] = ok ? (__bf16)v[s][e] : (__bf16)0.0f;  // round to nearest even
+  }
+  // lifted rows: the extra coordinate of this lane's row of each set
+  float ebar[2] = {0.0f, 0.0f};
+  if constexpr (LIFT) {
+    if (jb.rl) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int64_t r = min(row_w + 32 * nt + (lane & 31), rows - 1);
+        ebar[nt] = lift_coord(xb[nt], jb.rl[u * jb.rl_su + r * jb.rl_si]);
+      }
+    }
   }
 
   // appends: the first table block of each row block copies the raw key and
@@ -465,7 +594,17 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
         // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
         // cross-half swap leaves lane l with row l's halves and lane 32 + l
         // with row 32 + l's.
-        const auto sw = __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), sign_bits16(acc1), false, false);
+        uint32_t m0, m1;
+        if constexpr (LIFT) {
+          const int tl = min(tg + tt, t1 - 1);  // tiles past t1 are dropped
+          const uint4 wl[2] = {wlift[tl * 4 + 2 * half], wlift[tl * 4 + 2 * half + 1]};
+          m0 = sign_bits16_lift(acc0, ebar[0], wl);
+          m1 = sign_bits16_lift(acc1, ebar[1], wl);
+        } else {
+          m0 = sign_bits16(acc0);
+          m1 = sign_bits16(acc1);
+        }
+        const auto sw = __builtin_amdgcn_permlane32_swap(m0, m1, false, false);
         const uint32_t word = sw[0] | (sw[1] << 16);
         wd[tt] = word;
       }
@@ -514,9 +653,10 @@ constexpr int SM_TABLES = 4;                                   // tables per blo
 constexpr int SM_MAXT = 3;  // tiles a block touches: K <= 16 gives tpt >= 2, and 4 tables span <= 3 tiles
 static_assert(SM_MAXT <= 4, "one tile per wave");
 
-template <typename T>
+template <typename T, bool LIFT>
 __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1, int njobs, int blocks0,
-                                                           const uint4 *__restrict__ wp, int K, int L) {
+                                                           const uint4 *__restrict__ wp, int K, int L,
+                                                           const uint4 *__restrict__ wlift) {
   __shared__ uint32_t bits[64][SM_MAXT + 2];  // [row][tile - t0]
   const bool second = njobs > 1 && (int)blockIdx.x >= blocks0;
   const EncJob &jb = second ? j1 : j0;
@@ -581,6 +721,18 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
 #pragma unroll
       for (int e = 0; e < 8; ++e) xb[nt][s][e] = ok ? (__bf16)v[s][e] : (__bf16)0.0f;  // round to nearest even
   }
+  // lifted rows: the extra coordinate of this lane's row of each set
+  float ebar[2] = {0.0f, 0.0f};
+  if constexpr (LIFT) {
+    if (jb.rl) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int rr = min(32 * nt + (lane & 31), R - 1);
+        const int64_t uu = rr / (int)jb.rows, ii = rr % (int)jb.rows;
+        ebar[nt] = lift_coord(xb[nt], jb.rl[uu * jb.rl_su + ii * jb.rl_si]);
+      }
+    }
+  }
 
   // appends: block 0 copies the raw key and value rows into the caches (16
   // bytes per thread and step; both loads before both stores)
@@ -606,8 +758,16 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
       for (int s = 0; s < KSTEPS; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[s]), xb[1][s], acc1, 0, 0, 0);
     }
     // lane l ends with the tile's 32 bits of row l (as in the large encoder)
-    const auto sw =
-        __builtin_amdgcn_permlane32_swap(sign_bits16(acc0), two ? sign_bits16(acc1) : 0u, false, false);
+    uint32_t m0, m1;
+    if constexpr (LIFT) {
+      const uint4 wl[2] = {wlift[t * 4 + 2 * half], wlift[t * 4 + 2 * half + 1]};
+      m0 = sign_bits16_lift(acc0, ebar[0], wl);
+      m1 = two ? sign_bits16_lift(acc1, ebar[1], wl) : 0u;
+    } else {
+      m0 = sign_bits16(acc0);
+      m1 = two ? sign_bits16(acc1) : 0u;
+    }
+    const auto sw = __builtin_amdgcn_permlane32_swap(m0, m1, false, false);
     const uint32_t word = sw[0] | (sw[1] << 16);
     bits[lane][t - t0] = word;
   }
@@ -640,7 +800,8 @@ static void plan_job(EncJob &j, int K, int L, int64_t first_block) {
 
 static int64_t job_blocks(const EncJob &j) { return j.rblocks * j.units * j.tsplit; }
 
-hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s) {
+hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s,
+                              const uint16_t *wlift) {
   int64_t total = 0;
   EncJob j[2];
   int nj = 0;
@@ -655,20 +816,28 @@ hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp
   if (nj == 1) j[1] = j[0];
   bool small = true;
   for (int i = 0; i < nj; ++i) small = small && j[i].units * j[i].rows <= 64;
+  const uint4 *wl = (const uint4 *)wlift;
+  const bool lift = wlift != nullptr && K > 0;
+#define MP_ENC(KERNEL, G, B, ...)                                                           \
+  do {                                                                                      \
+    if (dtype == 0 && lift)                                                                 \
+      KERNEL<__bf16, true><<<G, B, 0, s>>>(__VA_ARGS__, wl);                                \
+    else if (dtype == 0)                                                                    \
+      KERNEL<__bf16, false><<<G, B, 0, s>>>(__VA_ARGS__, wl);                               \
+    else if (lift)                                                                          \
+      KERNEL<float, true><<<G, B, 0, s>>>(__VA_ARGS__, wl);                                 \
+    else                                                                                    \
+      KERNEL<float, false><<<G, B, 0, s>>>(__VA_ARGS__, wl);                                \
+  } while (0)
   if (small) {
     const int bpj = (L + SM_TABLES - 1) / SM_TABLES;
     const dim3 g((unsigned)(bpj * nj));
-    if (dtype == 0)
-      encode_small_kernel<__bf16><<<g, 256, 0, s>>>(j[0], j[1], nj, bpj, (const uint4 *)Wp, K, L);
-    else
-      encode_small_kernel<float><<<g, 256, 0, s>>>(j[0], j[1], nj, bpj, (const uint4 *)Wp, K, L);
+    MP_ENC(encode_small_kernel, g, 256, j[0], j[1], nj, bpj, (const uint4 *)Wp, K, L);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)total);
-  if (dtype == 0)
-    encode_kernel<__bf16><<<grid, 64 * ENC_NW, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
-  else
-    encode_kernel<float><<<grid, 64 * ENC_NW, 0, s>>>(j[0], j[1], nj, (const uint4 *)Wp, K, L);
+  MP_ENC(encode_kernel, grid, 64 * ENC_NW, j[0], j[1], nj, (const uint4 *)Wp, K, L);
+#undef MP_ENC
   return hipGetLastError();
 }
 

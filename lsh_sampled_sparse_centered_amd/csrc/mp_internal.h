@@ -94,6 +94,8 @@ struct EncJob {
   int64_t kc_su, kc_si;
   const void *vin;
   void *vcopy;
+  const float *rl;  // lifted rows (Equation 8): row i of unit u has radius rl[u*rl_su + i*rl_si]; NULL: not lifted
+  int64_t rl_su, rl_si;
   int64_t rblocks, first_block;
   int tsplit, tpb;
 };
@@ -122,8 +124,14 @@ inline EncJob make_job(const void *in, int64_t in_su, int64_t in_si, const float
   return j;
 }
 
-// Encodes up to two row sets in one launch.
-hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s);
+// Encodes up to two row sets in one launch.  wlift (lifted rows only): the
+// projections' extra row, [ntiles][32] bf16 in tile-word bit order.
+hipError_t launch_encode_jobs(int dtype, EncJob *jobs, int njobs, const void *Wp, int K, int L, hipStream_t s,
+                              const uint16_t *wlift = nullptr);
+// Lift radius per unit (Equation 8): rlift[u] = fp32(sqrt(max_i |bf16(K[u][i] - kmean[u])|^2)), fp64 sums.
+hipError_t launch_lift_radius(const void *Kc, int kv_dtype, int64_t U, int64_t n, int64_t cap, const float *kmean,
+                              double *partial, int nparts, float *rlift, hipStream_t s);
+hipError_t launch_proj_pack_lift(const float *W, int K, int L, uint16_t *wlift, hipStream_t s);
 hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si, const float *mu, int64_t mu_su,
                          int64_t mu_si, int64_t units, int64_t rows, const void *Wp, int K, int L, uint16_t *out,
                          int64_t out_su, int64_t out_si, int64_t out_sl, void *kcopy, int64_t kc_su, int64_t kc_si,
@@ -132,12 +140,14 @@ hipError_t launch_encode(int dtype, const void *in, int64_t in_su, int64_t in_si
 // dispatch, so they time exactly this launch (no queue gap before it).
 // Tiles below n_lists take their sampled keys from the workspace's bitmaps
 // (written by launch_bucket_lookup) instead of scanning.
+// rlift (nullable, [U]): the keys were hashed lifted (Equation 8) with these
+// radii, and the sampling angle is taken against the lifted key.
 hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *Vc, const uint16_t *codes,
                          const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                          int K, int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &ws,
                          bool want_idx, hipStream_t s, hipEvent_t ev_start = nullptr,
                          hipEvent_t ev_stop = nullptr, const uint32_t *planes = nullptr, int64_t n_planes = 0,
-                         int64_t n_lists = 0);
+                         int64_t n_lists = 0, const float *rlift = nullptr);
 // Bit-plane index of the code store: tiles [t0, t0 + nt) of every unit,
 // planes [U][ptiles][K][L][16] u32 (word j of row (b, l) of tile t = bit b of
 // table l's codes for keys 512 t + 32 j .. + 31).

@@ -286,3 +286,21 @@ def test_valid_arguments_pass_validation():
     assert _decode(T=1) not in (ARG, UNSUP) and _decode(T=75) not in (ARG, UNSUP)
     assert _decode(planes=None, np=12345) not in (ARG, UNSUP)  # ignored without planes
     assert _step(planes=FAKE, np=512, n=512, cap=1024) not in (ARG, UNSUP, CAP, WS)
+
+
+def test_lift_entry_points_reject_invalid_arguments():
+    L = mp.lib()
+    assert L.mp_proj_bytes_lift(128, 10, 150) == L.mp_proj_bytes(128, 10, 150) + 50 * 32 * 2
+    assert L.mp_proj_bytes_lift(128, 0, 150) == 0
+    assert L.mp_proj_pack_lift(None, 128, 8, 75, FAKE, None) == ARG
+    assert L.mp_proj_pack_lift(FAKE, 128, 0, 75, FAKE, None) == UNSUP
+    assert L.mp_build_codes_lift(FAKE, 0, 8, 100, 128, 128, FAKE, 8, 75, FAKE, None, FAKE, FAKE, 1 << 30,
+                                 None) == ARG  # rlift required
+    assert L.mp_build_codes_lift(FAKE, 0, 8, 100, 128, 128, FAKE, 0, 75, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                 None) == UNSUP
+    assert L.mp_build_codes_lift(FAKE, 0, 8, 100, 128, 128, FAKE, 8, 75, FAKE, FAKE, FAKE, FAKE, 10, None) == WS
+    assert L.mp_append_lift(FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, 128, FAKE, FAKE, FAKE, 8, 75, FAKE, None) == CAP
+    assert L.mp_append_lift(FAKE, FAKE, FAKE, FAKE, 0, 8, 10, 128, 128, FAKE, None, FAKE, 8, 75, FAKE, None) == ARG
+    assert L.mp_decode_attn_lift(FAKE, FAKE, FAKE, 0, FAKE, None, 0, None, 0, FAKE, None, FAKE, 1, 32, 8, 100, 128,
+                                 128, 8, 75, 2, 0, 0, None, None, FAKE, None, None, None, FAKE, 1 << 30,
+                                 None) == ARG  # rlift required
