@@ -20,10 +20,9 @@ BucketLayout bucket_layout(void *base, int64_t U, int64_t cap, int K, int L) {
   BucketLayout b;
   b.nbins = 1 << K;
   b.bchunks = (cap + BK_R - 1) / BK_R;
-  char *p = (char *)base;
   const size_t off_bytes = align256(sizeof(uint16_t) * (size_t)U * L * b.bchunks * (b.nbins + 1));
-  b.off = (uint16_t *)p;
-  b.keys = (uint16_t *)(p + off_bytes);
+  b.off = (uint16_t *)base;  // a NULL base asks for the size only
+  b.keys = base ? (uint16_t *)((char *)base + off_bytes) : nullptr;
   b.bytes = off_bytes + align256(sizeof(uint16_t) * (size_t)U * L * cap);
   return b;
 }

@@ -62,18 +62,19 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
   const int G = Hq / Hkv;
   const int64_t ncm = (cap + SCAN_TILE - 1) / SCAN_TILE;
   const int64_t ent_per_unit = 2 * ncm * SCAN_TILE;  // up to 1024 entries per block
+  // offsets first; pointers only into a real buffer (a NULL base asks for the size)
   size_t off = 0;
   DecodeWs w;
-  char *p = (char *)base;
-  w.qcodes = (uint16_t *)(p + off);
+  auto at = [base](size_t o) -> void * { return base ? (char *)base + o : nullptr; };
+  w.qcodes = (uint16_t *)at(off);
   off = align256(off + sizeof(uint16_t) * (size_t)B * Hq * L);
-  w.part = (float *)(p + off);
+  w.part = (float *)at(off);
   off = align256(off + sizeof(float) * (size_t)U * ncm * G * PSTRIDE);
-  w.ent = (uint32_t *)(p + off);
+  w.ent = (uint32_t *)at(off);
   off = align256(off + sizeof(uint32_t) * (size_t)U * ent_per_unit);
-  w.ent_cnt = (int32_t *)(p + off);
+  w.ent_cnt = (int32_t *)at(off);
   off = align256(off + sizeof(int32_t) * (size_t)U * ncm);
-  w.bits = (uint32_t *)(p + off);
+  w.bits = (uint32_t *)at(off);
   off = align256(off + sizeof(uint32_t) * (size_t)U * G * ncm * (SCAN_TILE / 32));
   w.bytes = off;
   return w;
