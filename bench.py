@@ -7,9 +7,13 @@ batch 1, SimHash (K, L) = (10, 150).  Inputs are synthetic (the cone-plus-sink
 generator in ``synth``), resident in HBM before timing starts.
 
 One step = for every layer: mp_decode_step, i.e. append the new token's
-key/value and codes and encode the 32 queries (one launch), scan + weight +
-split-attend (the sampling kernel) and merge.  The code store is built once
-beforehand (mp_build_codes), timed separately as the encoder.
+key/value and codes and encode the 32 queries (one launch), look the queries'
+buckets up in the bucketed hash tables of the prefill keys (one launch),
+select + weight + split-attend (the sampling kernel) and merge.  The code
+store and its index are built once beforehand (mp_build_codes,
+mp_build_buckets), timed separately.  By default the same steps are replayed
+with the bit-plane index and with a plain scan of the 16-bit codes, reported
+under "index_alternatives".
 
 Prints one JSON line.  ``value`` = context keys scanned per second over the
 whole step (all layers and KV heads); ``ms_per_step`` = decode-step latency.
@@ -58,7 +62,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
     ap.add_argument("--threshold", type=int, default=2,
                     help="collision threshold T: a key is sampled in at least T of the L tables (the pages' 2)")
-    ap.add_argument("--index", choices=("planes", "buckets", "codes"), default="planes",
+    ap.add_argument("--alternatives", choices=("on", "off"), default="on",
+                    help="also time the other two index choices on the same built layers (reported as context)")
+    ap.add_argument("--index", choices=("planes", "buckets", "codes"), default="buckets",
                     help="planes: build the bit-plane index of the code store at set-up (whole 512-key tiles of the "
                          "prefill keys) and let the threshold-2 scan read it; buckets: build the bucketed hash "
                          "tables and look the query's buckets up instead of scanning; codes: scan the 16-bit codes")
@@ -148,11 +154,11 @@ def main() -> int:
     lcfg = [((0, 2, 0, 0) if pages and l in (0, 16) else (K, L, 4 if pages else 0, 64 if pages else 0))
             for l in range(nlayers)]
     sampled_layers = [l for l in range(nlayers) if lcfg[l][0] > 0]
-    use_planes = args.index == "planes"
-    use_buckets = args.index == "buckets"
+    modes = [args.index] + ([m for m in ("buckets", "planes", "codes") if m != args.index]
+                            if args.alternatives == "on" else [])
+    use_planes = "planes" in modes
+    use_buckets = "buckets" in modes
     n_planes = (n0 // 512) * 512  # appended keys stay in the 16-bit codes (tiles past the index)
-    scan_planes = use_planes and args.threshold == 2
-    scan_buckets = use_buckets and args.threshold == 2
 
     # ------------------------------------------------------------------ inputs + code-store build
     layers = []
@@ -182,25 +188,30 @@ def main() -> int:
                 kn[s, u], vn[s, u] = synth.step_kv(args.seed, l, b, h, d, dt, step=s + 1)
                 qs[s, b, h * G:(h + 1) * G] = synth.unit_queries(args.seed, l, b, h, G, d, dt, step=s + 1)
         kn, vn, qs = kn.to(dev), vn.to(dev), qs.to(dev)
-        planes, buckets, pev = None, None, None
-        if (use_planes or use_buckets) and Kl > 0:  # the index of the prefill keys' whole tiles
-            pev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            pev[0].record()
+        planes, buckets, pev, bev = None, None, None, None
+        if Kl > 0:  # the indexes of the prefill keys' whole tiles
             if use_planes:
+                pev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                pev[0].record()
                 planes = torch.empty(U, (cap + 511) // 512, Kl, Ll, 16, dtype=torch.int32, device=dev)
                 mp.mp_build_planes(codes, Kl, n_planes, planes=planes)
-            else:
+                pev[1].record()
+            if use_buckets:
+                bev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                bev[0].record()
                 buckets = mp.mp_build_buckets(codes, Kl, n_planes)
-            pev[1].record()
+                bev[1].record()
         layers.append(dict(Kc=Kc, Vc=Vc, Wp=Wp, kmean=kmean, codes=codes, kn=kn, vn=vn, qs=qs, ev=(e0, e1),
-                           planes=planes, buckets=buckets, pev=pev))
+                           planes=planes, buckets=buckets, pev=pev, bev=bev))
     torch.cuda.synchronize()
     build_ms = [layers[l]["ev"][0].elapsed_time(layers[l]["ev"][1]) for l in sampled_layers]
-    planes_ms = [layers[l]["pev"][0].elapsed_time(layers[l]["pev"][1]) for l in sampled_layers
-                 if layers[l]["pev"] is not None]
-    log("built %d layers; build %.3f ms/layer (median)%s" %
-        (nlayers, float(np.median(build_ms)),
-         "; %s index %.3f ms/layer" % (args.index, float(np.median(planes_ms))) if planes_ms else ""))
+    index_ms = {}
+    for key, name in (("pev", "planes"), ("bev", "buckets")):
+        t = [layers[l][key][0].elapsed_time(layers[l][key][1]) for l in sampled_layers if layers[l][key] is not None]
+        if t:
+            index_ms[name] = float(np.median(t))
+    log("built %d layers; build %.3f ms/layer (median); index builds %s ms/layer" %
+        (nlayers, float(np.median(build_ms)), {k: round(v, 3) for k, v in index_ms.items()}))
 
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, cap, L, dev)
     outs = [torch.empty(w.batch, w.hq, d, dtype=torch.float32, device=dev) for _ in range(nlayers)]
@@ -208,45 +219,51 @@ def main() -> int:
 
     # ------------------------------------------------------------------ decode steps
     # one step = for every layer: mp_decode_step (append + query encode in one
-    # launch, then the sampling kernel and the merge).  In the last timed step
-    # the library attaches HIP events to every sampling-kernel dispatch; they
-    # cost about 4 us per launch, so the other timed steps run without them.
-    ev_steps = min(args.steps, 1)
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ev_steps * nlayers)]
-    for pair in kev:
-        for e in pair:
-            e.record()  # create the underlying events before handing them to the library
-    n_cur = n0
-    t0 = t1 = 0.0
-    step_ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-    n_timed = []
-    torch.cuda.synchronize()
-    for s in range(total_steps):
-        timed = s >= args.warmup
-        if s == args.warmup:
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            step_ev[0].record()
-        for l, lay in enumerate(layers):
-            k = s - (total_steps - ev_steps)
-            ev = kev[k * nlayers + l] if k >= 0 else None
-            mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
-                              lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
-                              n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev, T=args.threshold,
-                              planes=lay["planes"], n_planes=n_planes if lay["planes"] is not None else 0,
-                              buckets=lay["buckets"], n_buckets=n_planes if lay["buckets"] is not None else 0)
-        if timed:
-            n_timed.append(n_cur + 1)
-        n_cur += 1
-    step_ev[1].record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    ev_ms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
-    kern_all = np.array([a.elapsed_time(b) for a, b in kev])
-    kern_ms = kern_all[sampled_layers]  # the roofline is the sampled layers' kernel
-    log("step %.3f ms (wall) / %.3f ms (events); sample kernel %.2f us avg over %d launches" %
-        (wall_ms, ev_ms, kern_ms.mean() * 1e3, len(kern_ms)))
+    # launch, [bucket lookup,] the sampling kernel and the merge).  In the last
+    # timed step the library attaches HIP events to every sampling-kernel
+    # dispatch; they cost about 4 us per launch, so the other timed steps run
+    # without them.  Each index choice replays the same steps from n0 (the
+    # appended rows and codes are rewritten with the same values).
+    def run_steps(mode):
+        ev_steps = min(args.steps, 1)
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ev_steps * nlayers)]
+        for pair in kev:
+            for e in pair:
+                e.record()  # create the underlying events before handing them to the library
+        n_cur = n0
+        t0 = 0.0
+        step_ev = [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+        n_timed = []
+        torch.cuda.synchronize()
+        for s in range(total_steps):
+            if s == args.warmup:
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                step_ev[0].record()
+            for l, lay in enumerate(layers):
+                k = s - (total_steps - ev_steps)
+                ev = kev[k * nlayers + l] if k >= 0 else None
+                pl = lay["planes"] if mode == "planes" else None
+                bk = lay["buckets"] if mode == "buckets" else None
+                mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
+                                  lay["kmean"], lay["Wp"], w.hkv, n_cur, lcfg[l][0], ws, n_static_head=lcfg[l][2],
+                                  n_static_tail=lcfg[l][3], out=outs[l], lse=lses[l], sample_events=ev,
+                                  T=args.threshold, planes=pl, n_planes=n_planes if pl is not None else 0,
+                                  buckets=bk, n_buckets=n_planes if bk is not None else 0)
+            if s >= args.warmup:
+                n_timed.append(n_cur + 1)
+            n_cur += 1
+        step_ev[1].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        evms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
+        kern = np.array([a.elapsed_time(b) for a, b in kev])[sampled_layers]  # the sampled layers' kernel
+        log("[%s] step %.3f ms (wall) / %.3f ms (events); sample kernel %.2f us avg over %d launches" %
+            (mode, wall, evms, kern.mean() * 1e3, len(kern)))
+        return wall, evms, kern, n_timed, n_cur
+
+    timing = {m: run_steps(m) for m in modes}
+    wall_ms, ev_ms, kern_ms, n_timed, n_cur = timing[args.index]
     keys_per_step = float(np.mean(n_timed)) * U * nlayers
     value = keys_per_step / (wall_ms * 1e-3)
 
@@ -268,7 +285,7 @@ def main() -> int:
                 for g in range(G):
                     c = int(cnt[b, h * G + g])
                     mask[idx[b, h * G + g, :c].long()] = True
-                    if scan_buckets:
+                    if use_buckets:
                         cu = lay["codes"].view(torch.int16)[b * w.hkv + h, :, :n_planes]
                         bucket_entries += int((cu == qc_last[b, h * G + g][:, None]).sum())
                 union_sum += int(mask.sum())
@@ -277,19 +294,30 @@ def main() -> int:
     head_frac = head_sum / (len(sampled_layers) * w.batch * w.hq * n_cur)
     e = 2 if w.dtype == "bf16" else 4
     n_dec = float(np.mean(n_timed))
-    # algorithmic bytes of one sample launch (one layer): codes of every key once, each distinct sampled
-    # K and V row once, the queries, their codes and the key means
-    # (with the bit-plane index, K bits per key and table for the tiles it covers)
-    # (with the buckets: the query's bucket entries, 2 bytes each, and two 2-byte offsets per head, table and
-    # 4096-key chunk, for the keys below the index; 16-bit codes above)
-    if scan_buckets:
-        nbc = (n_planes + 4095) // 4096
-        code_bytes = (2 * bucket_entries / len(sampled_layers) / U + G * L * nbc * 4 + 2 * L * (n_dec - n_planes))
-    elif scan_planes:
-        code_bytes = K * L * n_planes / 8 + 2 * L * (n_dec - n_planes)
-    else:
-        code_bytes = 2 * L * n_dec
-    bytes_launch = U * (code_bytes + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
+
+    def launch_bytes(mode):
+        """Algorithmic bytes of one sampling-kernel launch (one layer): the
+        index or codes it reads, each distinct sampled K and V row once, the
+        queries, their codes and the key means.  planes: K bits per key and
+        table for the tiles the index covers; buckets: the lookup's sampled-key
+        words (64 bytes per head and tile) for those tiles; 16-bit codes for
+        the rest."""
+        T2 = args.threshold == 2
+        if mode == "buckets" and T2:
+            code = G * 64 * n_planes / 512 + 2 * L * (n_dec - n_planes)
+        elif mode == "planes" and T2:
+            code = K * L * n_planes / 8 + 2 * L * (n_dec - n_planes)
+        else:
+            code = 2 * L * n_dec
+        return U * (code + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
+
+    # the bucket lookup kernel (before the sampling kernel): the query's bucket
+    # entries (2 bytes each), two 2-byte offsets per head, table and 4096-key
+    # chunk, the query codes; it writes the sampled-key words
+    nbc = (n_planes + 4095) // 4096
+    lookup_bytes = (2 * bucket_entries / max(len(sampled_layers), 1) + U * G * L * (nbc * 4 + 2)
+                    + U * G * 64 * n_planes / 512) if use_buckets else None
+    bytes_launch = launch_bytes(args.index)
     achieved = bytes_launch / (kern_ms.mean() * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -298,11 +326,19 @@ def main() -> int:
         if (tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages and
                 args.threshold == 2 and tr.get("index") == args.index):
             traffic = tr.get("bytes_per_launch")
+    alternatives = {}
+    for m in modes[1:]:
+        wm, em, km, nt, _ = timing[m]
+        bl = launch_bytes(m)
+        alternatives[m] = {"ms_per_step": wm, "value": float(np.mean(nt)) * U * nlayers / (wm * 1e-3),
+                           "kernel_us": km.mean() * 1e3, "algorithmic_bytes_per_launch": bl,
+                           "frac": bl / (km.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS}
     # a dense layer reads its (two-table) codes and every key's K and V row
     dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
     step_bytes = len(sampled_layers) * bytes_launch + (nlayers - len(sampled_layers)) * dense_bytes
-    log("|S_h|/n = %.4f, union per unit %.0f keys (%.4f of n); %.1f MB algorithmic per launch" %
-        (head_frac, union_per_unit, union_per_unit / n_dec, bytes_launch / 1e6))
+    log("|S_h|/n = %.4f, union per unit %.0f keys (%.4f of n); %.1f MB algorithmic per launch%s" %
+        (head_frac, union_per_unit, union_per_unit / n_dec, bytes_launch / 1e6,
+         "; bucket lookup %.2f MB per launch" % (lookup_bytes / 1e6) if lookup_bytes else ""))
 
     # ------------------------------------------------------------------ encoder (build) figures
     flops_layer = 2.0 * d * K * L * n0 * U
@@ -361,8 +397,10 @@ def main() -> int:
         "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
         "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": d, "context": n0, "K": K, "L": L, "threshold": args.threshold,
-                   "code_scan": ("bit-plane index below key %d, 16-bit codes above" % n_planes if scan_planes
-                                 else "bucketed tables below key %d, 16-bit codes above" % n_planes if scan_buckets
+                   "code_scan": ("bit-plane index below key %d, 16-bit codes above" % n_planes
+                                 if args.index == "planes" and args.threshold == 2
+                                 else "bucketed tables below key %d, 16-bit codes above" % n_planes
+                                 if args.index == "buckets" and args.threshold == 2
                                  else "16-bit codes"),
                    "parallelism": "single GPU",
                    "policy": ("every layer sampled" if not pages else
@@ -371,14 +409,16 @@ def main() -> int:
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "sample_kernel (mp_decode_step / mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
                      "algorithmic_bytes_per_launch": bytes_launch, "device_copy_GBs": copy_gbs,
-                     "frac_of_device_copy": achieved / copy_gbs},
+                     "frac_of_device_copy": achieved / copy_gbs,
+                     "bucket_lookup_bytes_per_launch": lookup_bytes},
+        "index_alternatives": alternatives,
         "step": {"latency_ms": wall_ms, "latency_ms_events": ev_ms, "bytes_per_step": step_bytes,
                  "frac_hbm_step": step_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                  "sampled_frac_per_head": head_frac, "union_keys_per_unit": union_per_unit},
         "encoder": {"build_ms_per_layer": float(np.median(build_ms)), "tflops": enc_tflops,
                     "frac_mfma_bf16": enc_tflops / BF16_MFMA_PEAK_TFLOPS,
                     "note": "build = key mean + projection GEMM + sign pack, per layer",
-                    "index_build_ms_per_layer": float(np.median(planes_ms)) if planes_ms else None},
+                    "index_build_ms_per_layer": index_ms},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
@@ -390,8 +430,9 @@ def cpu_baseline(w, seed: int, budget_s: float, T: int = 2):
 
     Sample: KV heads 0..3 of layer 0 (batch 0) at the full context, with their
     query heads; keys/values regenerated on the host from the same recipe.
-    The oracle builds its own codes for them (untimed), then its decode over
-    those heads is repeated with successive queries until the budget is spent.
+    The oracle builds its own codes for them (timed once, reported under
+    "build" and extrapolated to a whole layer), then its decode over those
+    heads is repeated with successive queries until the budget is spent.
     """
     import numpy as np
     import torch
@@ -442,11 +483,25 @@ def cpu_baseline(w, seed: int, budget_s: float, T: int = 2):
     oracle.set_threads(threads)
     return {"value": keys_done / el, "unit": "keys/s", "cores": min(threads, nunits * G), "kind": "oracle",
             "sample": "%d decode passes over %d KV heads x %d keys (%d query heads each), layer 0; "
-                      "oracle build of their codes %.1fs untimed; one-thread figure: %d passes over KV head 0"
+                      "oracle build of their codes %.1fs (timed once); one-thread figure: %d passes over KV head 0"
                       % (reps, nunits, n, G, build_s, reps1),
             "value_1thread": reps1 * n / el1,
-            "cpu_model": platform.processor() or platform.machine(), "host_threads": threads,
-            "seconds": el + el1}
+            "build": {"seconds": build_s, "keys": nunits * n,
+                      "keys_per_s": nunits * n / build_s if build_s > 0 else None,
+                      "per_layer_s_extrapolated": build_s * w.batch * w.hkv / nunits},
+            "cpu_model": cpu_model(), "host_threads": threads,
+            "seconds": el + el1 + build_s}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
 
 
 if __name__ == "__main__":

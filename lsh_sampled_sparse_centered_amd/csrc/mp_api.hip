@@ -269,11 +269,10 @@ static int run_sample(int kv_dtype, const void *q, const void *Kc, const void *V
                       int L, int T, int64_t nsh, int64_t nst, const DecodeGeom &geo, const DecodeWs &w, bool want_idx,
                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, const uint32_t *planes, int64_t n_planes,
                       const void *buckets, int64_t nl, const float *rlift = nullptr) {
-  if (nl > 0) {  // the events then span the lookup and the sampling kernel
+  if (nl > 0) {  // the events stay on the sampling kernel's own dispatch
     const BucketLayout bl = bucket_layout((void *)buckets, (int64_t)B * Hkv, cap, K, L);
-    if (launch_bucket_lookup(qcodes, bl, B, Hq, Hkv, n, nl, cap, K, L, nsh, nst, geo, w, s, ev0) != hipSuccess)
+    if (launch_bucket_lookup(qcodes, bl, B, Hq, Hkv, n, nl, cap, K, L, nsh, nst, geo, w, s) != hipSuccess)
       return MP_ERR_HIP;
-    ev0 = nullptr;
   }
   return hip_status(launch_sample(kv_dtype, q, Kc, Vc, codes, kmean, qcodes, B, Hq, Hkv, n, cap, K, L, T, nsh, nst,
                                   geo, w, want_idx, s, ev0, ev1, planes, n_planes, nl, rlift));

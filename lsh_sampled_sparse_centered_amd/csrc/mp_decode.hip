@@ -117,22 +117,54 @@ __device__ inline float log_sampling_prob_t(float lnp, float p, int L, int T, fl
   return log1pf(-fminf(below, 1.0f));
 }
 
+// acos(x) / pi for x in [-1, 1]: acos(|x|) = sqrt(1 - |x|) * a(|x|) with the
+// degree-7 polynomial a of Abramowitz and Stegun, Handbook of Mathematical
+// Functions, 4.4.46 (absolute error <= 2e-8 on [0, 1]), and
+// acos(x) = pi - acos(-x) for x < 0.
+__device__ inline float acos_over_pi(float x) {
+  const float ax = fabsf(x);
+  float a = -0.0012624911f;
+  a = fmaf(a, ax, 0.0066700901f);
+  a = fmaf(a, ax, -0.0170881256f);
+  a = fmaf(a, ax, 0.0308918810f);
+  a = fmaf(a, ax, -0.0501743046f);
+  a = fmaf(a, ax, 0.0889789874f);
+  a = fmaf(a, ax, -0.2145988016f);
+  a = fmaf(a, ax, 1.5707963050f);
+  const float t = __builtin_amdgcn_sqrtf(1.0f - ax) * a * 0.318309886183790671538f;
+  return x < 0.0f ? 1.0f - t : t;
+}
+// ln(1 + x), x > -1, from the hardware logarithm with the rounding of 1 + x
+// compensated: w = fl(1 + x), ln(1 + x) = ln(w) * x / (w - 1) (Goldberg,
+// "What every computer scientist should know about floating-point
+// arithmetic", Theorem 4).
+__device__ inline float log1p_hw(float x) {
+  const float w = 1.0f + x, d = w - 1.0f;
+  return d == 0.0f ? x : __logf(w) * __fdividef(x, d);
+}
+// The threshold-2 form above with hardware logarithms and exponentials and
+// no divergent branch (both forms are evaluated and one is selected): all
+// lanes of a wave take the same ~60 instructions.
 __device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &cf) {
   if (K == 0) return 0.0f;  // p = 1: every table collides, P = 1
   c = fminf(1.0f, fmaxf(-1.0f, c));
-  const float u = acosf(-c) * 0.318309886183790671538f;
+  const float u = acos_over_pi(-c);
   const float lnp = (float)K * __logf(u);
   const float p = __expf(lnp);
   if (cf.T != 2) return log_sampling_prob_t(lnp, p, L, cf.T, cf.lnct);
   const float Lf = (float)L;
-  if (Lf * p < 1.0f) {
-    const float r = p * __frcp_rn(1.0f - p);
-    float sum = cf.a[LNP_TERMS - 1];
+  const float l1p = log1p_hw(-p);  // ln(1 - p)
+  // L p < 1: the binomial tail from j = 2 (no cancellation for small p)
+  const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
+  float sum = cf.a[LNP_TERMS - 1];
 #pragma unroll
-    for (int i = LNP_TERMS - 2; i >= 0; --i) sum = fmaf(sum, r, cf.a[i]);
-    return cf.lnc2 + 2.0f * lnp + (Lf - 2.0f) * log1pf(-p) + __logf(sum);
-  }
-  return logf(-expm1f((Lf - 1.0f) * log1pf(-p) + log1pf((Lf - 1.0f) * p)));
+  for (int i = LNP_TERMS - 2; i >= 0; --i) sum = fmaf(sum, r, cf.a[i]);
+  const float small = cf.lnc2 + 2.0f * lnp + (Lf - 2.0f) * l1p + __logf(sum);
+  // L p >= 1: ln(1 - e^y), y = (L-1) ln(1-p) + ln(1 + (L-1) p); there
+  // e^y <= 0.74, so 1 - e^y keeps its precision
+  const float y = (Lf - 1.0f) * l1p + __logf(1.0f + (Lf - 1.0f) * p);
+  const float large = __logf(1.0f - __expf(y));
+  return Lf * p < 1.0f ? small : large;
 }
 
 // Maximum and sum over each half (32 lanes) of the wave, every lane ending
@@ -271,7 +303,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
       float lnP = 0.0f;
       if (!(mk & FORCED)) {
         const float den = qn_sh[hh] * (rl > 0.0f ? rl : sqrtf(second ? n1 : n0));
-        const float cosv = den > 0.0f ? (dk - qmu_sh[hh]) / den : 0.0f;
+        const float cosv = den > 0.0f ? __fdividef(dk - qmu_sh[hh], den) : 0.0f;
         lnP = log_sampling_prob(cosv, K, L, cf);
       }
       w = dk * scale - lnP;
@@ -422,9 +454,30 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // tiles the bit-plane index covers are scanned there (threshold 2 only).
   const bool use_bits = c < nlt;
   const bool use_pl = !use_bits && planes != nullptr && K > 0 && cf.T == 2 && c < npt;
+  // A narrow tile (at most 256 keys: the appended keys past an index, a
+  // short last tile) needs fewer than 64 lanes per table row: P = 2^lgp lanes
+  // (one per group of 8 keys) read a row, so a wave reads S = 64 / P of its
+  // rows per load -- rows j0 + slot + S r -- and its chain of dependent load
+  // batches shrinks S-fold.  The lanes of one key group add their mismatch
+  // counts at the end.
+  const int nkg = (int)((tend - tbase + 7) >> 3);
+  const bool narrow = nkg <= 32;
+  const int lgp = !narrow ? 6 : nkg <= 1 ? 0 : 32 - __builtin_clz((unsigned)(nkg - 1));
+  const int nslot = 64 >> lgp, slot = lane >> lgp, kgrp = lane & ((1 << lgp) - 1);
+  const int64_t nlo = (tbase + 8 * kgrp < tend) ? 16 * kgrp : 0;
+  auto load_narrow = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < MP_SB; ++r)
+      if (j0 + nslot * r < ntw)  // uniform: some lane of the wave still has a row here
+        cw[r] = *(const uint4 *)(rows0 + (int64_t)min(j0 + slot + nslot * r, jlast) * rstride + nlo);
+  };
   if (!use_bits && !use_pl && ntw > 0) {
-    load_half(0, 0);
-    load_half(0, 1);
+    if (narrow) {
+      load_narrow(0);
+    } else {
+      load_half(0, 0);
+      load_half(0, 1);
+    }
   }
   // a tile with bitmaps: its words of every head, loaded with the prologue's loads
   uint32_t bword = 0u;
@@ -635,13 +688,45 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         }
       }
     };
+    if (narrow) {  // rows j0 + slot + S r of a batch; rows past the wave's last add no mismatch
+      for (int j0 = 0; j0 < ntw; j0 += nslot * MP_SB) {
+        if (j0 > 0) load_narrow(j0);
+#pragma unroll
+        for (int r = 0; r < MP_SB; ++r) {
+          if (j0 + nslot * r >= ntw) break;  // uniform
+          const int j = j0 + slot + nslot * r;
+          const bool live = j < ntw;
+          const int l = wave + 4 * min(j, jlast);
+          uint32_t Qa[GM];
+          if constexpr (GM != 8) qcodes_of(l, Qa);
+          const uint32_t a4[4] = {cw[r].x, cw[r].y, cw[r].z, cw[r].w};
+#pragma unroll
+          for (int h = 0; h < GM; ++h) {
+            const uint32_t Q = GM == 8 ? qpk[l * GM + h] : Qa[h];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              acc[h][w] += live ? __builtin_bit_cast(uint32_t, __builtin_elementwise_min(
+                                                                   __builtin_bit_cast(u16x2, a4[w] ^ Q), one))
+                                : 0u;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      // the slots of a key group hold disjoint tables: add their counts (two
+      // 16-bit counts per word, each at most the wave's table count)
+      for (int sh = 1 << lgp; sh < 64; sh <<= 1)
+#pragma unroll
+        for (int h = 0; h < GM; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[h][w] += (uint32_t)__shfl_xor((int)acc[h][w], sh);
+    }
     // whole batches (branch-free pairs), then the wave's last, partial batch
     // outside the loop (one code path per loop body keeps the counts in one
     // set of registers)
     // Two halves per batch: the next batch's half is issued as soon as this
     // half's rows have been counted, so a wave keeps loads in flight while
     // it computes.
-    int j0 = 0;
+    int j0 = narrow ? ntw : 0;
     for (; j0 + MP_SB <= ntw; j0 += MP_SB) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -853,7 +938,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
             float lnP = 0.0f;
             if (!(mk & FORCED)) {
               const float den = qn_sh[h] * (rl > 0.0f ? rl : sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
-              const float cosv = den > 0.0f ? (dk - qmu_sh[h]) / den : 0.0f;
+              const float cosv = den > 0.0f ? __fdividef(dk - qmu_sh[h], den) : 0.0f;
               lnP = log_sampling_prob(cosv, K, L, cf);
             }
             w = dk * scale - lnP;

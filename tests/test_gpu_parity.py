@@ -284,6 +284,25 @@ def test_decode_short_and_ragged_n(n):
         assert np.all(cnt == 0) and np.all(out == 0) and np.all(np.isneginf(lse))
 
 
+@pytest.mark.parametrize("name,tail,T,static", [
+    ("tiny", 1, 2, False), ("tiny", 65, 3, True), ("llama8b_layer", 8, 2, False), ("llama8b_layer", 9, 2, True),
+    ("llama8b_layer", 64, 2, False), ("llama8b_layer", 129, 3, False), ("llama8b_layer", 256, 2, True),
+    ("llama8b_layer", 257, 2, False), ("g8_ragged", 33, 2, True), ("g8_ragged", 200, 1, False),
+    ("g3_k16", 100, 2, False), ("g2_small", 250, 2, True), ("g4_f32", 17, 2, False), ("g7_bf16", 5, 2, False)])
+def test_decode_narrow_last_tile(name, tail, T, static):
+    """A last tile of at most 256 keys is scanned with several table rows per
+    load (a key group's lanes spread over the tables and add their counts):
+    tails of 1 to 257 keys, thresholds 1 to 3, forced ranges reaching into
+    the tail, every head count."""
+    w, lay, km, codes, margin, qc = case(name)
+    n = (lay["n"] - tail) // 512 * 512 + tail
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    nsh, nst = (4, 64) if static else (0, 0)
+    out, lse, idx, cnt = _run_decode(w, lay, kmean, gcodes, qcodes, n=n, nsh=nsh, nst=nst, T=T)
+    ref = oracle_decode(w, lay, km, codes, qc, n=n, nsh=nsh, nst=nst, T=T)
+    _compare(w, ref, out, lse, idx, cnt, "%s n=%d T=%d static=%s" % (name, n, T, static))
+
+
 def _dense_oracle(w, q, K, V, n):
     """The oracle's decode with K = 0 (every key sampled with P = 1), which
     the oracle's pins reduce to Equation 1; codes and query codes are 0."""
