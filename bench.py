@@ -74,53 +74,116 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="CPU-oracle baseline budget (0 = skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration under rocprofv3)")
+    ap.add_argument("--trace-stats", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel statistics of the timed decode steps from a rocprofv3 kernel trace of a "
+                         "run with the same --steps/--warmup/--layers/--workload and --alternatives off, and exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 counter_collection.csv files (FETCH_SIZE run, WRITE_SIZE run, both with "
-                         "--calib-copy-mib) into %s and exit" % os.path.relpath(TRAFFIC_FILE, ROOT))
+                         "--calib-copy-mib and --alternatives off, and the same --steps/--warmup/--layers as given "
+                         "here) into %s and exit" % os.path.relpath(TRAFFIC_FILE, ROOT))
     return ap.parse_args()
 
 
-def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, index: str) -> dict:
-    """HBM bytes per sampling-kernel launch from FETCH_SIZE / WRITE_SIZE (KiB per
-    dispatch), each scaled by what the same counter reads for the calibration
-    copy of calib_mib MiB (the largest __amd_rocclr_copyBuffer dispatch)."""
+def traffic_from_counters(fetch_csv: str, write_csv: str, calib_mib: int, workload: str, index: str,
+                          ndecode: int) -> dict:
+    """HBM bytes per launch of the sampling kernel (and of the bucket lookup)
+    in the decode steps from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the same counter reads for the calibration copy of
+    calib_mib MiB (the largest __amd_rocclr_copyBuffer dispatch).  Only the
+    first ndecode dispatches of a kernel count: the steps' (warmup + timed)
+    launches, not the decodes after timing that measure the sampled sets."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_kernel(path, counter, kernel):
         samp, calib = [], []
         with open(path) as f:
-            for r in csv.DictReader(f):
+            for r in sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"])):
                 if r["Counter_Name"] != counter:
                     continue
                 v = float(r["Counter_Value"])
-                if "sample_kernel" in r["Kernel_Name"]:
+                if kernel in r["Kernel_Name"]:
                     samp.append(v)
                 elif "copyBuffer" in r["Kernel_Name"]:
                     calib.append(v)
-        if not samp or not calib:
-            raise SystemExit("%s: no sample_kernel or calibration-copy rows for %s" % (path, counter))
-        return sum(samp) / len(samp), max(calib), len(samp)
+        if not calib:
+            raise SystemExit("%s: no calibration-copy rows for %s" % (path, counter))
+        samp = samp[:ndecode]
+        return (sum(samp) / len(samp) if samp else None), max(calib), len(samp)
 
-    f_s, f_c, nf = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_s, w_c, nw = per_kernel(write_csv, "WRITE_SIZE")
     calib_bytes = calib_mib * (1 << 20)
-    fetch_scale = calib_bytes / (f_c * 1024.0)
-    write_scale = calib_bytes / (w_c * 1024.0)
-    fetch_b = f_s * 1024.0 * fetch_scale
-    write_b = w_s * 1024.0 * write_scale
-    return {"workload": workload, "source_sha": source_sha(DECODE_SRC), "index": index,
-            "bytes_per_launch": fetch_b + write_b,
-            "fetch_bytes_per_launch": fetch_b, "write_bytes_per_launch": write_b,
-            "fetch_size_kib_per_launch": f_s, "write_size_kib_per_launch": w_s, "dispatches": [nf, nw],
-            "calibration": {"copy_mib": calib_mib, "fetch_size_kib": f_c, "write_size_kib": w_c,
-                            "fetch_scale": fetch_scale, "write_scale": write_scale}}
+    res = {"workload": workload, "source_sha": source_sha(DECODE_SRC), "index": index}
+    for kernel, key in (("sample_kernel", ""), ("bucket_lookup_kernel", "lookup_")):
+        f_s, f_c, nf = per_kernel(fetch_csv, "FETCH_SIZE", kernel)
+        w_s, w_c, nw = per_kernel(write_csv, "WRITE_SIZE", kernel)
+        if f_s is None or w_s is None:
+            if not key:
+                raise SystemExit("no sample_kernel rows in the counter files")
+            continue
+        fetch_scale = calib_bytes / (f_c * 1024.0)
+        write_scale = calib_bytes / (w_c * 1024.0)
+        fetch_b = f_s * 1024.0 * fetch_scale
+        write_b = w_s * 1024.0 * write_scale
+        res.update({key + "bytes_per_launch": fetch_b + write_b,
+                    key + "fetch_bytes_per_launch": fetch_b, key + "write_bytes_per_launch": write_b,
+                    key + "fetch_size_kib_per_launch": f_s, key + "write_size_kib_per_launch": w_s,
+                    key + "dispatches": [nf, nw]})
+        res["calibration"] = {"copy_mib": calib_mib, "fetch_size_kib": f_c, "write_size_kib": w_c,
+                              "fetch_scale": fetch_scale, "write_scale": write_scale}
+    return res
+
+
+def trace_stats(path: str, steps: int, warmup: int, nlayers: int) -> str:
+    """Markdown table of the kernels of the timed decode steps in a rocprofv3
+    kernel trace: the sampling-kernel dispatches warmup*nlayers ..
+    (warmup+steps)*nlayers - 1 (set-up launches none), widened back to the
+    launch after the last warmup merge and forward to the merge after the
+    last of them."""
+    import csv
+
+    with open(path) as f:
+        rows = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                       for r in csv.DictReader(f) if r["Kind"] == "KERNEL_DISPATCH"))
+    samp = [i for i, r in enumerate(rows) if "sample_kernel" in r[2]]
+    if len(samp) < (warmup + steps) * nlayers:
+        raise SystemExit("%s: %d sampling-kernel dispatches, expected at least %d" %
+                         (path, len(samp), (warmup + steps) * nlayers))
+    if warmup < 1:
+        raise SystemExit("--trace-stats needs --warmup >= 1 (the window starts after a warmup step's merge)")
+    lo, hi = samp[warmup * nlayers], samp[(warmup + steps) * nlayers - 1]
+    while lo > 0 and "merge_kernel" not in rows[lo - 1][2]:  # back to the previous step's last merge
+        lo -= 1
+    while hi + 1 < len(rows) and "merge_kernel" not in rows[hi][2]:
+        hi += 1
+    win = rows[lo:hi + 1]
+    by = {}
+    for s0, e0, name in win:
+        short = name.split("(")[0]
+        for key in ("encode_small_kernel", "encode_kernel", "bucket_lookup_kernel", "sample_kernel", "merge_kernel"):
+            if key in short:
+                short = key
+        by.setdefault(short, []).append((e0 - s0) / 1e3)
+    span = (win[-1][1] - win[0][0]) / 1e3
+    out = ["| kernel | calls | avg us | min us | max us | total us per step |", "|---|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        out.append("| %s | %d | %.2f | %.2f | %.2f | %.1f |" % (k, len(v), sum(v) / len(v), min(v), max(v),
+                                                              sum(v) / steps))
+    out.append("")
+    out.append("timed steps: %d; first to last dispatch %.1f us = %.1f us per step; kernel time %.1f us per step"
+               % (steps, span, span / steps, sum(sum(v) for v in by.values()) / steps))
+    return "\n".join(out)
 
 
 def main() -> int:
     args = parse()
+    if args.trace_stats:
+        w = __import__("synth").WORKLOADS[args.workload]
+        print(trace_stats(args.trace_stats, args.steps, args.warmup, args.layers or w.layers))
+        return 0
     if args.traffic:
+        w = __import__("synth").WORKLOADS[args.workload]
         tr = traffic_from_counters(args.traffic[0], args.traffic[1], args.calib_copy_mib, args.workload,
-                                   args.index if args.threshold == 2 else "codes")
+                                   args.index if args.threshold == 2 else "codes",
+                                   (args.steps + args.warmup) * (args.layers or w.layers))
         with open(TRAFFIC_FILE, "w") as f:
             json.dump(tr, f, indent=1)
         print(json.dumps(tr))
@@ -312,20 +375,21 @@ def main() -> int:
         return U * (code + 2 * d * e * union_per_unit + G * (d * e + 2 * L) + 4 * d)
 
     # the bucket lookup kernel (before the sampling kernel): the query's bucket
-    # entries (2 bytes each), two 2-byte offsets per head, table and 4096-key
+    # entries (2 bytes each), one 4-byte start/count word per head, table and
     # chunk, the query codes; it writes the sampled-key words
-    nbc = (n_planes + 4095) // 4096
+    nbc = (n_planes + mp.MP_BUCKET_CHUNK - 1) // mp.MP_BUCKET_CHUNK
     lookup_bytes = (2 * bucket_entries / max(len(sampled_layers), 1) + U * G * L * (nbc * 4 + 2)
                     + U * G * 64 * n_planes / 512) if use_buckets else None
     bytes_launch = launch_bytes(args.index)
     achieved = bytes_launch / (kern_ms.mean() * 1e-3) / 1e9
-    traffic = None
+    traffic = lookup_traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         if (tr.get("source_sha") == source_sha(DECODE_SRC) and tr.get("workload") == w.name and not pages and
                 args.threshold == 2 and tr.get("index") == args.index):
             traffic = tr.get("bytes_per_launch")
+            lookup_traffic = tr.get("lookup_bytes_per_launch")
     alternatives = {}
     for m in modes[1:]:
         wm, em, km, nt, _ = timing[m]
@@ -410,7 +474,8 @@ def main() -> int:
                      "kernel": "sample_kernel (mp_decode_step / mp_decode_sample)", "kernel_us": kern_ms.mean() * 1e3,
                      "algorithmic_bytes_per_launch": bytes_launch, "device_copy_GBs": copy_gbs,
                      "frac_of_device_copy": achieved / copy_gbs,
-                     "bucket_lookup_bytes_per_launch": lookup_bytes},
+                     "bucket_lookup_bytes_per_launch": lookup_bytes,
+                     "bucket_lookup_traffic_per_launch": lookup_traffic},
         "index_alternatives": alternatives,
         "step": {"latency_ms": wall_ms, "latency_ms_events": ev_ms, "bytes_per_step": step_bytes,
                  "frac_hbm_step": step_bytes / (wall_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -194,17 +194,19 @@ int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, in
  * key is in the query's bucket of table l exactly when codes[u][l][i] equals
  * the query's code of table l.
  * Layout (one buffer of mp_buckets_bytes(U, cap, K, L) bytes): keys are cut
- * into chunks of 4096; per (unit, table, chunk) a CSR of the chunk's keys
- * ordered by code --
- *   off   [U][L][ceil(cap/4096)][2^K + 1] uint16 at the buffer's start:
- *         bucket c of chunk r holds entries off[c] .. off[c+1] - 1;
+ * into chunks of MP_BUCKET_CHUNK (8192); per (unit, table, chunk) a CSR of
+ * the chunk's keys ordered by code --
+ *   off   [U][L][2^K][ceil(cap/8192)] uint32 at the buffer's start: word
+ *         (u, l, c, r) = start | count << 16, bucket c of chunk r holds
+ *         entries start .. start + count - 1 (a bucket's words for all
+ *         chunks are adjacent: a lookup reads one line of them per table);
  *   keys  [U][L][cap] uint16, starting at the next 256-byte boundary:
- *         entry j of chunk r of table l is keys[u][l][4096 r + j], the key's
+ *         entry j of chunk r of table l is keys[u][l][8192 r + j], the key's
  *         offset from the chunk's first key (the order inside a bucket is
  *         not fixed).
- * mp_build_buckets (re)builds the chunks [n0/4096, ceil(n1/4096)) from the
+ * mp_build_buckets (re)builds the chunks [n0/8192, ceil(n1/8192)) from the
  * codes of keys below n1 (written by mp_build_codes / mp_append); n0 a
- * multiple of 4096, n1 a multiple of 512, 0 <= n0 <= n1 <= cap.  Appends do
+ * multiple of 8192, n1 a multiple of 512, 0 <= n0 <= n1 <= cap.  Appends do
  * not update it: a decode uses the buckets for the 512-key tiles below its
  * n_buckets and the codes (or planes) above, so the caller rebuilds the
  * newest chunk once a tile has filled.  1 <= K <= 12.
@@ -212,6 +214,7 @@ int mp_build_planes(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, in
  * MP_ERR_UNSUPPORTED (shape), MP_ERR_WORKSPACE (buffer smaller than
  * mp_buckets_bytes), MP_ERR_HIP.
  */
+#define MP_BUCKET_CHUNK 8192
 size_t mp_buckets_bytes(int64_t U, int64_t cap, int K, int L);
 int mp_build_buckets(const uint16_t *codes, int64_t U, int64_t n0, int64_t n1, int64_t cap, int K, int L,
                      void *buckets, size_t buckets_bytes, void *stream);

@@ -68,6 +68,7 @@ _SIGS = {
 }
 
 MP_STATIC_SCRATCH_BYTES = 32 << 20  # size of the library's static scratch (include/magicpig.h)
+MP_BUCKET_CHUNK = 8192  # keys per chunk of the bucketed tables (magicpig.h)
 
 _lib = None
 
@@ -279,7 +280,7 @@ def mp_buckets_bytes(U: int, cap: int, K: int, L: int) -> int:
 def mp_build_buckets(codes: torch.Tensor, K: int, n1: int, n0: int = 0, buckets: Optional[torch.Tensor] = None,
                      stream=None) -> torch.Tensor:
     """Bucketed hash tables of ``codes`` ([U][L][cap] uint16) for the chunks
-    of 4096 keys from n0 (a multiple of 4096) up to n1 (a multiple of 512).
+    of MP_BUCKET_CHUNK keys from n0 (a multiple of MP_BUCKET_CHUNK) up to n1 (a multiple of 512).
 
     Returns (or fills) ``buckets``: a uint8 buffer of mp_buckets_bytes bytes."""
     U, L, cap = codes.shape

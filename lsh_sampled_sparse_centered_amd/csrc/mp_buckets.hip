@@ -20,8 +20,8 @@ BucketLayout bucket_layout(void *base, int64_t U, int64_t cap, int K, int L) {
   BucketLayout b;
   b.nbins = 1 << K;
   b.bchunks = (cap + BK_R - 1) / BK_R;
-  const size_t off_bytes = align256(sizeof(uint16_t) * (size_t)U * L * b.bchunks * (b.nbins + 1));
-  b.off = (uint16_t *)base;  // a NULL base asks for the size only
+  const size_t off_bytes = align256(sizeof(uint32_t) * (size_t)U * L * b.nbins * b.bchunks);
+  b.off = (uint32_t *)base;  // a NULL base asks for the size only
   b.keys = base ? (uint16_t *)((char *)base + off_bytes) : nullptr;
   b.bytes = off_bytes + align256(sizeof(uint16_t) * (size_t)U * L * cap);
   return b;
@@ -54,14 +54,14 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t *wsum, uint32_t 
 // --------------------------------------------------------------------------
 // Build: one block per (unit, table, chunk).  Counting sort of the chunk's
 // keys by code: a histogram of the 2^K codes in LDS (16-bit counters, two
-// per word), its exclusive prefix sum gives the bucket offsets, and each key
+// per word), its exclusive prefix sum gives the bucket starts, and each key
 // takes the next slot of its bucket (an LDS atomic: the order of equal codes
 // inside a bucket is not fixed, which the lookup does not depend on).
 constexpr int BB_KPT = BK_R / 256;  // keys per thread
 
 __global__ __launch_bounds__(256) void bucket_build_kernel(const uint16_t *__restrict__ codes, int64_t cap, int K,
                                                            int64_t c0, int64_t nc, int64_t n1, int64_t bchunks,
-                                                           uint16_t *__restrict__ boff,
+                                                           uint32_t *__restrict__ boff,
                                                            uint16_t *__restrict__ bkeys) {
   extern __shared__ uint32_t hist[];  // 2^K 16-bit counters, two per word
   __shared__ uint32_t wsum[4];
@@ -93,18 +93,17 @@ __global__ __launch_bounds__(256) void bucket_build_kernel(const uint16_t *__res
     for (int w = 0; w < wpt; ++w) sum += (hist[w0 + w] & 0xffffu) + (hist[w0 + w] >> 16);
   uint32_t total;
   uint32_t run = block_excl_scan(sum, wsum, &total);
-  uint16_t *off = boff + (ul * bchunks + ci) * (int64_t)(nbins + 1);
+  uint32_t *off = boff + ul * (int64_t)nbins * bchunks + ci;  // bucket c's word at off[c * bchunks]
   if (owns) {
     for (int w = 0; w < wpt; ++w) {
       const uint32_t h = hist[w0 + w];
       const uint32_t a = run, b = run + (h & 0xffffu);
-      off[2 * (w0 + w)] = (uint16_t)a;
-      off[2 * (w0 + w) + 1] = (uint16_t)b;
+      off[(int64_t)(2 * (w0 + w)) * bchunks] = a | ((h & 0xffffu) << 16);
+      off[(int64_t)(2 * (w0 + w) + 1) * bchunks] = b | ((h >> 16) << 16);
       hist[w0 + w] = a | (b << 16);  // the buckets' next free slots
       run = b + (h >> 16);
     }
   }
-  if (threadIdx.x == 0) off[nbins] = (uint16_t)nk;
   __syncthreads();
   uint16_t *dst = bkeys + ul * cap + r0;
 #pragma unroll
@@ -132,10 +131,10 @@ hipError_t launch_bucket_build(const uint16_t *codes, int64_t U, int64_t cap, in
 // --------------------------------------------------------------------------
 // Lookup (per decode step): one block per (unit, query head, chunk of BK_R
 // keys below nb).
-//  1. Segments: for table l the query's bucket c = qcode[l] is entries
-//     off[c] .. off[c+1] - 1 of the chunk's table l.  Thread t reads the
-//     offsets of tables t * spt .. (all loads in flight), and a block-wide
-//     prefix sum of the segment lengths numbers the entries.
+//  1. Segments: for table l the query's bucket c = qcode[l] holds the
+//     entries start .. start + count - 1 of the chunk's table l (one word).
+//     Thread t reads the words of tables t * spt .. (all loads in flight),
+//     and a block-wide prefix sum of the counts numbers the entries.
 //  2. Entries, in windows of BL_W: each thread writes its own segments'
 //     table number into an LDS slot per entry of the window, then thread t
 //     takes entries t, t + 256, ... of the window (all key loads in flight)
@@ -149,7 +148,7 @@ constexpr int BL_EPT = BL_W / 256;  // entries per thread and window
 constexpr int BL_WORDS = BK_R / 32;
 
 __global__ __launch_bounds__(256) void bucket_lookup_kernel(const uint16_t *__restrict__ qcodes,
-                                                            const uint16_t *__restrict__ boff,
+                                                            const uint32_t *__restrict__ boff,
                                                             const uint16_t *__restrict__ bkeys, int Hq, int Hkv, int G,
                                                             int64_t nb, int64_t cap, int K, int L, int64_t bchunks,
                                                             int64_t nbc, int64_t bwords, uint32_t *__restrict__ sbits) {
@@ -183,11 +182,10 @@ __global__ __launch_bounds__(256) void bucket_lookup_kernel(const uint16_t *__re
 #pragma unroll
     for (int k = 0; k < MAX_SPT; ++k) {
       const int l = min(l0 + k, L - 1);
-      const uint16_t *o = boff + ((u * L + l) * bchunks + ci) * (int64_t)(nbins + 1) + qc[k];
-      const uint32_t a = k < spt ? o[0] : 0u, b = k < spt ? o[1] : 0u;
+      const uint32_t wv = k < spt ? boff[((u * L + l) * nbins + qc[k]) * bchunks + ci] : 0u;
       const bool mine = k < spt && l0 + k < L;
-      src[k] = a;
-      len[k] = mine ? b - a : 0u;
+      src[k] = wv & 0xffffu;
+      len[k] = mine ? wv >> 16 : 0u;
     }
   }
   uint32_t part = 0;

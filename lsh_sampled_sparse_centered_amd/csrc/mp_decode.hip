@@ -30,9 +30,15 @@ constexpr uint32_t FORCED = 0x8000u;  // entry flag: forced key (probability 1)
 constexpr int ATT_E = 32;  // list entries per attention round
 constexpr int VT_STRIDE = 40;  // entries per row of the transposed value rows (32 + padding, 16-byte rows)
 
-LnPCoef lnp_coef(int L, int T) {
+LnPCoef lnp_coef(int K, int L, int T) {
   LnPCoef c{};
   c.T = T;
+  c.Kf = (float)K;
+  c.Lf = (float)L;
+  c.Lm1 = (float)(L - 1);
+  c.Lm2 = (float)(L - 2);
+  c.Tf = (float)T;
+  c.LmT = (float)(L - T);
   c.lnct = (float)(std::lgamma((double)L + 1.0) - std::lgamma((double)T + 1.0) - std::lgamma((double)(L - T) + 1.0));
   double a = 1.0;  // C(L, 2+i) / C(L, 2), by the ratio C(L, k+1) / C(L, k) = (L-k)/(k+1)
   for (int i = 0; i < LNP_TERMS; ++i) {
@@ -97,24 +103,35 @@ DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L
 //             t_{j+1}/t_j = (L-j)/(j+1) r; past the mode (<= T) the terms
 //             only fall, and the sum stops once a term is below 1e-8 of it;
 //   L p >  T: P = 1 - sum_{j<T} C(L,j) p^j (1-p)^(L-j) (P is not small there).
-__device__ inline float log_sampling_prob_t(float lnp, float p, int L, int T, float lnct) {
+__device__ inline float log_sampling_prob_t(float lnp, float p, int L, int T, const LnPCoef &cf) {
   if (p >= 1.0f) return 0.0f;
   const float l1p = log1pf(-p), r = p / (1.0f - p);
-  if ((float)L * p <= (float)T) {
+  if (cf.Lf * p <= cf.Tf) {
     float sum = 1.0f, term = 1.0f;
     for (int j = T; j < L; ++j) {
-      term *= (float)(L - j) / (float)(j + 1) * r;
+      term *= (float)(L - j) * __builtin_amdgcn_rcpf((float)(j + 1)) * r;
       sum += term;
       if (term < 1e-8f * sum) break;
     }
-    return lnct + (float)T * lnp + (float)(L - T) * l1p + __logf(sum);
+    return cf.lnct + cf.Tf * lnp + cf.LmT * l1p + __logf(sum);
   }
-  float term = __expf((float)L * l1p), below = term;  // j = 0
+  float term = __expf(cf.Lf * l1p), below = term;  // j = 0
   for (int j = 0; j + 1 < T; ++j) {
-    term *= (float)(L - j) / (float)(j + 1) * r;
+    term *= (float)(L - j) * __builtin_amdgcn_rcpf((float)(j + 1)) * r;
     below += term;
   }
   return log1pf(-fminf(below, 1.0f));
+}
+
+// The kernel arguments of the sampling kernel span five 64-byte lines, which
+// the compiler loads where each is first used -- in a chain of dependent
+// scalar loads, each a memory round trip when it misses.  One scalar load
+// per line at entry brings all five in together (reads only).
+__device__ inline void touch_kernargs() {
+  typedef const __attribute__((address_space(4))) uint32_t karg_t;
+  karg_t *kp = (karg_t *)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t x = kp[0] ^ kp[16] ^ kp[32] ^ kp[48] ^ kp[64];
+  asm volatile("" ::"s"(x));
 }
 
 // acos(x) / pi for x in [-1, 1]: acos(|x|) = sqrt(1 - |x|) * a(|x|) with the
@@ -134,13 +151,17 @@ __device__ inline float acos_over_pi(float x) {
   const float t = __builtin_amdgcn_sqrtf(1.0f - ax) * a * 0.318309886183790671538f;
   return x < 0.0f ? 1.0f - t : t;
 }
+// The hardware's base-2 logarithm and exponential (one instruction each,
+// about 1 ulp; no denormal scaling: their arguments here are normal or 0).
+__device__ inline float hw_ln(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+__device__ inline float hw_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.442695040888963407f); }
 // ln(1 + x), x > -1, from the hardware logarithm with the rounding of 1 + x
 // compensated: w = fl(1 + x), ln(1 + x) = ln(w) * x / (w - 1) (Goldberg,
 // "What every computer scientist should know about floating-point
 // arithmetic", Theorem 4).
 __device__ inline float log1p_hw(float x) {
   const float w = 1.0f + x, d = w - 1.0f;
-  return d == 0.0f ? x : __logf(w) * __fdividef(x, d);
+  return d == 0.0f ? x : hw_ln(w) * (x * __builtin_amdgcn_rcpf(d));
 }
 // The threshold-2 form above with hardware logarithms and exponentials and
 // no divergent branch (both forms are evaluated and one is selected): all
@@ -149,22 +170,21 @@ __device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &
   if (K == 0) return 0.0f;  // p = 1: every table collides, P = 1
   c = fminf(1.0f, fmaxf(-1.0f, c));
   const float u = acos_over_pi(-c);
-  const float lnp = (float)K * __logf(u);
-  const float p = __expf(lnp);
-  if (cf.T != 2) return log_sampling_prob_t(lnp, p, L, cf.T, cf.lnct);
-  const float Lf = (float)L;
+  const float lnp = cf.Kf * hw_ln(u);
+  const float p = hw_exp(lnp);
+  if (cf.T != 2) return log_sampling_prob_t(lnp, p, L, cf.T, cf);
   const float l1p = log1p_hw(-p);  // ln(1 - p)
   // L p < 1: the binomial tail from j = 2 (no cancellation for small p)
   const float r = p * __builtin_amdgcn_rcpf(1.0f - p);
   float sum = cf.a[LNP_TERMS - 1];
 #pragma unroll
   for (int i = LNP_TERMS - 2; i >= 0; --i) sum = fmaf(sum, r, cf.a[i]);
-  const float small = cf.lnc2 + 2.0f * lnp + (Lf - 2.0f) * l1p + __logf(sum);
+  const float small = cf.lnc2 + 2.0f * lnp + cf.Lm2 * l1p + hw_ln(sum);
   // L p >= 1: ln(1 - e^y), y = (L-1) ln(1-p) + ln(1 + (L-1) p); there
   // e^y <= 0.74, so 1 - e^y keeps its precision
-  const float y = (Lf - 1.0f) * l1p + __logf(1.0f + (Lf - 1.0f) * p);
-  const float large = __logf(1.0f - __expf(y));
-  return Lf * p < 1.0f ? small : large;
+  const float y = cf.Lm1 * l1p + hw_ln(fmaf(cf.Lm1, p, 1.0f));
+  const float large = hw_ln(1.0f - hw_exp(y));
+  return cf.Lf * p < 1.0f ? small : large;
 }
 
 // Maximum and sum over each half (32 lanes) of the wave, every lane ending
@@ -302,8 +322,8 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
     if ((mk >> hh) & 1u) {
       float lnP = 0.0f;
       if (!(mk & FORCED)) {
-        const float den = qn_sh[hh] * (rl > 0.0f ? rl : sqrtf(second ? n1 : n0));
-        const float cosv = den > 0.0f ? __fdividef(dk - qmu_sh[hh], den) : 0.0f;
+        const float den = qn_sh[hh] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(second ? n1 : n0));
+        const float cosv = den > 0.0f ? (dk - qmu_sh[hh]) * __builtin_amdgcn_rcpf(den) : 0.0f;
         lnP = log_sampling_prob(cosv, K, L, cf);
       }
       w = dk * scale - lnP;
@@ -354,7 +374,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     int64_t cap, int K, int L, int64_t nsh, int64_t nst, int64_t nchunks, float scale, uint32_t one2, LnPCoef cf,
     float *__restrict__ part, uint32_t *__restrict__ ent, int32_t *__restrict__ ent_cnt,
     const uint32_t *__restrict__ planes, int64_t npt, int64_t ptiles, const uint32_t *__restrict__ sbits,
-    int64_t bwords, int64_t nlt, const float *__restrict__ rlift) {
+    int64_t bwords, int64_t nlt, const float *__restrict__ rlift, int nunits) {
   // Per-wave match flags of the lane's 8 keys for every head: bit h*8+k of
   // words [0, FW) says "at least one of this wave's tables matched", of
   // words [FW, 2FW) "at least two".
@@ -399,6 +419,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   __shared__ float mrun[GM], alpha_sh[GM];  // per head: running maximum, this round's rescale factor
   __shared__ float lsum[GM];                 // per head: running normaliser (matrix-core rounds)
 
+  touch_kernargs();
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
   const int j16 = lane & 15, grp = tid >> 4;
@@ -409,12 +430,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // appended keys past the bucketed tables: a few per unit, each a chain of
   // dependent load batches) are dispatched first, so their scans overlap the
   // other tiles' attention instead of trailing it.
-  const int64_t U = (int64_t)gridDim.x / nchunks;
-  const int64_t u = blockIdx.x % U;
-  const int64_t cr = blockIdx.x / U, nscan = nchunks - nlt;
+  // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
+  const uint32_t bx = blockIdx.x, U32 = (uint32_t)nunits;
+  const int64_t u = (int64_t)(bx % U32);
+  const int64_t cr = (int64_t)(bx / U32), nscan = nchunks - nlt;
   const int64_t c = nlt > 0 ? (cr < nscan ? nlt + cr : cr - nscan) : cr;
-  const int64_t b = u / Hkv, kvh = u % Hkv;
-  const int64_t qrow0 = b * Hq + kvh * G;  // first query head of this unit
+  const int b = (int)u / Hkv, kvh = (int)u % Hkv;
+  const int64_t qrow0 = (int64_t)b * Hq + (int64_t)kvh * G;  // first query head of this unit
   // keys hashed lifted (Equation 8): the sampling angle is taken against the
   // lifted key, whose norm is the unit's radius (0: not lifted)
   const float rl = rlift ? rlift[u] : 0.0f;
@@ -937,8 +959,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
             const float dk = sm.m.sdot[0][h][e] + sm.m.sdot[1][h][e];
             float lnP = 0.0f;
             if (!(mk & FORCED)) {
-              const float den = qn_sh[h] * (rl > 0.0f ? rl : sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
-              const float cosv = den > 0.0f ? __fdividef(dk - qmu_sh[h], den) : 0.0f;
+              const float den = qn_sh[h] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
+              const float cosv = den > 0.0f ? (dk - qmu_sh[h]) * __builtin_amdgcn_rcpf(den) : 0.0f;
               lnP = log_sampling_prob(cosv, K, L, cf);
             }
             w = dk * scale - lnP;
@@ -947,11 +969,11 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         const float mr = xor32_max(w);  // within the 32 lanes of h
         const float mo = mrun[h];
         const float mn = fmaxf(mo, mr);
-        const float pe = mn > -INFINITY ? __expf(w - mn) : 0.0f;  // 0 for -inf
+        const float pe = mn > -INFINITY ? hw_exp(w - mn) : 0.0f;  // 0 for -inf
         const float ps = xor32_sum(pe);
         sm.m.p[h][e] = pe;
         if (e == 0) {
-          const float alpha = mn > -INFINITY ? __expf(mo - mn) : 1.0f;  // 0 while mo = -inf
+          const float alpha = mn > -INFINITY ? hw_exp(mo - mn) : 1.0f;  // 0 while mo = -inf
           alpha_sh[h] = alpha;
           mrun[h] = mn;
           lsum[h] = lsum[h] * alpha + ps;
@@ -1048,9 +1070,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       for (int sh = ATT_E / 2; sh > 0; sh >>= 1) mr = fmaxf(mr, __shfl_xor(mr, sh));  // within the 32 lanes of h
       const float mo = mrun[h];
       const float mn = fmaxf(mo, mr);
-      if (h < G && e < ne) sm.a.lw[h][e] = mn > -INFINITY ? __expf(x - mn) : 0.0f;  // 0 for -inf
+      if (h < G && e < ne) sm.a.lw[h][e] = mn > -INFINITY ? hw_exp(x - mn) : 0.0f;  // 0 for -inf
       if (e == 0) {
-        alpha_sh[h] = mn > -INFINITY ? __expf(mo - mn) : 1.0f;  // 0 while mo = -inf
+        alpha_sh[h] = mn > -INFINITY ? hw_exp(mo - mn) : 1.0f;  // 0 while mo = -inf
         mrun[h] = mn;
       }
     }
@@ -1147,7 +1169,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
   const uint32_t one2 = 0x00010001u;
-  const LnPCoef cf = lnp_coef(L, Tthr);
+  const LnPCoef cf = lnp_coef(K, L, Tthr);
   uint32_t *ent = want_idx ? ws.ent : nullptr;
   int32_t *ent_cnt = want_idx ? ws.ent_cnt : nullptr;
   const int64_t npt = planes ? n_planes / SCAN_TILE : 0;  // tiles the plane index covers
@@ -1157,7 +1179,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
                         nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles, ws.bits, \
-                        geo.nchunks_max * (SCAN_TILE / 32), nlt, rlift)
+                        geo.nchunks_max * (SCAN_TILE / 32), nlt, rlift, (int)geo.U)
 #define MP_SAMPLE_G(T) \
   do {                 \
     if (G == 1)        \

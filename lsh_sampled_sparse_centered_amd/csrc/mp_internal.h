@@ -47,8 +47,9 @@ struct LnPCoef {
   float lnc2;
   float lnct;
   int T;  // collision threshold: a key is sampled in at least T of L tables
+  float Kf, Lf, Lm1, Lm2, Tf, LmT;  // K, L, L - 1, L - 2, T, L - T as floats (no conversions in the kernel)
 };
-LnPCoef lnp_coef(int L, int T);
+LnPCoef lnp_coef(int K, int L, int T);
 
 struct DecodeGeom {
   int64_t U;          // units = B * Hkv
@@ -158,14 +159,16 @@ hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGe
 
 // ---------------------------------------------------------------- bucketed tables
 // Per (unit, table, chunk of BK_R keys) a table of 2^K buckets: the chunk's
-// keys ordered by their code (CSR).  off [U][L][bchunks][2^K + 1] uint16
-// (bucket c of the chunk holds entries off[c] .. off[c+1] - 1), keys
-// [U][L][cap] uint16 (entry j of chunk r at keys[u][l][r * BK_R + j], the key's
-// offset from the chunk's first key).
-constexpr int BK_R = 4096;  // keys per bucket chunk (8 scan tiles)
+// keys ordered by their code (CSR).  off [U][L][2^K][bchunks] uint32: word
+// (u, l, c, r) = start | count << 16 of bucket c in chunk r (its entries
+// are keys[u][l][r * BK_R + start ..]; the words of one bucket over all
+// chunks are adjacent, so a lookup of a (unit, head, table) touches one
+// line of offsets); keys [U][L][cap] uint16 (the key's offset from its
+// chunk's first key).
+constexpr int BK_R = 8192;  // keys per bucket chunk (16 scan tiles); starts and counts fit 16 bits
 constexpr int MAX_BK_K = 12;  // bits per table the bucketed tables support (2^K buckets per chunk)
 struct BucketLayout {
-  uint16_t *off;
+  uint32_t *off;
   uint16_t *keys;
   int64_t bchunks;  // chunks per unit for the capacity
   int nbins;        // 2^K

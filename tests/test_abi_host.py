@@ -167,8 +167,9 @@ def test_build_planes_rejects_invalid_arguments():
 
 def test_build_buckets_rejects_invalid_arguments():
     L = mp.lib()
-    # offsets: 2^K + 1 per (unit, table, 4096-key chunk), then the keys, each part 256-byte aligned
-    off = 8 * 150 * 25 * 1025 * 2
+    # offsets: one 4-byte word per (unit, table, bucket, 8192-key chunk), then the keys, each part
+    # 256-byte aligned
+    off = 8 * 150 * 1024 * 13 * 4
     assert L.mp_buckets_bytes(8, 98368, 10, 150) == (off + 255) // 256 * 256 + 8 * 150 * 98368 * 2
     assert L.mp_buckets_bytes(2, 1024, 0, 75) == 0
     assert L.mp_buckets_bytes(2, 1024, 13, 75) == 0
@@ -183,7 +184,8 @@ def test_build_buckets_rejects_invalid_arguments():
     assert b(codes=None) == ARG
     assert b(bk=None) == ARG
     assert b(bk=FAKE + 4) == ARG
-    assert b(n0=512) == ARG  # chunk starts are multiples of 4096
+    assert b(n0=512) == ARG  # chunk starts are multiples of 8192
+    assert b(n0=4096, n1=4096, cap=8192) == ARG
     assert b(n1=1000) == ARG
     assert b(n1=1536) == ARG  # past cap
     assert b(K=0) == UNSUP

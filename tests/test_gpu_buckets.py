@@ -2,7 +2,7 @@
 decode that looks the query's buckets up instead of scanning.
 
 A key sits in bucket c of table l exactly when its code of table l is c, so:
-(1) unpacked on the host, every bucket of every (unit, table, 4096-key
+(1) unpacked on the host, every bucket of every (unit, table, 8192-key
 chunk) holds exactly the keys whose code is that bucket's; (2) a decode that
 takes the tiles below n_buckets from the buckets gives the same sampled index
 lists, counts and outputs as the decode that scans the codes, bit for bit,
@@ -21,29 +21,34 @@ from tests.test_gpu_parity import CASES, _compare, _inject, case, gpu_build
 
 pytestmark = pytest.mark.gpu
 
-CHUNK = 4096
+CHUNK = mp.MP_BUCKET_CHUNK
 
 
 def unpack_buckets(buf: np.ndarray, U: int, L: int, cap: int, K: int):
-    """Host view of the layout: off [U][L][chunks][2^K + 1], keys [U][L][cap] (uint16)."""
+    """Host view of the layout: words [U][L][2^K][chunks] (start | count << 16), keys [U][L][cap]
+    (uint16).  Returns the bucket offsets as [U][L][chunks][2^K + 1] (bucket c of chunk r: entries
+    off[c] .. off[c+1] - 1), checking that each bucket starts where the one before it ends."""
     nb = 1 << K
     chunks = (cap + CHUNK - 1) // CHUNK
-    noff = U * L * chunks * (nb + 1)
-    off_bytes = (2 * noff + 255) // 256 * 256
-    off = buf[:2 * noff].view(np.uint16).reshape(U, L, chunks, nb + 1)
+    noff = U * L * nb * chunks
+    off_bytes = (4 * noff + 255) // 256 * 256
+    words = buf[:4 * noff].view(np.uint32).reshape(U, L, nb, chunks).transpose(0, 1, 3, 2).astype(np.int64)
+    start, count = words & 0xffff, words >> 16
+    off = np.concatenate([start, (start[..., -1:] + count[..., -1:])], axis=3)
     keys = buf[off_bytes:off_bytes + 2 * U * L * cap].view(np.uint16).reshape(U, L, cap)
-    return off, keys
+    return off, keys, start, count
 
 
 def check_buckets_hold_their_codes(buf, codes, K, n1, n0=0):
-    """Every bucket of the chunks [n0/4096, ceil(n1/4096)) holds exactly the keys with its code."""
+    """Every bucket of the chunks [n0/CHUNK, ceil(n1/CHUNK)) holds exactly the keys with its code."""
     U, L, cap = codes.shape
-    off, keys = unpack_buckets(buf, U, L, cap, K)
+    off, keys, start, count = unpack_buckets(buf, U, L, cap, K)
     nb = 1 << K
     for ci in range(n0 // CHUNK, (n1 + CHUNK - 1) // CHUNK):
         r0, r1 = ci * CHUNK, min((ci + 1) * CHUNK, n1)
         o = off[:, :, ci].astype(np.int64)  # [U][L][nb + 1]
         assert np.all(o[:, :, 0] == 0) and np.all(o[:, :, nb] == r1 - r0)
+        assert np.array_equal(start[:, :, ci, 1:], start[:, :, ci, :-1] + count[:, :, ci, :-1])  # contiguous
         assert np.all(np.diff(o, axis=2) >= 0)
         c = codes[:, :, r0:r1].astype(np.int64)
         k = keys[:, :, r0:r1].astype(np.int64)  # entries of the chunk, ordered by bucket
