@@ -157,13 +157,16 @@ __global__ __launch_bounds__(256) void bucket_lookup_kernel(const uint16_t *__re
   __shared__ uint16_t eseg[BL_W];
   __shared__ uint32_t wsum[4];
   const int tid = threadIdx.x;
+  touch_kernargs<2>();  // 96 bytes of arguments
   // blocks run chunk-major (the sampling grid's order): chunk, unit, head
-  const int64_t UG = (int64_t)gridDim.x / nbc;
-  const int64_t ci = (int64_t)blockIdx.x / UG;
-  const int64_t ug = (int64_t)blockIdx.x % UG;  // unit * G + head
-  const int64_t u = ug / G;
-  const int h = (int)(ug % G);
-  const int64_t qrow = (u / Hkv) * Hq + (u % Hkv) * G + h;
+  // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
+  const uint32_t UG = gridDim.x / (uint32_t)nbc, bx = blockIdx.x;
+  const int64_t ci = (int64_t)(bx / UG);
+  const int64_t ug = (int64_t)(bx % UG);  // unit * G + head
+  const int ui = (int)ug / G;
+  const int64_t u = ui;
+  const int h = (int)ug % G;
+  const int64_t qrow = (int64_t)(ui / Hkv) * Hq + (int64_t)(ui % Hkv) * G + h;
   const int64_t r0 = ci * BK_R, r1 = min(r0 + BK_R, nb);
   const int nbins = 1 << K;
   for (int i = tid; i < BL_WORDS; i += 256) {

@@ -123,17 +123,6 @@ __device__ inline float log_sampling_prob_t(float lnp, float p, int L, int T, co
   return log1pf(-fminf(below, 1.0f));
 }
 
-// The kernel arguments of the sampling kernel span five 64-byte lines, which
-// the compiler loads where each is first used -- in a chain of dependent
-// scalar loads, each a memory round trip when it misses.  One scalar load
-// per line at entry brings all five in together (reads only).
-__device__ inline void touch_kernargs() {
-  typedef const __attribute__((address_space(4))) uint32_t karg_t;
-  karg_t *kp = (karg_t *)__builtin_amdgcn_kernarg_segment_ptr();
-  const uint32_t x = kp[0] ^ kp[16] ^ kp[32] ^ kp[48] ^ kp[64];
-  asm volatile("" ::"s"(x));
-}
-
 // acos(x) / pi for x in [-1, 1]: acos(|x|) = sqrt(1 - |x|) * a(|x|) with the
 // degree-7 polynomial a of Abramowitz and Stegun, Handbook of Mathematical
 // Functions, 4.4.46 (absolute error <= 2e-8 on [0, 1]), and
@@ -419,7 +408,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   __shared__ float mrun[GM], alpha_sh[GM];  // per head: running maximum, this round's rescale factor
   __shared__ float lsum[GM];                 // per head: running normaliser (matrix-core rounds)
 
-  touch_kernargs();
+  touch_kernargs<5>();  // 292 bytes of arguments
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: table bases stay scalar
   const int j16 = lane & 15, grp = tid >> 4;

@@ -658,6 +658,7 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
                                                            const uint4 *__restrict__ wp, int K, int L,
                                                            const uint4 *__restrict__ wlift) {
   __shared__ uint32_t bits[64][SM_MAXT + 2];  // [row][tile - t0]
+  touch_kernargs<7>();  // 400 bytes of arguments (two jobs of 184)
   const bool second = njobs > 1 && (int)blockIdx.x >= blocks0;
   const EncJob &jb = second ? j1 : j0;
   const int lb = second ? (int)blockIdx.x - blocks0 : (int)blockIdx.x;

@@ -83,6 +83,21 @@ int kmean_parts(int64_t n);
 // of table l written to out + u*out_su + i*out_si + l*out_sl; when kcopy is
 // set the raw row (and vin's row) are also copied to kcopy/vcopy + u*kc_su +
 // i*kc_si.  The launcher fills the grid fields.
+// A kernel's explicit arguments span LINES 64-byte lines, which the compiler
+// loads where each is first used -- a chain of dependent scalar loads, each
+// a memory round trip when it misses.  One scalar load per line at entry
+// brings them in together (reads only; every line touched starts inside the
+// explicit arguments).
+template <int LINES>
+__device__ inline void touch_kernargs() {
+  typedef const __attribute__((address_space(4))) uint32_t karg_t;
+  karg_t *kp = (karg_t *)__builtin_amdgcn_kernarg_segment_ptr();
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < LINES; ++i) x ^= kp[16 * i];
+  asm volatile("" ::"s"(x));
+}
+
 struct EncJob {
   const void *in;
   int64_t in_su, in_si;

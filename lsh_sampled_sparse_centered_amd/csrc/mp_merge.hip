@@ -33,12 +33,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   __shared__ int wsum[16];
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the same XCD as the blocks that wrote its partials
-  const int64_t U = (int64_t)gridDim.x / G;
-  const int64_t u = blockIdx.x % U;
-  const int hg = (int)(blockIdx.x / U);
-  const int64_t b = u / Hkv;
-  const int64_t h = (u % Hkv) * G + hg;
-  const int64_t bh = b * Hq + h;
+  touch_kernargs<2>();  // 96 bytes of arguments
+  // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
+  const uint32_t U32 = gridDim.x / (uint32_t)G, bx = blockIdx.x;
+  const int64_t u = (int64_t)(bx % U32);
+  const int hg = (int)(bx / U32);
+  const int b = (int)u / Hkv;
+  const int h = ((int)u % Hkv) * G + hg;
+  const int64_t bh = (int64_t)b * Hq + h;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;
