@@ -10,10 +10,13 @@
 namespace mp {
 
 // ---------------------------------------------------------------------------
-// Projection packing: W[d][K*L] fp32 -> bf16 tiles in matrix-core A-operand
-// order.  Element e of lane l in k-step s of tile t is
-//   W[16 s + 8 (l / 32) + e][K (t tpt + j) + b],  K j + b = enc_row_col(l % 32),
-// and 0 where j >= tpt or t tpt + j >= L.
+// Projection packing: W[d][K*L] fp32 -> negated bf16 tiles in matrix-core
+// A-operand order.  Element e of lane l in k-step s of tile t is
+//   -W[16 s + 8 (l / 32) + e][K (t tpt + j) + b],  K j + b = enc_row_col(l % 32),
+// and 0 where j >= tpt or t tpt + j >= L.  The tiles hold -bf16(W) (negation
+// is exact and commutes with rounding), so the encoders' accumulators hold
+// -z for each projection z and the sign bit of an accumulator is (z > 0)
+// directly (see sign_bits16).
 // One thread per (tile, k-step, lane) writes 16 bytes.
 __global__ void proj_pack_kernel(const float *__restrict__ W, int K, int L, int ntiles, uint4 *__restrict__ Wp) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -30,7 +33,7 @@ __global__ void proj_pack_kernel(const float *__restrict__ W, int K, int L, int 
   const int d0 = 16 * s + 8 * (lane >> 5);
   bf16x8 v;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = (__bf16)(live ? W[(int64_t)(d0 + e) * ncol + col] : 0.0f);
+  for (int e = 0; e < 8; ++e) v[e] = (__bf16)(live ? -W[(int64_t)(d0 + e) * ncol + col] : 0.0f);
   Wp[gid] = __builtin_bit_cast(uint4, v);
 }
 
@@ -274,16 +277,18 @@ __device__ inline float lift_coord(const bf16x8 (&xr)[KSTEPS], float r) {
   return (float)(__bf16)(float)sqrt(rem > 0.0 ? rem : 0.0);
 }
 
-// Sign bits of lifted projections: z = acc[r] + e * W[d][bit 16 half + r]
-// (one fp32 fma), then bit r = (z > 0) as in sign_bits16.  wl holds the 16
-// bf16 extra-row values of this lane half's bits.
+// Sign bits of lifted projections: the accumulator holds -z over the first d
+// dims (negated tiles), the extra row W[d] is packed as is, and
+// fl(-e w + (-z)) = -fl(z + e w) (one fp32 fma), so its sign bit is bit r =
+// (z + e w > 0) as in sign_bits16 (an exact zero rounds to +0: bit 0).  wl
+// holds the 16 bf16 extra-row values of this lane half's bits.
 __device__ inline uint32_t sign_bits16_lift(const f32x16 &a, float e, const uint4 (&wl)[2]) {
   const bf16x8 w0 = __builtin_bit_cast(bf16x8, wl[0]), w1 = __builtin_bit_cast(bf16x8, wl[1]);
   uint32_t pos = 0;
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
     const float w = r < 8 ? (float)w0[r & 7] : (float)w1[r & 7];
-    const float nz = 0.0f - fmaf(e, w, a[r]);
+    const float nz = fmaf(-e, w, a[r]);
     pos = __builtin_amdgcn_alignbit(pos, __builtin_bit_cast(uint32_t, nz), 31u);
   }
   return pos & 0xffffu;
@@ -323,19 +328,22 @@ __device__ inline void store_row8<__bf16>(__bf16 *p, const float (&v)[8]) {
   *(bf16x8 *)p = a;
 }
 
-// Bit r of the result is (a[r] > 0).  0 - a[r] has its sign bit set exactly
-// when a[r] > 0: a positive value turns negative, a negative one positive,
-// and both zeros give +0 (x - x rounds to +0).  The sign bits of 0 - a[r]
-// are shifted in one per element (a funnel shift of (word, element) by 31,
-// from element 15 down to 0).  An exactly zero projection -- a zero row, a
-// zero projection column, or an exact cancellation -- therefore gives bit 0,
-// as (z > 0) does.  Each element is copied to a scalar before the bit cast.
+// Bit r of the result is (z_r > 0) where the accumulator holds a[r] = -z_r
+// (the packed tiles are negated, and the matrix core's products and sums
+// are symmetric under negation): -z_r has its sign bit set exactly when
+// z_r > 0.  An exactly zero projection -- a zero row, a zero projection
+// column, or an exact cancellation -- accumulates to +0 from the +0 start
+// (x + (-x) and +0 + (-0) round to +0), so it gives bit 0, as (z > 0) does.
+// The sign bits are shifted in one per element (a funnel shift of (word,
+// element) by 31, from element 15 down to 0).  Each element is copied to a
+// scalar before the bit cast (a bit cast of the vector element itself has
+// been compiled to a read of element 0 for every r).
 __device__ inline uint32_t sign_bits16(const f32x16 &a) {
   uint32_t pos = 0;
 #pragma unroll
   for (int r = 15; r >= 0; --r) {
-    const float nz = 0.0f - a[r];
-    pos = __builtin_amdgcn_alignbit(pos, __builtin_bit_cast(uint32_t, nz), 31u);  // (pos << 1) | (a[r] > 0)
+    const float x = a[r];
+    pos = __builtin_amdgcn_alignbit(pos, __float_as_uint(x), 31u);  // (pos << 1) | (z_r > 0)
   }
   return pos & 0xffffu;
 }
@@ -344,7 +352,7 @@ __device__ inline uint32_t sign_bits16(const f32x16 &a) {
 // append and the queries of a decode step) and maps its linear block index
 // onto (job, row block, unit, table group).
 template <typename T, bool LIFT>
-__global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
+__global__ __launch_bounds__(64 * ENC_NW, MP_ENC_OCC) void encode_kernel(EncJob j0, EncJob j1, int njobs, const uint4 *__restrict__ wp,
                                                         int K, int L, const uint4 *__restrict__ wlift) {
   __shared__ uint4 wsh[2][ENC_TG * KSTEPS * 64];
   __shared__ uint16_t cst[ENC_NW][ENC_CST][64];  // a wave's codes of one stage, [table][row]
@@ -574,39 +582,53 @@ __global__ __launch_bounds__(64 * ENC_NW, 2) void encode_kernel(EncJob j0, EncJo
       // vector work for the scheduler; tiles past t1 read stale LDS and are
       // dropped).  The next tile's A operands are read from LDS while the
       // current tile's matrix-core ops run.
+      // Software pipeline over the stage's tiles: tile tt's matrix-core ops
+      // are issued before tile tt-1's sign bits are formed, so the vector
+      // work of one tile runs while the matrix core works on the next.
       bf16x8 ap[2][KSTEPS];
 #pragma unroll
       for (int s = 0; s < KSTEPS; ++s) ap[0][s] = __builtin_bit_cast(bf16x8, wsh[buf][s * 64 + lane]);
+      f32x16 acc[2][2];
 #pragma unroll
-      for (int tt = 0; tt < ENC_TG; ++tt) {
-        f32x16 acc0 = {}, acc1 = {};
-        if (tt + 1 < ENC_TG) {
+      for (int tt = 0; tt <= ENC_TG; ++tt) {
+        if (tt < ENC_TG) {
+          if (tt + 1 < ENC_TG) {
 #pragma unroll
-          for (int s = 0; s < KSTEPS; ++s)
-            ap[(tt + 1) & 1][s] = __builtin_bit_cast(bf16x8, wsh[buf][((tt + 1) * KSTEPS + s) * 64 + lane]);
-        }
+            for (int s = 0; s < KSTEPS; ++s)
+              ap[(tt + 1) & 1][s] = __builtin_bit_cast(bf16x8, wsh[buf][((tt + 1) * KSTEPS + s) * 64 + lane]);
+          }
+          // the next tile's operand reads stay ahead of this tile's
+          // matrix-core ops (left to itself the scheduler moves each read
+          // next to its use, and every pair of ops then waits for LDS)
+          __builtin_amdgcn_sched_barrier(0);
+          f32x16 a0 = {}, a1 = {};
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) {
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[0][s], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[1][s], acc1, 0, 0, 0);
+          for (int s = 0; s < KSTEPS; ++s) {
+            a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[0][s], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ap[tt & 1][s], xb[1][s], a1, 0, 0, 0);
+          }
+          acc[tt & 1][0] = a0;
+          acc[tt & 1][1] = a1;
         }
-        // lane l < 32 holds bits 0-15 of row l in m0 and bits 0-15 of row
-        // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
-        // cross-half swap leaves lane l with row l's halves and lane 32 + l
-        // with row 32 + l's.
-        uint32_t m0, m1;
-        if constexpr (LIFT) {
-          const int tl = min(tg + tt, t1 - 1);  // tiles past t1 are dropped
-          const uint4 wl[2] = {wlift[tl * 4 + 2 * half], wlift[tl * 4 + 2 * half + 1]};
-          m0 = sign_bits16_lift(acc0, ebar[0], wl);
-          m1 = sign_bits16_lift(acc1, ebar[1], wl);
-        } else {
-          m0 = sign_bits16(acc0);
-          m1 = sign_bits16(acc1);
+        if (tt > 0) {
+          const int tp = tt - 1;
+          // lane l < 32 holds bits 0-15 of row l in m0 and bits 0-15 of row
+          // 32 + l in m1; lane 32 + l holds bits 16-31 of the same rows.  One
+          // cross-half swap leaves lane l with row l's halves and lane 32 + l
+          // with row 32 + l's.
+          uint32_t m0, m1;
+          if constexpr (LIFT) {
+            const int tl = min(tg + tp, t1 - 1);  // tiles past t1 are dropped
+            const uint4 wl[2] = {wlift[tl * 4 + 2 * half], wlift[tl * 4 + 2 * half + 1]};
+            m0 = sign_bits16_lift(acc[tp & 1][0], ebar[0], wl);
+            m1 = sign_bits16_lift(acc[tp & 1][1], ebar[1], wl);
+          } else {
+            m0 = sign_bits16(acc[tp & 1][0]);
+            m1 = sign_bits16(acc[tp & 1][1]);
+          }
+          const auto sw = __builtin_amdgcn_permlane32_swap(m0, m1, false, false);
+          wd[tp] = sw[0] | (sw[1] << 16);
         }
-        const auto sw = __builtin_amdgcn_permlane32_swap(m0, m1, false, false);
-        const uint32_t word = sw[0] | (sw[1] << 16);
-        wd[tt] = word;
       }
       tpend = tg;
       npend = min(ENC_TG, t1 - tg);

@@ -26,7 +26,13 @@ constexpr int KSTEPS = D / 16;  // k-steps of one 32x32x16 bf16 matrix-core op o
 // bit 16*a + r, i.e. each lane's 16 sign bits come out in bit order.
 constexpr int ENC_NW = 4;       // waves per encoder block (64 rows each)
 constexpr int ENC_ROWS = 64 * ENC_NW;  // rows (keys or queries) per encoder block
-constexpr int ENC_TG = 2;       // tiles staged in LDS per stage (8 KB each, double buffered)
+#ifndef MP_ENC_OCC
+#define MP_ENC_OCC 2  // encoder waves per SIMD the kernel is compiled for
+#endif
+#ifndef MP_ENC_TG
+#define MP_ENC_TG 2
+#endif
+constexpr int ENC_TG = MP_ENC_TG;  // tiles staged in LDS per stage (8 KB each, double buffered)
 constexpr int ENC_CST = (ENC_TG - 1) * 8 + 8;  // LDS code slots per wave and stage (8 per tile)
 __host__ __device__ inline int enc_tpt(int K) { return K > 0 ? 32 / K : 0; }
 __host__ __device__ inline int enc_ntiles(int K, int L) { return K > 0 ? (L + enc_tpt(K) - 1) / enc_tpt(K) : 0; }
