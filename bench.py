@@ -59,7 +59,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_96k")
     ap.add_argument("--seed", type=int, default=2024)
-    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0 = workload's)")
+    ap.add_argument("--layers", type=int, default=0, help="override the resident layer count (0 = workload's)")
+    ap.add_argument("--step-layers", type=int, default=0,
+                    help="layer decodes per step (0 = the resident layers); more cycle through the resident layers, "
+                         "for a workload whose caches exceed one GPU's memory at the real per-layer shape")
     ap.add_argument("--threshold", type=int, default=2,
                     help="collision threshold T: a key is sampled in at least T of the L tables (the pages' 2)")
     ap.add_argument("--alternatives", choices=("on", "off"), default="on",
@@ -177,7 +180,7 @@ def main() -> int:
     args = parse()
     if args.trace_stats:
         w = __import__("synth").WORKLOADS[args.workload]
-        print(trace_stats(args.trace_stats, args.steps, args.warmup, args.layers or w.layers))
+        print(trace_stats(args.trace_stats, args.steps, args.warmup, args.step_layers or args.layers or w.layers))
         return 0
     if args.traffic:
         w = __import__("synth").WORKLOADS[args.workload]
@@ -217,6 +220,9 @@ def main() -> int:
     lcfg = [((0, 2, 0, 0) if pages and l in (0, 16) else (K, L, 4 if pages else 0, 64 if pages else 0))
             for l in range(nlayers)]
     sampled_layers = [l for l in range(nlayers) if lcfg[l][0] > 0]
+    step_layers = args.step_layers or nlayers
+    step_lids = [i % nlayers for i in range(step_layers)]  # resident layer of each of a step's layer decodes
+    step_sampled = [i for i, l in enumerate(step_lids) if lcfg[l][0] > 0]
     modes = [args.index] + ([m for m in ("buckets", "planes", "codes") if m != args.index]
                             if args.alternatives == "on" else [])
     use_planes = "planes" in modes
@@ -289,7 +295,7 @@ def main() -> int:
     # appended rows and codes are rewritten with the same values).
     def run_steps(mode):
         ev_steps = min(args.steps, 1)
-        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ev_steps * nlayers)]
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(ev_steps * step_layers)]
         for pair in kev:
             for e in pair:
                 e.record()  # create the underlying events before handing them to the library
@@ -303,9 +309,10 @@ def main() -> int:
                 torch.cuda.synchronize()
                 t0 = time.perf_counter()
                 step_ev[0].record()
-            for l, lay in enumerate(layers):
+            for i, l in enumerate(step_lids):
+                lay = layers[l]
                 k = s - (total_steps - ev_steps)
-                ev = kev[k * nlayers + l] if k >= 0 else None
+                ev = kev[k * step_layers + i] if k >= 0 else None
                 pl = lay["planes"] if mode == "planes" else None
                 bk = lay["buckets"] if mode == "buckets" else None
                 mp.mp_decode_step(lay["kn"][s], lay["vn"][s], lay["qs"][s], lay["Kc"], lay["Vc"], lay["codes"],
@@ -320,14 +327,14 @@ def main() -> int:
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / args.steps
         evms = step_ev[0].elapsed_time(step_ev[1]) / args.steps
-        kern = np.array([a.elapsed_time(b) for a, b in kev])[sampled_layers]  # the sampled layers' kernel
+        kern = np.array([a.elapsed_time(b) for a, b in kev])[step_sampled]  # the sampled layers' kernel
         log("[%s] step %.3f ms (wall) / %.3f ms (events); sample kernel %.2f us avg over %d launches" %
             (mode, wall, evms, kern.mean() * 1e3, len(kern)))
         return wall, evms, kern, n_timed, n_cur
 
     timing = {m: run_steps(m) for m in modes}
     wall_ms, ev_ms, kern_ms, n_timed, n_cur = timing[args.index]
-    keys_per_step = float(np.mean(n_timed)) * U * nlayers
+    keys_per_step = float(np.mean(n_timed)) * U * step_layers
     value = keys_per_step / (wall_ms * 1e-3)
 
     # ------------------------------------------------------------------ sampled-set sizes (after timing)
@@ -394,12 +401,12 @@ def main() -> int:
     for m in modes[1:]:
         wm, em, km, nt, _ = timing[m]
         bl = launch_bytes(m)
-        alternatives[m] = {"ms_per_step": wm, "value": float(np.mean(nt)) * U * nlayers / (wm * 1e-3),
+        alternatives[m] = {"ms_per_step": wm, "value": float(np.mean(nt)) * U * step_layers / (wm * 1e-3),
                            "kernel_us": km.mean() * 1e3, "algorithmic_bytes_per_launch": bl,
                            "frac": bl / (km.mean() * 1e-3) / 1e9 / HBM_PEAK_GBS}
     # a dense layer reads its (two-table) codes and every key's K and V row
     dense_bytes = U * (2 * 2 * n_dec + 2 * d * e * n_dec + G * (d * e + 4) + 4 * d)
-    step_bytes = len(sampled_layers) * bytes_launch + (nlayers - len(sampled_layers)) * dense_bytes
+    step_bytes = len(step_sampled) * bytes_launch + (step_layers - len(step_sampled)) * dense_bytes
     log("|S_h|/n = %.4f, union per unit %.0f keys (%.4f of n); %.1f MB algorithmic per launch%s" %
         (head_frac, union_per_unit, union_per_unit / n_dec, bytes_launch / 1e6,
          "; bucket lookup %.2f MB per launch" % (lookup_bytes / 1e6) if lookup_bytes else ""))
@@ -459,7 +466,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic cone-plus-sink keys/queries, N(0,1) values and projections, resident in HBM",
-        "config": {"workload": w.name, "layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
+        "config": {"workload": w.name, "layers": step_layers, "resident_layers": nlayers, "batch": w.batch, "q_heads": w.hq, "kv_heads": w.hkv,
                    "head_dim": d, "context": n0, "K": K, "L": L, "threshold": args.threshold,
                    "code_scan": ("bit-plane index below key %d, 16-bit codes above" % n_planes
                                  if args.index == "planes" and args.threshold == 2
