@@ -176,34 +176,39 @@ __device__ inline float log_sampling_prob(float c, int K, int L, const LnPCoef &
   return cf.Lf * p < 1.0f ? small : large;
 }
 
-// Maximum and sum over each half (32 lanes) of the wave, every lane ending
-// with its half's result: lane-xor swizzles (no lane-index registers).
+// Lane exchanges within a DPP row of 16 lanes (quad_perm [1,0,3,2] and
+// [2,3,0,1], row_half_mirror, row_mirror: after the four steps every lane of
+// the row has combined all 16) and a lane-xor swizzle across rows.
+template <int CTRL>
+__device__ inline float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
 template <int XM>
 __device__ inline float swz_xor(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), (XM << 10) | 0x1f));
 }
+// Sum / maximum over the 16 lanes of a DPP row (each lane ends with the row's).
+__device__ inline float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  return x + dpp_mov<0x140>(x);
+}
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  return fmaxf(x, dpp_mov<0x140>(x));
+}
+// Maximum and sum over each half (32 lanes) of the wave, every lane ending
+// with its half's result: the row's, then one swizzle between the two rows.
 __device__ inline float xor32_max(float x) {
-  x = fmaxf(x, swz_xor<16>(x));
-  x = fmaxf(x, swz_xor<8>(x));
-  x = fmaxf(x, swz_xor<4>(x));
-  x = fmaxf(x, swz_xor<2>(x));
-  return fmaxf(x, swz_xor<1>(x));
+  x = row16_max(x);
+  return fmaxf(x, swz_xor<16>(x));
 }
 __device__ inline float xor32_sum(float x) {
-  x += swz_xor<16>(x);
-  x += swz_xor<8>(x);
-  x += swz_xor<4>(x);
-  x += swz_xor<2>(x);
-  return x + swz_xor<1>(x);
-}
-
-// Sum over the 16 lanes of a DPP row (each lane ends with the row sum).
-__device__ inline float row16_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
-  return x;
+  x = row16_sum(x);
+  return x + swz_xor<16>(x);
 }
 
 template <typename T>
@@ -553,15 +558,20 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   }
   __syncthreads();
 
-  for (int h = wave; h < GM; h += 4) {  // |q_h| and q_h . mu
-    float a = qsh[h][lane] * qsh[h][lane] + qsh[h][lane + 64] * qsh[h][lane + 64];
-    float bq = qsh[h][lane] * msh[lane] + qsh[h][lane + 64] * msh[lane + 64];
+  if (tid < 16 * GM) {  // |q_h| and q_h . mu: a DPP row (16 lanes, 8 dims each) per head
+    const int h = tid >> 4;
+    float qv[8], mv[8];
+    ld8<float>(&qsh[h][8 * j16], qv);
+    ld8<float>(msh + 8 * j16, mv);
+    float a = 0.0f, bq = 0.0f;
 #pragma unroll
-    for (int sh = 32; sh > 0; sh >>= 1) {
-      a += __shfl_xor(a, sh);
-      bq += __shfl_xor(bq, sh);
+    for (int e = 0; e < 8; ++e) {
+      a = fmaf(qv[e], qv[e], a);
+      bq = fmaf(qv[e], mv[e], bq);
     }
-    if (lane == 0) {
+    a = row16_sum(a);
+    bq = row16_sum(bq);
+    if (j16 == 0) {
       qn_sh[h] = sqrtf(a);
       qmu_sh[h] = bq;
     }
@@ -905,6 +915,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
           kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
           vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
         }
+
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
         float n2 = 0.0f;
         const int hq = li < GM ? li : 0;

@@ -565,6 +565,7 @@ __global__ __launch_bounds__(64 * ENC_NW, MP_ENC_OCC) void encode_kernel(EncJob 
   auto run_stages = [&](auto tptc) {
     constexpr int TPT = decltype(tptc)::value;  // 0: general path
     constexpr int NST = ENC_TG * (TPT > 0 ? TPT : 1);
+    static_assert(NST < 64, "the vector-memory count of s_waitcnt has 6 bits");
     int buf = 0;
     for (int tg = t0; tg < t1; tg += ENC_TG) {
       const int tnext = tg + ENC_TG;
