@@ -158,14 +158,17 @@ __global__ __launch_bounds__(256) void bucket_lookup_kernel(const uint16_t *__re
   __shared__ uint32_t wsum[4];
   const int tid = threadIdx.x;
   touch_kernargs<2>();  // 96 bytes of arguments
-  // blocks run chunk-major (the sampling grid's order): chunk, unit, head
+  // unit-minor order, as the sampling grid: block i serves unit i % U, so
+  // (with U a multiple of the 8 XCDs) it runs on the XCD whose blocks read
+  // its words; then head, then chunk
   // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
-  const uint32_t UG = gridDim.x / (uint32_t)nbc, bx = blockIdx.x;
-  const int64_t ci = (int64_t)(bx / UG);
-  const int64_t ug = (int64_t)(bx % UG);  // unit * G + head
-  const int ui = (int)ug / G;
+  const uint32_t U32 = gridDim.x / ((uint32_t)nbc * (uint32_t)G), bx = blockIdx.x;
+  const int ui = (int)(bx % U32);
+  const uint32_t hc = bx / U32;
+  const int h = (int)(hc % (uint32_t)G);
+  const int64_t ci = (int64_t)(hc / (uint32_t)G);
   const int64_t u = ui;
-  const int h = (int)ug % G;
+  const int64_t ug = u * G + h;  // unit * G + head
   const int64_t qrow = (int64_t)(ui / Hkv) * Hq + (int64_t)(ui % Hkv) * G + h;
   const int64_t r0 = ci * BK_R, r1 = min(r0 + BK_R, nb);
   const int nbins = 1 << K;

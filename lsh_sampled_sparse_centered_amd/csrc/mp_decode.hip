@@ -274,8 +274,7 @@ template <typename T, int GM>
 __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Raw8<T> &k1, const Raw8<T> &v1,
                                   bool ok1, int e0, int e1, uint32_t mk0, uint32_t mk1, int j16, int G, int K, int L,
                                   const LnPCoef &cf, float scale, const float (*qsh)[D], const float *msh,
-                                  const float *qn_sh, const float *qmu_sh, T (*vrows)[D], float (*lw)[ATT_E],
-                                  float rl) {
+                                  const f32x4 *hst, T (*vrows)[D], float (*lw)[ATT_E], float rl) {
   float kv0[8], kv1[8], mv[8];
   k0.get(kv0);
   k1.get(kv1);
@@ -316,8 +315,9 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
     if ((mk >> hh) & 1u) {
       float lnP = 0.0f;
       if (!(mk & FORCED)) {
-        const float den = qn_sh[hh] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(second ? n1 : n0));
-        const float cosv = den > 0.0f ? (dk - qmu_sh[hh]) * __builtin_amdgcn_rcpf(den) : 0.0f;
+        const f32x4 hs = hst[hh];
+        const float den = hs[0] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(second ? n1 : n0));
+        const float cosv = den > 0.0f ? (dk - hs[1]) * __builtin_amdgcn_rcpf(den) : 0.0f;
         lnP = log_sampling_prob(cosv, K, L, cf);
       }
       w = dk * scale - lnP;
@@ -405,13 +405,14 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   uint32_t *qpk = (uint32_t *)qpk4;
   __shared__ float qsh[GM][D];
   __shared__ float msh[D];
-  __shared__ float qn_sh[GM], qmu_sh[GM];
+  // per head: |q_h|, q_h . mu, running maximum m, running normaliser l (one
+  // 16-byte LDS word, so that the weight phase reads all four at once)
+  __shared__ f32x4 hst[GM];
   __shared__ uint16_t lkey[2 * SCAN_TILE];   // union list: key offset from the block's first key
   __shared__ uint16_t lmask[2 * SCAN_TILE];  // head bits | FORCED
   __shared__ int wtot[4];
   __shared__ int hcnt[GM];
-  __shared__ float mrun[GM], alpha_sh[GM];  // per head: running maximum, this round's rescale factor
-  __shared__ float lsum[GM];                 // per head: running normaliser (matrix-core rounds)
+  __shared__ float alpha_sh[GM];  // per head: this round's rescale factor
 
   touch_kernargs<5>();  // 292 bytes of arguments
   const int tid = threadIdx.x, lane = tid & 63;
@@ -553,8 +554,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   }
   if (tid < GM) {
     hcnt[tid] = 0;
-    mrun[tid] = -INFINITY;
-    lsum[tid] = 0.0f;
+    hst[tid][2] = -INFINITY;
+    hst[tid][3] = 0.0f;
   }
   __syncthreads();
 
@@ -572,8 +573,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     a = row16_sum(a);
     bq = row16_sum(bq);
     if (j16 == 0) {
-      qn_sh[h] = sqrtf(a);
-      qmu_sh[h] = bq;
+      hst[h][0] = sqrtf(a);
+      hst[h][1] = bq;
     }
   }
 
@@ -903,18 +904,30 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     f32x4 oacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};  // heads 4 qd + j, dim 16 (2 wave + b) + li
     const __bf16 *Kb = (const __bf16 *)Kc + (u * cap + tbase) * D + 8 * qd;
     const __bf16 *Vb = (const __bf16 *)Vc + (u * cap + tbase) * D + 8 * qd;
+    // this lane's key and value pieces of the round starting at entry r0
+    // (entries past the list read the tile's first key: a valid row, discarded)
+    uint4 kr[2], vr[2];
+    auto load_round = [&](int r0) {
+      const int e = 16 * (wave & 1) + li, kh = wave >> 1;
+      const int64_t key = e < nu - r0 ? lkey[r0 + e] : 0;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
+        vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
+      }
+    };
+    // With four or more heads per block the next round's rows are requested
+    // as soon as this round's are consumed (end of (a)), so they arrive while
+    // (b) and (c) run (the barriers wait for LDS operations only); with
+    // fewer heads (short (b) and (c), many blocks) at the start of the round.
+    constexpr bool early = GM >= 4;
+    if (nu > 0) load_round(0);
     for (int e0 = 0; e0 < nu; e0 += ATT_E) {
       const int ne = min(ATT_E, nu - e0);
+      if (!early && e0 > 0) load_round(e0);
       {  // (a)
         const int e = 16 * (wave & 1) + li, kh = wave >> 1;
         const bool ok = e < ne;
-        const int64_t key = ok ? lkey[e0 + e] : 0;  // the tile's first key: a valid row, discarded
-        uint4 kr[2], vr[2];
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
-          vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
-        }
 
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
         float n2 = 0.0f;
@@ -948,10 +961,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
 #pragma unroll
           for (int j = 0; j < 8; ++j) sm.m.vT[64 * kh + 32 * st + 8 * qd + j][e] = ok ? vb[j] : (__bf16)0.0f;
         }
+        if (early && e0 + ATT_E < nu) load_round(e0 + ATT_E);
       }
       __syncthreads();
       if (tid < GM * ATT_E) {  // (b)
         const int h = tid / ATT_E, e = tid % ATT_E;
+        const f32x4 hs = hst[h];
         float w = -INFINITY;
         if (h < G && e < ne) {
           const uint32_t mk = lmask[e0 + e];
@@ -959,15 +974,15 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
             const float dk = sm.m.sdot[0][h][e] + sm.m.sdot[1][h][e];
             float lnP = 0.0f;
             if (!(mk & FORCED)) {
-              const float den = qn_sh[h] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
-              const float cosv = den > 0.0f ? (dk - qmu_sh[h]) * __builtin_amdgcn_rcpf(den) : 0.0f;
+              const float den = hs[0] * (rl > 0.0f ? rl : __builtin_amdgcn_sqrtf(sm.m.nrm[0][e] + sm.m.nrm[1][e]));
+              const float cosv = den > 0.0f ? (dk - hs[1]) * __builtin_amdgcn_rcpf(den) : 0.0f;
               lnP = log_sampling_prob(cosv, K, L, cf);
             }
             w = dk * scale - lnP;
           }
         }
         const float mr = xor32_max(w);  // within the 32 lanes of h
-        const float mo = mrun[h];
+        const float mo = hs[2];
         const float mn = fmaxf(mo, mr);
         const float pe = mn > -INFINITY ? hw_exp(w - mn) : 0.0f;  // 0 for -inf
         const float ps = xor32_sum(pe);
@@ -975,8 +990,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         if (e == 0) {
           const float alpha = mn > -INFINITY ? hw_exp(mo - mn) : 1.0f;  // 0 while mo = -inf
           alpha_sh[h] = alpha;
-          mrun[h] = mn;
-          lsum[h] = lsum[h] * alpha + ps;
+          hst[h][2] = mn;
+          hst[h][3] = hs[3] * alpha + ps;
         }
       }
       __syncthreads();
@@ -1018,8 +1033,8 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     }
     if (tid < G) {
       float *rec = rec0 + tid * PSTRIDE;
-      rec[0] = mrun[tid];
-      rec[1] = lsum[tid];
+      rec[0] = hst[tid][2];
+      rec[1] = hst[tid][3];
       rec[2] = __builtin_bit_cast(float, hcnt[tid]);
       rec[3] = 0.0f;
     }
@@ -1055,7 +1070,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         v1.zero();
       }
       entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[e0 + el0], mk1, j16, G, K, L, cf, scale, qsh, msh,
-                        qn_sh, qmu_sh, sm.a.v, sm.a.lw, rl);
+                        hst, sm.a.v, sm.a.lw, rl);
     }
     __syncthreads();
     // (b) one thread per (head, entry) turns the log-weights into
@@ -1068,12 +1083,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       float mr = x;
 #pragma unroll
       for (int sh = ATT_E / 2; sh > 0; sh >>= 1) mr = fmaxf(mr, __shfl_xor(mr, sh));  // within the 32 lanes of h
-      const float mo = mrun[h];
+      const float mo = hst[h][2];
       const float mn = fmaxf(mo, mr);
       if (h < G && e < ne) sm.a.lw[h][e] = mn > -INFINITY ? hw_exp(x - mn) : 0.0f;  // 0 for -inf
       if (e == 0) {
         alpha_sh[h] = mn > -INFINITY ? hw_exp(mo - mn) : 1.0f;  // 0 while mo = -inf
-        mrun[h] = mn;
+        hst[h][2] = mn;
       }
     }
     __syncthreads();
@@ -1106,7 +1121,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
 #pragma unroll
     for (int i = 0; i < DPT; ++i) rec[4 + od + i] = oacc[i];
     if (tid % TPH == 0) {
-      rec[0] = mrun[oh];
+      rec[0] = hst[oh][2];
       rec[1] = ol;
       rec[2] = __builtin_bit_cast(float, hcnt[oh]);
       rec[3] = 0.0f;
