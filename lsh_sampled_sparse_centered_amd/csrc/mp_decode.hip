@@ -408,10 +408,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // per head: |q_h|, q_h . mu, running maximum m, running normaliser l (one
   // 16-byte LDS word, so that the weight phase reads all four at once)
   __shared__ f32x4 hst[GM];
-  __shared__ uint16_t lkey[2 * SCAN_TILE];   // union list: key offset from the block's first key
-  __shared__ uint16_t lmask[2 * SCAN_TILE];  // head bits | FORCED
+  // union list, one segment of up to 128 entries per wave (the wave's 128
+  // keys), read through lslot: key offset from the block's first key, and
+  // head bits | FORCED
+  __shared__ uint16_t lkey[SCAN_TILE];
+  __shared__ uint16_t lmask[SCAN_TILE];
   __shared__ int wtot[4];
-  __shared__ int hcnt[GM];
+  __shared__ int hcw[4][GM];  // per wave and head: sampled keys
   __shared__ float alpha_sh[GM];  // per head: this round's rescale factor
 
   touch_kernargs<5>();  // 292 bytes of arguments
@@ -553,7 +556,6 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     } while (i0 < nq);
   }
   if (tid < GM) {
-    hcnt[tid] = 0;
     hst[tid][2] = -INFINITY;
     hst[tid][3] = 0.0f;
   }
@@ -578,7 +580,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     }
   }
 
-  int nu = 0;  // entries in the union list so far
+  int nu = 0;  // entries in the union list
+  int lp1 = 0, lp2 = 0, lp3 = 0;  // list entries before waves 1, 2, 3's segments
+  // LDS slot of list entry e: the list is the waves' segments in wave order
+  // (ascending keys)
+  auto lslot = [&](int e) {
+    return e < lp1 ? e : e < lp2 ? 128 + e - lp1 : e < lp3 ? 256 + e - lp2 : 384 + e - lp3;
+  };
   uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
   {
     const int64_t sbase = tbase;
@@ -858,26 +866,30 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     for (int h = 0; h < GM; ++h) {
       if (h < G) {
         const int ch = __popcll(__ballot((mlo >> h) & 1)) + __popcll(__ballot((mhi >> h) & 1));
-        if (lane == 0 && ch) atomicAdd(&hcnt[h], ch);
+        if (lane == 0) hcw[wave][h] = ch;
       }
     }
-    __syncthreads();
-    int off = nu;
-    for (int w = 0; w < wave; ++w) off += wtot[w];
-    nu += wtot[0] + wtot[1] + wtot[2] + wtot[3];
+    // each wave writes its own segment (no offsets across waves needed yet)
     const int kloc = (int)(klo - tbase);  // offset from the block's first key
+    const int sb = 128 * wave + pre;
     if (flo) {
-      lkey[off + pre] = (uint16_t)kloc;
-      lmask[off + pre] = (uint16_t)mlo;
-      if (uent) uent[off + pre] = (uint32_t)kloc | ((mlo & headbits) << 16);
+      lkey[sb] = (uint16_t)kloc;
+      lmask[sb] = (uint16_t)mlo;
     }
     if (fhi) {
-      const int p2 = off + pre + (flo ? 1 : 0);
-      lkey[p2] = (uint16_t)(kloc + 1);
-      lmask[p2] = (uint16_t)mhi;
-      if (uent) uent[p2] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
+      lkey[sb + (flo ? 1 : 0)] = (uint16_t)(kloc + 1);
+      lmask[sb + (flo ? 1 : 0)] = (uint16_t)mhi;
     }
     __syncthreads();  // list complete
+    lp1 = wtot[0];
+    lp2 = lp1 + wtot[1];
+    lp3 = lp2 + wtot[2];
+    nu = lp3 + wtot[3];
+    if (uent) {  // the index list in key order
+      const int off = (wave == 0 ? 0 : wave == 1 ? lp1 : wave == 2 ? lp2 : lp3) + pre;
+      if (flo) uent[off] = (uint32_t)kloc | ((mlo & headbits) << 16);
+      if (fhi) uent[off + (flo ? 1 : 0)] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
+    }
   }
   if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;
 
@@ -909,7 +921,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     uint4 kr[2], vr[2];
     auto load_round = [&](int r0) {
       const int e = 16 * (wave & 1) + li, kh = wave >> 1;
-      const int64_t key = e < nu - r0 ? lkey[r0 + e] : 0;
+      const int64_t key = e < nu - r0 ? lkey[lslot(r0 + e)] : 0;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
@@ -969,7 +981,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         const f32x4 hs = hst[h];
         float w = -INFINITY;
         if (h < G && e < ne) {
-          const uint32_t mk = lmask[e0 + e];
+          const uint32_t mk = lmask[lslot(e0 + e)];
           if ((mk >> h) & 1u) {
             const float dk = sm.m.sdot[0][h][e] + sm.m.sdot[1][h][e];
             float lnP = 0.0f;
@@ -1035,7 +1047,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       float *rec = rec0 + tid * PSTRIDE;
       rec[0] = hst[tid][2];
       rec[1] = hst[tid][3];
-      rec[2] = __builtin_bit_cast(float, hcnt[tid]);
+      rec[2] = __builtin_bit_cast(float, hcw[0][tid] + hcw[1][tid] + hcw[2][tid] + hcw[3][tid]);
       rec[3] = 0.0f;
     }
     return;
@@ -1056,20 +1068,20 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     if (el0 < ne) {  // (a) gather both entries, then dots and log-weights
       const bool ok1 = el1 < ne;
       Raw8<T> k0, v0, k1, v1;
-      const int64_t key0 = lkey[e0 + el0];
+      const int64_t key0 = lkey[lslot(e0 + el0)];
       k0.load(Ku + key0 * D);
       v0.load(Vu + key0 * D);
       uint32_t mk1 = 0;
       if (ok1) {
-        const int64_t key1 = lkey[e0 + el1];
+        const int64_t key1 = lkey[lslot(e0 + el1)];
         k1.load(Ku + key1 * D);
         v1.load(Vu + key1 * D);
-        mk1 = lmask[e0 + el1];
+        mk1 = lmask[lslot(e0 + el1)];
       } else {
         k1.zero();
         v1.zero();
       }
-      entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[e0 + el0], mk1, j16, G, K, L, cf, scale, qsh, msh,
+      entry_pair<T, GM>(k0, v0, k1, v1, ok1, el0, el1, lmask[lslot(e0 + el0)], mk1, j16, G, K, L, cf, scale, qsh, msh,
                         hst, sm.a.v, sm.a.lw, rl);
     }
     __syncthreads();
@@ -1123,7 +1135,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     if (tid % TPH == 0) {
       rec[0] = hst[oh][2];
       rec[1] = ol;
-      rec[2] = __builtin_bit_cast(float, hcnt[oh]);
+      rec[2] = __builtin_bit_cast(float, hcw[0][oh] + hcw[1][oh] + hcw[2][oh] + hcw[3][oh]);
       rec[3] = 0.0f;
     }
   }
