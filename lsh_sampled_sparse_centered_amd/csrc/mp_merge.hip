@@ -170,11 +170,108 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   }
 }
 
+// --------------------------------------------------------------------------
+// The same merge without the index list, spread four times wider: one block
+// of 256 threads per (query head, quarter of the output dims), so that a
+// head's partial records are read by four compute units.  Thread (phase,
+// j) owns dims 32 q + 4 j .. + 3 of chunks phase, phase + 32, ...; each
+// block reads every chunk's m and l, the first quarter also its count.
+constexpr int MQ_PH = 32;  // chunk phases per block (x 8 threads of 4 dims = 256 threads)
+
+__global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
+                                                      int64_t nchunks, float *__restrict__ out,
+                                                      float *__restrict__ lse, int32_t *__restrict__ count) {
+  __shared__ f32x4 red_o[MQ_PH][8];
+  __shared__ float red_m[MQ_PH], red_l[MQ_PH];
+  __shared__ int red_c[MQ_PH];
+  touch_kernargs<1>();  // 48 bytes of arguments
+  // unit-minor order, as the sampling kernel's grid: block i serves unit
+  // i % U, so it runs on the XCD of the blocks that wrote its partials
+  // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
+  const uint32_t U32 = gridDim.x / (4u * (uint32_t)G), bx = blockIdx.x;
+  const int64_t u = (int64_t)(bx % U32);
+  const uint32_t rest = bx / U32;
+  const int hg = (int)(rest % (uint32_t)G), qq = (int)(rest / (uint32_t)G);
+  const int b = (int)u / Hkv;
+  const int h = ((int)u % Hkv) * G + hg;
+  const int64_t bh = (int64_t)b * Hq + h;
+  const int t = threadIdx.x;
+  const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
+  const int64_t cs = (int64_t)G * PSTRIDE;
+  const int ph = t >> 3, j = t & 7;
+  const int d0 = 32 * qq + 4 * j;
+  const bool counts = qq == 0;
+  float m = -INFINITY, l = 0.0f;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  int cnt = 0;
+  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MQ_PH * MERGE_CPT) {
+    // every load of the pass is issued before any is used (chunks past the
+    // last re-read the last one and are dropped)
+    f32x2 ml[MERGE_CPT];
+    int cn[MERGE_CPT];
+    f32x4 oc[MERGE_CPT];
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const int64_t ci = min(c0 + (int64_t)k * MQ_PH, nchunks - 1);
+      const float *r = p0 + ci * cs;
+      ml[k] = *(const f32x2 *)r;  // m, l
+      cn[k] = counts ? __builtin_bit_cast(int, r[2]) : 0;
+      oc[k] = *(const f32x4 *)(r + 4 + d0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const bool live = c0 + (int64_t)k * MQ_PH < nchunks;
+      const float mc = live ? ml[k][0] : -INFINITY;
+      const float mn = fmaxf(m, mc);
+      const float a = m > -INFINITY ? __expf(m - mn) : 0.0f;
+      const float bsc = mc > -INFINITY ? __expf(mc - mn) : 0.0f;
+      l = l * a + ml[k][1] * bsc;
+      acc = acc * a + oc[k] * bsc;
+      m = mn;
+      cnt += live ? cn[k] : 0;
+    }
+  }
+  red_o[ph][j] = acc;
+  if (j == 0) {
+    red_m[ph] = m;
+    red_l[ph] = l;
+    red_c[ph] = cnt;
+  }
+  __syncthreads();
+  if (t < 8) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < MQ_PH; ++p) M = fmaxf(M, red_m[p]);
+    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+    float ls = 0.0f;
+    int cs_ = 0;
+#pragma unroll
+    for (int p = 0; p < MQ_PH; ++p) {
+      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
+      o += red_o[p][t] * sc;
+      ls += red_l[p] * sc;
+      cs_ += red_c[p];
+    }
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+    *(f32x4 *)(out + bh * D + 32 * qq + 4 * t) = o * inv;
+    if (t == 0 && counts) {
+      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
+      if (count) count[bh] = cs_;
+    }
+  }
+}
+
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
                         float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s) {
   (void)n;
   (void)L;
   const int G = Hq / Hkv;
+  if (!idx) {
+    merge_q_kernel<<<dim3((unsigned)(4 * (int64_t)B * Hq)), 256, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, out, lse,
+                                                                         count);
+    return hipGetLastError();
+  }
   merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
                                                                  lse, count, idx, cap, ws.ent, ws.ent_cnt);
   return hipGetLastError();
