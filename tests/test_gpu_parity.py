@@ -414,6 +414,24 @@ def test_decode_stages_equal_composite_and_are_deterministic():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
+@pytest.mark.parametrize("name", ["g8_ragged", "llama8b_layer", "tiny", "g6_bf16", "g4_f32", "mha_b3"])
+def test_merge_without_index_lists_equals_merge_with_them(name):
+    """The merge runs as a wider kernel when no index lists are asked for;
+    both fold the per-tile partial records in the same order, so the output,
+    log-sum-exp and counts agree bit for bit."""
+    w, lay, km, codes, margin, qc = case(name)
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    a = _run_decode(w, lay, kmean, gcodes, qcodes)
+    out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K, 0, 0,
+                      qcodes_in=qcodes, out=out, lse=lse, count=cnt)
+    torch.cuda.synchronize()
+    for x, y in zip((a[0], a[1], a[3]), (out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy())):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
 @pytest.mark.parametrize("name", ["llama8b_layer", "tiny"])
 def test_append_then_decode(name):
     """Append a decoded token per unit (frozen mean): cache rows copied exactly,
