@@ -21,6 +21,75 @@ namespace mp {
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
 constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
 
+// One thread's share of a head's merge: chunks ph, ph + MERGE_PH, ... of the
+// records at p0 (record stride cs), dims d0 .. d0 + 3.  A pass loads
+// MERGE_CPT records at once (independent loads; chunks past the last re-read
+// the last one and are dropped), then folds them in with a running maximum
+// (rescaled sums).  The records' counts are summed when `counts` is set.
+struct MergePart {
+  float m, l;
+  f32x4 o;
+  int cnt;
+};
+__device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs, int64_t nchunks, int ph, int d0,
+                                       bool counts) {
+  MergePart r{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, 0};
+  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
+    f32x2 ml[MERGE_CPT];
+    int cn[MERGE_CPT];
+    f32x4 oc[MERGE_CPT];
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const int64_t ci = min(c0 + (int64_t)k * MERGE_PH, nchunks - 1);
+      const float *rec = p0 + ci * cs;
+      ml[k] = *(const f32x2 *)rec;  // m, l
+      cn[k] = counts ? __builtin_bit_cast(int, rec[2]) : 0;
+      oc[k] = *(const f32x4 *)(rec + 4 + d0);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pass is issued before any result is used
+    // branch-free fold (a branch would let the compiler sink the loads into
+    // it, one round trip each); an empty side gets weight 0
+#pragma unroll
+    for (int k = 0; k < MERGE_CPT; ++k) {
+      const bool live = c0 + (int64_t)k * MERGE_PH < nchunks;
+      const float mc = live ? ml[k][0] : -INFINITY;
+      const float mn = fmaxf(r.m, mc);
+      const float a = r.m > -INFINITY ? __expf(r.m - mn) : 0.0f;
+      const float bsc = mc > -INFINITY ? __expf(mc - mn) : 0.0f;
+      r.l = r.l * a + ml[k][1] * bsc;
+      r.o = r.o * a + oc[k] * bsc;
+      r.m = mn;
+      r.cnt += live ? cn[k] : 0;
+    }
+  }
+  return r;
+}
+
+// The MERGE_PH phases' states (in LDS) folded in phase order for the 4 dims
+// of slot s: writes out[0..3], and the log-sum-exp and count when asked.
+template <int NS>
+__device__ inline void merge_finish(const f32x4 (&red_o)[MERGE_PH][NS], const float (&red_m)[MERGE_PH],
+                                    const float (&red_l)[MERGE_PH], const int (&red_c)[MERGE_PH], int s,
+                                    float *__restrict__ out, float *lse, int32_t *count) {
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
+  f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+  float ls = 0.0f;
+  int cs_ = 0;
+#pragma unroll
+  for (int p = 0; p < MERGE_PH; ++p) {
+    const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
+    o += red_o[p][s] * sc;
+    ls += red_l[p] * sc;
+    cs_ += red_c[p];
+  }
+  const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+  *(f32x4 *)out = o * inv;
+  if (lse) *lse = ls > 0.0f ? M + logf(ls) : -INFINITY;
+  if (count) *count = cs_;
+}
+
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                      int64_t nchunks, int64_t chunk, float *__restrict__ out,
                                                      float *__restrict__ lse, int32_t *__restrict__ count,
@@ -46,75 +115,18 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const int64_t cs = (int64_t)G * PSTRIDE;
 
   // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...
-  // A pass loads MERGE_CPT records at once (independent loads), then merges
-  // them online (running maximum, rescaled sums).
   const int ph = t >> 5, j = t & 31;
-  float m = -INFINITY, l = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int cnt = 0;
-  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
-    // loads are unconditional (chunks past the last re-read the last one and
-    // are dropped), so all of them are in flight at once
-    f32x2 ml[MERGE_CPT];
-    int cn[MERGE_CPT];
-    f32x4 oc[MERGE_CPT];
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const int64_t ci = min(c0 + (int64_t)k * MERGE_PH, nchunks - 1);
-      const float *r = p0 + ci * cs;
-      ml[k] = *(const f32x2 *)r;  // m, l
-      cn[k] = __builtin_bit_cast(int, r[2]);
-      oc[k] = *(const f32x4 *)(r + 4 + 4 * j);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the pass is issued before any result is used
-    float mc[MERGE_CPT], lc[MERGE_CPT];
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const bool live = c0 + (int64_t)k * MERGE_PH < nchunks;
-      mc[k] = live ? ml[k][0] : -INFINITY;
-      lc[k] = ml[k][1];
-      cnt += live ? cn[k] : 0;
-    }
-    // branch-free fold (a branch would let the compiler sink the loads into
-    // it, one round trip each); an empty side gets weight 0
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const float mn = fmaxf(m, mc[k]);
-      const float a = m > -INFINITY ? __expf(m - mn) : 0.0f;
-      const float bsc = mc[k] > -INFINITY ? __expf(mc[k] - mn) : 0.0f;
-      l = l * a + lc[k] * bsc;
-      acc = acc * a + oc[k] * bsc;
-      m = mn;
-    }
-  }
-  red_o[ph][j] = acc;
+  const MergePart mpart = merge_fold(p0, cs, nchunks, ph, 4 * j, true);
+  red_o[ph][j] = mpart.o;
   if (j == 0) {
-    red_m[ph] = m;
-    red_l[ph] = l;
-    red_c[ph] = cnt;
+    red_m[ph] = mpart.m;
+    red_l[ph] = mpart.l;
+    red_c[ph] = mpart.cnt;
   }
   __syncthreads();
-  if (t < 32) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    float ls = 0.0f;
-    int cs_ = 0;
-#pragma unroll
-    for (int p = 0; p < MERGE_PH; ++p) {
-      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
-      o += red_o[p][t] * sc;
-      ls += red_l[p] * sc;
-      cs_ += red_c[p];
-    }
-    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
-    *(f32x4 *)(out + bh * D + 4 * t) = o * inv;
-    if (t == 0) {
-      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
-      if (count) count[bh] = cs_;
-    }
-  }
+  if (t < 32)
+    merge_finish<32>(red_o, red_m, red_l, red_c, t, out + bh * D + 4 * t, t == 0 && lse ? lse + bh : nullptr,
+                     t == 0 && count ? count + bh : nullptr);
   if (!idx) return;
   // Index list: chunk c's keys of this head start at the sum of the earlier
   // chunks' counts (their partial records hold them).  Chunks are taken 1024
@@ -176,14 +188,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 // head's partial records are read by four compute units.  Thread (phase,
 // j) owns dims 32 q + 4 j .. + 3 of chunks phase, phase + 32, ...; each
 // block reads every chunk's m and l, the first quarter also its count.
-constexpr int MQ_PH = 32;  // chunk phases per block (x 8 threads of 4 dims = 256 threads)
 
 __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                       int64_t nchunks, float *__restrict__ out,
                                                       float *__restrict__ lse, int32_t *__restrict__ count) {
-  __shared__ f32x4 red_o[MQ_PH][8];
-  __shared__ float red_m[MQ_PH], red_l[MQ_PH];
-  __shared__ int red_c[MQ_PH];
+  __shared__ f32x4 red_o[MERGE_PH][8];
+  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
+  __shared__ int red_c[MERGE_PH];
   touch_kernargs<1>();  // 48 bytes of arguments
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the XCD of the blocks that wrote its partials
@@ -199,67 +210,18 @@ __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ 
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;
   const int ph = t >> 3, j = t & 7;
-  const int d0 = 32 * qq + 4 * j;
-  const bool counts = qq == 0;
-  float m = -INFINITY, l = 0.0f;
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  int cnt = 0;
-  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MQ_PH * MERGE_CPT) {
-    // every load of the pass is issued before any is used (chunks past the
-    // last re-read the last one and are dropped)
-    f32x2 ml[MERGE_CPT];
-    int cn[MERGE_CPT];
-    f32x4 oc[MERGE_CPT];
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const int64_t ci = min(c0 + (int64_t)k * MQ_PH, nchunks - 1);
-      const float *r = p0 + ci * cs;
-      ml[k] = *(const f32x2 *)r;  // m, l
-      cn[k] = counts ? __builtin_bit_cast(int, r[2]) : 0;
-      oc[k] = *(const f32x4 *)(r + 4 + d0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const bool live = c0 + (int64_t)k * MQ_PH < nchunks;
-      const float mc = live ? ml[k][0] : -INFINITY;
-      const float mn = fmaxf(m, mc);
-      const float a = m > -INFINITY ? __expf(m - mn) : 0.0f;
-      const float bsc = mc > -INFINITY ? __expf(mc - mn) : 0.0f;
-      l = l * a + ml[k][1] * bsc;
-      acc = acc * a + oc[k] * bsc;
-      m = mn;
-      cnt += live ? cn[k] : 0;
-    }
-  }
-  red_o[ph][j] = acc;
+  const bool counts = qq == 0;  // the first quarter also writes the log-sum-exp and the count
+  const MergePart mpart = merge_fold(p0, cs, nchunks, ph, 32 * qq + 4 * j, counts);
+  red_o[ph][j] = mpart.o;
   if (j == 0) {
-    red_m[ph] = m;
-    red_l[ph] = l;
-    red_c[ph] = cnt;
+    red_m[ph] = mpart.m;
+    red_l[ph] = mpart.l;
+    red_c[ph] = mpart.cnt;
   }
   __syncthreads();
-  if (t < 8) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < MQ_PH; ++p) M = fmaxf(M, red_m[p]);
-    f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
-    float ls = 0.0f;
-    int cs_ = 0;
-#pragma unroll
-    for (int p = 0; p < MQ_PH; ++p) {
-      const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
-      o += red_o[p][t] * sc;
-      ls += red_l[p] * sc;
-      cs_ += red_c[p];
-    }
-    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
-    *(f32x4 *)(out + bh * D + 32 * qq + 4 * t) = o * inv;
-    if (t == 0 && counts) {
-      if (lse) lse[bh] = ls > 0.0f ? M + logf(ls) : -INFINITY;
-      if (count) count[bh] = cs_;
-    }
-  }
+  if (t < 8)
+    merge_finish<8>(red_o, red_m, red_l, red_c, t, out + bh * D + 32 * qq + 4 * t,
+                    t == 0 && counts && lse ? lse + bh : nullptr, t == 0 && counts && count ? count + bh : nullptr);
 }
 
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
