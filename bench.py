@@ -153,15 +153,19 @@ def trace_stats(path: str, steps: int, warmup: int, nlayers: int) -> str:
     if warmup < 1:
         raise SystemExit("--trace-stats needs --warmup >= 1 (the window starts after a warmup step's merge)")
     lo, hi = samp[warmup * nlayers], samp[(warmup + steps) * nlayers - 1]
-    while lo > 0 and "merge_kernel" not in rows[lo - 1][2]:  # back to the previous step's last merge
+    def is_merge(name):  # the merge with index lists (merge_kernel) or without them (merge_q_kernel)
+        return "merge_kernel" in name or "merge_q_kernel" in name
+
+    while lo > 0 and not is_merge(rows[lo - 1][2]):  # back to the previous step's last merge
         lo -= 1
-    while hi + 1 < len(rows) and "merge_kernel" not in rows[hi][2]:
+    while hi + 1 < len(rows) and not is_merge(rows[hi][2]):
         hi += 1
     win = rows[lo:hi + 1]
     by = {}
     for s0, e0, name in win:
         short = name.split("(")[0]
-        for key in ("encode_small_kernel", "encode_kernel", "bucket_lookup_kernel", "sample_kernel", "merge_kernel"):
+        for key in ("encode_small_kernel", "encode_kernel", "bucket_lookup_kernel", "sample_kernel", "merge_q_kernel",
+                    "merge_kernel"):
             if key in short:
                 short = key
         by.setdefault(short, []).append((e0 - s0) / 1e3)

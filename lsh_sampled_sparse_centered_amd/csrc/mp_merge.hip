@@ -183,7 +183,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 }
 
 // --------------------------------------------------------------------------
-// The same merge without the index list, spread four times wider: one block
+// The same merge without the index list (up to four heads per unit),
+// spread four times wider: one block
 // of 256 threads per (query head, quarter of the output dims), so that a
 // head's partial records are read by four compute units.  Thread (phase,
 // j) owns dims 32 q + 4 j .. + 3 of chunks phase, phase + 32, ...; each
@@ -229,7 +230,10 @@ hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGe
   (void)n;
   (void)L;
   const int G = Hq / Hkv;
-  if (!idx) {
+  // the wider merge pays with up to four heads per unit (measured: 96K
+  // 4.96 -> 3.9 us, one head per unit 13.9 -> 10.5 us) but not with eight
+  // (5.3 -> 6.4 us)
+  if (!idx && G <= 4) {
     merge_q_kernel<<<dim3((unsigned)(4 * (int64_t)B * Hq)), 256, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, out, lse,
                                                                          count);
     return hipGetLastError();

@@ -416,9 +416,9 @@ def test_decode_stages_equal_composite_and_are_deterministic():
 
 @pytest.mark.parametrize("name", ["g8_ragged", "llama8b_layer", "tiny", "g6_bf16", "g4_f32", "mha_b3"])
 def test_merge_without_index_lists_equals_merge_with_them(name):
-    """The merge runs as a wider kernel when no index lists are asked for;
-    both fold the per-tile partial records in the same order, so the output,
-    log-sum-exp and counts agree bit for bit."""
+    """The merge runs as a wider kernel when no index lists are asked for
+    (up to four heads per KV head); both fold the per-tile partial records in
+    the same order, so the output, log-sum-exp and counts agree bit for bit."""
     w, lay, km, codes, margin, qc = case(name)
     kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
     a = _run_decode(w, lay, kmean, gcodes, qcodes)
