@@ -414,7 +414,8 @@ def test_decode_stages_equal_composite_and_are_deterministic():
         assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
 
 
-@pytest.mark.parametrize("name", ["g8_ragged", "llama8b_layer", "tiny", "g6_bf16", "g4_f32", "mha_b3"])
+@pytest.mark.parametrize("name", ["g8_ragged", "llama8b_layer", "tiny", "g6_bf16", "g4_f32", "mha_b3", "g2_small",
+                                  "g3_k16"])
 def test_merge_without_index_lists_equals_merge_with_them(name):
     """The merge runs as a wider kernel when no index lists are asked for
     (up to four heads per KV head); both fold the per-tile partial records in
