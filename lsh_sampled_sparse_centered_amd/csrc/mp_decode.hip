@@ -273,7 +273,7 @@ __device__ inline void ldv(const T *p, float (&v)[N]) {
 template <typename T, int GM>
 __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Raw8<T> &k1, const Raw8<T> &v1,
                                   bool ok1, int e0, int e1, uint32_t mk0, uint32_t mk1, int j16, int G, int K, int L,
-                                  const LnPCoef &cf, float scale, const float (*qsh)[D], const float *msh,
+                                  const LnPCoef &cf, float scale, const T (*qsh)[D], const float *msh,
                                   const f32x4 *hst, T (*vrows)[D], float (*lw)[ATT_E], float rl) {
   float kv0[8], kv1[8], mv[8];
   k0.get(kv0);
@@ -297,7 +297,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
   for (int h = 0; h < GM; ++h) {
     if (h < G) {
       float qv[8];
-      ld8<float>(&qsh[h][8 * j16], qv);
+      ld8<T>(&qsh[h][8 * j16], qv);
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -403,7 +403,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   __shared__ uint32_t pw2[GM][16];  // plane scan: per head, the tile's sampled-key words
   extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
   uint32_t *qpk = (uint32_t *)qpk4;
-  __shared__ float qsh[GM][D];
+  // the queries in the caches' type; with bf16 caches they are the
+  // matrix-core rounds' B operands as they stand, row GM (and the rows of
+  // heads past G) zero: the padding columns
+  __shared__ alignas(16) T qsh[std::is_same<T, __bf16>::value ? GM + 1 : GM][D];
   __shared__ float msh[D];
   // per head: |q_h|, q_h . mu, running maximum m, running normaliser l (one
   // 16-byte LDS word, so that the weight phase reads all four at once)
@@ -548,9 +551,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
 #pragma unroll
         for (int k = 0; k < QV; ++k) {
           const int i = tid + 256 * k;
-          if (i < GM * D) qsh[i / D][i % D] = i / D < G ? (float)qv[k] : 0.0f;
+          if (i < GM * D) qsh[i / D][i % D] = i / D < G ? qv[k] : (T)0.0f;
         }
         if (tid < D) msh[tid] = mv;
+        if constexpr (std::is_same<T, __bf16>::value) {
+          if (tid < D) qsh[GM][tid] = (T)0.0f;
+        }
       }
       i0 += 256 * QPASS;
     } while (i0 < nq);
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   if (tid < 16 * GM) {  // |q_h| and q_h . mu: a DPP row (16 lanes, 8 dims each) per head
     const int h = tid >> 4;
     float qv[8], mv[8];
-    ld8<float>(&qsh[h][8 * j16], qv);
+    ld8<T>(&qsh[h][8 * j16], qv);
     ld8<float>(msh + 8 * j16, mv);
     float a = 0.0f, bq = 0.0f;
 #pragma unroll
@@ -583,9 +589,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   int nu = 0;  // entries in the union list
   int lp1 = 0, lp2 = 0, lp3 = 0;  // list entries before waves 1, 2, 3's segments
   // LDS slot of list entry e: the list is the waves' segments in wave order
-  // (ascending keys)
+  // (ascending keys); branch-free: each segment boundary passed adds the gap
+  // to the next segment's start
   auto lslot = [&](int e) {
-    return e < lp1 ? e : e < lp2 ? 128 + e - lp1 : e < lp3 ? 256 + e - lp2 : 384 + e - lp3;
+    return e + (e >= lp1 ? 128 - lp1 : 0) + (e >= lp2 ? 128 + lp1 - lp2 : 0) + (e >= lp3 ? 128 + lp2 - lp3 : 0);
   };
   uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
   {
@@ -943,20 +950,18 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
 
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
         float n2 = 0.0f;
-        const int hq = li < GM ? li : 0;
+        const int hq = li < G ? li : GM;  // row GM: zeros
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int d0 = 64 * kh + 32 * st + 8 * qd;
           const bf16x8 kb = __builtin_bit_cast(bf16x8, kr[st]);
-          float mv[8], qv[8];
+          float mv[8];
           ld8<float>(msh + d0, mv);
-          ld8<float>(&qsh[hq][d0], qv);
-          bf16x8 qb;
+          const bf16x8 qb = *(const bf16x8 *)&qsh[hq][d0];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float cj = (float)kb[j] - mv[j];
             n2 += cj * cj;
-            qb[j] = li < G ? (__bf16)qv[j] : (__bf16)0.0f;  // exact: the queries are bf16
           }
           sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qb, sacc, 0, 0, 0);
         }
