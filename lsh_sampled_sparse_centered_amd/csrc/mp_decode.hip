@@ -329,7 +329,10 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 // --------------------------------------------------------------------------
 // One block = one 512-key tile of one unit (batch, KV head), for all G query
 // heads of that KV head.  Blocks are small and many so that the hardware
-// keeps several per compute unit and balances them dynamically.
+// keeps several per compute unit and balances them dynamically.  With SP > 1
+// a block takes up to SP consecutive tiles whose sampled keys come from the
+// bucket lookup's bitmaps (their lists concatenated, one set of attention
+// rounds, one record).
 //
 // Scan: lane l of wave w reads 16 bytes (8 keys) of the codes of tables w,
 // w+4, w+8, ... (non-temporal loads, eight rows in flight) and counts, for
@@ -361,7 +364,7 @@ __device__ inline void entry_pair(const Raw8<T> &k0, const Raw8<T> &v0, const Ra
 //      softmax).
 // The query codes, queries and key mean are fetched while the first batch
 // of codes is in flight.  One partial record (m, l, count, o) per head.
-template <typename T, int GM>
+template <typename T, int GM, int SP>
 __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F32) : MP_OCC8)) void sample_kernel(
     const T *__restrict__ q, const T *__restrict__ Kc, const T *__restrict__ Vc, const uint16_t *__restrict__ codes,
     const float *__restrict__ kmean, const uint16_t *__restrict__ qcodes, int Hq, int Hkv, int G, int64_t n,
@@ -400,7 +403,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     PlaneLds p;
     MfmaLds m;
   } sm;  // scan and attention phases never overlap in time
-  __shared__ uint32_t pw2[GM][16];  // plane scan: per head, the tile's sampled-key words
+  // per head, a tile's sampled-key words: the bucket lookup's bitmaps of the
+  // block's tiles, or the plane scan's result
+  __shared__ uint32_t pw2[SP][GM][16];
   extern __shared__ u32x4 qpk4[];  // [L][GM] query codes, each twice per word (16-byte aligned)
   uint32_t *qpk = (uint32_t *)qpk4;
   // the queries in the caches' type; with bf16 caches they are the
@@ -411,12 +416,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // per head: |q_h|, q_h . mu, running maximum m, running normaliser l (one
   // 16-byte LDS word, so that the weight phase reads all four at once)
   __shared__ f32x4 hst[GM];
-  // union list, one segment of up to 128 entries per wave (the wave's 128
-  // keys), read through lslot: key offset from the block's first key, and
-  // head bits | FORCED
-  __shared__ uint16_t lkey[SCAN_TILE];
-  __shared__ uint16_t lmask[SCAN_TILE];
-  __shared__ int wtot[4];
+  // union list, read through lslot: key offset from the block's first key,
+  // and head bits | FORCED.  One tile: a segment of up to 128 entries per wave
+  // (the wave's 128 keys); several tiles: contiguous, tile after tile
+  __shared__ uint16_t lkey[SP * SCAN_TILE];
+  __shared__ uint16_t lmask[SP * SCAN_TILE];
+  __shared__ int wtot[2][4];  // per wave: a tile's list entries (two buffers, alternating over the tiles)
   __shared__ int hcw[4][GM];  // per wave and head: sampled keys
   __shared__ float alpha_sh[GM];  // per head: this round's rescale factor
 
@@ -431,11 +436,16 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   // appended keys past the bucketed tables: a few per unit, each a chain of
   // dependent load batches) are dispatched first, so their scans overlap the
   // other tiles' attention instead of trailing it.
+  // A tile with bitmaps may share its block with the next ones: SP of them
+  // per block (one prologue and fuller attention rounds, for grids many
+  // times what the chip holds at once), the block's record in its first
+  // tile's slot and empty records in the others.
   // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
   const uint32_t bx = blockIdx.x, U32 = (uint32_t)nunits;
   const int64_t u = (int64_t)(bx % U32);
   const int64_t cr = (int64_t)(bx / U32), nscan = nchunks - nlt;
-  const int64_t c = nlt > 0 ? (cr < nscan ? nlt + cr : cr - nscan) : cr;
+  const int64_t c = cr < nscan ? nlt + cr : (cr - nscan) * SP;  // the block's (first) tile
+  const int nsub = (SP == 1 || c >= nlt) ? 1 : (int)min((int64_t)SP, nlt - c);  // its tiles
   const int b = (int)u / Hkv, kvh = (int)u % Hkv;
   const int64_t qrow0 = (int64_t)b * Hq + (int64_t)kvh * G;  // first query head of this unit
   // keys hashed lifted (Equation 8): the sampling angle is taken against the
@@ -502,11 +512,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       load_half(0, 1);
     }
   }
-  // a tile with bitmaps: its words of every head, loaded with the prologue's loads
-  uint32_t bword = 0u;
-  if (use_bits && tid < GM * 16) {
-    const int h = tid >> 4;
-    if (h < G) bword = sbits[(u * G + h) * bwords + c * 16 + (tid & 15)];
+  // tiles with bitmaps: their words of every head, loaded with the prologue's loads
+  uint32_t bword[SP];
+#pragma unroll
+  for (int t = 0; t < SP; ++t) {
+    bword[t] = 0u;
+    if (use_bits && t < nsub && tid < GM * 16 && (tid >> 4) < G)
+      bword[t] = sbits[(u * G + (tid >> 4)) * bwords + (c + t) * 16 + (tid & 15)];
   }
 
   // ---- prologue: query codes (packed twice per word), queries, key mean.
@@ -565,6 +577,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     hst[tid][2] = -INFINITY;
     hst[tid][3] = 0.0f;
   }
+  if (tid < GM * 16) {
+#pragma unroll
+    for (int t = 0; t < SP; ++t) pw2[t][tid >> 4][tid & 15] = bword[t];
+  }
   __syncthreads();
 
   if (tid < 16 * GM) {  // |q_h| and q_h . mu: a DPP row (16 lanes, 8 dims each) per head
@@ -587,16 +603,20 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   }
 
   int nu = 0;  // entries in the union list
-  int lp1 = 0, lp2 = 0, lp3 = 0;  // list entries before waves 1, 2, 3's segments
-  // LDS slot of list entry e: the list is the waves' segments in wave order
-  // (ascending keys); branch-free: each segment boundary passed adds the gap
-  // to the next segment's start
+  int lp1 = 0, lp2 = 0, lp3 = 0;  // one tile per block: list entries before waves 1, 2, 3's segments
+  // LDS slot of list entry e.  One tile per block: the list is the waves'
+  // segments in wave order (ascending keys); branch-free, each segment
+  // boundary passed adds the gap to the next segment's start.  Several
+  // tiles: the list is contiguous.
   auto lslot = [&](int e) {
-    return e + (e >= lp1 ? 128 - lp1 : 0) + (e >= lp2 ? 128 + lp1 - lp2 : 0) + (e >= lp3 ? 128 + lp2 - lp3 : 0);
+    if constexpr (SP > 1) {
+      return e;
+    } else {
+      return e + (e >= lp1 ? 128 - lp1 : 0) + (e >= lp2 ? 128 + lp1 - lp2 : 0) + (e >= lp3 ? 128 + lp2 - lp3 : 0);
+    }
   };
   uint32_t *uent = ent ? ent + (u * nchunks + c) * (2 * SCAN_TILE) : nullptr;
   {
-    const int64_t sbase = tbase;
     // query codes of table l for every head (GM >= 4: 16-byte LDS reads)
     auto qcodes_of = [&](int l, uint32_t (&Q)[GM]) {
       if constexpr (GM >= 4) {
@@ -613,19 +633,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         for (int h = 0; h < GM; ++h) Q[h] = qpk[l * GM + h];
       }
     };
-    const int64_t klo = sbase + 2 * tid;
-    uint32_t mlo = 0, mhi = 0;
+    uint32_t mlo = 0, mhi = 0;  // keys 2*tid, 2*tid+1 of the tile: heads that sampled them
     if (use_bits) {
-      // the tile's sampled-key words of every head, as the bucket lookup wrote them
-      if (tid < GM * 16) pw2[tid >> 4][tid & 15] = bword;
-      __syncthreads();
-      const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
-#pragma unroll
-      for (int h = 0; h < GM; ++h) {
-        const uint32_t wv = pw2[h][wj];
-        mlo |= ((wv >> k0) & 1u) << h;
-        mhi |= ((wv >> (k0 + 1)) & 1u) << h;
-      }
+      // decoded per tile below
     } else if (use_pl) {
       // Bit-plane scan: the tile's planes are one contiguous region, row
       // (b, l) = bit b of table l's codes for the tile's 512 keys (16 words).
@@ -682,13 +692,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
           a2 |= b2 | (a1 & b1);
           a1 |= b1;
         }
-        pw2[h][jj] = h < G ? a2 : 0u;
+        pw2[0][h][jj] = h < G ? a2 : 0u;
       }
       __syncthreads();
       const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
 #pragma unroll
       for (int h = 0; h < GM; ++h) {
-        const uint32_t wv = pw2[h][wj];
+        const uint32_t wv = pw2[0][h][wj];
         mlo |= ((wv >> k0) & 1u) << h;
         mhi |= ((wv >> (k0 + 1)) & 1u) << h;
       }
@@ -860,45 +870,82 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       }
     }
     }
-    if (klo < nsh || klo >= n - nst) mlo = headbits | FORCED;
-    if (klo + 1 < nsh || klo + 1 >= n - nst) mhi = headbits | FORCED;
-    if (klo >= tend) mlo = 0;
-    if (klo + 1 >= tend) mhi = 0;
-    const bool flo = (mlo & headbits) != 0, fhi = (mhi & headbits) != 0;
-    const uint64_t blo = __ballot(flo), bhi = __ballot(fhi);
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int pre = __popcll(blo & lt) + __popcll(bhi & lt);
-    if (lane == 0) wtot[wave] = __popcll(blo) + __popcll(bhi);
+    for (int t = 0; t < nsub; ++t) {
+      const int64_t tb = tbase + t * SCAN_TILE, te = min(n, tb + SCAN_TILE);
+      const int64_t klo = tb + 2 * tid;
+      if (use_bits) {
+        // the tile's sampled-key words of every head, as the bucket lookup
+        // wrote them (staged with the prologue)
+        const int wj = tid >> 4, k0 = (2 * tid) & 31;  // keys 2*tid, 2*tid+1: word wj, bits k0, k0+1
+        mlo = mhi = 0u;
 #pragma unroll
-    for (int h = 0; h < GM; ++h) {
-      if (h < G) {
-        const int ch = __popcll(__ballot((mlo >> h) & 1)) + __popcll(__ballot((mhi >> h) & 1));
-        if (lane == 0) hcw[wave][h] = ch;
+        for (int h = 0; h < GM; ++h) {
+          const uint32_t wv = pw2[t][h][wj];
+          mlo |= ((wv >> k0) & 1u) << h;
+          mhi |= ((wv >> (k0 + 1)) & 1u) << h;
+        }
+      }
+      if (klo < nsh || klo >= n - nst) mlo = headbits | FORCED;
+      if (klo + 1 < nsh || klo + 1 >= n - nst) mhi = headbits | FORCED;
+      if (klo >= te) mlo = 0;
+      if (klo + 1 >= te) mhi = 0;
+      const bool flo = (mlo & headbits) != 0, fhi = (mhi & headbits) != 0;
+      const uint64_t blo = __ballot(flo), bhi = __ballot(fhi);
+      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+      const int pre = __popcll(blo & lt) + __popcll(bhi & lt);
+      if (lane == 0) wtot[t & 1][wave] = __popcll(blo) + __popcll(bhi);
+#pragma unroll
+      for (int h = 0; h < GM; ++h) {
+        if (h < G) {
+          const int ch = __popcll(__ballot((mlo >> h) & 1)) + __popcll(__ballot((mhi >> h) & 1));
+          if (lane == 0) hcw[wave][h] = (t > 0 ? hcw[wave][h] : 0) + ch;
+        }
+      }
+      const int kloc = (int)(klo - tbase);  // offset from the block's first key
+      if constexpr (SP == 1) {
+        // each wave writes its own segment (no offsets across waves needed yet)
+        const int sb = 128 * wave + pre;
+        if (flo) {
+          lkey[sb] = (uint16_t)kloc;
+          lmask[sb] = (uint16_t)mlo;
+        }
+        if (fhi) {
+          lkey[sb + (flo ? 1 : 0)] = (uint16_t)(kloc + 1);
+          lmask[sb + (flo ? 1 : 0)] = (uint16_t)mhi;
+        }
+        __syncthreads();  // list complete
+        lp1 = wtot[0][0];
+        lp2 = lp1 + wtot[0][1];
+        lp3 = lp2 + wtot[0][2];
+        nu = lp3 + wtot[0][3];
+        if (uent) {  // the index list in key order
+          const int off = (wave == 0 ? 0 : wave == 1 ? lp1 : wave == 2 ? lp2 : lp3) + pre;
+          if (flo) uent[off] = (uint32_t)kloc | ((mlo & headbits) << 16);
+          if (fhi) uent[off + (flo ? 1 : 0)] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
+        }
+      } else {
+        // the tile's entries follow the earlier tiles' (the wave counts go
+        // through LDS, in two buffers that alternate over the tiles)
+        __syncthreads();
+        const int w0 = wtot[t & 1][0], w1 = wtot[t & 1][1], w2 = wtot[t & 1][2], w3 = wtot[t & 1][3];
+        const int off = nu + (wave > 0 ? w0 : 0) + (wave > 1 ? w1 : 0) + (wave > 2 ? w2 : 0) + pre;
+        if (flo) {
+          lkey[off] = (uint16_t)kloc;
+          lmask[off] = (uint16_t)mlo;
+          if (uent) uent[off] = (uint32_t)kloc | ((mlo & headbits) << 16);
+        }
+        if (fhi) {
+          const int o2 = off + (flo ? 1 : 0);
+          lkey[o2] = (uint16_t)(kloc + 1);
+          lmask[o2] = (uint16_t)mhi;
+          if (uent) uent[o2] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
+        }
+        nu += w0 + w1 + w2 + w3;
       }
     }
-    // each wave writes its own segment (no offsets across waves needed yet)
-    const int kloc = (int)(klo - tbase);  // offset from the block's first key
-    const int sb = 128 * wave + pre;
-    if (flo) {
-      lkey[sb] = (uint16_t)kloc;
-      lmask[sb] = (uint16_t)mlo;
-    }
-    if (fhi) {
-      lkey[sb + (flo ? 1 : 0)] = (uint16_t)(kloc + 1);
-      lmask[sb + (flo ? 1 : 0)] = (uint16_t)mhi;
-    }
-    __syncthreads();  // list complete
-    lp1 = wtot[0];
-    lp2 = lp1 + wtot[1];
-    lp3 = lp2 + wtot[2];
-    nu = lp3 + wtot[3];
-    if (uent) {  // the index list in key order
-      const int off = (wave == 0 ? 0 : wave == 1 ? lp1 : wave == 2 ? lp2 : lp3) + pre;
-      if (flo) uent[off] = (uint32_t)kloc | ((mlo & headbits) << 16);
-      if (fhi) uent[off + (flo ? 1 : 0)] = (uint32_t)(kloc + 1) | ((mhi & headbits) << 16);
-    }
+    if constexpr (SP > 1) __syncthreads();  // list complete
   }
-  if (ent_cnt && tid == 0) ent_cnt[u * nchunks + c] = nu;
+  if (ent_cnt && tid < nsub) ent_cnt[u * nchunks + c + tid] = tid == 0 ? nu : 0;
 
   // ---- attention over the union list
   if constexpr (std::is_same<T, __bf16>::value) {
@@ -1055,6 +1102,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       rec[2] = __builtin_bit_cast(float, hcw[0][tid] + hcw[1][tid] + hcw[2][tid] + hcw[3][tid]);
       rec[3] = 0.0f;
     }
+    if constexpr (SP > 1) {  // the block's other tiles: empty records (m = -inf, l = 0, count 0)
+      if (tid < G * (nsub - 1)) *(f32x4 *)(rec0 + (G + tid) * PSTRIDE) = f32x4{-INFINITY, 0.0f, 0.0f, 0.0f};
+    }
     return;
   }
   constexpr int TPH = (256 / GM) < 128 ? (256 / GM) : 128;  // output threads per head
@@ -1198,7 +1248,6 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
                          bool want_idx, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
                          const uint32_t *planes, int64_t n_planes, int64_t n_lists, const float *rlift) {
   const int G = Hq / Hkv;
-  const dim3 grid((unsigned)(geo.nchunks * geo.U));
   const float scale = 1.0f / sqrtf((float)D);
   const uint32_t one2 = 0x00010001u;
   const LnPCoef cf = lnp_coef(K, L, Tthr);
@@ -1207,26 +1256,37 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   const int64_t npt = planes ? n_planes / SCAN_TILE : 0;  // tiles the plane index covers
   const int64_t ptiles = (cap + SCAN_TILE - 1) / SCAN_TILE;
   const int64_t nlt = n_lists / SCAN_TILE;  // tiles whose sampled-key bitmaps the bucket lookup wrote
-#define MP_SAMPLE(T, GMV)                                                                                    \
-  hipExtLaunchKernelGGL(sample_kernel<T, GMV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
+  // Bitmap tiles SPAN_TILES per block (bf16 caches, one or two query heads
+  // per unit) when one tile per block would make a grid of at least
+  // SPAN_MIN_BLOCKS blocks: four times what the chip keeps resident.
+  const int span = (dtype == 0 && G <= 2 && nlt >= 2 && geo.U * geo.nchunks >= SPAN_MIN_BLOCKS) ? SPAN_TILES : 1;
+  const dim3 grid((unsigned)(geo.U * (geo.nchunks - nlt + (nlt + span - 1) / span)));
+#define MP_SAMPLE(T, GMV, SPV)                                                                               \
+  hipExtLaunchKernelGGL(sample_kernel<T, GMV, SPV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \
                         (const T *)q, (const T *)Kc, (const T *)Vc, codes, kmean, qcodes, Hq, Hkv, G, n, cap, K, L,  \
                         nsh, nst, geo.nchunks, scale, one2, cf, ws.part, ent, ent_cnt, planes, npt, ptiles, ws.bits, \
                         geo.nchunks_max * (SCAN_TILE / 32), nlt, rlift, (int)geo.U)
-#define MP_SAMPLE_G(T) \
-  do {                 \
-    if (G == 1)        \
-      MP_SAMPLE(T, 1); \
-    else if (G == 2)   \
-      MP_SAMPLE(T, 2); \
-    else if (G <= 4)   \
-      MP_SAMPLE(T, 4); \
-    else               \
-      MP_SAMPLE(T, 8); \
+#define MP_SAMPLE_G(T)    \
+  do {                    \
+    if (G == 1)           \
+      MP_SAMPLE(T, 1, 1); \
+    else if (G == 2)      \
+      MP_SAMPLE(T, 2, 1); \
+    else if (G <= 4)      \
+      MP_SAMPLE(T, 4, 1); \
+    else                  \
+      MP_SAMPLE(T, 8, 1); \
   } while (0)
-  if (dtype == 0)
+  if (span > 1) {
+    if (G == 1)
+      MP_SAMPLE(__bf16, 1, SPAN_TILES);
+    else
+      MP_SAMPLE(__bf16, 2, SPAN_TILES);
+  } else if (dtype == 0) {
     MP_SAMPLE_G(__bf16);
-  else
+  } else {
     MP_SAMPLE_G(float);
+  }
 #undef MP_SAMPLE_G
 #undef MP_SAMPLE
   return hipGetLastError();

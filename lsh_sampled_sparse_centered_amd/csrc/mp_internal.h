@@ -77,6 +77,14 @@ struct DecodeWs {
 };
 
 DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap);
+// Tiles with bucket-lookup bitmaps taken SPAN_TILES per sampling block (one
+// or two query heads per unit, bf16 caches) when one tile per block would
+// make a grid of at least SPAN_MIN_BLOCKS blocks, four times what the chip
+// keeps resident (256 compute units x 7 blocks): one prologue per block and
+// fuller attention rounds.  The block's record goes to its first tile's
+// slot, empty records (m = -inf, l = 0) to the others.
+constexpr int SPAN_TILES = 4;
+constexpr int64_t SPAN_MIN_BLOCKS = 4 * 256 * 7;
 DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L);
 
 // Launchers (defined in the .hip files); they return hipError_t of the launch.

@@ -57,7 +57,8 @@ __device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs,
       const float a = r.m > -INFINITY ? __expf(r.m - mn) : 0.0f;
       const float bsc = mc > -INFINITY ? __expf(mc - mn) : 0.0f;
       r.l = r.l * a + ml[k][1] * bsc;
-      r.o = r.o * a + oc[k] * bsc;
+      // an empty record's o need not have been written (m = -inf, l = 0)
+      r.o = bsc > 0.0f ? r.o * a + oc[k] * bsc : r.o * a;
       r.m = mn;
       r.cnt += live ? cn[k] : 0;
     }
@@ -162,7 +163,9 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     for (int k = wave; k < ng; k += 16) {
       const int64_t cc = g0 + k;
       // clamp: stays inside the workspace even if the entries were not written
-      const int ne = min(max(ent_cnt[u * nchunks + cc], 0), (int)(2 * chunk));
+      // (a sampling block that took several tiles keeps their entries in
+      // its first tile's region and the ones after it)
+      const int ne = (int)min((int64_t)max(ent_cnt[u * nchunks + cc], 0), (nchunks - cc) * 2 * chunk);
       const uint32_t *src = ent + (u * nchunks + cc) * (2 * chunk);
       int o = coff[k];
       for (int e0 = 0; e0 < ne; e0 += 64) {

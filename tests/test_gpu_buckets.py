@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import lsh_sampled_sparse_centered_amd as mp
+import oracle
 import synth
 from tests.common import layer, oracle_decode, variant
 from tests.test_gpu_parity import CASES, _compare, _inject, case, gpu_build
@@ -214,3 +215,69 @@ def test_index_maintenance_across_tile_boundaries(name):
     # the rebuilt buckets hold their codes
     buf = runs["buckets"]["buckets"].cpu().numpy()
     check_buckets_hold_their_codes(buf, runs["buckets"]["codes"].cpu().numpy(), w.K, n_idx)
+
+
+# One or two query heads per KV head and at least 4 x 256 x 7 = 7,168 one-tile
+# sampling blocks: the sampling kernel takes the bitmap tiles four per block
+# (the record in the first tile's slot, empty records in the others).
+SPAN_CASES = {
+    # one query head per KV head: 224 units x 33 tiles
+    "mha_span": variant("codellama13b_b16", layers=1, batch=16, hq=14, hkv=14, n=16600, K=8, L=75),
+    # two query heads per KV head: 224 units x 33 tiles
+    "g2_span": variant("llama8b_layer", batch=28, hq=16, hkv=8, n=16600, K=8, L=75),
+}
+_span_cache = {}
+
+
+def span_case(name):
+    """Seeded keys, values and queries; the oracle's key means and query codes and seeded uniform
+    codes for every unit (the same on both sides), injected into the device's stores."""
+    if name not in _span_cache:
+        w = SPAN_CASES[name]
+        U = w.batch * w.hkv
+        print("[gpu parity] span case %s: B=%d Hq=%d Hkv=%d n=%d K=%d L=%d" % (name, w.batch, w.hq, w.hkv, w.n,
+                                                                             w.K, w.L), flush=True)
+        lay = layer(w, seed=4321)
+        cap, n = lay["cap"], lay["n"]
+        h = lay["host"]
+        keys = h["K"].reshape(U, cap, w.d)
+        km = np.stack([oracle.key_mean(keys[u, :n]) for u in range(U)])
+        codes = np.stack([synth.unit_codes(4321, 0, u // w.hkv, u % w.hkv, w.K, w.L, cap).numpy().astype(np.uint16)
+                          for u in range(U)])
+        qc = oracle.encode(h["q"].reshape(-1, w.d), h["W"], w.K, w.L).reshape(w.batch, w.hq, w.L)
+        _span_cache[name] = (w, lay, km, codes, qc)
+    return _span_cache[name]
+
+
+@pytest.mark.parametrize("name,nb_tiles,nsh,nst", [
+    ("mha_span", 32, 0, 0),   # eight blocks of four bitmap tiles; the short last tile scanned
+    ("mha_span", 31, 4, 64),  # a last block of three bitmap tiles, two tiles scanned; forced ranges
+    ("g2_span", 30, 0, 0),
+])
+def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
+    """Index lists and counts equal the code scan's (one tile per block) and
+    the oracle's; outputs and lse within the oracle's bars and within
+    rounding of the scan's; the merge without index lists gives the same bits."""
+    w, lay, km, codes, qc = span_case(name)
+    U = w.batch * w.hkv
+    assert w.group <= 2 and U * ((lay["n"] + 511) // 512) >= 4 * 256 * 7
+    kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
+    nb = nb_tiles * 512
+    buf = mp.mp_build_buckets(gcodes, w.K, nb)
+    got = _decode(w, lay, kmean, gcodes, qcodes, buf, nb, nsh, nst)
+    base = _decode(w, lay, kmean, gcodes, qcodes, None, 0, nsh, nst)
+    assert np.array_equal(got[2], base[2]) and np.array_equal(got[3], base[3])
+    assert np.allclose(got[0], base[0], rtol=1e-5, atol=1e-6)
+    fin = np.isfinite(base[1])
+    assert np.array_equal(fin, np.isfinite(got[1])) and np.allclose(got[1][fin], base[1][fin], rtol=0, atol=1e-5)
+    # the merge without index lists (four heads or fewer per unit: the wider merge) gives the same bits
+    out = torch.empty(w.batch, w.hq, w.d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
+    cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
+    mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K, nsh, nst,
+                      qcodes_in=qcodes, out=out, lse=lse, count=cnt, buckets=buf, n_buckets=nb)
+    torch.cuda.synchronize()
+    for a, b in zip((out, lse, cnt), got[:2] + got[3:]):
+        assert np.array_equal(a.cpu().numpy().view(np.uint8), b.view(np.uint8))
+    ref = oracle_decode(w, lay, km, codes, qc, nsh=nsh, nst=nst)
+    _compare(w, ref, *got, "%s buckets<%d nsh=%d nst=%d (four tiles per block)" % (name, nb, nsh, nst))

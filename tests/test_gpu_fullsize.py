@@ -18,6 +18,10 @@ reads comes from memory the HIP path writes.  Checked per layer:
 * a decode with the oracle's query codes injected: index lists exact and
   outputs within 2e-3 for every checked unit.
 
+The prefill keys' whole tiles are found through the bit-plane index or the
+bucketed hash tables (the benchmark's default), built from the injected
+codes, or by scanning the codes; the appended keys are always scanned.
+
 Which units are checked at which step: every unit at the first and last
 step; at the steps in between, the code subset.
 """
@@ -66,9 +70,9 @@ def code_subset(w, layers):
 class LayerRun:
     """One layer on the device, decoded step by step, checked against the oracle."""
 
-    def __init__(self, w, layer_idx, code_units, T=2, planes=False, nsh=0, nst=0):
+    def __init__(self, w, layer_idx, code_units, T=2, index=None, nsh=0, nst=0):
         self.w, self.li, self.T, self.nsh, self.nst = w, layer_idx, T, nsh, nst
-        self.use_planes, self.planes, self.n_planes = planes, None, 0
+        self.index, self.planes, self.n_planes, self.buckets, self.n_buckets = index, None, 0, None, 0
         self.code_units = sorted(code_units)
         lay = synth.layer_inputs(w, SEED, layer_idx, device="cuda")
         self.U, self.cap, self.n0 = w.batch * w.hkv, lay["cap"], lay["n"]
@@ -144,13 +148,22 @@ class LayerRun:
         _say("layer %d: %d key means bitwise; %d of %d subset codes differ, all inside the band" %
              (self.li, self.U, ndiff, total))
 
-    def build_planes(self):
-        """Bit-plane index of the (injected) codes for the prefill keys' whole
-        tiles, as the benchmark builds it; appended keys stay past it."""
-        self.n_planes = (self.n0 // 512) * 512
-        self.planes = mp.mp_build_planes(self.codes, self.w.K, self.n_planes)
+    def build_index(self):
+        """The bit-plane index or the bucketed tables of the (injected) codes
+        for the prefill keys' whole tiles, as the benchmark builds them;
+        appended keys stay past them."""
+        nw = (self.n0 // 512) * 512
+        if self.index == "planes":
+            self.n_planes = nw
+            self.planes = mp.mp_build_planes(self.codes, self.w.K, nw)
+        elif self.index == "buckets":
+            self.n_buckets = nw
+            self.buckets = mp.mp_build_buckets(self.codes, self.w.K, nw)
         torch.cuda.synchronize()
-        _say("layer %d: bit-plane index of keys [0, %d)" % (self.li, self.n_planes))
+        _say("layer %d: %s of keys [0, %d)" % (self.li, self.index, nw))
+
+    def _index_args(self):
+        return dict(planes=self.planes, n_planes=self.n_planes, buckets=self.buckets, n_buckets=self.n_buckets)
 
     # ------------------------------------------------------------ one step
     def step(self, s, check_units):
@@ -169,8 +182,8 @@ class LayerRun:
         lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
         cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
         mp.mp_decode_step(kn, vn, q, self.Kc, self.Vc, self.codes, self.kmean, self.Wp, w.hkv, n, w.K, self.ws,
-                          out=out, lse=lse, count=cnt, T=self.T, planes=self.planes, n_planes=self.n_planes,
-                          n_static_head=self.nsh, n_static_tail=self.nst)
+                          out=out, lse=lse, count=cnt, T=self.T, n_static_head=self.nsh, n_static_tail=self.nst,
+                          **self._index_args())
         torch.cuda.synchronize()
         assert torch.equal(self.Kc[:, n], kn) and torch.equal(self.Vc[:, n], vn)
         # appended codes (frozen means) of every unit
@@ -204,7 +217,7 @@ class LayerRun:
         idx = torch.full((w.batch, w.hq, self.cap), -1, dtype=torch.int32, device="cuda")
         mp.mp_decode_attn(q, self.Kc, self.Vc, self.codes, self.kmean, None, w.hkv, self.n, w.K, self.nsh, self.nst,
                           qcodes_in=qc16.view(torch.uint16), out=out2, idx=idx, count=cnt2, ws=self.ws, T=self.T,
-                          planes=self.planes, n_planes=self.n_planes)
+                          **self._index_args())
         torch.cuda.synchronize()
         o1, l1, c1 = out.cpu().numpy(), lse.cpu().numpy(), cnt.cpu().numpy()
         o2, c2, ix = out2.cpu().numpy(), cnt2.cpu().numpy(), idx.cpu().numpy()
@@ -238,24 +251,25 @@ class LayerRun:
                     if own:
                         assert np.max(np.abs(o1[b, hh] - ref["out"][j, g])) <= OUT_TOL, (s, u, g)
                         assert abs(float(l1[b, hh]) - float(ref["lse"][j, g])) <= LSE_TOL, (s, u, g)
-        _say("layer %d step %d (n=%d, K=%d, T=%d, forced %d+%d, index below %d): %d units checked (%d on the step's "
+        _say("layer %d step %d (n=%d, K=%d, T=%d, forced %d+%d, %s below %d): %d units checked (%d on the step's "
              "own outputs); sets exact; worst |out - oracle| %.3g; mean |S| %.0f" %
-             (self.li, s, self.n, w.K, self.T, self.nsh, self.nst, self.n_planes, len(check_units), direct, worst,
-              float(np.mean(sizes))))
+             (self.li, s, self.n, w.K, self.T, self.nsh, self.nst, self.index, max(self.n_planes, self.n_buckets),
+              len(check_units), direct, worst, float(np.mean(sizes))))
 
 
-def _run_layers(w, layers, steps=1, check_every=None, T=2, planes=True, layer_cfg=None):
+def _run_layers(w, layers, steps=1, check_every=None, T=2, index="planes", layer_cfg=None):
     """Each layer: build, check and inject; then ``steps`` appending decode
-    steps.  ``layer_cfg(layer) -> (workload, forced head, forced tail)``
-    gives a layer its own table shape and forced ranges (the pages' policy)."""
+    steps.  ``index``: "planes", "buckets" or None (scan the codes).
+    ``layer_cfg(layer) -> (workload, forced head, forced tail)`` gives a
+    layer its own table shape and forced ranges (the pages' policy)."""
     subset = code_subset(w, layers)
     for li in layers:
         wl, nsh, nst = layer_cfg(li) if layer_cfg else (w, 0, 0)
-        use_planes = planes and wl.K > 0
-        run = LayerRun(wl, li, [u for l, u in subset if l == li], T=T, planes=use_planes, nsh=nsh, nst=nst)
+        ix = index if wl.K > 0 else None
+        run = LayerRun(wl, li, [u for l, u in subset if l == li], T=T, index=ix, nsh=nsh, nst=nst)
         run.check_build_and_inject()
-        if use_planes:
-            run.build_planes()
+        if ix:
+            run.build_index()
         allu = list(range(run.U))
         sub = run.code_units
         for s in range(1, steps + 1):
@@ -268,15 +282,16 @@ def _run_layers(w, layers, steps=1, check_every=None, T=2, planes=True, layer_cf
 @pytest.mark.parametrize("part", range(4))
 def test_llama8b_96k_all_layers(part):
     """Llama-3.1-8B shape at 96K context (32 q / 8 KV heads, K=10, L=150):
-    every unit of 8 of the 32 layers, one appending step, scanning the
-    bit-plane index of the prefill keys as the benchmark does."""
+    every unit of 8 of the 32 layers, one appending step, the prefill keys
+    found through the bucketed tables (the benchmark's default: layers 0-15)
+    or the bit-plane index (layers 16-31)."""
     w = synth.WORKLOADS["llama8b_96k"]
-    _run_layers(w, list(range(8 * part, 8 * part + 8)))
+    _run_layers(w, list(range(8 * part, 8 * part + 8)), index="buckets" if part < 2 else "planes")
 
 
 def test_llama8b_96k_codes_only():
     """The 96K layer shape scanning only the 16-bit codes (no index)."""
-    _run_layers(synth.WORKLOADS["llama8b_96k"], [7], planes=False)
+    _run_layers(synth.WORKLOADS["llama8b_96k"], [7], index=None)
 
 
 @pytest.mark.parametrize("T", [1, 3])
@@ -286,10 +301,11 @@ def test_llama8b_96k_threshold(T):
     _run_layers(synth.WORKLOADS["llama8b_96k"], [5], T=T)
 
 
-@pytest.mark.parametrize("layer_idx", [0, 39])
-def test_codellama13b_b16_layer(layer_idx):
-    """CodeLlama-13B shape, batch 16, MHA (640 units per layer, K=9, L=120), one appending step."""
-    _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx], planes=layer_idx == 0)
+@pytest.mark.parametrize("layer_idx,index", [(0, "planes"), (39, "buckets"), (20, None)])
+def test_codellama13b_b16_layer(layer_idx, index):
+    """CodeLlama-13B shape, batch 16, MHA (640 units per layer, K=9, L=120), one appending step; with the
+    bucketed tables the sampling blocks take four bitmap tiles each (21,120 tiles per layer)."""
+    _run_layers(synth.WORKLOADS["codellama13b_b16"], [layer_idx], index=index)
 
 
 @pytest.mark.parametrize("part", range(6))
@@ -299,7 +315,8 @@ def test_codellama34b_b4_64_steps(part):
     seeded 5% code subset at every step in between (every appended key and
     every query's codes at every step)."""
     w = synth.WORKLOADS["codellama34b_b4"]
-    _run_layers(w, list(range(8 * part, 8 * part + 8)), steps=64, check_every=1)
+    _run_layers(w, list(range(8 * part, 8 * part + 8)), steps=64, check_every=1,
+                index="buckets" if part < 3 else "planes")
 
 
 @pytest.mark.parametrize("part", range(2))
