@@ -335,13 +335,15 @@ static int decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dty
     if (e != hipSuccess) return MP_ERR_HIP;
     qc = dst;
   }
+  const int64_t nlt = list_keys(buckets, n_buckets, T) / SCAN_TILE;  // tiles with bitmaps
   if (geo.nchunks > 0) {
     st = run_sample(kv_dtype, q, Kc, Vc, codes, kmean, qc, B, Hq, Hkv, n, cap, K, L, T, n_static_head, n_static_tail,
                     geo, w, idx != nullptr, s, nullptr, nullptr, planes, n_planes, buckets,
                     list_keys(buckets, n_buckets, T), rlift);
     if (st) return st;
   }
-  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s));
+  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, s, nlt,
+                                 sample_span(kv_dtype, Hq / Hkv, nlt, geo)));
 }
 
 int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
@@ -451,7 +453,9 @@ int decode_step(const void *k_new, const void *v_new, const void *q, void *Kc, v
   } else if (ev && (hipEventRecord(ev[0], s) != hipSuccess || hipEventRecord(ev[1], s) != hipSuccess)) {
     return MP_ERR_HIP;
   }
-  return hip_status(launch_merge(B, Hq, Hkv, nd, L, geo, w, out, lse, idx, cap, count, s));
+  const int64_t nlt = list_keys(buckets, n_buckets, T) / SCAN_TILE;  // tiles with bitmaps
+  return hip_status(launch_merge(B, Hq, Hkv, nd, L, geo, w, out, lse, idx, cap, count, s, nlt,
+                                 sample_span(kv_dtype, Hq / Hkv, nlt, geo)));
 }
 
 }  // namespace

@@ -1259,7 +1259,7 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
   // Bitmap tiles SPAN_TILES per block (bf16 caches, one or two query heads
   // per unit) when one tile per block would make a grid of at least
   // SPAN_MIN_BLOCKS blocks: four times what the chip keeps resident.
-  const int span = (dtype == 0 && G <= 2 && nlt >= 2 && geo.U * geo.nchunks >= SPAN_MIN_BLOCKS) ? SPAN_TILES : 1;
+  const int span = sample_span(dtype, G, nlt, geo);
   const dim3 grid((unsigned)(geo.U * (geo.nchunks - nlt + (nlt + span - 1) / span)));
 #define MP_SAMPLE(T, GMV, SPV)                                                                               \
   hipExtLaunchKernelGGL(sample_kernel<T, GMV, SPV>, grid, dim3(256), sizeof(uint32_t) * L * GMV, s, ev_start, ev_stop, 0, \

@@ -379,7 +379,6 @@ __global__ __launch_bounds__(64 * ENC_NW, MP_ENC_OCC) void encode_kernel(EncJob 
   const int64_t row_w = rb * ENC_ROWS + wave * 64;  // first row of this wave
   const int l0 = zt * tables_per_block;
   const int l1 = min(L, l0 + tables_per_block);
-  const bool copy_rows = zt == 0;  // table-split blocks share rows
 
   // tiles [t0, t1) hold tables [l0, l1) (l0 is a multiple of tpt)
   const int tpt = enc_tpt(K);
@@ -405,6 +404,26 @@ __global__ __launch_bounds__(64 * ENC_NW, MP_ENC_OCC) void encode_kernel(EncJob 
   // the first stage's loads are issued before the rows are read, so the two
   // latencies overlap (this is what bounds small jobs)
   if (K > 0) MP_FETCH(0, t0);
+
+  // appends: the table blocks of a row block copy the raw key and value rows
+  // into the caches, each its share of the 16-byte pieces.  A thread's first
+  // piece is loaded with the operand rows (one memory round trip for both)
+  // and stored once they have arrived; further pieces (few blocks) follow.
+  constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
+  const int64_t cr0 = rb * ENC_ROWS;
+  const int cnp = (kcopy && vcopy) ? (int)min((int64_t)ENC_ROWS, rows - cr0) * CPR : 0;  // pieces
+  const int cfirst = zt * NT + (int)threadIdx.x, cstep = (int)jb.tsplit * NT;
+  auto piece_src = [&](const T *base, int c) {
+    return (const uint4 *)((const char *)(base + u * in_su + (cr0 + c / CPR) * in_si) + 16 * (c % CPR));
+  };
+  auto piece_dst = [&](T *base, int c) {
+    return (uint4 *)((char *)(base + u * kc_su + (cr0 + c / CPR) * kc_si) + 16 * (c % CPR));
+  };
+  uint4 kx0 = {0u, 0u, 0u, 0u}, vx0 = {0u, 0u, 0u, 0u};
+  if (cfirst < cnp) {
+    kx0 = *piece_src(in, cfirst);
+    vx0 = *piece_src(vin, cfirst);
+  }
 
   // B operands: rows row_w + 32*nt + lane%32, dims 16 s + 8 half + e.  All
   // loads of a 32-row set are issued before any is used (one memory round
@@ -450,21 +469,14 @@ __global__ __launch_bounds__(64 * ENC_NW, MP_ENC_OCC) void encode_kernel(EncJob 
     }
   }
 
-  // appends: the first table block of each row block copies the raw key and
-  // value rows into the caches (16 bytes per thread and step; both loads
-  // before both stores, after the operand loads so those are not held up)
-  if (kcopy && vcopy && copy_rows) {
-    constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
-    const int64_t r0 = rb * ENC_ROWS;
-    const int nr = (int)min((int64_t)ENC_ROWS, rows - r0);
-    for (int c = threadIdx.x; c < nr * CPR; c += NT) {
-      const int64_t r = r0 + c / CPR;
-      const int pc = c % CPR;
-      const uint4 kx = *(const uint4 *)((const char *)(in + u * in_su + r * in_si) + 16 * pc);
-      const uint4 vx = *(const uint4 *)((const char *)(vin + u * in_su + r * in_si) + 16 * pc);
-      *(uint4 *)((char *)(kcopy + u * kc_su + r * kc_si) + 16 * pc) = kx;
-      *(uint4 *)((char *)(vcopy + u * kc_su + r * kc_si) + 16 * pc) = vx;
-    }
+  if (cfirst < cnp) {
+    *piece_dst(kcopy, cfirst) = kx0;
+    *piece_dst(vcopy, cfirst) = vx0;
+  }
+  for (int c = cfirst + cstep; c < cnp; c += cstep) {  // both loads before both stores
+    const uint4 kx = *piece_src(in, c), vx = *piece_src(vin, c);
+    *piece_dst(kcopy, c) = kx;
+    *piece_dst(vcopy, c) = vx;
   }
 
   const int64_t my_row = row_w + lane;  // row whose 32-bit words this lane assembles
@@ -758,11 +770,12 @@ __global__ __launch_bounds__(256) void encode_small_kernel(EncJob j0, EncJob j1,
     }
   }
 
-  // appends: block 0 copies the raw key and value rows into the caches (16
-  // bytes per thread and step; both loads before both stores)
-  if (kcopy && vcopy && lb == 0) {
+  // appends: the job's blocks copy the raw key and value rows into the
+  // caches, each its share of the 16-byte pieces (one per thread for up to
+  // blocks0 * 256 pieces; both loads before both stores)
+  if (kcopy && vcopy) {
     constexpr int CPR = D * (int)sizeof(T) / 16;  // 16-byte pieces per row
-    for (int c = threadIdx.x; c < R * CPR; c += 256) {
+    for (int c = lb * 256 + (int)threadIdx.x; c < R * CPR; c += blocks0 * 256) {
       const int r = c / CPR, pc = c % CPR;
       const int64_t u = r / (int)jb.rows, i = r % (int)jb.rows;
       const uint4 kx = *(const uint4 *)((const char *)(in + u * jb.in_su + i * jb.in_si) + 16 * pc);

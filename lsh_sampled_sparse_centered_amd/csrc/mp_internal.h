@@ -85,6 +85,11 @@ DecodeGeom decode_geom(int B, int Hkv, int Hq, int64_t n, int64_t cap);
 // slot, empty records (m = -inf, l = 0) to the others.
 constexpr int SPAN_TILES = 4;
 constexpr int64_t SPAN_MIN_BLOCKS = 4 * 256 * 7;
+// Bitmap tiles per sampling block for a launch (dtype 0: bf16 caches; nlt:
+// tiles with bitmaps).
+inline int sample_span(int dtype, int G, int64_t nlt, const DecodeGeom &g) {
+  return (dtype == 0 && G <= 2 && nlt >= 2 && g.U * g.nchunks >= SPAN_MIN_BLOCKS) ? SPAN_TILES : 1;
+}
 DecodeWs decode_ws_layout(void *base, int B, int Hq, int Hkv, int64_t cap, int L);
 
 // Launchers (defined in the .hip files); they return hipError_t of the launch.
@@ -183,8 +188,12 @@ hipError_t launch_sample(int dtype, const void *q, const void *Kc, const void *V
 // table l's codes for keys 512 t + 32 j .. + 31).
 hipError_t launch_plane_build(const uint16_t *codes, int64_t U, int64_t cap, int K, int L, int64_t t0, int64_t nt,
                               uint32_t *planes, hipStream_t s);
+// With (nlt, span) from the sampling launch, the merge reads only the
+// records that launch filled (one per block); with the defaults it reads
+// every tile's (the empty ones weigh nothing).
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
-                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s);
+                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s,
+                        int64_t nlt = 0, int span = 1);
 
 // ---------------------------------------------------------------- bucketed tables
 // Per (unit, table, chunk of BK_R keys) a table of 2^K buckets: the chunk's

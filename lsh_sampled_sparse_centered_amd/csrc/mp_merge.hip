@@ -21,26 +21,30 @@ namespace mp {
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
 constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
 
-// One thread's share of a head's merge: chunks ph, ph + MERGE_PH, ... of the
-// records at p0 (record stride cs), dims d0 .. d0 + 3.  A pass loads
-// MERGE_CPT records at once (independent loads; chunks past the last re-read
-// the last one and are dropped), then folds them in with a running maximum
-// (rescaled sums).  The records' counts are summed when `counts` is set.
+// One thread's share of a head's merge: records ph, ph + MERGE_PH, ... of
+// nrec at p0 (record stride cs), dims d0 .. d0 + 3.  Record r is chunk r's,
+// or, when the sampling blocks took the bitmap chunks `span` at a time,
+// chunk r * span for r < nsp and chunk nlt + r - nsp after.  A pass loads
+// MERGE_CPT records at once (independent loads; records past the last
+// re-read the last one and are dropped), then folds them in with a running
+// maximum (rescaled sums).  The records' counts are summed when `counts` is
+// set.
 struct MergePart {
   float m, l;
   f32x4 o;
   int cnt;
 };
-__device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs, int64_t nchunks, int ph, int d0,
-                                       bool counts) {
+__device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs, int64_t nrec, int ph, int d0,
+                                       bool counts, int64_t nsp = 0, int span = 1, int64_t nlt = 0) {
   MergePart r{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, 0};
-  for (int64_t c0 = ph; c0 < nchunks; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
+  for (int64_t c0 = ph; c0 < nrec; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
     f32x2 ml[MERGE_CPT];
     int cn[MERGE_CPT];
     f32x4 oc[MERGE_CPT];
 #pragma unroll
     for (int k = 0; k < MERGE_CPT; ++k) {
-      const int64_t ci = min(c0 + (int64_t)k * MERGE_PH, nchunks - 1);
+      const int64_t ri = min(c0 + (int64_t)k * MERGE_PH, nrec - 1);
+      const int64_t ci = ri < nsp ? ri * span : nlt + ri - nsp;
       const float *rec = p0 + ci * cs;
       ml[k] = *(const f32x2 *)rec;  // m, l
       cn[k] = counts ? __builtin_bit_cast(int, rec[2]) : 0;
@@ -51,7 +55,7 @@ __device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs,
     // it, one round trip each); an empty side gets weight 0
 #pragma unroll
     for (int k = 0; k < MERGE_CPT; ++k) {
-      const bool live = c0 + (int64_t)k * MERGE_PH < nchunks;
+      const bool live = c0 + (int64_t)k * MERGE_PH < nrec;
       const float mc = live ? ml[k][0] : -INFINITY;
       const float mn = fmaxf(r.m, mc);
       const float a = r.m > -INFINITY ? __expf(r.m - mn) : 0.0f;
@@ -96,14 +100,14 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
                                                      float *__restrict__ lse, int32_t *__restrict__ count,
                                                      int32_t *__restrict__ idx, int64_t cap,
                                                      const uint32_t *__restrict__ ent,
-                                                     const int32_t *__restrict__ ent_cnt) {
+                                                     const int32_t *__restrict__ ent_cnt, int64_t nlt, int span) {
   __shared__ f32x4 red_o[MERGE_PH][32];
   __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
   __shared__ int red_c[MERGE_PH];
   __shared__ int wsum[16];
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the same XCD as the blocks that wrote its partials
-  touch_kernargs<2>();  // 96 bytes of arguments
+  touch_kernargs<2>();  // 112 bytes of arguments
   // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
   const uint32_t U32 = gridDim.x / (uint32_t)G, bx = blockIdx.x;
   const int64_t u = (int64_t)(bx % U32);
@@ -115,9 +119,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;
 
-  // thread (phase, j): dims 4j..4j+3 of chunks phase, phase + MERGE_PH, ...
+  // thread (phase, j): dims 4j..4j+3 of records phase, phase + MERGE_PH, ...
+  // (the records the sampling blocks filled, in the same order as the merge
+  // without index lists, so that both give the same bits)
   const int ph = t >> 5, j = t & 31;
-  const MergePart mpart = merge_fold(p0, cs, nchunks, ph, 4 * j, true);
+  const int64_t nsp = (nlt + span - 1) / span;  // records of the bitmap chunks
+  const MergePart mpart = merge_fold(p0, cs, nsp + nchunks - nlt, ph, 4 * j, true, nsp, span, nlt);
   red_o[ph][j] = mpart.o;
   if (j == 0) {
     red_m[ph] = mpart.m;
@@ -190,16 +197,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 // spread four times wider: one block
 // of 256 threads per (query head, quarter of the output dims), so that a
 // head's partial records are read by four compute units.  Thread (phase,
-// j) owns dims 32 q + 4 j .. + 3 of chunks phase, phase + 32, ...; each
-// block reads every chunk's m and l, the first quarter also its count.
+// j) owns dims 32 q + 4 j .. + 3 of records phase, phase + 32, ...; each
+// block reads every record's m and l, the first quarter also its count.
+// With span > 1 only the records the sampling blocks filled are read (one per
+// block: chunks 0, span, 2 span, ... below nlt, every chunk from nlt on).
 
 __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
-                                                      int64_t nchunks, float *__restrict__ out,
-                                                      float *__restrict__ lse, int32_t *__restrict__ count) {
+                                                      int64_t nchunks, int64_t nlt, int span,
+                                                      float *__restrict__ out, float *__restrict__ lse,
+                                                      int32_t *__restrict__ count) {
   __shared__ f32x4 red_o[MERGE_PH][8];
   __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
   __shared__ int red_c[MERGE_PH];
-  touch_kernargs<1>();  // 48 bytes of arguments
+  touch_kernargs<1>();  // 64 bytes of arguments
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the XCD of the blocks that wrote its partials
   // (32-bit index arithmetic: a 64-bit division is a long instruction chain)
@@ -215,7 +225,8 @@ __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ 
   const int64_t cs = (int64_t)G * PSTRIDE;
   const int ph = t >> 3, j = t & 7;
   const bool counts = qq == 0;  // the first quarter also writes the log-sum-exp and the count
-  const MergePart mpart = merge_fold(p0, cs, nchunks, ph, 32 * qq + 4 * j, counts);
+  const int64_t nsp = (nlt + span - 1) / span;  // records of the bitmap chunks
+  const MergePart mpart = merge_fold(p0, cs, nsp + nchunks - nlt, ph, 32 * qq + 4 * j, counts, nsp, span, nlt);
   red_o[ph][j] = mpart.o;
   if (j == 0) {
     red_m[ph] = mpart.m;
@@ -229,7 +240,8 @@ __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ 
 }
 
 hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGeom &geo, const DecodeWs &ws,
-                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s) {
+                        float *out, float *lse, int32_t *idx, int64_t cap, int32_t *count, hipStream_t s,
+                        int64_t nlt, int span) {
   (void)n;
   (void)L;
   const int G = Hq / Hkv;
@@ -237,12 +249,13 @@ hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGe
   // 4.96 -> 3.9 us, one head per unit 13.9 -> 10.5 us) but not with eight
   // (5.3 -> 6.4 us)
   if (!idx && G <= 4) {
-    merge_q_kernel<<<dim3((unsigned)(4 * (int64_t)B * Hq)), 256, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, out, lse,
-                                                                         count);
+    merge_q_kernel<<<dim3((unsigned)(4 * (int64_t)B * Hq)), 256, 0, s>>>(
+        ws.part, Hq, Hkv, G, geo.nchunks, span > 1 ? nlt : 0, span > 1 ? span : 1, out, lse, count);
     return hipGetLastError();
   }
   merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
-                                                                 lse, count, idx, cap, ws.ent, ws.ent_cnt);
+                                                                 lse, count, idx, cap, ws.ent, ws.ent_cnt,
+                                                                 span > 1 ? nlt : 0, span > 1 ? span : 1);
   return hipGetLastError();
 }
 
