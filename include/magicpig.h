@@ -292,15 +292,19 @@ int mp_decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, 
  * merge of Section 4.4 "On-device cache") into out / lse / count / idx.
  * Both must see the same arguments and the same ws; want_idx must be
  * non-zero in mp_decode_sample when mp_decode_merge receives idx.
- * qcodes is required here ([B][Hq][L]).
+ * qcodes is required here ([B][Hq][L]).  mp_decode_merge takes the
+ * sampling stage's kv_dtype, T and n_buckets (0 when it had no buckets):
+ * with them it reads the partial records that stage filled, in the same
+ * order as mp_decode_attn, whose results it then reproduces bit for bit.
  */
 int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,
                      const uint32_t *planes, int64_t n_planes, const void *buckets, int64_t n_buckets,
                      const float *kmean, const uint16_t *qcodes, int B, int Hq, int Hkv, int64_t n, int64_t cap,
                      int d, int K, int L, int T, int64_t n_static_head, int64_t n_static_tail, int want_idx, void *ws,
                      size_t ws_bytes, void *stream);
-int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
-                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream);
+int mp_decode_merge(int kv_dtype, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, int T,
+                    int64_t n_buckets, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                    size_t ws_bytes, void *stream);
 
 /*
  * One decode step of one layer in three launches: append the new token's key

@@ -57,7 +57,8 @@ _SIGS = {
     "mp_decode_sample": ([_vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int, _c_int,
                           _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _vp, _c_sz, _vp],
                          _c_int),
-    "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp, _c_sz, _vp],
+    "mp_decode_merge": ([_c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_i64, _vp, _vp, _vp,
+                         _vp, _vp, _c_sz, _vp],
                         _c_int),
     "mp_decode_step": ([_vp, _vp, _vp, _vp, _vp, _c_int, _vp, _vp, _c_i64, _vp, _c_i64, _vp, _vp, _c_int, _c_int,
                         _c_int, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_int, _c_i64, _c_i64, _vp, _vp, _vp, _vp,
@@ -421,11 +422,14 @@ def mp_decode_sample(q, Kc, Vc, codes, kmean, qcodes, Hkv: int, n: int, K: int, 
 
 def mp_decode_merge(B: int, Hq: int, Hkv: int, n: int, cap: int, L: int, out: torch.Tensor, ws: torch.Tensor,
                     lse: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
-                    count: Optional[torch.Tensor] = None, d: int = D, stream=None) -> None:
-    """Log-sum-exp merge of the sampled partials (second stage of mp_decode_attn)."""
+                    count: Optional[torch.Tensor] = None, d: int = D, stream=None,
+                    kv_dtype: torch.dtype = torch.bfloat16, T: int = 2, n_buckets: int = 0) -> None:
+    """Log-sum-exp merge of the sampled partials (second stage of mp_decode_attn); ``kv_dtype``, ``T``
+    and ``n_buckets`` as the sampling stage had them (0 without buckets)."""
     _need(out, torch.float32, (B, Hq, d), "out")
-    st = lib().mp_decode_merge(B, Hq, Hkv, n, cap, d, L, _p(out), _p(lse), _p(idx), _p(count), _p(ws), ws.numel(),
-                               _stream(stream))
+    code = MP_BF16 if kv_dtype == torch.bfloat16 else MP_F32 if kv_dtype == torch.float32 else -1
+    st = lib().mp_decode_merge(code, B, Hq, Hkv, n, cap, d, L, T, n_buckets, _p(out), _p(lse), _p(idx), _p(count),
+                               _p(ws), ws.numel(), _stream(stream))
     _check("mp_decode_merge", st)
 
 

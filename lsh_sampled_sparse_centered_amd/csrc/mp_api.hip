@@ -297,18 +297,23 @@ int mp_decode_sample(const void *q, const void *Kc, const void *Vc, int kv_dtype
                     buckets, list_keys(buckets, n_buckets, T));
 }
 
-int mp_decode_merge(int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, float *out, float *lse,
-                    int32_t *idx, int32_t *count, void *ws, size_t ws_bytes, void *stream) {
+int mp_decode_merge(int kv_dtype, int B, int Hq, int Hkv, int64_t n, int64_t cap, int d, int L, int T,
+                    int64_t n_buckets, float *out, float *lse, int32_t *idx, int32_t *count, void *ws,
+                    size_t ws_bytes, void *stream) {
   int st = check_heads(B, Hq, Hkv);
   if (st) return st;
-  if (d != D || L < 2 || L > MAX_L) return MP_ERR_UNSUPPORTED;
+  if ((st = check_dtype(kv_dtype))) return st;
+  if (d != D || L < 2 || L > MAX_L || T < 1 || T > L) return MP_ERR_UNSUPPORTED;
   if (!out || cap < 1 || cap % 8) return MP_ERR_ARG;
   if (!all_a16(out, ws)) return MP_ERR_ARG;
   if (n < 0 || n > cap) return MP_ERR_CAPACITY;
+  if (n_buckets < 0 || n_buckets > n || n_buckets % SCAN_TILE) return MP_ERR_ARG;
   if (!ws || ws_bytes < mp_decode_ws_bytes(B, Hq, Hkv, cap, d, L)) return MP_ERR_WORKSPACE;
   const DecodeGeom geo = decode_geom(B, Hkv, Hq, n, cap);
   const DecodeWs w = decode_ws_layout(ws, B, Hq, Hkv, cap, L);
-  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, as_stream(stream)));
+  const int64_t nlt = (T == 2 ? n_buckets : 0) / SCAN_TILE;  // tiles the sampling stage took from bitmaps
+  return hip_status(launch_merge(B, Hq, Hkv, n, L, geo, w, out, lse, idx, cap, count, as_stream(stream), nlt,
+                                 sample_span(kv_dtype, Hq / Hkv, nlt, geo)));
 }
 
 static int decode_attn(const void *q, const void *Kc, const void *Vc, int kv_dtype, const uint16_t *codes,

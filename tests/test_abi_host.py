@@ -206,8 +206,14 @@ def test_decode_stages_reject_invalid_arguments():
                               75, 2, 0, 0, 0, FAKE, 1 << 30, None) == ARG  # planes past n
     assert L.mp_decode_sample(FAKE, FAKE, FAKE, 0, FAKE, None, 0, FAKE, 512, FAKE, FAKE, 1, 32, 8, 100, 128, 128, 8,
                               75, 2, 0, 0, 0, FAKE, 1 << 30, None) == ARG  # buckets past n
-    assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, None, None, None, None, FAKE, 1 << 30, None) == ARG
-    assert L.mp_decode_merge(1, 32, 8, 100, 128, 128, 75, FAKE, None, None, None, FAKE, 10, None) == WS
+    assert L.mp_decode_merge(0, 1, 32, 8, 100, 128, 128, 75, 2, 0, None, None, None, None, FAKE, 1 << 30, None) == ARG
+    assert L.mp_decode_merge(0, 1, 32, 8, 100, 128, 128, 75, 2, 0, FAKE, None, None, None, FAKE, 10, None) == WS
+    assert L.mp_decode_merge(0, 1, 32, 8, 100, 128, 128, 75, 2, 512, FAKE, None, None, None, FAKE, 1 << 30,
+                             None) == ARG  # buckets past n
+    assert L.mp_decode_merge(0, 1, 32, 8, 100, 128, 128, 75, 0, 0, FAKE, None, None, None, FAKE, 1 << 30,
+                             None) == UNSUP  # threshold 0
+    assert L.mp_decode_merge(7, 1, 32, 8, 100, 128, 128, 75, 2, 0, FAKE, None, None, None, FAKE, 1 << 30,
+                             None) != OK  # no such dtype
 
 
 def test_encode_queries_rejects_invalid_arguments():

@@ -257,7 +257,8 @@ def span_case(name):
 def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
     """Index lists and counts equal the code scan's (one tile per block) and
     the oracle's; outputs and lse within the oracle's bars and within
-    rounding of the scan's; the merge without index lists gives the same bits."""
+    rounding of the scan's; the merge without index lists, and the two stages
+    called apart, give the same bits."""
     w, lay, km, codes, qc = span_case(name)
     U = w.batch * w.hkv
     assert w.group <= 2 and U * ((lay["n"] + 511) // 512) >= 4 * 256 * 7
@@ -278,6 +279,16 @@ def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
                       qcodes_in=qcodes, out=out, lse=lse, count=cnt, buckets=buf, n_buckets=nb)
     torch.cuda.synchronize()
     for a, b in zip((out, lse, cnt), got[:2] + got[3:]):
+        assert np.array_equal(a.cpu().numpy().view(np.uint8), b.view(np.uint8))
+    # the two stages called apart, the merge told the sampling stage's bucket bound: the same bits
+    ws = mp.decode_workspace(w.batch, w.hq, w.hkv, lay["cap"], w.L, "cuda")
+    mp.mp_decode_sample(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, qcodes, w.hkv, lay["n"], w.K, ws,
+                        n_static_head=nsh, n_static_tail=nst, want_idx=True, buckets=buf, n_buckets=nb)
+    idx = torch.full((w.batch, w.hq, lay["cap"]), -7, dtype=torch.int32, device="cuda")
+    mp.mp_decode_merge(w.batch, w.hq, w.hkv, lay["n"], lay["cap"], w.L, out, ws, lse=lse, idx=idx, count=cnt,
+                       n_buckets=nb)
+    torch.cuda.synchronize()
+    for a, b in zip((out, lse, idx, cnt), got):
         assert np.array_equal(a.cpu().numpy().view(np.uint8), b.view(np.uint8))
     ref = oracle_decode(w, lay, km, codes, qc, nsh=nsh, nst=nst)
     _compare(w, ref, *got, "%s buckets<%d nsh=%d nst=%d (four tiles per block)" % (name, nb, nsh, nst))
