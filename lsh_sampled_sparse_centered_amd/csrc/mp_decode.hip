@@ -982,11 +982,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
       }
     };
-    // With four or more heads per block the next round's rows are requested
-    // as soon as this round's are consumed (end of (a)), so they arrive while
-    // (b) and (c) run (the barriers wait for LDS operations only); with
-    // fewer heads (short (b) and (c), many blocks) at the start of the round.
-    constexpr bool early = GM >= 4;
+    // With four or more heads per block, or several tiles (several rounds),
+    // the next round's rows are requested as soon as this round's are
+    // consumed (end of (a)), so they arrive while (b) and (c) run (the
+    // barriers wait for LDS operations only); with one tile of fewer heads
+    // (short (b) and (c), many blocks) at the start of the round.
+    constexpr bool early = GM >= 4 || SP > 1;
     if (nu > 0) load_round(0);
     for (int e0 = 0; e0 < nu; e0 += ATT_E) {
       const int ne = min(ATT_E, nu - e0);
