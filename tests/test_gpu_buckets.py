@@ -225,6 +225,8 @@ SPAN_CASES = {
     "mha_span": variant("codellama13b_b16", layers=1, batch=16, hq=14, hkv=14, n=16600, K=8, L=75),
     # two query heads per KV head: 224 units x 33 tiles
     "g2_span": variant("llama8b_layer", batch=28, hq=16, hkv=8, n=16600, K=8, L=75),
+    # whole tiles only: 224 units x 32 tiles, every tile from the buckets (no tile scans)
+    "mha_span_whole": variant("codellama13b_b16", layers=1, batch=16, hq=14, hkv=14, n=16384, K=8, L=75),
 }
 _span_cache = {}
 
@@ -249,12 +251,14 @@ def span_case(name):
     return _span_cache[name]
 
 
-@pytest.mark.parametrize("name,nb_tiles,nsh,nst", [
-    ("mha_span", 32, 0, 0),   # eight blocks of four bitmap tiles; the short last tile scanned
-    ("mha_span", 31, 4, 64),  # a last block of three bitmap tiles, two tiles scanned; forced ranges
-    ("g2_span", 30, 0, 0),
+@pytest.mark.parametrize("name,nb_tiles,nsh,nst,pl_tiles", [
+    ("mha_span", 32, 0, 0, 0),    # eight blocks of four bitmap tiles; the short last tile scanned
+    ("mha_span", 31, 4, 64, 0),   # a last block of three bitmap tiles, two tiles scanned; forced ranges
+    ("mha_span", 17, 0, 0, 32),   # bitmap tiles below 17 (a last block of one), planes to 32, codes above
+    ("g2_span", 30, 0, 0, 0),
+    ("mha_span_whole", 32, 0, 0, 0),  # every tile from the bitmaps
 ])
-def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
+def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst, pl_tiles):
     """Index lists and counts equal the code scan's (one tile per block) and
     the oracle's; outputs and lse within the oracle's bars and within
     rounding of the scan's; the merge without index lists, and the two stages
@@ -263,9 +267,10 @@ def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
     U = w.batch * w.hkv
     assert w.group <= 2 and U * ((lay["n"] + 511) // 512) >= 4 * 256 * 7
     kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
-    nb = nb_tiles * 512
+    nb, npl = nb_tiles * 512, pl_tiles * 512
     buf = mp.mp_build_buckets(gcodes, w.K, nb)
-    got = _decode(w, lay, kmean, gcodes, qcodes, buf, nb, nsh, nst)
+    planes = mp.mp_build_planes(gcodes, w.K, npl) if npl else None
+    got = _decode(w, lay, kmean, gcodes, qcodes, buf, nb, nsh, nst, planes=planes, n_planes=npl)
     base = _decode(w, lay, kmean, gcodes, qcodes, None, 0, nsh, nst)
     assert np.array_equal(got[2], base[2]) and np.array_equal(got[3], base[3])
     assert np.allclose(got[0], base[0], rtol=1e-5, atol=1e-6)
@@ -276,14 +281,16 @@ def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
     lse = torch.empty(w.batch, w.hq, dtype=torch.float32, device="cuda")
     cnt = torch.empty(w.batch, w.hq, dtype=torch.int32, device="cuda")
     mp.mp_decode_attn(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, None, w.hkv, lay["n"], w.K, nsh, nst,
-                      qcodes_in=qcodes, out=out, lse=lse, count=cnt, buckets=buf, n_buckets=nb)
+                      qcodes_in=qcodes, out=out, lse=lse, count=cnt, buckets=buf, n_buckets=nb, planes=planes,
+                      n_planes=npl)
     torch.cuda.synchronize()
     for a, b in zip((out, lse, cnt), got[:2] + got[3:]):
         assert np.array_equal(a.cpu().numpy().view(np.uint8), b.view(np.uint8))
     # the two stages called apart, the merge told the sampling stage's bucket bound: the same bits
     ws = mp.decode_workspace(w.batch, w.hq, w.hkv, lay["cap"], w.L, "cuda")
     mp.mp_decode_sample(lay["q"], lay["Kc"], lay["Vc"], gcodes, kmean, qcodes, w.hkv, lay["n"], w.K, ws,
-                        n_static_head=nsh, n_static_tail=nst, want_idx=True, buckets=buf, n_buckets=nb)
+                        n_static_head=nsh, n_static_tail=nst, want_idx=True, buckets=buf, n_buckets=nb,
+                        planes=planes, n_planes=npl)
     idx = torch.full((w.batch, w.hq, lay["cap"]), -7, dtype=torch.int32, device="cuda")
     mp.mp_decode_merge(w.batch, w.hq, w.hkv, lay["n"], lay["cap"], w.L, out, ws, lse=lse, idx=idx, count=cnt,
                        n_buckets=nb)
@@ -291,4 +298,4 @@ def test_bitmap_tiles_shared_by_sampling_blocks(name, nb_tiles, nsh, nst):
     for a, b in zip((out, lse, idx, cnt), got):
         assert np.array_equal(a.cpu().numpy().view(np.uint8), b.view(np.uint8))
     ref = oracle_decode(w, lay, km, codes, qc, nsh=nsh, nst=nst)
-    _compare(w, ref, *got, "%s buckets<%d nsh=%d nst=%d (four tiles per block)" % (name, nb, nsh, nst))
+    _compare(w, ref, *got, "%s buckets<%d planes<%d nsh=%d nst=%d (four tiles per block)" % (name, nb, npl, nsh, nst))
