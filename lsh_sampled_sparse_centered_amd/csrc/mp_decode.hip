@@ -971,11 +971,13 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     const __bf16 *Kb = (const __bf16 *)Kc + (u * cap + tbase) * D + 8 * qd;
     const __bf16 *Vb = (const __bf16 *)Vc + (u * cap + tbase) * D + 8 * qd;
     // this lane's key and value pieces of the round starting at entry r0
-    // (entries past the list read the tile's first key: a valid row, discarded)
+    // (r0 < nu).  Slots past the list read the list's last key again: a
+    // sampled key's rows, whose dot products are dropped and whose value rows
+    // meet weight 0 (finite, so the products are exact zeros)
     uint4 kr[2], vr[2];
     auto load_round = [&](int r0) {
       const int e = 16 * (wave & 1) + li, kh = wave >> 1;
-      const int64_t key = e < nu - r0 ? lkey[lslot(r0 + e)] : 0;
+      const int64_t key = lkey[lslot(r0 + min(e, nu - r0 - 1))];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
@@ -994,7 +996,6 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
       if (!early && e0 > 0) load_round(e0);
       {  // (a)
         const int e = 16 * (wave & 1) + li, kh = wave >> 1;
-        const bool ok = e < ne;
 
         f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f};
         float n2 = 0.0f;
@@ -1024,7 +1025,7 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         for (int st = 0; st < 2; ++st) {
           const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[st]);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) sm.m.vT[64 * kh + 32 * st + 8 * qd + j][e] = ok ? vb[j] : (__bf16)0.0f;
+          for (int j = 0; j < 8; ++j) sm.m.vT[64 * kh + 32 * st + 8 * qd + j][e] = vb[j];
         }
         if (early && e0 + ATT_E < nu) load_round(e0 + ATT_E);
       }
