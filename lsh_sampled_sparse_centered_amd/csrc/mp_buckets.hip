@@ -140,7 +140,8 @@ hipError_t launch_bucket_build(const uint16_t *codes, int64_t U, int64_t cap, in
 //     takes entries t, t + 256, ... of the window (all key loads in flight)
 //     and records each collision in the head's LDS bitmaps: "seen in one
 //     table" and, when already seen, "seen in two" (an atomic OR returns the
-//     old word).
+//     old word; a thread's ORs of a window are all issued before it reads
+//     any old word).
 //  3. The "seen in two tables" bitmap of the chunk is written to the head's
 //     bitmap in the workspace; the sampling kernel compacts it per tile.
 constexpr int BL_W = 2048;       // entries per window
@@ -228,14 +229,19 @@ __global__ __launch_bounds__(256) void bucket_lookup_kernel(const uint16_t *__re
       const int l = eseg[e - w0];
       key[k] = kbase[(int64_t)l * cap + segsrc[l] + (e - segbeg[l])];
     }
+    // every atomic OR of the window goes out before any old word is looked
+    // at (one LDS round trip instead of one per entry); slots past the
+    // window issue none (they would all hit the window's last key's word)
+    uint32_t bit[BL_EPT], old[BL_EPT];
 #pragma unroll
     for (int k = 0; k < BL_EPT; ++k) {
-      if (w0 + (uint32_t)tid + 256u * k < w1) {
-        const uint32_t bit = 1u << (key[k] & 31u);
-        const uint32_t old = atomicOr(&seen1[key[k] >> 5], bit);
-        if (old & bit) atomicOr(&seen2[key[k] >> 5], bit);
-      }
+      bit[k] = 1u << (key[k] & 31u);
+      old[k] = 0u;
+      if (w0 + (uint32_t)tid + 256u * k < w1) old[k] = atomicOr(&seen1[key[k] >> 5], bit[k]);
     }
+#pragma unroll
+    for (int k = 0; k < BL_EPT; ++k)
+      if (old[k] & bit[k]) atomicOr(&seen2[key[k] >> 5], bit[k]);
     __syncthreads();  // the window's slots are rewritten next
   }
   __syncthreads();
