@@ -392,7 +392,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
   };
   struct MfmaLds {  // matrix-core rounds (bf16 caches)
     alignas(16) __bf16 vT[D][VT_STRIDE];  // value rows transposed: [dim][entry]
-    alignas(16) float p[GM][ATT_E];       // exp(w - m) per head and entry
+    // exp(w - m) per head and entry as two bf16 parts (hi + lo: 16
+    // significant bits); row GM zero (the padding heads' row)
+    alignas(16) __bf16 ph[GM + 1][ATT_E];
+    alignas(16) __bf16 pl[GM + 1][ATT_E];
     float sdot[2][GM][ATT_E];             // q_h . k per head and entry: dims 0-63, 64-127
     float nrm[2][ATT_E];                  // |k - mu|^2 per entry: dims 0-63, 64-127
   };
@@ -960,12 +963,11 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     //  (b) one thread per (head, entry) forms the log-weight
     //      s = q.k / sqrt(d) - ln P (or -inf where the head did not sample the
     //      key), the head's new running maximum m (a 32-lane max), exp(s - m)
-    //      and the round's sum, and records m, the rescale factor and the
-    //      running normaliser;
+    //      -- stored as two bf16 parts (hi + lo, 16 significant bits) so the
+    //      weights keep fp32-like precision -- and the round's sum, and
+    //      records m, the rescale factor and the running normaliser;
     //  (c) wave w accumulates the output dims 32 w .. 32 w + 31 of every head
-    //      as O = O * alpha + P V, with P split into two bf16 parts
-    //      (hi + lo, 16 significant bits) so the weights keep fp32-like
-    //      precision.
+    //      as O = O * alpha + P V (P's two parts, two operations each).
     const int qd = lane >> 4, li = lane & 15;
     f32x4 oacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};  // heads 4 qd + j, dim 16 (2 wave + b) + li
     const __bf16 *Kb = (const __bf16 *)Kc + (u * cap + tbase) * D + 8 * qd;
@@ -990,6 +992,10 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     // barriers wait for LDS operations only); with one tile of fewer heads
     // (short (b) and (c), many blocks) at the start of the round.
     constexpr bool early = GM >= 4 || SP > 1;
+    if (tid < ATT_E) {  // the padding heads' weights (no phase writes this row)
+      sm.m.ph[GM][tid] = (__bf16)0.0f;
+      sm.m.pl[GM][tid] = (__bf16)0.0f;
+    }
     if (nu > 0) load_round(0);
     for (int e0 = 0; e0 < nu; e0 += ATT_E) {
       const int ne = min(ATT_E, nu - e0);
@@ -1052,7 +1058,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
         const float mn = fmaxf(mo, mr);
         const float pe = mn > -INFINITY ? hw_exp(w - mn) : 0.0f;  // 0 for -inf
         const float ps = xor32_sum(pe);
-        sm.m.p[h][e] = pe;
+        const __bf16 phi = (__bf16)pe;  // 0 for the heads past G
+        sm.m.ph[h][e] = phi;
+        sm.m.pl[h][e] = (__bf16)(pe - (float)phi);
         if (e == 0) {
           const float alpha = mn > -INFINITY ? hw_exp(mo - mn) : 1.0f;  // 0 while mo = -inf
           alpha_sh[h] = alpha;
@@ -1069,16 +1077,9 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
           oacc[0][j] *= a;
           oacc[1][j] *= a;
         }
-        float pv[8];
-        ld8<float>(&sm.m.p[li < GM ? li : 0][8 * qd], pv);
-        bf16x8 ph, pl;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = li < GM ? pv[j] : 0.0f;
-          const __bf16 hi = (__bf16)x;
-          ph[j] = hi;
-          pl[j] = (__bf16)(x - (float)hi);
-        }
+        const int hr = li < GM ? li : GM;
+        const bf16x8 ph = *(const bf16x8 *)&sm.m.ph[hr][8 * qd];
+        const bf16x8 pl = *(const bf16x8 *)&sm.m.pl[hr][8 * qd];
 #pragma unroll
         for (int b2 = 0; b2 < 2; ++b2) {
           const bf16x8 vb = *(const bf16x8 *)&sm.m.vT[16 * (2 * wave + b2) + li][8 * qd];
