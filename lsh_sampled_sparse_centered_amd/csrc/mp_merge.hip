@@ -20,42 +20,66 @@ namespace mp {
 // the chunks' union entries.
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
 constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
+// A head with at most MERGE_PH_FEW * MERGE_CPT records is merged in
+// MERGE_PH_FEW phases (one pass of loads each): fewer waves per block, so a
+// grid of many small heads is resident at once.  Both merges pick the phase
+// count the same way, so they fold the records in the same order.
+constexpr int MERGE_PH_FEW = 8;
+__host__ __device__ constexpr int merge_phases(int64_t nrec) {
+  return nrec <= (int64_t)MERGE_PH_FEW * MERGE_CPT ? MERGE_PH_FEW : MERGE_PH;
+}
 
-// One thread's share of a head's merge: records ph, ph + MERGE_PH, ... of
+// One thread's share of a head's merge: records ph, ph + PH, ... of
 // nrec at p0 (record stride cs), dims d0 .. d0 + 3.  Record r is chunk r's,
 // or, when the sampling blocks took the bitmap chunks `span` at a time,
 // chunk r * span for r < nsp and chunk nlt + r - nsp after.  A pass loads
 // MERGE_CPT records at once (independent loads; records past the last
-// re-read the last one and are dropped), then folds them in with a running
-// maximum (rescaled sums).  The records' counts are summed when `counts` is
-// set.
+// re-read the last one and are dropped, or with few phases are not read),
+// then folds them in with a running maximum (rescaled sums).  The records'
+// counts are summed when `counts` is set.
 struct MergePart {
   float m, l;
   f32x4 o;
   int cnt;
 };
+template <int PH>
 __device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs, int64_t nrec, int ph, int d0,
                                        bool counts, int64_t nsp = 0, int span = 1, int64_t nlt = 0) {
   MergePart r{-INFINITY, 0.0f, {0.0f, 0.0f, 0.0f, 0.0f}, 0};
-  for (int64_t c0 = ph; c0 < nrec; c0 += (int64_t)MERGE_PH * MERGE_CPT) {
+  for (int64_t c0 = ph; c0 < nrec; c0 += (int64_t)PH * MERGE_CPT) {
     f32x2 ml[MERGE_CPT];
     int cn[MERGE_CPT];
     f32x4 oc[MERGE_CPT];
-#pragma unroll
-    for (int k = 0; k < MERGE_CPT; ++k) {
-      const int64_t ri = min(c0 + (int64_t)k * MERGE_PH, nrec - 1);
+    auto load = [&](int k) {
+      const int64_t ri = min(c0 + (int64_t)k * PH, nrec - 1);
       const int64_t ci = ri < nsp ? ri * span : nlt + ri - nsp;
       const float *rec = p0 + ci * cs;
       ml[k] = *(const f32x2 *)rec;  // m, l
       cn[k] = counts ? __builtin_bit_cast(int, rec[2]) : 0;
       oc[k] = *(const f32x4 *)(rec + 4 + d0);
+    };
+    // with few phases (one pass), the loads the wave's first phase (lane 0's,
+    // the lowest) has no record for are skipped wave-wide; with many, every
+    // load is issued (measured: the skips' branches cost more there)
+    if constexpr (PH == MERGE_PH) {
+#pragma unroll
+      for (int k = 0; k < MERGE_CPT; ++k) load(k);
+    } else {
+      const int64_t cw = (int64_t)__builtin_amdgcn_readfirstlane((int)c0);
+#pragma unroll
+      for (int k = 0; k < MERGE_CPT; ++k) {
+        ml[k] = f32x2{-INFINITY, 0.0f};
+        cn[k] = 0;
+        oc[k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (cw + (int64_t)k * PH < nrec) load(k);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);  // every load of the pass is issued before any result is used
     // branch-free fold (a branch would let the compiler sink the loads into
     // it, one round trip each); an empty side gets weight 0
 #pragma unroll
     for (int k = 0; k < MERGE_CPT; ++k) {
-      const bool live = c0 + (int64_t)k * MERGE_PH < nrec;
+      const bool live = c0 + (int64_t)k * PH < nrec;
       const float mc = live ? ml[k][0] : -INFINITY;
       const float mn = fmaxf(r.m, mc);
       const float a = r.m > -INFINITY ? __expf(r.m - mn) : 0.0f;
@@ -70,20 +94,20 @@ __device__ inline MergePart merge_fold(const float *__restrict__ p0, int64_t cs,
   return r;
 }
 
-// The MERGE_PH phases' states (in LDS) folded in phase order for the 4 dims
+// The PH phases' states (in LDS) folded in phase order for the 4 dims
 // of slot s: writes out[0..3], and the log-sum-exp and count when asked.
-template <int NS>
-__device__ inline void merge_finish(const f32x4 (&red_o)[MERGE_PH][NS], const float (&red_m)[MERGE_PH],
-                                    const float (&red_l)[MERGE_PH], const int (&red_c)[MERGE_PH], int s,
+template <int NS, int PH>
+__device__ inline void merge_finish(const f32x4 (&red_o)[PH][NS], const float (&red_m)[PH],
+                                    const float (&red_l)[PH], const int (&red_c)[PH], int s,
                                     float *__restrict__ out, float *lse, int32_t *count) {
   float M = -INFINITY;
 #pragma unroll
-  for (int p = 0; p < MERGE_PH; ++p) M = fmaxf(M, red_m[p]);
+  for (int p = 0; p < PH; ++p) M = fmaxf(M, red_m[p]);
   f32x4 o = {0.0f, 0.0f, 0.0f, 0.0f};
   float ls = 0.0f;
   int cs_ = 0;
 #pragma unroll
-  for (int p = 0; p < MERGE_PH; ++p) {
+  for (int p = 0; p < PH; ++p) {
     const float sc = red_m[p] > -INFINITY ? __expf(red_m[p] - M) : 0.0f;
     o += red_o[p][s] * sc;
     ls += red_l[p] * sc;
@@ -95,15 +119,16 @@ __device__ inline void merge_finish(const f32x4 (&red_o)[MERGE_PH][NS], const fl
   if (count) *count = cs_;
 }
 
+template <int PH>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void merge_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                      int64_t nchunks, int64_t chunk, float *__restrict__ out,
                                                      float *__restrict__ lse, int32_t *__restrict__ count,
                                                      int32_t *__restrict__ idx, int64_t cap,
                                                      const uint32_t *__restrict__ ent,
                                                      const int32_t *__restrict__ ent_cnt, int64_t nlt, int span) {
-  __shared__ f32x4 red_o[MERGE_PH][32];
-  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
-  __shared__ int red_c[MERGE_PH];
+  __shared__ f32x4 red_o[PH][32];
+  __shared__ float red_m[PH], red_l[PH];
+  __shared__ int red_c[PH];
   __shared__ int wsum[16];
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the same XCD as the blocks that wrote its partials
@@ -119,21 +144,24 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const float *p0 = part + (u * nchunks * G + hg) * PSTRIDE;
   const int64_t cs = (int64_t)G * PSTRIDE;
 
-  // thread (phase, j): dims 4j..4j+3 of records phase, phase + MERGE_PH, ...
-  // (the records the sampling blocks filled, in the same order as the merge
-  // without index lists, so that both give the same bits)
+  // thread (phase, j) of the first PH phases: dims 4j..4j+3 of records
+  // phase, phase + PH, ... (the records the sampling blocks filled, in the
+  // same order as the merge without index lists, so that both give the same
+  // bits)
   const int ph = t >> 5, j = t & 31;
   const int64_t nsp = (nlt + span - 1) / span;  // records of the bitmap chunks
-  const MergePart mpart = merge_fold(p0, cs, nsp + nchunks - nlt, ph, 4 * j, true, nsp, span, nlt);
-  red_o[ph][j] = mpart.o;
-  if (j == 0) {
-    red_m[ph] = mpart.m;
-    red_l[ph] = mpart.l;
-    red_c[ph] = mpart.cnt;
+  if (ph < PH) {
+    const MergePart mpart = merge_fold<PH>(p0, cs, nsp + nchunks - nlt, ph, 4 * j, true, nsp, span, nlt);
+    red_o[ph][j] = mpart.o;
+    if (j == 0) {
+      red_m[ph] = mpart.m;
+      red_l[ph] = mpart.l;
+      red_c[ph] = mpart.cnt;
+    }
   }
   __syncthreads();
   if (t < 32)
-    merge_finish<32>(red_o, red_m, red_l, red_c, t, out + bh * D + 4 * t, t == 0 && lse ? lse + bh : nullptr,
+    merge_finish<32, PH>(red_o, red_m, red_l, red_c, t, out + bh * D + 4 * t, t == 0 && lse ? lse + bh : nullptr,
                      t == 0 && count ? count + bh : nullptr);
   if (!idx) return;
   // Index list: chunk c's keys of this head start at the sum of the earlier
@@ -197,18 +225,19 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 // spread four times wider: one block
 // of 256 threads per (query head, quarter of the output dims), so that a
 // head's partial records are read by four compute units.  Thread (phase,
-// j) owns dims 32 q + 4 j .. + 3 of records phase, phase + 32, ...; each
+// j) owns dims 32 q + 4 j .. + 3 of records phase, phase + PH, ...; each
 // block reads every record's m and l, the first quarter also its count.
 // With span > 1 only the records the sampling blocks filled are read (one per
 // block: chunks 0, span, 2 span, ... below nlt, every chunk from nlt on).
 
+template <int PH>
 __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ part, int Hq, int Hkv, int G,
                                                       int64_t nchunks, int64_t nlt, int span,
                                                       float *__restrict__ out, float *__restrict__ lse,
                                                       int32_t *__restrict__ count) {
-  __shared__ f32x4 red_o[MERGE_PH][8];
-  __shared__ float red_m[MERGE_PH], red_l[MERGE_PH];
-  __shared__ int red_c[MERGE_PH];
+  __shared__ f32x4 red_o[PH][8];
+  __shared__ float red_m[PH], red_l[PH];
+  __shared__ int red_c[PH];
   touch_kernargs<1>();  // 64 bytes of arguments
   // unit-minor order, as the sampling kernel's grid: block i serves unit
   // i % U, so it runs on the XCD of the blocks that wrote its partials
@@ -226,7 +255,7 @@ __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ 
   const int ph = t >> 3, j = t & 7;
   const bool counts = qq == 0;  // the first quarter also writes the log-sum-exp and the count
   const int64_t nsp = (nlt + span - 1) / span;  // records of the bitmap chunks
-  const MergePart mpart = merge_fold(p0, cs, nsp + nchunks - nlt, ph, 32 * qq + 4 * j, counts, nsp, span, nlt);
+  const MergePart mpart = merge_fold<PH>(p0, cs, nsp + nchunks - nlt, ph, 32 * qq + 4 * j, counts, nsp, span, nlt);
   red_o[ph][j] = mpart.o;
   if (j == 0) {
     red_m[ph] = mpart.m;
@@ -235,7 +264,7 @@ __global__ __launch_bounds__(256) void merge_q_kernel(const float *__restrict__ 
   }
   __syncthreads();
   if (t < 8)
-    merge_finish<8>(red_o, red_m, red_l, red_c, t, out + bh * D + 32 * qq + 4 * t,
+    merge_finish<8, PH>(red_o, red_m, red_l, red_c, t, out + bh * D + 32 * qq + 4 * t,
                     t == 0 && counts && lse ? lse + bh : nullptr, t == 0 && counts && count ? count + bh : nullptr);
 }
 
@@ -248,14 +277,28 @@ hipError_t launch_merge(int B, int Hq, int Hkv, int64_t n, int L, const DecodeGe
   // the wider merge pays with up to four heads per unit (measured: 96K
   // 4.96 -> 3.9 us, one head per unit 13.9 -> 10.5 us) but not with eight
   // (5.3 -> 6.4 us)
+  const int64_t nl = span > 1 ? nlt : 0;
+  const int sp = span > 1 ? span : 1;
+  const int64_t nrec = (nl + sp - 1) / sp + geo.nchunks - nl;  // records per head
+  const bool few = merge_phases(nrec) == MERGE_PH_FEW;
   if (!idx && G <= 4) {
-    merge_q_kernel<<<dim3((unsigned)(4 * (int64_t)B * Hq)), 256, 0, s>>>(
-        ws.part, Hq, Hkv, G, geo.nchunks, span > 1 ? nlt : 0, span > 1 ? span : 1, out, lse, count);
+    // a block of PH * 8 threads per (head, quarter of the dims)
+    const dim3 grid((unsigned)(4 * (int64_t)B * Hq));
+    if (few)
+      merge_q_kernel<MERGE_PH_FEW><<<grid, MERGE_PH_FEW * 8, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, nl, sp, out,
+                                                                      lse, count);
+    else
+      merge_q_kernel<MERGE_PH><<<grid, MERGE_PH * 8, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, nl, sp, out, lse,
+                                                              count);
     return hipGetLastError();
   }
-  merge_kernel<<<dim3((unsigned)((int64_t)B * Hq)), 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out,
-                                                                 lse, count, idx, cap, ws.ent, ws.ent_cnt,
-                                                                 span > 1 ? nlt : 0, span > 1 ? span : 1);
+  const dim3 grid((unsigned)((int64_t)B * Hq));
+  if (few)
+    merge_kernel<MERGE_PH_FEW><<<grid, 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out, lse, count,
+                                                     idx, cap, ws.ent, ws.ent_cnt, nl, sp);
+  else
+    merge_kernel<MERGE_PH><<<grid, 1024, 0, s>>>(ws.part, Hq, Hkv, G, geo.nchunks, geo.chunk, out, lse, count, idx,
+                                                 cap, ws.ent, ws.ent_cnt, nl, sp);
   return hipGetLastError();
 }
 
