@@ -45,6 +45,10 @@ CASES = {
     "g5_f32": variant("llama8b_layer", hq=10, hkv=2, n=1800, dtype="f32"),
     "g6_bf16": variant("codellama34b_b4", layers=1, batch=2, hq=12, hkv=2, n=3000, steps=0),
     "g7_bf16": variant("codellama13b_b16", layers=1, batch=1, hq=7, hkv=1, n=2100),
+    # the merges' two phase counts: 64 partial records per head (the most merged in 8 phases) and 65
+    # (the fewest merged in 32)
+    "mha_64rec": variant("codellama13b_b16", layers=1, batch=1, hq=2, hkv=2, n=64 * 512),
+    "g4_65rec": variant("llama8b_layer", hq=4, hkv=1, n=64 * 512 + 232),
 }
 
 _cache = {}
@@ -415,7 +419,7 @@ def test_decode_stages_equal_composite_and_are_deterministic():
 
 
 @pytest.mark.parametrize("name", ["g8_ragged", "llama8b_layer", "tiny", "g6_bf16", "g4_f32", "mha_b3", "g2_small",
-                                  "g3_k16"])
+                                  "g3_k16", "mha_64rec", "g4_65rec"])
 def test_merge_without_index_lists_equals_merge_with_them(name):
     """The merge runs as a wider kernel when no index lists are asked for
     (up to four heads per KV head); both fold the per-tile partial records in
