@@ -62,7 +62,7 @@ def check_buckets_hold_their_codes(buf, codes, K, n1, n0=0):
                 assert np.array_equal(np.sort(k[u, l]), np.arange(r1 - r0)), (u, l, ci)  # each key once
 
 
-@pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged", "mha_b3", "g2_small", "g4_f32", "tiny"])
+@pytest.mark.parametrize("name", ["llama8b_layer", "g8_ragged", "mha_b3", "g2_small", "g4_f32", "tiny", "l512_g2"])
 def test_buckets_hold_their_codes(name):
     w, lay, km, codes, margin, qc = case(name)
     kmean, gcodes, qcodes = _inject(w, lay, km, codes, qc)
@@ -98,6 +98,8 @@ def _decode(w, lay, kmean, gcodes, qcodes, buckets=None, n_buckets=0, nsh=0, nst
     ("g6_bf16", 0, 0, 1.0),
     ("g7_bf16", 0, 0, 1.0),
     ("tiny", 0, 0, 1.0),
+    ("l512_g2", 0, 0, 1.0),
+    ("l512_g8", 4, 64, 1.0),
 ])
 def test_decode_with_buckets(name, nsh, nst, part):
     """Sets, counts, outputs and lse bit-identical to the code scan, and within the oracle's bars."""

@@ -49,6 +49,9 @@ CASES = {
     # (the fewest merged in 32)
     "mha_64rec": variant("codellama13b_b16", layers=1, batch=1, hq=2, hkv=2, n=64 * 512),
     "g4_65rec": variant("llama8b_layer", hq=4, hkv=1, n=64 * 512 + 232),
+    # the most tables (L = 512, K * L = 4096): two tables per lookup thread, the largest query-code tables
+    "l512_g2": variant("llama8b_layer", hq=4, hkv=2, n=3000, K=8, L=512),
+    "l512_g8": variant("codellama34b_b4", layers=1, batch=1, n=1100, K=8, L=512, steps=0),
 }
 
 _cache = {}

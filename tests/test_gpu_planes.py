@@ -84,6 +84,8 @@ def _decode(w, lay, kmean, gcodes, qcodes, planes=None, n_planes=0, nsh=0, nst=0
     ("g2_small", 0, 0, 2, 1.0),
     ("g3_k16", 0, 0, 2, 1.0),
     ("tiny", 0, 0, 2, 1.0),
+    ("l512_g2", 0, 0, 2, 1.0),
+    ("l512_g8", 0, 0, 2, 1.0),
 ])
 def test_decode_scans_planes(name, nsh, nst, T, part):
     w, lay, km, codes, margin, qc = case(name)
