@@ -12,12 +12,13 @@ namespace mp {
 // recursive-attention merge of Section 4.4): with M = max_c m_c,
 //   l = sum_c l_c e^{m_c - M},  out = sum_c o_c e^{m_c - M} / l,
 //   lse = M + ln l.
-// One block of 1024 threads per head: thread (phase, j) owns dims 4j..4j+3 of
-// chunks phase, phase + 32, ...; it loads 8 of its chunk records at once (so
-// every load of a pass is in flight together), then folds them in with a
-// running maximum.  The 32 phases are combined through LDS.  When idx is
-// requested the block then assembles the ascending sampled-index list from
-// the chunks' union entries.
+// One block of 1024 threads per head: thread (phase, j) of the first PH
+// phases (32, or 8 for a head with few records) owns dims 4j..4j+3 of chunks
+// phase, phase + PH, ...; it loads 8 of its chunk records at once (so every
+// load of a pass is in flight together), then folds them in with a running
+// maximum.  The PH phases are combined through LDS.  When idx is requested
+// the block then assembles the ascending sampled-index list from the chunks'
+// union entries.
 constexpr int MERGE_PH = 32;  // chunk phases per head (x 32 threads of 4 dims = 1024 threads)
 constexpr int MERGE_CPT = 8;  // chunks a thread loads before combining them
 // A head with at most MERGE_PH_FEW * MERGE_CPT records is merged in
