@@ -970,8 +970,11 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     //      as O = O * alpha + P V (P's two parts, two operations each).
     const int qd = lane >> 4, li = lane & 15;
     f32x4 oacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};  // heads 4 qd + j, dim 16 (2 wave + b) + li
-    const __bf16 *Kb = (const __bf16 *)Kc + (u * cap + tbase) * D + 8 * qd;
-    const __bf16 *Vb = (const __bf16 *)Vc + (u * cap + tbase) * D + 8 * qd;
+    // the block's rows (scalar bases) and a lane's 32-bit byte offsets from
+    // them (the rows of up to SP tiles: below 2^20 bytes), so no lane holds a
+    // 64-bit pointer
+    const char *Kb = (const char *)((const __bf16 *)Kc + (u * cap + tbase) * D);
+    const char *Vb = (const char *)((const __bf16 *)Vc + (u * cap + tbase) * D);
     // this lane's key and value pieces of the round starting at entry r0
     // (r0 < nu).  Slots past the list read the list's last key again: a
     // sampled key's rows, whose dot products are dropped and whose value rows
@@ -979,11 +982,12 @@ __global__ __launch_bounds__(256, (GM <= 4 ? (sizeof(T) == 2 ? MP_OCC : MP_OCC_F
     uint4 kr[2], vr[2];
     auto load_round = [&](int r0) {
       const int e = 16 * (wave & 1) + li, kh = wave >> 1;
-      const int64_t key = lkey[lslot(r0 + min(e, nu - r0 - 1))];
+      const uint32_t key = lkey[lslot(r0 + min(e, nu - r0 - 1))];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        kr[st] = *(const uint4 *)(Kb + key * D + 64 * kh + 32 * st);
-        vr[st] = *(const uint4 *)(Vb + key * D + 64 * kh + 32 * st);
+        const uint32_t bo = 2u * (key * D + 8u * qd + 64u * kh + 32u * st);
+        kr[st] = *(const uint4 *)(Kb + bo);
+        vr[st] = *(const uint4 *)(Vb + bo);
       }
     };
     // With four or more heads per block, or several tiles (several rounds),
